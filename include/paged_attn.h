@@ -1,0 +1,124 @@
+/*
+ * paged_attn.h -- C-ABI of the MI355X (gfx950) PagedAttention decode library.
+ *
+ * The operation (all entry points below compute it):
+ *   For every sequence s and query head h, with G = num_q_heads / num_kv_heads
+ *   and g = h / G, the single decode query q[s,h,:] attends over the
+ *   context_lens[s] tokens of its sequence.  Token t lives in physical block
+ *   block_tables[s][t / block_size], slot t % block_size.  Scores are
+ *   scale * q . k_t; ONE softmax runs over all tokens of the sequence (not per
+ *   block); out[s,h,:] = sum_t softmax_t * v_t.
+ *   Passages: ybb.press page "LLM 推理 KV Cache 内存管理深度工程实践：从
+ *   PageAttention 到推测解码", section 2.2 (block-table addressing, valid
+ *   slots min(block_size, n - j*block_size), zero output for an empty context,
+ *   q.K^T * scale) and section 6.2 (G consecutive query heads share one KV
+ *   head); t6page "KV cache" page, section "PagedAttention 的算子" (contiguous
+ *   K/V inside a block, softmax after merging all blocks).
+ *
+ * Layouts (all row-major, all pointers are DEVICE memory owned by the caller):
+ *   q             bf16  [num_seqs, num_q_heads, head_dim]
+ *   k_cache       bf16  [num_blocks, block_size, num_kv_heads, head_dim]
+ *   v_cache       bf16  same layout as k_cache
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens  int32 [num_seqs]
+ *   out           fp32  [num_seqs, num_q_heads, head_dim]
+ *   The per-layer slices of a layered cache [2, L, num_blocks, block_size,
+ *   num_kv_heads, head_dim] (nano-vLLM page, physical memory layout section)
+ *   are passed as k_cache = base + (0*L + l)*slice, v_cache = base + (1*L + l)
+ *   * slice; the library needs nothing else for that layout.
+ *
+ * Ownership and state: the library allocates nothing and keeps no per-call
+ * state.  Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ * null stream) and stream-ordered with the caller's other work.
+ *
+ * Errors: every entry point returns PA_OK (0) or a negative PA_ERR_* code.
+ * Argument errors are detected on the host before anything is launched, and
+ * `out` is then left untouched.  Not checked (it would need a device read):
+ * context_lens[s] <= max_blocks_per_seq * block_size and every table entry
+ * j < ceil(context_lens[s] / block_size) in [0, num_blocks).  Entries at or
+ * beyond that count, token slots at or beyond the context length and blocks
+ * no table references are never read.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_OK 0
+#define PA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define PA_ERR_SHAPE (-2)       /* non-positive size, q heads not a multiple of kv heads, ... */
+#define PA_ERR_UNSUPPORTED (-3) /* head_dim or block_size with no compiled kernel */
+#define PA_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than paged_attn_workspace_bytes */
+#define PA_ERR_LAUNCH (-5)      /* the HIP runtime reported a launch error */
+
+typedef struct pa_shape {
+    int32_t num_seqs;           /* S  >= 0 (0 is a no-op) */
+    int32_t num_q_heads;        /* Hq >= 1 */
+    int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0 */
+    int32_t head_dim;           /* 64 or 128 */
+    int32_t block_size;         /* tokens per block: a positive multiple of 16 */
+    int32_t max_blocks_per_seq; /* row length of block_tables, >= 1 */
+    int32_t num_blocks;         /* blocks in the pool, >= 1 */
+    int32_t split_tokens;       /* context partition size in tokens (multiple of 16), 0 = auto */
+} pa_shape;
+
+/*
+ * Split plan the decode entry points will use for `shape`: the context of a
+ * sequence is cut into ceil(context_len / split_tokens) partitions of
+ * split_tokens tokens, at most *max_splits of them.  With *max_splits == 1 no
+ * workspace is used and no reduction kernel runs.  Returns PA_OK or an error.
+ */
+int paged_attn_plan(const pa_shape *shape, int32_t *split_tokens, int32_t *max_splits);
+
+/*
+ * Device workspace (bytes) a decode call with `shape` needs: partial results
+ * of every partition, fp32 [S, Hq, max_splits, head_dim] plus fp32
+ * [S, Hq, max_splits, 2].  0 when there is a single partition.  Returns 0 on
+ * an invalid shape as well; the decode call then reports the shape error.
+ */
+size_t paged_attn_workspace_bytes(const pa_shape *shape);
+
+/*
+ * bf16 KV cache decode.  `scale` is the softmax scale (1/sqrt(head_dim) for
+ * standard attention).  `workspace` must hold paged_attn_workspace_bytes
+ * bytes (it may be NULL when that is 0); it is scratch, overwritten by the
+ * call, and must not be shared by calls that may run concurrently.
+ */
+int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens, float scale,
+                      float *out, const pa_shape *shape, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/*
+ * int8 KV cache decode: symmetric codes with one fp32 scale per (block,
+ * slot, kv head) for K and for V separately, the dequantized value being
+ * code * scale (ybb.press page, section 6.1, per-row amax/127 quantization).
+ *   k_cache, v_cache    int8 [num_blocks, block_size, num_kv_heads, head_dim]
+ *   k_scales, v_scales  fp32 [num_blocks, block_size, num_kv_heads]
+ * Dequantization is fused into the kernel; everything else as
+ * paged_attn_decode.
+ */
+int paged_attn_decode_int8(const void *q, const int8_t *k_cache, const int8_t *v_cache,
+                           const float *k_scales, const float *v_scales,
+                           const int32_t *block_tables, const int32_t *context_lens, float scale,
+                           float *out, const pa_shape *shape, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Static description of an error code; never NULL. */
+const char *paged_attn_strerror(int code);
+
+/* ABI version of this header (incremented on incompatible changes). */
+int paged_attn_abi_version(void);
+
+#define PA_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,182 @@
+"""fp64 CPU oracle for PagedAttention decode -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the bench's ``cpu_baseline`` leg may
+import this package.  It shares no code with the HIP library or with the
+product package: the arithmetic lives in ``oracle.c`` (plain C, fp64,
+OpenMP over (sequence, query head) rows) and this module only marshals numpy
+arrays through ctypes.
+
+Every function here cites the passage it follows in ``oracle.c``'s header:
+the ybb.press page "LLM 推理 KV Cache 内存管理深度工程实践" sections 2.2
+(paged attention forward), 6.1 (INT8 KV quantization) and 6.2 (GQA sharing),
+and the t6page "KV cache" page, section "PagedAttention 的算子" (softmax after
+merging all blocks).
+
+Pins: every function is pinned by the CPU tests (``tests/test_oracle_pins.py``)
+against closed forms, invariants and a library routine (torch SDPA in fp64);
+none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SOURCE = os.path.join(_HERE, "oracle.c")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile oracle.c with gcc into liboracle.so (strict IEEE, no contraction)."""
+    import subprocess
+
+    cmd = [
+        "gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+        "-fPIC", "-shared", SOURCE, "-o", LIB_PATH + ".tmp", "-lm",
+    ]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+class OracleLib:
+    """ctypes handle on one build of oracle.c (the default build, or a test's own)."""
+
+    def __init__(self, path: str = LIB_PATH):
+        if not os.path.exists(path):
+            raise RuntimeError(f"oracle library missing: {path} (run __graft_entry__.build())")
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int
+        i64 = ctypes.c_int64
+        lib.oracle_paged_decode_bf16.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                                 i64, ctypes.c_float, P]
+        lib.oracle_paged_decode_bf16.restype = i32
+        lib.oracle_paged_decode_int8.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                                 i32, i64, ctypes.c_float, P]
+        lib.oracle_paged_decode_int8.restype = i32
+        lib.oracle_quantize_int8_rows.argtypes = [P, i64, i32, P, P]
+        lib.oracle_quantize_int8_rows.restype = None
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = i32
+        lib.oracle_set_num_threads.argtypes = [i32]
+        lib.oracle_set_num_threads.restype = None
+        self.lib = lib
+        self.path = path
+
+
+_default = None
+
+
+def _load() -> "ctypes.CDLL":
+    global _default
+    if _default is None:
+        _default = OracleLib(LIB_PATH)
+    return _default.lib
+
+
+def build_to(path: str, source_text: str) -> str:
+    """Compile a given oracle source text into `path` (used by mutation tests)."""
+    import subprocess
+    import tempfile
+
+    with tempfile.NamedTemporaryFile("w", suffix=".c", delete=False) as f:
+        f.write(source_text)
+        src = f.name
+    try:
+        subprocess.check_call(["gcc", "-O1", "-std=c11", "-fopenmp", "-ffp-contract=off",
+                               "-fPIC", "-shared", src, "-o", path, "-lm"])
+    finally:
+        os.unlink(src)
+    return path
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    _load().oracle_set_num_threads(int(n))
+
+
+def _check_shapes(q, k, block_tables, context_lens):
+    S, Hq, D = q.shape
+    NB, BS, Hkv, D2 = k.shape
+    if D2 != D:
+        raise ValueError("head_dim mismatch between q and the cache")
+    if block_tables.ndim != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, MB] and context_lens [S]")
+    return S, Hq, Hkv, D, BS, block_tables.shape[1], NB
+
+
+def paged_decode_bf16(q_bits, k_bits, v_bits, block_tables, context_lens, scale,
+                      lib: "OracleLib | None" = None) -> np.ndarray:
+    """out[s,h,:] (float64) for a bf16 cache given as raw uint16 bit patterns."""
+    q_bits = _c(q_bits, np.uint16)
+    k_bits = _c(k_bits, np.uint16)
+    v_bits = _c(v_bits, np.uint16)
+    bt = _c(block_tables, np.int32)
+    cl = _c(context_lens, np.int32)
+    if v_bits.shape != k_bits.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    S, Hq, Hkv, D, BS, MB, NB = _check_shapes(q_bits, k_bits, bt, cl)
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    L = lib.lib if lib is not None else _load()
+    rc = L.oracle_paged_decode_bf16(_ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(bt),
+                                    _ptr(cl), S, Hq, Hkv, D, BS, MB, NB,
+                                    ctypes.c_float(scale), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return out
+
+
+def paged_decode_int8(q_bits, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens,
+                      scale, lib: "OracleLib | None" = None) -> np.ndarray:
+    """out[s,h,:] (float64) for an int8 cache with fp32 per-(slot, kv head) scales."""
+    q_bits = _c(q_bits, np.uint16)
+    k_codes = _c(k_codes, np.int8)
+    v_codes = _c(v_codes, np.int8)
+    k_scales = _c(k_scales, np.float32)
+    v_scales = _c(v_scales, np.float32)
+    bt = _c(block_tables, np.int32)
+    cl = _c(context_lens, np.int32)
+    S, Hq, Hkv, D, BS, MB, NB = _check_shapes(q_bits, k_codes, bt, cl)
+    if v_codes.shape != k_codes.shape or k_scales.shape != (NB, BS, Hkv) or \
+            v_scales.shape != (NB, BS, Hkv):
+        raise ValueError("int8 cache / scale shapes disagree")
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    L = lib.lib if lib is not None else _load()
+    rc = L.oracle_paged_decode_int8(_ptr(q_bits), _ptr(k_codes), _ptr(v_codes),
+                                    _ptr(k_scales), _ptr(v_scales), _ptr(bt), _ptr(cl),
+                                    S, Hq, Hkv, D, BS, MB, NB, ctypes.c_float(scale),
+                                    _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return out
+
+
+def quantize_int8_rows(x, lib: "OracleLib | None" = None) -> tuple[np.ndarray, np.ndarray]:
+    """(codes int8 [..., D], scales fp32 [...]) for fp32 rows x [..., D]."""
+    x = _c(x, np.float32)
+    D = x.shape[-1]
+    rows = int(np.prod(x.shape[:-1]))
+    codes = np.zeros(x.shape, dtype=np.int8)
+    scales = np.zeros(x.shape[:-1], dtype=np.float32)
+    L = lib.lib if lib is not None else _load()
+    L.oracle_quantize_int8_rows(_ptr(x), rows, D, _ptr(codes), _ptr(scales))
+    return codes, scales

@@ -1,0 +1,235 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for PagedAttention decode.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * bench's cpu_baseline leg may load this library.  It shares no code, header,
+ * table or helper with the HIP library; it is compiled with gcc on its own.
+ *
+ * What it computes (the plain definition, no blocking, no online softmax, no
+ * splits):
+ *
+ *   For every sequence s and query head h, with G = Hq / Hkv, g = h / G and
+ *   n = context_lens[s]:
+ *     - n == 0            -> out[s,h,:] = 0
+ *     - token t in [0,n)  -> physical block b = block_tables[s][t / BS],
+ *                            slot r = t % BS, key k_t = K[b, r, g, :],
+ *                            value v_t = V[b, r, g, :]
+ *     - score             s_t = scale * sum_i q[s,h,i] * k_t[i]
+ *     - softmax over ALL n tokens of the sequence (two passes: max, then
+ *       exp/sum), out[s,h,:] = sum_t e_t v_t / sum_t e_t.
+ *
+ * Passages followed:
+ *   - page "LLM 推理 KV Cache 内存管理深度工程实践：从 PageAttention 到推测解码"
+ *     (ybb.press), section 2.2 (paged attention): the logical block index
+ *     maps through the block table to a physical block, a block holds
+ *     block_size token slots, only min(block_size, n - j*block_size) slots of
+ *     block j are valid, the output starts at zero, scores are q.K^T * scale.
+ *     Its per-block softmax is read as ONE softmax over the whole context, as
+ *     the next passage states.
+ *   - page "KV cache" (t6page.pages.dev), section "PagedAttention 的算子":
+ *     K/V are contiguous inside a block, and the scaled dot product and the
+ *     softmax are taken after all blocks are merged.
+ *   - same ybb.press page, section 6.2 (GQA/MQA cache sharing): each group of
+ *     G consecutive query heads shares one KV head (read as g = h / G).
+ *   - same ybb.press page, section 6.1 (INT8 KV): symmetric quantization with
+ *     scale = amax(|x|) / 127 over the head dimension; the int8 entry point
+ *     dequantizes k_t = code * scale before the definition above.
+ *
+ * Precision: every input is widened exactly to double (bf16 -> double and
+ * int8 -> double are exact; the fp32 scale is taken as double(scale_f32)).
+ * The caller contract (valid block ids for every logical block below
+ * ceil(n/BS)) is CHECKED here: the oracle returns a negative code instead of
+ * reading out of bounds.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_ERR_ARG (-1)
+#define ORC_ERR_TABLE (-2)
+#define ORC_ERR_NOMEM (-3)
+
+static double bf16_bits_to_double(uint16_t bits)
+{
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* Element kinds of the KV cache. */
+enum { KV_BF16 = 0, KV_INT8 = 1 };
+
+typedef struct {
+    int kind;
+    const void *k;          /* [NB, BS, Hkv, D] bf16 bits or int8 codes */
+    const void *v;
+    const float *k_scales;  /* [NB, BS, Hkv], int8 only */
+    const float *v_scales;
+} kv_src;
+
+/* Key or value element i of token slot (b, r) for kv head g, widened to double. */
+static double kv_elem(const kv_src *src, int which_v, int64_t b, int r, int g, int i,
+                      int BS, int Hkv, int D)
+{
+    int64_t slot = (b * BS + r) * (int64_t)Hkv + g;
+    if (src->kind == KV_BF16) {
+        const uint16_t *base = (const uint16_t *)(which_v ? src->v : src->k);
+        return bf16_bits_to_double(base[slot * D + i]);
+    } else {
+        const int8_t *base = (const int8_t *)(which_v ? src->v : src->k);
+        const float *sc = which_v ? src->v_scales : src->k_scales;
+        return (double)base[slot * D + i] * (double)sc[slot];
+    }
+}
+
+static int decode_common(const uint16_t *q, const kv_src *src,
+                         const int32_t *block_tables, const int32_t *context_lens,
+                         int S, int Hq, int Hkv, int D, int BS, int MB, int64_t NB,
+                         float scale, double *out)
+{
+    if (!q || !src->k || !src->v || !block_tables || !context_lens || !out) return ORC_ERR_ARG;
+    if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || MB < 0 || NB < 0) return ORC_ERR_ARG;
+    if (Hq % Hkv != 0) return ORC_ERR_ARG;
+    if (src->kind == KV_INT8 && (!src->k_scales || !src->v_scales)) return ORC_ERR_ARG;
+
+    /* Check the caller contract before any gather. */
+    for (int s = 0; s < S; ++s) {
+        int n = context_lens[s];
+        if (n < 0 || (int64_t)n > (int64_t)MB * BS) return ORC_ERR_TABLE;
+        int nblk = (n + BS - 1) / BS;
+        for (int j = 0; j < nblk; ++j) {
+            int32_t b = block_tables[(int64_t)s * MB + j];
+            if (b < 0 || (int64_t)b >= NB) return ORC_ERR_TABLE;
+        }
+    }
+
+    const int G = Hq / Hkv;
+    const double sc = (double)scale;
+    int err = ORC_OK;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t row = 0; row < (int64_t)S * Hq; ++row) {
+        const int s = (int)(row / Hq);
+        const int h = (int)(row % Hq);
+        const int g = h / G;
+        const int n = context_lens[s];
+        double *o = out + row * D;
+        for (int i = 0; i < D; ++i) o[i] = 0.0;
+        if (n == 0) continue;
+
+        double *scores = (double *)malloc(sizeof(double) * (size_t)n);
+        double *qd = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!scores || !qd) {
+            free(scores);
+            free(qd);
+#pragma omp atomic write
+            err = ORC_ERR_NOMEM;
+            continue;
+        }
+        for (int i = 0; i < D; ++i) qd[i] = bf16_bits_to_double(q[row * D + i]);
+
+        /* Pass 1: scores over the gathered context, and their maximum. */
+        double m = -INFINITY;
+        for (int t = 0; t < n; ++t) {
+            int64_t b = block_tables[(int64_t)s * MB + t / BS];
+            int r = t % BS;
+            double dot = 0.0;
+            for (int i = 0; i < D; ++i) dot += qd[i] * kv_elem(src, 0, b, r, g, i, BS, Hkv, D);
+            scores[t] = sc * dot;
+            if (scores[t] > m) m = scores[t];
+        }
+        /* Pass 2: exponentials, their sum, and the weighted sum of values. */
+        double denom = 0.0;
+        for (int t = 0; t < n; ++t) {
+            int64_t b = block_tables[(int64_t)s * MB + t / BS];
+            int r = t % BS;
+            double e = exp(scores[t] - m);
+            denom += e;
+            for (int i = 0; i < D; ++i) o[i] += e * kv_elem(src, 1, b, r, g, i, BS, Hkv, D);
+        }
+        for (int i = 0; i < D; ++i) o[i] /= denom;
+        free(scores);
+        free(qd);
+    }
+    return err;
+}
+
+/*
+ * bf16 KV cache.  q: bf16 bits [S, Hq, D]; k_cache / v_cache: bf16 bits
+ * [NB, BS, Hkv, D]; block_tables: int32 [S, MB]; context_lens: int32 [S];
+ * out: double [S, Hq, D].  Returns 0, or a negative code.
+ */
+int oracle_paged_decode_bf16(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                             const int32_t *block_tables, const int32_t *context_lens,
+                             int S, int Hq, int Hkv, int D, int BS, int MB, int64_t NB,
+                             float scale, double *out)
+{
+    kv_src src = {KV_BF16, k_cache, v_cache, NULL, NULL};
+    return decode_common(q, &src, block_tables, context_lens, S, Hq, Hkv, D, BS, MB, NB, scale, out);
+}
+
+/*
+ * int8 KV cache with one fp32 scale per (token slot, kv head), for K and V
+ * separately.  k_cache / v_cache: int8 [NB, BS, Hkv, D]; k_scales /
+ * v_scales: fp32 [NB, BS, Hkv].  The rest as in the bf16 entry point.
+ */
+int oracle_paged_decode_int8(const uint16_t *q, const int8_t *k_cache, const int8_t *v_cache,
+                             const float *k_scales, const float *v_scales,
+                             const int32_t *block_tables, const int32_t *context_lens,
+                             int S, int Hq, int Hkv, int D, int BS, int MB, int64_t NB,
+                             float scale, double *out)
+{
+    kv_src src = {KV_INT8, k_cache, v_cache, k_scales, v_scales};
+    return decode_common(q, &src, block_tables, context_lens, S, Hq, Hkv, D, BS, MB, NB, scale, out);
+}
+
+/*
+ * Symmetric per-row int8 quantizer, in fp32 as the page's tensor code does it
+ * (page "LLM 推理 KV Cache 内存管理深度工程实践", section 6.1): the row's scale
+ * is amax(|x|)/127 and each code is x/scale rounded half-to-even.  A row of
+ * zeros gets scale 0 and codes 0 (the page's formula would divide by zero).
+ * x: fp32 [rows, D]; codes: int8 [rows, D]; scales: fp32 [rows].
+ */
+void oracle_quantize_int8_rows(const float *x, int64_t rows, int D, int8_t *codes, float *scales)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *xr = x + r * D;
+        float amax = 0.0f;
+        for (int i = 0; i < D; ++i) {
+            float a = fabsf(xr[i]);
+            if (a > amax) amax = a;
+        }
+        float s = amax / 127.0f;
+        scales[r] = s;
+        for (int i = 0; i < D; ++i) {
+            float c = (s == 0.0f) ? 0.0f : nearbyintf(xr[i] / s);
+            if (c > 127.0f) c = 127.0f;
+            if (c < -127.0f) c = -127.0f;
+            codes[r * D + i] = (int8_t)c;
+        }
+    }
+}

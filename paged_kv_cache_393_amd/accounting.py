@@ -1,0 +1,42 @@
+"""Byte and flop accounting for PagedAttention decode.
+
+KV bytes per token follow the formula of the t6page "KV cache" page (equation
+kv-per-token): 2 (K and V) x layers x kv heads x head_dim x bytes per element;
+that page works it out as 131,072 B/token for Llama 3 8B (equation
+kv-llama3-8b) and tabulates 1K / 4K / 32K / 128K contexts.
+
+Algorithmic bytes of ONE decode call (one layer) are what the operation must
+move at least once: every valid K and V element (plus the int8 scales), q,
+out, the valid block-table entries and the context lengths.  Split partials
+are overhead and are not counted.
+"""
+from __future__ import annotations
+
+from typing import Iterable
+
+
+def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int,
+                       bytes_per_elem: int = 2) -> int:
+    return 2 * num_layers * num_kv_heads * head_dim * bytes_per_elem
+
+
+def decode_bytes(context_lens: Iterable[int], num_q_heads: int, num_kv_heads: int,
+                 head_dim: int, block_size: int, kv_dtype: str = "bf16") -> int:
+    ctx = [int(c) for c in context_lens]
+    tokens = sum(ctx)
+    if kv_dtype == "bf16":
+        kv = tokens * kv_bytes_per_token(1, num_kv_heads, head_dim, 2)
+    elif kv_dtype == "int8":
+        kv = tokens * (kv_bytes_per_token(1, num_kv_heads, head_dim, 1) + 2 * num_kv_heads * 4)
+    else:
+        raise ValueError(kv_dtype)
+    S = len(ctx)
+    q = S * num_q_heads * head_dim * 2
+    out = S * num_q_heads * head_dim * 4
+    tables = sum((c + block_size - 1) // block_size for c in ctx) * 4
+    return kv + q + out + tables + S * 4
+
+
+def decode_flops(context_lens: Iterable[int], num_q_heads: int, head_dim: int) -> int:
+    """QK and PV multiply-adds (2 flops each) over every (query head, context token)."""
+    return 4 * head_dim * num_q_heads * sum(int(c) for c in context_lens)

@@ -1,0 +1,84 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each mutant is a copy of oracle.c with one plausible slip planted in it; it is
+compiled to a temporary library and the pins of ``test_oracle_pins`` are run
+against it.  Every mutant must fail at least one pin -- otherwise the pins
+would not be able to tell that slip from the correct oracle.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+SRC = open(oracle.SOURCE).read()
+
+MUTANTS = {
+    "gqa_h_mod_G": ("const int g = h / G;", "const int g = h % G;"),
+    "block_index_mod": ("block_tables[(int64_t)s * MB + t / BS]", "block_tables[(int64_t)s * MB + t % BS]"),
+    "slot_index_div": ("int r = t % BS;", "int r = t / BS;"),
+    "no_scale": ("scores[t] = sc * dot;", "scores[t] = dot;"),
+    "sign_of_dot": ("dot += qd[i] *", "dot -= qd[i] *"),
+    "k_used_as_v": ("o[i] += e * kv_elem(src, 1,", "o[i] += e * kv_elem(src, 0,"),
+    "v_used_as_k": ("dot += qd[i] * kv_elem(src, 0,", "dot += qd[i] * kv_elem(src, 1,"),
+    "no_normalisation": ("for (int i = 0; i < D; ++i) o[i] /= denom;", ""),
+    "one_token_short": ("for (int t = 0; t < n; ++t) {\n            int64_t b", "for (int t = 0; t < n - 1; ++t) {\n            int64_t b"),
+    "head_major_slot": ("int64_t slot = (b * BS + r) * (int64_t)Hkv + g;",
+                        "int64_t slot = (b * Hkv + g) * (int64_t)BS + r;"),
+    "int8_no_dequant": ("return (double)base[slot * D + i] * (double)sc[slot];",
+                        "return (double)base[slot * D + i];"),
+    "int8_k_scales_for_v": ("const float *sc = which_v ? src->v_scales : src->k_scales;",
+                            "const float *sc = src->k_scales;"),
+    "quant_divisor_128": ("float s = amax / 127.0f;", "float s = amax / 128.0f;"),
+    "quant_truncates": ("nearbyintf(xr[i] / s)", "truncf(xr[i] / s)"),
+    "max_not_subtracted_in_exp": ("double e = exp(scores[t] - m);", "double e = exp(scores[t] - 2.0 * m);"),
+}
+
+PIN_FUNCS = [
+    "test_context_one_returns_v_exactly",
+    "test_context_zero_gives_zero_row",
+    "test_gqa_groups_are_consecutive_heads",
+    "test_scale_zero_gives_mean_over_exactly_the_valid_tokens",
+    "test_two_tokens_closed_form_logistic",
+    "test_uniform_keys_give_mean_of_values",
+    "test_tiny_workload_matches_sdpa",
+    "test_int8_matches_sdpa_on_dequantized_cache",
+    "test_quantizer_closed_form_properties",
+    "test_int8_matches_bf16_on_lossless_values",
+    "test_generator_int8_synthesis_matches_oracle_quantizer",
+]
+
+RUNNER = r"""
+import sys
+sys.path.insert(0, {root!r})
+import oracle
+oracle._default = oracle.OracleLib({path!r})
+from tests import test_oracle_pins as PINS
+for name in {pins!r}:
+    try:
+        getattr(PINS, name)()
+    except (AssertionError, ValueError, FloatingPointError):
+        print("CAUGHT_BY", name)
+        sys.exit(1)
+print("SURVIVED")
+sys.exit(0)
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) >= 1, f"mutation site for {name} not found"
+    path = os.path.join(str(tmp_path), f"liboracle_{name}.so")
+    oracle.build_to(path, SRC.replace(old, new))
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = RUNNER.format(root=root, path=path, pins=PIN_FUNCS)
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True,
+                       timeout=300, env=env)
+    # A pin failing (exit 1) or the mutant crashing (killed by a signal) both
+    # mean the slip is detected; exit 0 means it survived every pin.
+    caught = (r.returncode == 1 and "CAUGHT_BY" in r.stdout) or r.returncode < 0
+    assert caught, f"mutant {name} not caught (rc {r.returncode}): {r.stdout[-300:]} {r.stderr[-800:]}"
