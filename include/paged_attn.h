@@ -55,13 +55,14 @@ extern "C" {
 #define PA_ERR_UNSUPPORTED (-3) /* head_dim or block_size with no compiled kernel */
 #define PA_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than paged_attn_workspace_bytes */
 #define PA_ERR_LAUNCH (-5)      /* the HIP runtime reported a launch error */
+#define PA_ERR_ALIGNMENT (-6)   /* q, k_cache, v_cache, out or workspace not 16-byte aligned */
 
 typedef struct pa_shape {
     int32_t num_seqs;           /* S  >= 0 (0 is a no-op) */
     int32_t num_q_heads;        /* Hq >= 1 */
     int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0 */
     int32_t head_dim;           /* 64 or 128 */
-    int32_t block_size;         /* tokens per block: a positive multiple of 16 */
+    int32_t block_size;         /* tokens per block: a power of two, 16 .. 4096 */
     int32_t max_blocks_per_seq; /* row length of block_tables, >= 1 */
     int32_t num_blocks;         /* blocks in the pool, >= 1 */
     int32_t split_tokens;       /* context partition size in tokens (multiple of 16), 0 = auto */

@@ -1,0 +1,197 @@
+"""ctypes binding of libpagedattn.so (C-ABI in include/paged_attn.h).
+
+Argument marshalling only: torch tensors are checked for dtype/shape/device
+and passed as raw device pointers with sizes; every step of the decode runs
+in the library's HIP kernels.  There is no fallback: if the library is
+missing or a call fails, this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "paged_attn.h")
+
+PA_OK = 0
+PA_ERR_NULL = -1
+PA_ERR_SHAPE = -2
+PA_ERR_UNSUPPORTED = -3
+PA_ERR_WORKSPACE = -4
+PA_ERR_LAUNCH = -5
+PA_ERR_ALIGNMENT = -6
+
+
+class PaShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
+        "max_blocks_per_seq", "num_blocks", "split_tokens")]
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"paged_attn error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    SP = ctypes.POINTER(PaShape)
+    lib.paged_attn_plan.argtypes = [SP, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.paged_attn_plan.restype = ctypes.c_int
+    lib.paged_attn_workspace_bytes.argtypes = [SP]
+    lib.paged_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.paged_attn_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, SP, P, ctypes.c_size_t, P]
+    lib.paged_attn_decode.restype = ctypes.c_int
+    lib.paged_attn_decode_int8.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, SP, P,
+                                           ctypes.c_size_t, P]
+    lib.paged_attn_decode_int8.restype = ctypes.c_int
+    lib.paged_attn_strerror.argtypes = [ctypes.c_int]
+    lib.paged_attn_strerror.restype = ctypes.c_char_p
+    lib.paged_attn_abi_version.argtypes = []
+    lib.paged_attn_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/paged_attn.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(paged_attn_\w+)\s*\(", text)))
+
+
+def strerror(code: int) -> str:
+    return load().paged_attn_strerror(code).decode()
+
+
+def _check(rc: int):
+    if rc != PA_OK:
+        raise PagedAttnError(rc, strerror(rc))
+
+
+def make_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+               num_blocks, split_tokens=0) -> PaShape:
+    return PaShape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                   max_blocks_per_seq, num_blocks, split_tokens)
+
+
+def plan(shape: PaShape):
+    st = ctypes.c_int32()
+    ms = ctypes.c_int32()
+    _check(load().paged_attn_plan(ctypes.byref(shape), ctypes.byref(st), ctypes.byref(ms)))
+    return st.value, ms.value
+
+
+def workspace_bytes(shape: PaShape) -> int:
+    return int(load().paged_attn_workspace_bytes(ctypes.byref(shape)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def shape_of(q, k_cache, block_tables, split_tokens=0) -> PaShape:
+    S, Hq, D = q.shape
+    NB, bs, Hkv, D2 = k_cache.shape
+    if D2 != D:
+        raise ValueError("head_dim of q and cache differ")
+    return make_shape(S, Hq, Hkv, D, bs, block_tables.shape[1], NB, split_tokens)
+
+
+def _validate(q, k_cache, v_cache, block_tables, context_lens, kv_dtype):
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_tables", block_tables), ("context_lens", context_lens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bf16")
+    if k_cache.dtype != kv_dtype or v_cache.dtype != kv_dtype:
+        raise TypeError(f"cache must be {kv_dtype}")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+
+
+def alloc_workspace(shape: PaShape, device) -> Optional[torch.Tensor]:
+    n = workspace_bytes(shape)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out=None,
+           split_tokens: int = 0, workspace=None, stream=None) -> torch.Tensor:
+    """out fp32 [S, Hq, D] = paged_attn_decode(...) on the current (or given) stream."""
+    _validate(q, k_cache, v_cache, block_tables, context_lens, torch.bfloat16)
+    shape = shape_of(q, k_cache, block_tables, split_tokens)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(shape, q.device)
+    ws_n = workspace.numel() if workspace is not None else 0
+    rc = load().paged_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                  _ptr(context_lens), ctypes.c_float(scale), _ptr(out),
+                                  ctypes.byref(shape), _ptr(workspace), ctypes.c_size_t(ws_n),
+                                  _stream_handle(stream))
+    _check(rc)
+    return out
+
+
+def decode_int8(q, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens,
+                scale: float, out=None, split_tokens: int = 0, workspace=None,
+                stream=None) -> torch.Tensor:
+    """out fp32 [S, Hq, D] = paged_attn_decode_int8(...)."""
+    _validate(q, k_cache, v_cache, block_tables, context_lens, torch.int8)
+    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be a contiguous fp32 device tensor")
+        if tuple(t.shape) != tuple(k_cache.shape[:3]):
+            raise ValueError(f"{name} must be [num_blocks, block_size, num_kv_heads]")
+    shape = shape_of(q, k_cache, block_tables, split_tokens)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(shape, q.device)
+    ws_n = workspace.numel() if workspace is not None else 0
+    rc = load().paged_attn_decode_int8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
+                                       _ptr(v_scales), _ptr(block_tables), _ptr(context_lens),
+                                       ctypes.c_float(scale), _ptr(out), ctypes.byref(shape),
+                                       _ptr(workspace), ctypes.c_size_t(ws_n),
+                                       _stream_handle(stream))
+    _check(rc)
+    return out
+
+
+def decode_views(views: dict, out=None, split_tokens: int = 0, workspace=None, stream=None):
+    """Decode one layer given the per-layer views of the input generator."""
+    if "k_scales" in views:
+        return decode_int8(views["q"], views["k_cache"], views["v_cache"], views["k_scales"],
+                           views["v_scales"], views["block_tables"], views["context_lens"],
+                           views["scale"], out=out, split_tokens=split_tokens,
+                           workspace=workspace, stream=stream)
+    return decode(views["q"], views["k_cache"], views["v_cache"], views["block_tables"],
+                  views["context_lens"], views["scale"], out=out, split_tokens=split_tokens,
+                  workspace=workspace, stream=stream)
