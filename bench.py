@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""PagedAttention decode bench on one MI355X.
+
+A step is one decode of the whole batch: every sequence's single query token
+attends over its paged context (all layers of the workload), through the
+C-ABI library -- the main kernel plus, when the context is partitioned, the
+reduction kernel.  Inputs are seeded, synthetic and resident in HBM before
+timing starts.  Each timed step is preceded (outside the timed events) by a
+2 GiB device READ that evicts the KV cache from the 256 MB MALL and the L2s
+with clean lines, so the KV bytes really come from HBM.  (A write-based
+flush would leave the MALL full of dirty lines whose write-back then
+competes with the timed kernel.)
+
+Prints ONE JSON line.  `value` is decode tokens/s (sequences decoded per
+second: each step produces one token per sequence); `roofline` relates the
+algorithmic bytes of one step to its measured duration against the 8 TB/s
+HBM peak; `cpu_baseline` is the fp64 oracle timed on the host's cores on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload llama3_8b]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+METRIC = ("decode attention tokens/s and achieved KV-read HBM GB/s (% of peak), "
+          "Llama-3-8B shape")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--split-tokens", type=int, default=None,
+                    help="context partition size (default: the workload's, else the library's)")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON with measured HBM bytes per decode call (from rocprofv3 counters)")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the decode path has no multi-GPU leg in this build.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from paged_kv_cache_393_amd import accounting as A
+    from paged_kv_cache_393_amd import binding as B
+    from paged_kv_cache_393_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    B.load()   # fails loudly if the HIP library is missing
+    wl = I.WORKLOADS[args.workload]
+    split = wl.split_tokens if args.split_tokens is None else args.split_tokens
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    inp = I.make_inputs(wl, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs for {wl.name} ready in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    L = wl.num_layers
+    layers = [I.layer_views(inp, l) for l in range(L)]
+    shape = B.shape_of(layers[0]["q"], layers[0]["k_cache"], layers[0]["block_tables"], split)
+    plan_split, plan_parts = B.plan(shape)
+    workspace = B.alloc_workspace(shape, dev)
+    outs = [torch.empty(v["q"].shape, dtype=torch.float32, device=dev) for v in layers]
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for v, o in zip(layers, outs):
+            B.decode_views(v, out=o, split_tokens=split, workspace=workspace, stream=stream)
+
+    flush_buf = None
+    if not args.no_flush:
+        flush_buf = torch.ones((2 << 30) // 4, dtype=torch.float32, device=dev)
+
+    def evict():
+        if flush_buf is not None:
+            flush_buf.amax()      # a read of 2 GiB: clean eviction of MALL and L2
+
+    for i in range(args.warmup):
+        evict()
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        evict()
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_sorted = sorted(ms)
+    ms_mean = statistics.fmean(ms)
+    pct = lambda q: ms_sorted[min(len(ms_sorted) - 1, int(q * len(ms_sorted)))]
+
+    ctx = inp["context_lens"].cpu().tolist()
+    S = wl.num_seqs
+    step_bytes = L * A.decode_bytes(ctx, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                    wl.block_size, wl.kv_dtype)
+    kv_bytes = L * sum(ctx) * (A.kv_bytes_per_token(1, wl.num_kv_heads, wl.head_dim,
+                                                     1 if wl.kv_dtype == "int8" else 2)
+                               + (2 * wl.num_kv_heads * 4 if wl.kv_dtype == "int8" else 0))
+    flops = L * A.decode_flops(ctx, wl.num_q_heads, wl.head_dim)
+    t_s = ms_mean / 1e3
+    gbps = step_bytes / t_s / 1e9
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        tr = json.load(open(args.traffic))
+        if tr.get("workload") == wl.name:
+            traffic = tr.get("bytes_per_call")
+
+    record = {
+        "metric": METRIC,
+        "value": S / t_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_mean,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, shuffled block pool)",
+        "config": {
+            "workload": wl.name,
+            "num_seqs": S, "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+            "head_dim": wl.head_dim, "block_size": wl.block_size, "layers": L,
+            "context_tokens": sum(ctx), "ctx_min": min(ctx), "ctx_max": max(ctx),
+            "num_blocks": inp["num_blocks"], "kv_dtype": wl.kv_dtype,
+            "split_tokens": plan_split, "partitions": plan_parts,
+            "cache_evict_between_steps": "2 GiB read" if flush_buf is not None else None,
+        },
+        "kv_gbps": kv_bytes / t_s / 1e9,
+        "pct_of_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
+        "ms_p10": pct(0.10), "ms_median": pct(0.50), "ms_p90": pct(0.90),
+        "wall_ms_per_step_incl_evict": wall / args.steps * 1e3,
+        "tflops": flops / t_s / 1e12,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "one decode call: pa_decode_kernel (+ pa_reduce_kernel when partitioned)",
+            "achieved": gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_step": step_bytes,
+            "launches_per_step": L * (2 if plan_parts > 1 else 1),
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        record["cpu_baseline"] = cpu_baseline(wl, layers[0], outs[0], ctx, L, args.cpu_seconds)
+
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+def cpu_baseline(wl, views0, out0, ctx, n_layers, budget_s):
+    """fp64 oracle on a bounded sample of layer 0, scaled to the whole step by token count."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_cache_393_amd import inputs as I
+
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    threads = oracle.num_threads()
+
+    def run(ids):
+        sub = I.select_sequences(views0, ids, wl.block_size)
+        qb = I.bf16_bits(sub["q"])
+        bt = sub["block_tables"].numpy()
+        cl = sub["context_lens"].numpy()
+        t = time.perf_counter()
+        if "k_scales" in sub:
+            ref = oracle.paged_decode_int8(qb, sub["k_cache"].numpy(), sub["v_cache"].numpy(),
+                                           sub["k_scales"].numpy(), sub["v_scales"].numpy(),
+                                           bt, cl, sub["scale"])
+        else:
+            ref = oracle.paged_decode_bf16(qb, I.bf16_bits(sub["k_cache"]),
+                                           I.bf16_bits(sub["v_cache"]), bt, cl, sub["scale"])
+        return time.perf_counter() - t, ref
+
+    order = list(range(len(ctx)))
+    t1, _ = run(order[:1])
+    per_token = t1 / max(1, ctx[0])
+    avg = sum(ctx) / len(ctx)
+    n = max(1, min(len(ctx), int(budget_s / max(per_token * avg, 1e-9))))
+    ids = order[:n]
+    t_sample, ref = run(ids)
+    got = out0[ids].double().cpu().numpy()
+    sample_tokens = sum(ctx[i] for i in ids)
+    t_full = t_sample * (sum(ctx) / sample_tokens) * n_layers
+    return {
+        "value": len(ctx) / t_full,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{n} of {len(ctx)} sequences of layer 0 of {n_layers} "
+                   f"({sample_tokens} of {sum(ctx)} context tokens), {t_sample:.2f}s, "
+                   "scaled to the full step by context-token count"),
+        "parity_max_abs_vs_gpu": float(np.abs(got - ref).max()),
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

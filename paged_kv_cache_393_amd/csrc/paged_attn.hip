@@ -9,13 +9,14 @@
 // "KV cache" page, section "PagedAttention 的算子").  The int8 variant
 // dequantizes code * per-(slot, kv head) scale (same ybb.press page, 6.1).
 //
-// Work decomposition.  One workgroup (4 waves) owns one context partition of
-// one (sequence, kv head, chunk of <= 16 query heads of the group).  Inside
-// it the 16-token tiles of the partition are dealt round-robin to the waves;
-// each wave keeps its own online-softmax state and the four are merged in
-// LDS at the end.  With several partitions per sequence each workgroup writes
-// an unnormalised partial (acc, max, sum) and a reduction kernel merges them
-// (log-sum-exp weights, fixed partition order, so results are reproducible).
+// Work decomposition.  One wave owns one (sequence, kv head, chunk of <= 16
+// query heads of the group, context partition) and streams the partition's
+// 16-token tiles with a private online-softmax state; a workgroup holds four
+// such waves for four kv heads of the same (sequence, partition), so the
+// token rows of a block (all kv heads side by side) are read together.  With
+// several partitions per sequence each wave writes an unnormalised partial
+// (acc, max, sum) and a reduction kernel merges them (log-sum-exp weights,
+// fixed partition order, so results are reproducible).
 //
 // Per tile and wave:
 //   * K: lane l loads 16 B of token l%16 (dims chosen so that the four lane
@@ -32,13 +33,15 @@
 //     rounding of probabilities).
 //   * the next tile's K/V loads are issued before the current tile is
 //     processed (register double buffering).
-// Tokens past the context end inside the last tile are never loaded: their
-// loads are clamped to the last valid token and their scores set to -inf, so
-// their weight is exactly 0 and padding contents cannot reach the output.
+// Rows of the last tile past the context end are slots of the same allocated
+// block; they are loaded with the tile but selected away (score -inf, V and
+// int8 V scale replaced by 0), so padding contents cannot reach the output.
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "paged_attn.h"
 
@@ -53,7 +56,10 @@ constexpr int kTile = 16;           // tokens per tile (MFMA rows)
 constexpr int kWaves = 4;           // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxChunkHeads = 16;  // query heads per workgroup (MFMA columns)
+constexpr int kMaxPartitionBlocks = 64;    // blocks one partition may span (one wave of ids)
 constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw (unformatted, stride 0) buffer resource on CDNA3/CDNA4.
+constexpr int kRsrcFlags = 0x00020000;
 
 struct DecodeParams {
     const uint16_t *q;       // bf16 [S, Hq, D]
@@ -137,7 +143,8 @@ struct TileRegs {
     using L = Layout<D, INT8>;
     u32x4_t k[L::kKLoads];
     typename L::VReg v[L::kVLoads];
-    float sc;   // int8: lanes 0..15 K scale of token lane, 16..31 V scale of token lane-16
+    float ks;   // int8: K scale of token row l%16 (every lane group holds the same)
+    float vs;   // int8: V scale of token row l%16
 };
 
 template <int D, int GT, bool INT8>
@@ -149,18 +156,24 @@ __global__ __launch_bounds__(kThreads) void pa_decode_kernel(const DecodeParams 
     __shared__ __attribute__((aligned(16))) float lds_p[kWaves][GT][kTile];
     __shared__ float lds_alpha[kWaves][GT];
     __shared__ __attribute__((aligned(16))) float lds_sc[kWaves][2 * kTile];
-    __shared__ float lds_acc[kWaves][GT][D];
-    __shared__ float lds_m[kWaves][GT];
-    __shared__ float lds_l[kWaves][GT];
+    __shared__ float lds_ml[kWaves][2][GT];
 
-    const int split = blockIdx.x;
-    const int g = blockIdx.y / p.n_chunks;
-    const int chunk = blockIdx.y - g * p.n_chunks;
+    // Grid: x = group of kWaves (kv head, head chunk) units, y = partition,
+    // z = sequence.  Each wave owns one unit and streams the whole partition,
+    // so the waves of a workgroup read the same blocks' token rows (their kv
+    // heads side by side) at about the same time.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
+    const int unit = blockIdx.x * kWaves + wave;
+    const int Hkv = p.num_kv_heads;
+    if (unit >= Hkv * p.n_chunks) return;            // whole wave; no workgroup barrier follows
+    const int g = unit / p.n_chunks;
+    const int chunk = unit - g * p.n_chunks;
+    const int split = blockIdx.y;
     const int s = blockIdx.z;
     const int ctx = p.context_lens[s];
     const int t_begin = split * p.split_tokens;
     const bool single = p.max_splits == 1;
-    if (!single && t_begin >= ctx) return;   // empty partition; the reduction skips it
+    if (!single && t_begin >= ctx) return;           // empty partition; the reduction skips it
     const int t_end = min(ctx, t_begin + p.split_tokens);
     const int n_tiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
 
@@ -168,7 +181,6 @@ __global__ __launch_bounds__(kThreads) void pa_decode_kernel(const DecodeParams 
     const int h_base = g * p.group + chunk * GT;
     const int n_heads = min(GT, p.group - chunk * GT);
 
-    const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int lg = lane >> 4;      // lane group (MFMA k group / score rows)
     const int l16 = lane & 15;     // token row of K, head column of Q and scores
@@ -177,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void pa_decode_kernel(const DecodeParams 
 
     const int bs_log2 = p.log2_block_size;
     const int bs_mask = (1 << bs_log2) - 1;
-    const int64_t row_bytes = (int64_t)p.num_kv_heads * D * L::kElem;   // one token slot
+    const int64_t row_bytes = (int64_t)Hkv * D * L::kElem;   // one token slot, all kv heads
     const char *kbase = (const char *)p.k + (int64_t)g * D * L::kElem;
     const char *vbase = (const char *)p.v + (int64_t)g * D * L::kElem;
     const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
@@ -195,45 +207,63 @@ __global__ __launch_bounds__(kThreads) void pa_decode_kernel(const DecodeParams 
         }
     }
 
-    // Block-table entries of this partition, 64 at a time: lane i holds entry tbl_base + i.
+    // Block ids of this partition as a register window: lane i holds table
+    // entry blk_first + i (a partition spans at most 64 blocks), loaded once
+    // before the tile loop; a tile's id is then read with readlane, so the loop
+    // itself makes no dependent memory access.
     const int blk_first = t_begin >> bs_log2;
     const int blk_last = t_end > t_begin ? ((t_end - 1) >> bs_log2) + 1 : blk_first;
-    int tbl_base = blk_first;
-    int tbl_val = (blk_first + lane < blk_last) ? table[blk_first + lane] : 0;
+    const int win = (lane < blk_last - blk_first) ? table[blk_first + lane] : 0;
 
-    // Token-slot index phys * block_size + slot of the first token of tile `tile`.
-    auto tile_slot = [&](int tile) -> int64_t {
+    // Token-slot index phys * block_size + slot of the first token of tile `tile` (uniform).
+    auto tile_slot = [&](int tile) __attribute__((always_inline)) -> int64_t {
         const int t0 = t_begin + tile * kTile;
-        const int blk = t0 >> bs_log2;
-        if (blk - tbl_base >= 64) {          // wave-uniform: refill the table window
-            tbl_base = blk;
-            tbl_val = (blk + lane < blk_last) ? table[blk + lane] : 0;
-        }
-        const int phys = __builtin_amdgcn_readlane(tbl_val, blk - tbl_base);
+        const int phys = __builtin_amdgcn_readlane(win, (t0 >> bs_log2) - blk_first);
         return ((int64_t)phys << bs_log2) + (t0 & bs_mask);
     };
 
-    auto load_tile = [&](TileRegs<D, INT8> &r, int tile) {
-        const int t0 = t_begin + tile * kTile;
-        const int last = t_end - 1 - t0;                 // last valid row of this tile
+    // Tile loads are raw buffer loads: a uniform buffer resource per tile whose
+    // range is the tile's valid rows, plus per-lane byte offsets that are fixed
+    // for the whole loop -- no per-tile vector address arithmetic.  A tile never
+    // crosses a block (block_size is a multiple of 16).  Rows at or past the
+    // context end fall outside the resource's range: the hardware returns 0 for
+    // them without touching memory, and they are also selected away below
+    // (score -inf, V and int8 V scale 0), so padding cannot reach the output.
+    const uint32_t rb32 = (uint32_t)row_bytes;
+    const int k_off = (int)((uint32_t)l16 * rb32 + (uint32_t)(L::step_dim(0, lg) * L::kElem));
+    int v_off[L::kVLoads];
+#pragma unroll
+    for (int j = 0; j < L::kVLoads; ++j)
+        v_off[j] = (int)((uint32_t)(vr * L::kVLoads + j) * rb32 + (uint32_t)(vc * 8 * L::kElem));
+    const int s_off = (int)(((uint32_t)l16 * (uint32_t)Hkv + (uint32_t)g) * 4u);
+
+    auto load_tile = [&](TileRegs<D, INT8> &r, int tile) __attribute__((always_inline)) {
         const int64_t slot0 = tile_slot(tile);
-        const int64_t off = slot0 * row_bytes;
-        const int kt = min(l16, last);
-        const char *kp = kbase + off + kt * row_bytes;
+        const int rows = min(kTile, t_end - (t_begin + tile * kTile));
+        const int range = rows * (int)rb32;
+        const __amdgpu_buffer_rsrc_t kr =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + slot0 * row_bytes), 0, range, kRsrcFlags);
+        const __amdgpu_buffer_rsrc_t vrs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + slot0 * row_bytes), 0, range, kRsrcFlags);
 #pragma unroll
         for (int m = 0; m < L::kKLoads; ++m)
-            r.k[m] = *(const u32x4_t *)(kp + (L::step_dim(m * L::kStepsPerLoad, lg)) * L::kElem);
+            r.k[m] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         kr, k_off + m * 4 * L::kKElemsPerLoad * L::kElem, 0, 0));
 #pragma unroll
         for (int j = 0; j < L::kVLoads; ++j) {
-            const int vt = min(vr * L::kVLoads + j, last);
-            r.v[j] = *(const typename L::VReg *)(vbase + off + vt * row_bytes +
-                                                 vc * 8 * L::kElem);
+            if constexpr (INT8)
+                r.v[j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(vrs, v_off[j], 0, 0));
+            else
+                r.v[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_off[j], 0, 0));
         }
         if constexpr (INT8) {
-            const int st = min(l16, last);
-            const int64_t slot = slot0 + st;
-            const float *sp = (lane & 16) ? p.v_scales : p.k_scales;
-            r.sc = sp[slot * p.num_kv_heads + g];
+            const int srange = rows * Hkv * 4;
+            const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.k_scales + slot0 * Hkv), 0, srange, kRsrcFlags);
+            const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.v_scales + slot0 * Hkv), 0, srange, kRsrcFlags);
+            r.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksr, s_off, 0, 0));
+            r.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsr, s_off, 0, 0));
         }
     };
 
@@ -246,11 +276,12 @@ __global__ __launch_bounds__(kThreads) void pa_decode_kernel(const DecodeParams 
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
-    auto compute_tile = [&](const TileRegs<D, INT8> &r, int tile) {
+    auto compute_tile = [&](const TileRegs<D, INT8> &r, int tile) __attribute__((always_inline)) {
         const int t0 = t_begin + tile * kTile;
         wave_lds_sync();
         if constexpr (INT8) {
-            if (lane < 2 * kTile) lds_sc[wave][lane] = r.sc;
+            if (lane < kTile) lds_sc[wave][lane] = r.ks;
+            else if (lane < 2 * kTile) lds_sc[wave][lane] = r.vs;
         }
         // S = K Q^T on the matrix cores: rows = tokens, columns = heads.
         f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
@@ -296,64 +327,93 @@ __global__ __launch_bounds__(kThreads) void pa_decode_kernel(const DecodeParams 
         l_run = l_run * alpha + psum;
         m_run = m_new;
         if (l16 < GT) {
-            f32x4_t pw = {pr[0] * vsc[0], pr[1] * vsc[1], pr[2] * vsc[2], pr[3] * vsc[3]};
+            // Masked rows: p is exactly 0, and an int8 V scale there may be anything.
+            f32x4_t pw;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                pw[i] = INT8 ? (sc[i] == -INFINITY ? 0.f : pr[i] * vsc[i]) : pr[i];
             *(f32x4_t *)&lds_p[wave][l16][4 * lg] = pw;
             if (lg == 0) lds_alpha[wave][l16] = alpha;
         }
         wave_lds_sync();
         // O += P V with fp32 FMAs; this lane owns dims 8*vc..8*vc+7 of token rows vr*kVLoads+j.
-        float vf[L::kVLoads][8];
-#pragma unroll
-        for (int j = 0; j < L::kVLoads; ++j) {
-            if constexpr (INT8) {
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    vf[j][b] = i8_at(r.v[j].x, b);
-                    vf[j][4 + b] = i8_at(r.v[j].y, b);
-                }
-            } else {
-                vf[j][0] = bf16_lo(r.v[j].x); vf[j][1] = bf16_hi(r.v[j].x);
-                vf[j][2] = bf16_lo(r.v[j].y); vf[j][3] = bf16_hi(r.v[j].y);
-                vf[j][4] = bf16_lo(r.v[j].z); vf[j][5] = bf16_hi(r.v[j].z);
-                vf[j][6] = bf16_lo(r.v[j].w); vf[j][7] = bf16_hi(r.v[j].w);
-            }
-        }
+        float pw[GT][L::kVLoads];
 #pragma unroll
         for (int h = 0; h < GT; ++h) {
             const float a = lds_alpha[wave][h];
-            float pw[L::kVLoads];
 #pragma unroll
-            for (int j = 0; j < L::kVLoads; ++j) pw[j] = lds_p[wave][h][vr * L::kVLoads + j];
+            for (int j = 0; j < L::kVLoads; ++j) pw[h][j] = lds_p[wave][h][vr * L::kVLoads + j];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x = acc[h][e] * a;
+            for (int e = 0; e < 8; ++e) acc[h][e] *= a;
+        }
+        // Rows past the context end (last tile only) are replaced by zeros.
+        const int last_row = t_end - 1 - t0;                 // uniform
+        const bool partial = last_row < kTile - 1;
 #pragma unroll
-                for (int j = 0; j < L::kVLoads; ++j) x = fmaf(pw[j], vf[j][e], x);
-                acc[h][e] = x;
+        for (int j = 0; j < L::kVLoads; ++j) {
+            typename L::VReg vr_j = r.v[j];
+            if (partial && vr * L::kVLoads + j > last_row) vr_j = typename L::VReg{};
+            float vf[8];
+            if constexpr (INT8) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    vf[b] = i8_at(vr_j.x, b);
+                    vf[4 + b] = i8_at(vr_j.y, b);
+                }
+            } else {
+                vf[0] = bf16_lo(vr_j.x); vf[1] = bf16_hi(vr_j.x);
+                vf[2] = bf16_lo(vr_j.y); vf[3] = bf16_hi(vr_j.y);
+                vf[4] = bf16_lo(vr_j.z); vf[5] = bf16_hi(vr_j.z);
+                vf[6] = bf16_lo(vr_j.w); vf[7] = bf16_hi(vr_j.w);
             }
+#pragma unroll
+            for (int h = 0; h < GT; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[h][j], vf[e], acc[h][e]);
         }
     };
 
-    if (wave < n_tiles) {
-        TileRegs<D, INT8> ra, rb;
-        int tile = wave;
-        load_tile(ra, tile);
-        for (;;) {
-            const int t1 = tile + kWaves;
-            const bool more1 = t1 < n_tiles;
-            load_tile(rb, more1 ? t1 : tile);      // unconditional: keeps the loads in flight
-            compute_tile(ra, tile);
-            if (!more1) break;
-            const int t2 = t1 + kWaves;
-            const bool more2 = t2 < n_tiles;
-            load_tile(ra, more2 ? t2 : t1);
-            compute_tile(rb, t1);
-            if (!more2) break;
-            tile = t2;
+    // Register pipeline of kStages tile buffers: while the wave processes one
+    // tile, the loads of its next kStages-1 tiles are in flight.  The scheduling
+    // barriers keep each prefetch issued before the processing of the current
+    // tile starts.  The loop runs whole rounds of kStages tiles (one back edge,
+    // no early exit), so the set of pending loads at its head is the same on
+    // entry and on every iteration; the last 0..kStages-1 tiles, already in
+    // flight, are processed after it.  Prefetches past the end re-load the last
+    // tile (a cache hit), which keeps every load unconditional.
+    constexpr int kStages = 3;
+    if (n_tiles > 0) {
+        TileRegs<D, INT8> buf[kStages];
+        auto tile_of = [&](int k) __attribute__((always_inline)) { return min(k, n_tiles - 1); };
+        // One pipeline step on buffer I (a compile-time index): prefetch tile
+        // k + kStages - 1 into the buffer freed by the previous step, then
+        // process tile k.
+        auto step = [&](auto I, int k) __attribute__((always_inline)) {
+            constexpr int i = decltype(I)::value;
+            load_tile(buf[(i + kStages - 1) % kStages], tile_of(k + kStages - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute_tile(buf[i], k);
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        static_assert(kStages == 3, "three explicit steps below");
+        load_tile(buf[0], tile_of(0));
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(buf[1], tile_of(1));
+        __builtin_amdgcn_sched_barrier(0);
+        const int rounds = n_tiles / kStages;
+        for (int rd = 0; rd < rounds; ++rd) {
+            step(I0{}, rd * kStages);
+            step(I1{}, rd * kStages + 1);
+            step(I2{}, rd * kStages + 2);
         }
+        const int rem = n_tiles - rounds * kStages;
+        if (rem > 0) compute_tile(buf[0], rounds * kStages);
+        if (rem > 1) compute_tile(buf[1], rounds * kStages + 1);
     }
 
-    // Merge inside the wave: the four score-lane groups hold partial sums, the
+    // Finish inside the wave: the four score-lane groups hold partial sums, the
     // V token rows hold partial accumulators over different tokens.
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
@@ -363,43 +423,43 @@ __global__ __launch_bounds__(kThreads) void pa_decode_kernel(const DecodeParams 
         for (int h = 0; h < GT; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+    wave_lds_sync();
     if (lane < GT) {
-        lds_m[wave][lane] = m_run;
-        lds_l[wave][lane] = l_run;
+        lds_ml[wave][0][lane] = m_run;
+        lds_ml[wave][1][lane] = l_run;
     }
+    wave_lds_sync();
     if (vr == 0) {
 #pragma unroll
-        for (int h = 0; h < GT; ++h)
+        for (int h = 0; h < GT; ++h) {
+            if (h >= n_heads) continue;                      // uniform; keeps the loop unrollable
+            const int64_t row = (int64_t)s * Hq + h_base + h;
+            const float lsum = lds_ml[wave][1][h];
+            f32x4_t o0, o1;
+            if (single) {
+                const float inv = lsum > 0.f ? 1.f / lsum : 0.f;   // lsum == 0 only for ctx == 0
 #pragma unroll
-            for (int e = 0; e < 8; ++e) lds_acc[wave][h][vc * 8 + e] = acc[h][e];
-    }
-    __syncthreads();
-
-    // Merge across waves and write the result (or this partition's partial).
-    for (int idx = threadIdx.x; idx < GT * D; idx += kThreads) {
-        const int h = idx / D;
-        const int d = idx - h * D;
-        if (h >= n_heads) continue;
-        float M = -INFINITY;
+                for (int e = 0; e < 4; ++e) {
+                    o0[e] = acc[h][e] * inv;
+                    o1[e] = acc[h][4 + e] * inv;
+                }
+                float *dst = p.out + row * D + vc * 8;
+                *(f32x4_t *)dst = o0;
+                *(f32x4_t *)(dst + 4) = o1;
+            } else {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds_m[w][h]);
-        float Lsum = 0.f, A = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float mw = lds_m[w][h];
-            const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-            Lsum = fmaf(f, lds_l[w][h], Lsum);
-            A = fmaf(f, lds_acc[w][h][d], A);
-        }
-        const int64_t row = (int64_t)s * Hq + h_base + h;
-        if (single) {
-            p.out[row * D + d] = Lsum > 0.f ? A / Lsum : 0.f;
-        } else {
-            const int64_t pr = row * p.max_splits + split;
-            p.part_acc[pr * D + d] = A;
-            if (d == 0) {
-                p.part_ml[2 * pr] = M;
-                p.part_ml[2 * pr + 1] = Lsum;
+                for (int e = 0; e < 4; ++e) {
+                    o0[e] = acc[h][e];
+                    o1[e] = acc[h][4 + e];
+                }
+                const int64_t pr = row * p.max_splits + split;
+                float *dst = p.part_acc + pr * D + vc * 8;
+                *(f32x4_t *)dst = o0;
+                *(f32x4_t *)(dst + 4) = o1;
+                if (vc == 0) {
+                    p.part_ml[2 * pr] = lds_ml[wave][0][h];
+                    p.part_ml[2 * pr + 1] = lsum;
+                }
             }
         }
     }
@@ -474,6 +534,9 @@ int make_plan(const pa_shape *sh, Plan *pl) {
     pl->log2_bs = ilog2(sh->block_size);
     int T = sh->split_tokens;
     if (T == 0) T = 512;            // default partition; one partition if the context is shorter
+    // A partition may span at most kMaxPartitionBlocks blocks (its ids fit one wave).
+    const int64_t t_cap = (int64_t)(kMaxPartitionBlocks - 1) * sh->block_size / kTile * kTile;
+    if (T > t_cap) T = (int)t_cap;
     if ((int64_t)T >= max_ctx) {
         pl->split_tokens = (int)((max_ctx + kTile - 1) / kTile * kTile);
         pl->max_splits = 1;
@@ -481,8 +544,7 @@ int make_plan(const pa_shape *sh, Plan *pl) {
         pl->split_tokens = T;
         pl->max_splits = (int)((max_ctx + T - 1) / T);
     }
-    if ((int64_t)sh->num_kv_heads * pl->n_chunks > 65535 || sh->num_seqs > 65535)
-        return PA_ERR_UNSUPPORTED;
+    if (pl->max_splits > 65535 || sh->num_seqs > 65535) return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
 
@@ -495,7 +557,7 @@ size_t workspace_for(const pa_shape *sh, const Plan &pl) {
 
 template <int D, bool INT8>
 int launch_decode_d(const DecodeParams &prm, const Plan &pl, int S, int Hkv, hipStream_t st) {
-    dim3 grid(pl.max_splits, Hkv * pl.n_chunks, S);
+    dim3 grid((Hkv * pl.n_chunks + kWaves - 1) / kWaves, pl.max_splits, S);
     dim3 block(kThreads);
     switch (pl.chunk_heads) {
         case 1: hipLaunchKernelGGL((pa_decode_kernel<D, 1, INT8>), grid, block, 0, st, prm); break;
