@@ -167,14 +167,14 @@ def main() -> int:
         "tflops": flops / t_s / 1e12,
         "roofline": {
             "bound": "hbm",
-            "kernel": "one decode call: pa_decode_kernel (+ pa_reduce_kernel when partitioned)",
+            "kernel": "pa_decode_kernel (one launch per layer; split sequences merged in-kernel)",
             "achieved": gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": gbps / HBM_PEAK_GBPS,
             "traffic": traffic,
             "algorithmic_bytes_per_step": step_bytes,
-            "launches_per_step": L * (2 if plan_parts > 1 else 1),
+            "launches_per_step": L,
         },
         "cpu_baseline": None,
     }

@@ -65,30 +65,41 @@ typedef struct pa_shape {
     int32_t block_size;         /* tokens per block: a power of two, 16 .. 4096 */
     int32_t max_blocks_per_seq; /* row length of block_tables, >= 1 */
     int32_t num_blocks;         /* blocks in the pool, >= 1 */
-    int32_t split_tokens;       /* context partition size in tokens (multiple of 16), 0 = auto */
+    int32_t split_tokens;       /* work item length in tokens (multiple of 16); 0 = balanced */
 } pa_shape;
 
 /*
- * Split plan the decode entry points will use for `shape`: the context of a
- * sequence is cut into ceil(context_len / split_tokens) partitions of
- * split_tokens tokens, at most *max_splits of them.  With *max_splits == 1 no
- * workspace is used and no reduction kernel runs.  Returns PA_OK or an error.
+ * How the work is split.  The contexts of all sequences, cut into 16-token
+ * tiles, form one list; each workgroup of the (persistent) grid processes
+ * "items" of that list.  With split_tokens == 0 the list is divided evenly
+ * among the workgroups the device holds at once (at least 4 tiles per item);
+ * otherwise items are split_tokens long.  A sequence that spans several items
+ * is computed in parts whose (max, sum, weighted values) are merged with
+ * log-sum-exp weights in a fixed order (the cross-split softmax reduction of a
+ * split-context decode), so results are reproducible run to run.  Which
+ * sequences are split depends only on the context lengths and the plan, never
+ * on the block tables.
+ * *split_tokens receives the item length (0 = balanced) and *max_splits the
+ * largest number of items a call can use.  Returns PA_OK or an error.
  */
 int paged_attn_plan(const pa_shape *shape, int32_t *split_tokens, int32_t *max_splits);
 
 /*
  * Device workspace (bytes) a decode call with `shape` needs: partial results
- * of every partition, fp32 [S, Hq, max_splits, head_dim] plus fp32
- * [S, Hq, max_splits, 2].  0 when there is a single partition.  Returns 0 on
- * an invalid shape as well; the decode call then reports the shape error.
+ * fp32 [ceil(units/4), S + max_splits, 4, min(G, 16), head_dim + 2] (units =
+ * Hkv * ceil(G / 16), G = Hq / Hkv), then int32 [S, 2] (the first and last
+ * item holding each sequence), each part rounded up to 256 bytes.  It does
+ * not depend on the device.  The contents need no initialisation; calls that
+ * may run concurrently must not share a workspace.  Returns 0 on an invalid
+ * shape; the decode call then reports the shape error.
  */
 size_t paged_attn_workspace_bytes(const pa_shape *shape);
 
 /*
  * bf16 KV cache decode.  `scale` is the softmax scale (1/sqrt(head_dim) for
  * standard attention).  `workspace` must hold paged_attn_workspace_bytes
- * bytes (it may be NULL when that is 0); it is scratch, overwritten by the
- * call, and must not be shared by calls that may run concurrently.
+ * bytes.  Two kernel launches on `stream`: the decode kernel, sized to the
+ * current device, and the merge of the sequences it split.
  */
 int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *block_tables, const int32_t *context_lens, float scale,

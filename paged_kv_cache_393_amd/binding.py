@@ -137,9 +137,12 @@ def _validate(q, k_cache, v_cache, block_tables, context_lens, kv_dtype):
         raise TypeError("block_tables and context_lens must be int32")
 
 
-def alloc_workspace(shape: PaShape, device) -> Optional[torch.Tensor]:
+def alloc_workspace(shape: PaShape, device) -> torch.Tensor:
+    """Scratch workspace for decode calls of `shape` (no initialisation needed)."""
     n = workspace_bytes(shape)
-    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+    if n <= 0:
+        raise PagedAttnError(PA_ERR_SHAPE, "no workspace size for this shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out=None,

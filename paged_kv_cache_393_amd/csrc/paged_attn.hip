@@ -9,33 +9,48 @@
 // "KV cache" page, section "PagedAttention 的算子").  The int8 variant
 // dequantizes code * per-(slot, kv head) scale (same ybb.press page, 6.1).
 //
-// Work decomposition.  One wave owns one (sequence, kv head, chunk of <= 16
-// query heads of the group, context partition) and streams the partition's
-// 16-token tiles with a private online-softmax state; a workgroup holds four
-// such waves for four kv heads of the same (sequence, partition), so the
-// token rows of a block (all kv heads side by side) are read together.  With
-// several partitions per sequence each wave writes an unnormalised partial
-// (acc, max, sum) and a reduction kernel merges them (log-sum-exp weights,
-// fixed partition order, so results are reproducible).
+// Work decomposition.  A "unit" is (kv head, chunk of <= 16 query heads of
+// its group); one wave serves one unit.  A workgroup holds four waves for four
+// consecutive units (a "unit group"), which read the same tokens: the kv
+// heads' rows of a token slot are adjacent in memory.  The context of every
+// sequence is cut into 16-token tiles, and the tiles of all sequences are laid
+// end to end (sequence-major) into one work list, the same for every unit
+// group.  The grid is persistent -- as many workgroups as the GPU holds at
+// once -- and each workgroup takes an equal share ("item") of the list, so
+// every compute unit streams about the same number of bytes whatever the mix
+// of context lengths.  An item may hold the tail of one sequence, whole
+// sequences and the head of another; each such piece is a run of tiles with a
+// private online-softmax state.  A piece that covers a whole sequence writes
+// the output directly.  Otherwise it stores an unnormalised partial (acc, max,
+// sum), and a second kernel merges the partials of each split sequence with
+// log-sum-exp weights, in a fixed order, so results are reproducible.  (The
+// kernel boundary is what makes the partials of all workgroups visible: the
+// L2 caches of the eight XCDs are not coherent with each other, and making
+// them so inside the kernel costs a full L2 write-back per partial.)
 //
-// Per tile and wave:
-//   * K: lane l loads 16 B of token l%16 (dims chosen so that the four lane
-//     groups cover complementary dims) -> the A operand of
-//     v_mfma_f32_16x16x16_bf16 with tokens as rows; the group's query heads
-//     (zero-padded to 16) are the B operand, loaded once.  The MFMA result
-//     gives lane l the scores of head l%16 for tokens 4*(l/16)..+3.
-//   * softmax: tile max over the 16 tokens (two xor-shuffles), running max and
-//     rescale factor, p = 2^(s*scale*log2e - m); p and the rescale factor go to
-//     a per-wave LDS slot.
-//   * V: lane l loads 16 B (8 dims) of one token per load, fully coalesced
-//     (head_dim/8 lanes per token row), converts to fp32 and accumulates
-//     p * v for every head of the chunk with fp32 FMAs (fp32 P, no bf16
-//     rounding of probabilities).
-//   * the next tile's K/V loads are issued before the current tile is
-//     processed (register double buffering).
+// Per 16-token tile and wave, on the matrix cores (v_mfma_f32_16x16x16_bf16):
+//   * S = K Q^T: K rows (tokens) are the A operand, loaded 16 B per lane
+//     (token l%16; the four lane groups take complementary dims); the unit's
+//     query heads (zero-padded to 16) are the B operand, loaded once per piece.
+//     Lane l gets the scores of head l%16 for tokens 4*(l/16)..+3.
+//   * online softmax in those registers: tile max over the 16 tokens (two
+//     xor-shuffles), running max, rescale factor, p = 2^(s*scale*log2e - m).
+//   * O^T += V^T P^T: the probabilities already sit in the B operand layout
+//     (token rows 4*(l/16).., head column l%16).  They are split into a bf16
+//     high part and a bf16 remainder (v_cvt_pk_bf16_f32, round to nearest
+//     even), two MFMAs per output block, which keeps the weights exact to
+//     2^-17 relative.  V is the A operand: lane l
+//     loads dims (l%16)*(D/16) .. +D/16-1 of tokens 4*(l/16)+i, so one load
+//     instruction reads four whole token rows, and a byte permute turns them
+//     into the operand of each output block (block j, row m = dim m*(D/16)+j).
+//     The fp32 accumulator then holds, in lane l, head l%16 and the
+//     4*(D/16) dims starting at 4*(D/16)*(l/16).
+//   * the loads of the next tiles are in flight while a tile is processed
+//     (register pipeline).
 // Rows of the last tile past the context end are slots of the same allocated
-// block; they are loaded with the tile but selected away (score -inf, V and
-// int8 V scale replaced by 0), so padding contents cannot reach the output.
+// block; the loads do not touch them (buffer range) and they are selected away
+// (score -inf, V and int8 V scale replaced by 0), so padding cannot reach the
+// output.
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -51,17 +66,30 @@ typedef short bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kTile = 16;           // tokens per tile (MFMA rows)
-constexpr int kWaves = 4;           // waves per workgroup
+// Tuning knobs (compile-time): tiles in flight per wave, and the minimum
+// number of waves per SIMD the register allocation must allow.
+#ifndef PA_STAGES
+#define PA_STAGES 3
+#endif
+#ifndef PA_WAVES_PER_EU
+#define PA_WAVES_PER_EU 2
+#endif
+
+constexpr int kTile = 16;           // tokens per tile (MFMA rows of S, k of PV)
+constexpr int kWaves = 4;           // waves (units) per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxChunkHeads = 16;  // query heads per workgroup (MFMA columns)
-constexpr int kMaxPartitionBlocks = 64;    // blocks one partition may span (one wave of ids)
+constexpr int kHeads = 16;          // query heads per unit (MFMA columns)
+constexpr int kWindow = 128;        // block ids held in registers (two per lane)
+constexpr int kMinItemTiles = 4;    // shortest balanced item
+constexpr int kMaxItems = 4096;     // balanced items per unit group (>= workgroups launched)
 constexpr float kLog2e = 1.4426950408889634f;
 // Word 3 of a raw (unformatted, stride 0) buffer resource on CDNA3/CDNA4.
 constexpr int kRsrcFlags = 0x00020000;
 
-struct DecodeParams {
+struct Params {
     const uint16_t *q;       // bf16 [S, Hq, D]
     const void *k;           // [NB, bs, Hkv, D] bf16 or int8
     const void *v;
@@ -70,46 +98,41 @@ struct DecodeParams {
     const int32_t *block_tables;
     const int32_t *context_lens;
     float *out;              // fp32 [S, Hq, D]
-    float *part_acc;         // fp32 [S, Hq, P, D]      (P > 1 only)
-    float *part_ml;          // fp32 [S, Hq, P, 2]
+    float *part;             // partial records (workspace)
+    int32_t *seg_items;      // [S, 2] first and last item holding each sequence (workspace)
     float scale_log2;        // softmax scale * log2(e)
+    int num_seqs;
     int num_q_heads;
     int num_kv_heads;
     int group;               // Hq / Hkv
-    int n_chunks;            // ceil(group / chunk heads)
+    int n_chunks;            // ceil(group / kHeads)
+    int units;               // Hkv * n_chunks
+    int rec_heads;           // min(group, kHeads): heads per partial record
     int max_blocks_per_seq;
+    int max_ctx;             // max_blocks_per_seq * block_size
     int log2_block_size;
-    int split_tokens;        // multiple of kTile
-    int max_splits;
-};
-
-struct ReduceParams {
-    const int32_t *context_lens;
-    const float *part_acc;
-    const float *part_ml;
-    float *out;
-    int num_q_heads;
-    int split_tokens;
-    int max_splits;
+    int item_tiles;          // > 0: fixed item length in tiles; 0: balanced
+    int max_pieces;          // partial records per (unit group, wave)
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Four signed bytes -> four bf16 (exact: |code| <= 128 has at most 8 significant bits).
-__device__ __forceinline__ bf16x4_t i8x4_to_bf16x4(uint32_t w) {
-    float f0 = (float)(int)(int8_t)(w & 0xffu);
-    float f1 = (float)(int)(int8_t)((w >> 8) & 0xffu);
-    float f2 = (float)(int)(int8_t)((w >> 16) & 0xffu);
-    float f3 = (float)(int)(int8_t)(w >> 24);
-    u32x2_t r;
-    r.x = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-    r.y = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
-    return __builtin_bit_cast(bf16x4_t, r);
-}
-
+// Signed byte b of w as float (exact).
 __device__ __forceinline__ float i8_at(uint32_t w, int b) {
     return (float)(int)(int8_t)((w >> (8 * b)) & 0xffu);
+}
+
+// Bits of the bf16 pair (x, y), x in the low half, from two floats whose low
+// 16 bits are zero or are to be dropped.
+__device__ __forceinline__ uint32_t pack_hi16(float x, float y) {
+    return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
+}
+
+// Four signed bytes -> four bf16 (exact: |code| <= 128 has at most 8 significant bits).
+__device__ __forceinline__ bf16x4_t i8x4_to_bf16x4(uint32_t w) {
+    return __builtin_bit_cast(bf16x4_t, u32x2_t{pack_hi16(i8_at(w, 0), i8_at(w, 1)),
+                                                pack_hi16(i8_at(w, 2), i8_at(w, 3))});
 }
 
 // Order this wave's LDS writes before its following LDS reads (other lanes'
@@ -120,18 +143,51 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1 (compile-time unrolled).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Tiles of a sequence in the work list; an empty context still takes one
+// (empty) tile, so that its output row is written.
+__device__ __forceinline__ int tiles_of(int ctx) { return ctx > 0 ? (ctx + kTile - 1) / kTile : 1; }
+
+// Items of the work list: either fixed-length (`fixed` tiles each) or an even
+// split of the T tiles into n items; item j covers tiles [lo(j), lo(j + 1)).
+struct Items {
+    int T;
+    int n;
+    int fixed;
+    __device__ __forceinline__ int lo(int j) const {
+        if (fixed) return (int)min((int64_t)j * fixed, (int64_t)T);
+        return (int)((int64_t)j * T / n);
+    }
+    // Index of the item holding tile x (0 <= x < T).  For the even split every
+    // item is non-empty (n <= T), so the estimate is off by at most one.
+    __device__ __forceinline__ int of(int x) const {
+        if (fixed) return x / fixed;
+        int c = (int)((int64_t)x * n / T);
+        if (c + 1 < n && lo(c + 1) <= x) ++c;
+        return c;
+    }
+};
+
 template <int D, bool INT8>
 struct Layout {
     static constexpr int kElem = INT8 ? 1 : 2;                 // bytes per cache element
     static constexpr int kKElemsPerLoad = 16 / kElem;          // K dims per 16-B load
     static constexpr int kKLoads = D / (4 * kKElemsPerLoad);   // 16-B K loads per lane per tile
-    static constexpr int kSteps = D / 16;                      // MFMA k-steps (4 dims x 4 groups)
+    static constexpr int kSteps = D / 16;                      // QK MFMA k-steps (4 dims x 4 groups)
     static constexpr int kStepsPerLoad = kKElemsPerLoad / 4;
-    static constexpr int kLanesPerRow = D / 8;                 // V: 8 dims per lane
-    static constexpr int kRows = 64 / kLanesPerRow;            // V tokens per load instruction
-    static constexpr int kVLoads = kTile / kRows;              // V loads per lane per tile
-    using VReg = typename std::conditional<INT8, u32x2_t, u32x4_t>::type;
-    // First dim of MFMA step `st` for lane group `lg`; the step covers 4 dims.
+    static constexpr int kDpl = D / 16;                        // V dims per lane and token = PV blocks
+    static constexpr int kVBytes = kDpl * kElem;               // 16, 8 or 4
+    using VReg = typename std::conditional<
+        kVBytes == 16, u32x4_t, typename std::conditional<kVBytes == 8, u32x2_t, uint32_t>::type>::type;
+    // First dim of QK step `st` for lane group `lg`; the step covers 4 dims.
     __device__ static constexpr int step_dim(int st, int lg) {
         return (st / kStepsPerLoad) * 4 * kKElemsPerLoad + kKElemsPerLoad * lg +
                4 * (st % kStepsPerLoad);
@@ -142,367 +198,502 @@ template <int D, bool INT8>
 struct TileRegs {
     using L = Layout<D, INT8>;
     u32x4_t k[L::kKLoads];
-    typename L::VReg v[L::kVLoads];
-    float ks;   // int8: K scale of token row l%16 (every lane group holds the same)
-    float vs;   // int8: V scale of token row l%16
+    typename L::VReg v[4];   // token rows 4*(l/16) + i
+    float ks;                // int8: K scale of token row l%16
+    float vs;                // int8: V scale of token row l%16
 };
 
-template <int D, int GT, bool INT8>
-__global__ __launch_bounds__(kThreads) void pa_decode_kernel(const DecodeParams p) {
+// 32-bit word w of a V register.
+template <typename VR>
+__device__ __forceinline__ uint32_t vword(const VR &r, int w) {
+    if constexpr (std::is_same<VR, uint32_t>::value) return r;
+    else return r[w];
+}
+
+// A operand of PV block j: element j of the four token rows, as bf16x4.
+template <int D, bool INT8>
+__device__ __forceinline__ bf16x4_t v_operand(const typename Layout<D, INT8>::VReg (&v)[4], int j) {
+    u32x2_t r;
+    if constexpr (INT8) {
+        const int w = j >> 2, b = j & 3;
+        r.x = pack_hi16(i8_at(vword(v[0], w), b), i8_at(vword(v[1], w), b));
+        r.y = pack_hi16(i8_at(vword(v[2], w), b), i8_at(vword(v[3], w), b));
+    } else {
+        const int w = j >> 1;
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        r.x = __builtin_amdgcn_perm(vword(v[1], w), vword(v[0], w), sel);
+        r.y = __builtin_amdgcn_perm(vword(v[3], w), vword(v[2], w), sel);
+    }
+    return __builtin_bit_cast(bf16x4_t, r);
+}
+
+template <int D, bool INT8>
+__global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(const Params p) {
     using L = Layout<D, INT8>;
-    static_assert(GT >= 1 && GT <= kMaxChunkHeads, "chunk heads");
-    static_assert(L::kKLoads >= 1 && L::kVLoads >= 1, "head_dim");
+    constexpr int kDpl = L::kDpl;
+    static_assert(L::kKLoads >= 1, "head_dim");
 
-    __shared__ __attribute__((aligned(16))) float lds_p[kWaves][GT][kTile];
-    __shared__ float lds_alpha[kWaves][GT];
+    __shared__ int lds_red[kWaves];
+    __shared__ int lds_found[2];
     __shared__ __attribute__((aligned(16))) float lds_sc[kWaves][2 * kTile];
-    __shared__ float lds_ml[kWaves][2][GT];
 
-    // Grid: x = group of kWaves (kv head, head chunk) units, y = partition,
-    // z = sequence.  Each wave owns one unit and streams the whole partition,
-    // so the waves of a workgroup read the same blocks' token rows (their kv
-    // heads side by side) at about the same time.
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
-    const int unit = blockIdx.x * kWaves + wave;
-    const int Hkv = p.num_kv_heads;
-    if (unit >= Hkv * p.n_chunks) return;            // whole wave; no workgroup barrier follows
-    const int g = unit / p.n_chunks;
-    const int chunk = unit - g * p.n_chunks;
-    const int split = blockIdx.y;
-    const int s = blockIdx.z;
-    const int ctx = p.context_lens[s];
-    const int t_begin = split * p.split_tokens;
-    const bool single = p.max_splits == 1;
-    if (!single && t_begin >= ctx) return;           // empty partition; the reduction skips it
-    const int t_end = min(ctx, t_begin + p.split_tokens);
-    const int n_tiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
-
-    const int Hq = p.num_q_heads;
-    const int h_base = g * p.group + chunk * GT;
-    const int n_heads = min(GT, p.group - chunk * GT);
-
     const int lane = threadIdx.x & 63;
-    const int lg = lane >> 4;      // lane group (MFMA k group / score rows)
-    const int l16 = lane & 15;     // token row of K, head column of Q and scores
-    const int vr = lane / L::kLanesPerRow;   // V token row
-    const int vc = lane % L::kLanesPerRow;   // V 8-dim column
+    const int lg = lane >> 4;      // lane group: score rows / PV k rows
+    const int l16 = lane & 15;     // K token row, head column
+    const int S = p.num_seqs;
+    const int ug = blockIdx.y;                    // unit group
+    const int unit = ug * kWaves + wave;          // this wave's unit
+    const bool active = unit < p.units;
+    // Context length as used here: clamped to what the table row can address.
+    auto ctx_of = [&](int s) __attribute__((always_inline)) {
+        return min(max(p.context_lens[s], 0), p.max_ctx);
+    };
 
+    // ---- Work list length (the host checked that it fits in int). ----
+    int local = 0;
+    for (int s = threadIdx.x; s < S; s += kThreads) local += tiles_of(ctx_of(s));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) local += __shfl_xor(local, off);
+    if (lane == 0) lds_red[wave] = local;
+    __syncthreads();
+    Items items;
+    items.T = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) items.T += lds_red[w];
+    __syncthreads();
+    items.fixed = p.item_tiles;
+    items.n = p.item_tiles ? (items.T + p.item_tiles - 1) / p.item_tiles
+                           : min((int)gridDim.x, (items.T + kMinItemTiles - 1) / kMinItemTiles);
+
+    // Unit constants.
+    const int g = active ? unit / p.n_chunks : 0;
+    const int chunk = active ? unit - g * p.n_chunks : 0;
+    const int h_base = g * p.group + chunk * kHeads;
+    const int n_heads = min(kHeads, p.group - chunk * kHeads);
+    const int Hq = p.num_q_heads;
+    const int Hkv = p.num_kv_heads;
     const int bs_log2 = p.log2_block_size;
     const int bs_mask = (1 << bs_log2) - 1;
     const int64_t row_bytes = (int64_t)Hkv * D * L::kElem;   // one token slot, all kv heads
+    const uint32_t rb32 = (uint32_t)row_bytes;
     const char *kbase = (const char *)p.k + (int64_t)g * D * L::kElem;
     const char *vbase = (const char *)p.v + (int64_t)g * D * L::kElem;
-    const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+    const size_t rec_floats = (size_t)p.rec_heads * (D + 2);
+    float *rec_base = p.part + ((size_t)ug * p.max_pieces * kWaves + wave) * rec_floats;
+    const size_t rec_stride = (size_t)kWaves * rec_floats;   // between pieces
+    const bool live = l16 < n_heads;                          // lane's head column is real
+    const int dim0 = lg * 4 * kDpl;   // first of this lane's 4*kDpl output dims
 
-    // Query operand (B of the MFMA): head l16 of the chunk, zero for padding heads.
-    bf16x4_t qop[L::kSteps];
-    {
-        const bool live = l16 < n_heads;
-        const uint16_t *qrow = p.q + ((int64_t)s * Hq + h_base + (live ? l16 : 0)) * D;
-#pragma unroll
-        for (int st = 0; st < L::kSteps; ++st) {
-            u32x2_t w = *(const u32x2_t *)(qrow + L::step_dim(st, lg));
-            if (!live) w = u32x2_t{0u, 0u};
-            qop[st] = __builtin_bit_cast(bf16x4_t, w);
-        }
-    }
-
-    // Block ids of this partition as a register window: lane i holds table
-    // entry blk_first + i (a partition spans at most 64 blocks), loaded once
-    // before the tile loop; a tile's id is then read with readlane, so the loop
-    // itself makes no dependent memory access.
-    const int blk_first = t_begin >> bs_log2;
-    const int blk_last = t_end > t_begin ? ((t_end - 1) >> bs_log2) + 1 : blk_first;
-    const int win = (lane < blk_last - blk_first) ? table[blk_first + lane] : 0;
-
-    // Token-slot index phys * block_size + slot of the first token of tile `tile` (uniform).
-    auto tile_slot = [&](int tile) __attribute__((always_inline)) -> int64_t {
-        const int t0 = t_begin + tile * kTile;
-        const int phys = __builtin_amdgcn_readlane(win, (t0 >> bs_log2) - blk_first);
-        return ((int64_t)phys << bs_log2) + (t0 & bs_mask);
-    };
-
-    // Tile loads are raw buffer loads: a uniform buffer resource per tile whose
-    // range is the tile's valid rows, plus per-lane byte offsets that are fixed
-    // for the whole loop -- no per-tile vector address arithmetic.  A tile never
-    // crosses a block (block_size is a multiple of 16).  Rows at or past the
-    // context end fall outside the resource's range: the hardware returns 0 for
-    // them without touching memory, and they are also selected away below
-    // (score -inf, V and int8 V scale 0), so padding cannot reach the output.
-    const uint32_t rb32 = (uint32_t)row_bytes;
+    // Per-lane byte offsets of a tile's loads, fixed for the whole kernel.
     const int k_off = (int)((uint32_t)l16 * rb32 + (uint32_t)(L::step_dim(0, lg) * L::kElem));
-    int v_off[L::kVLoads];
+    int v_off[4];
 #pragma unroll
-    for (int j = 0; j < L::kVLoads; ++j)
-        v_off[j] = (int)((uint32_t)(vr * L::kVLoads + j) * rb32 + (uint32_t)(vc * 8 * L::kElem));
+    for (int i = 0; i < 4; ++i)
+        v_off[i] = (int)((uint32_t)(4 * lg + i) * rb32 + (uint32_t)(l16 * L::kVBytes));
     const int s_off = (int)(((uint32_t)l16 * (uint32_t)Hkv + (uint32_t)g) * 4u);
 
-    auto load_tile = [&](TileRegs<D, INT8> &r, int tile) __attribute__((always_inline)) {
-        const int64_t slot0 = tile_slot(tile);
-        const int rows = min(kTile, t_end - (t_begin + tile * kTile));
-        const int range = rows * (int)rb32;
-        const __amdgpu_buffer_rsrc_t kr =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + slot0 * row_bytes), 0, range, kRsrcFlags);
-        const __amdgpu_buffer_rsrc_t vrs =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + slot0 * row_bytes), 0, range, kRsrcFlags);
+    // One piece: tiles [ta, tb) of sequence s for this wave's unit.  Items
+    // `first` .. `last` are those that hold the sequence; `item` holds this piece.
+    auto process = [&](int s, int ctx, int ta, int tb, int first, int last, int item)
+        __attribute__((always_inline)) {
+        const int64_t row0 = (int64_t)s * Hq + h_base;   // output row of head column 0
+        if (ctx == 0) {   // empty context: the output row is zero (always one whole piece)
+            if (live) {
+                float *dst = p.out + (row0 + l16) * D + dim0;
 #pragma unroll
-        for (int m = 0; m < L::kKLoads; ++m)
-            r.k[m] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                         kr, k_off + m * 4 * L::kKElemsPerLoad * L::kElem, 0, 0));
-#pragma unroll
-        for (int j = 0; j < L::kVLoads; ++j) {
-            if constexpr (INT8)
-                r.v[j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(vrs, v_off[j], 0, 0));
-            else
-                r.v[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_off[j], 0, 0));
-        }
-        if constexpr (INT8) {
-            const int srange = rows * Hkv * 4;
-            const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(p.k_scales + slot0 * Hkv), 0, srange, kRsrcFlags);
-            const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(p.v_scales + slot0 * Hkv), 0, srange, kRsrcFlags);
-            r.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksr, s_off, 0, 0));
-            r.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsr, s_off, 0, 0));
-        }
-    };
-
-    // Online-softmax state of this wave.  Score lanes: head l16, rows 4*lg..4*lg+3.
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    float acc[GT][8];
-#pragma unroll
-    for (int h = 0; h < GT; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-
-    auto compute_tile = [&](const TileRegs<D, INT8> &r, int tile) __attribute__((always_inline)) {
-        const int t0 = t_begin + tile * kTile;
-        wave_lds_sync();
-        if constexpr (INT8) {
-            if (lane < kTile) lds_sc[wave][lane] = r.ks;
-            else if (lane < 2 * kTile) lds_sc[wave][lane] = r.vs;
-        }
-        // S = K Q^T on the matrix cores: rows = tokens, columns = heads.
-        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < L::kSteps; ++st) {
-            const int m = st / L::kStepsPerLoad;
-            const int sub = st % L::kStepsPerLoad;
-            bf16x4_t a;
-            if constexpr (INT8) {
-                a = i8x4_to_bf16x4(r.k[m][sub]);
-            } else {
-                u32x2_t w = sub == 0 ? u32x2_t{r.k[m].x, r.k[m].y} : u32x2_t{r.k[m].z, r.k[m].w};
-                a = __builtin_bit_cast(bf16x4_t, w);
+                for (int e = 0; e < 4 * kDpl; e += 4) *(f32x4_t *)(dst + e) = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
-            sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, qop[st], sacc, 0, 0, 0);
+            return;
         }
-        float ks[4] = {1.f, 1.f, 1.f, 1.f}, vsc[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (INT8) {
-            wave_lds_sync();
-            f32x4_t kv4 = *(const f32x4_t *)&lds_sc[wave][4 * lg];
-            f32x4_t vv4 = *(const f32x4_t *)&lds_sc[wave][kTile + 4 * lg];
-            ks[0] = kv4.x; ks[1] = kv4.y; ks[2] = kv4.z; ks[3] = kv4.w;
-            vsc[0] = vv4.x; vsc[1] = vv4.y; vsc[2] = vv4.z; vsc[3] = vv4.w;
-        }
-        float sc[4];
+        const int t_begin = ta * kTile;
+        const int t_end = min(ctx, tb * kTile);
+        const int n_tiles = tb - ta;
+
+        // Query operand (B of S = K Q^T): head l16 of the unit, zero for padding heads.
+        bf16x4_t qop[L::kSteps];
+        {
+            const uint16_t *qrow = p.q + (row0 + (live ? l16 : 0)) * D;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float x = sacc[i] * (INT8 ? p.scale_log2 * ks[i] : p.scale_log2);
-            sc[i] = (t0 + 4 * lg + i < t_end) ? x : -INFINITY;
+            for (int st = 0; st < L::kSteps; ++st) {
+                u32x2_t w = *(const u32x2_t *)(qrow + L::step_dim(st, lg));
+                if (!live) w = u32x2_t{0u, 0u};
+                qop[st] = __builtin_bit_cast(bf16x4_t, w);
+            }
         }
-        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);              // finite: a tile has a valid token
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        float pr[4];
-        float psum = 0.f;
+
+        // Block ids of the piece as a register window of kWindow entries (lane
+        // i holds ids win_first + i and win_first + 64 + i), refilled when a
+        // tile leaves it, so the tile loop makes no dependent memory access
+        // unless a piece spans more than kWindow blocks.
+        const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+        const int blk_end = ((t_end - 1) >> bs_log2) + 1;
+        int win_first = t_begin >> bs_log2;
+        int win0 = 0, win1 = 0;
+        auto fill_window = [&]() __attribute__((always_inline)) {
+            win0 = (win_first + lane < blk_end) ? table[win_first + lane] : 0;
+            win1 = (win_first + 64 + lane < blk_end) ? table[win_first + 64 + lane] : 0;
+        };
+        fill_window();
+        // Token-slot index phys * block_size + slot of the first token of tile `tile` (uniform).
+        auto tile_slot = [&](int tile) __attribute__((always_inline)) -> int64_t {
+            const int t0 = t_begin + tile * kTile;
+            const int blk = t0 >> bs_log2;
+            if (blk - win_first >= kWindow) {
+                win_first = blk;
+                fill_window();
+            }
+            const int idx = blk - win_first;
+            const int phys = idx < 64 ? __builtin_amdgcn_readlane(win0, idx)
+                                      : __builtin_amdgcn_readlane(win1, idx - 64);
+            return ((int64_t)phys << bs_log2) + (t0 & bs_mask);
+        };
+
+        // Tile loads are raw buffer loads: a uniform buffer resource per tile
+        // whose range is the tile's valid rows, plus the fixed per-lane offsets.
+        // A tile never crosses a block (block_size is a multiple of 16); rows
+        // at or past the context end fall outside the range and read as 0
+        // without touching memory.
+        auto load_tile = [&](TileRegs<D, INT8> &r, int tile) __attribute__((always_inline)) {
+            const int64_t slot0 = tile_slot(tile);
+            const int rows = min(kTile, t_end - (t_begin + tile * kTile));
+            const int range = rows * (int)rb32;
+            const __amdgpu_buffer_rsrc_t kr =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + slot0 * row_bytes), 0, range, kRsrcFlags);
+            const __amdgpu_buffer_rsrc_t vr =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + slot0 * row_bytes), 0, range, kRsrcFlags);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
-            psum += pr[i];
+            for (int m = 0; m < L::kKLoads; ++m)
+                r.k[m] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                             kr, k_off + m * 4 * L::kKElemsPerLoad * L::kElem, 0, 0));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (L::kVBytes == 16)
+                    r.v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vr, v_off[i], 0, 0));
+                else if constexpr (L::kVBytes == 8)
+                    r.v[i] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(vr, v_off[i], 0, 0));
+                else
+                    r.v[i] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_off[i], 0, 0);
+            }
+            if constexpr (INT8) {
+                const int srange = rows * Hkv * 4;
+                const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(p.k_scales + slot0 * Hkv), 0, srange, kRsrcFlags);
+                const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(p.v_scales + slot0 * Hkv), 0, srange, kRsrcFlags);
+                r.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksr, s_off, 0, 0));
+                r.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsr, s_off, 0, 0));
+            }
+        };
+
+        // Online-softmax state of head l16 (the same in the four lane groups)
+        // and the PV accumulator: block j, element i = dim kDpl*(4*lg+i)+j.
+        float m_run = -INFINITY;
+        float l_run = 0.f;   // this lane's share (its four token rows)
+        f32x4_t acc[kDpl];
+#pragma unroll
+        for (int j = 0; j < kDpl; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        auto compute_tile = [&](TileRegs<D, INT8> &r, int tile) __attribute__((always_inline)) {
+            const int t0 = t_begin + tile * kTile;
+            if constexpr (INT8) {
+                wave_lds_sync();
+                if (lane < kTile) lds_sc[wave][lane] = r.ks;
+                else if (lane < 2 * kTile) lds_sc[wave][lane] = r.vs;
+            }
+            // S = K Q^T: rows = tokens, columns = heads.
+            f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < L::kSteps; ++st) {
+                const int m = st / L::kStepsPerLoad;
+                const int sub = st % L::kStepsPerLoad;
+                bf16x4_t a;
+                if constexpr (INT8) {
+                    a = i8x4_to_bf16x4(r.k[m][sub]);
+                } else {
+                    u32x2_t w = sub == 0 ? u32x2_t{r.k[m].x, r.k[m].y} : u32x2_t{r.k[m].z, r.k[m].w};
+                    a = __builtin_bit_cast(bf16x4_t, w);
+                }
+                sacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, qop[st], sacc, 0, 0, 0);
+            }
+            float ks[4] = {1.f, 1.f, 1.f, 1.f}, vsc[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (INT8) {
+                wave_lds_sync();
+                f32x4_t kv4 = *(const f32x4_t *)&lds_sc[wave][4 * lg];
+                f32x4_t vv4 = *(const f32x4_t *)&lds_sc[wave][kTile + 4 * lg];
+                ks[0] = kv4.x; ks[1] = kv4.y; ks[2] = kv4.z; ks[3] = kv4.w;
+                vsc[0] = vv4.x; vsc[1] = vv4.y; vsc[2] = vv4.z; vsc[3] = vv4.w;
+            }
+            bool valid[4];
+            float sc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                valid[i] = t0 + 4 * lg + i < t_end;
+                const float x = sacc[i] * (INT8 ? p.scale_log2 * ks[i] : p.scale_log2);
+                sc[i] = valid[i] ? x : -INFINITY;
+            }
+            float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx);              // finite: a tile has a valid token
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            float pr[4];
+            float psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);   // 0 for masked rows
+                psum += pr[i];
+            }
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+            if (__ballot(alpha != 1.f)) {   // the running max moved for some head
+#pragma unroll
+                for (int j = 0; j < kDpl; ++j) acc[j] *= alpha;
+            }
+            // B operand of PV: the weights (times the int8 V scale) as a bf16
+            // high part plus a bf16 remainder, both rounded to nearest even:
+            // hi + lo equals the fp32 weight to within 2^-17 relative.
+            f32x2_t w01, w23;
+            if constexpr (INT8) {
+                w01 = f32x2_t{valid[0] ? pr[0] * vsc[0] : 0.f, valid[1] ? pr[1] * vsc[1] : 0.f};
+                w23 = f32x2_t{valid[2] ? pr[2] * vsc[2] : 0.f, valid[3] ? pr[3] * vsc[3] : 0.f};
+            } else {
+                w01 = f32x2_t{pr[0], pr[1]};
+                w23 = f32x2_t{pr[2], pr[3]};
+            }
+            const uint32_t h01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(w01, bf16x2_t));
+            const uint32_t h23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(w23, bf16x2_t));
+            const f32x2_t r01 = w01 - f32x2_t{bf16_lo(h01), bf16_hi(h01)};
+            const f32x2_t r23 = w23 - f32x2_t{bf16_lo(h23), bf16_hi(h23)};
+            const bf16x4_t bhi = __builtin_bit_cast(bf16x4_t, u32x2_t{h01, h23});
+            const bf16x4_t blo = __builtin_bit_cast(
+                bf16x4_t, u32x2_t{__builtin_bit_cast(uint32_t, __builtin_convertvector(r01, bf16x2_t)),
+                                  __builtin_bit_cast(uint32_t, __builtin_convertvector(r23, bf16x2_t))});
+            // Rows past the context end (last tile only) are replaced by zeros.
+            if (t_end - t0 < kTile) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!valid[i]) r.v[i] = typename L::VReg{};
+            }
+#pragma unroll
+            for (int j = 0; j < kDpl; ++j) {
+                const bf16x4_t a = v_operand<D, INT8>(r.v, j);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bhi, acc[j], 0, 0, 0);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, blo, acc[j], 0, 0, 0);
+            }
+        };
+
+        // Register pipeline of kStages tile buffers: while the wave processes
+        // one tile, the loads of its next kStages-1 tiles are in flight.  The
+        // scheduling barriers keep each prefetch issued before the processing
+        // of the current tile starts.  The loop runs whole rounds of kStages
+        // tiles (one back edge, no early exit), so the set of pending loads at
+        // its head is the same on entry and on every iteration; the last
+        // 0..kStages-1 tiles, already in flight, are processed after it.
+        // Prefetches past the end re-load the last tile (a cache hit), which
+        // keeps every load unconditional.
+        constexpr int kStages = PA_STAGES;
+        static_assert(kStages >= 2 && kStages <= 6, "pipeline depth");
+        {
+            TileRegs<D, INT8> buf[kStages];
+            auto tile_of = [&](int k) __attribute__((always_inline)) { return min(k, n_tiles - 1); };
+            static_for<0, kStages - 1>([&](auto I) __attribute__((always_inline)) {
+                load_tile(buf[decltype(I)::value], tile_of(decltype(I)::value));
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            const int rounds = n_tiles / kStages;
+            for (int rd = 0; rd < rounds; ++rd) {
+                // Step i: prefetch tile k + kStages - 1 into the buffer the
+                // previous step freed, then process tile k = rd * kStages + i.
+                static_for<0, kStages>([&](auto I) __attribute__((always_inline)) {
+                    constexpr int i = decltype(I)::value;
+                    const int k = rd * kStages + i;
+                    load_tile(buf[(i + kStages - 1) % kStages], tile_of(k + kStages - 1));
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute_tile(buf[i], k);
+                });
+            }
+            const int rem = n_tiles - rounds * kStages;
+            static_for<0, kStages - 1>([&](auto I) __attribute__((always_inline)) {
+                constexpr int i = decltype(I)::value;
+                if (rem > i) compute_tile(buf[i], rounds * kStages + i);
+            });
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (l16 < GT) {
-            // Masked rows: p is exactly 0, and an int8 V scale there may be anything.
-            f32x4_t pw;
+
+        // The four lane groups hold partial sums over different token rows.
+        l_run += __shfl_xor(l_run, 16);
+        l_run += __shfl_xor(l_run, 32);
+        if (first == last) {   // the piece is the whole sequence: final output
+            if (live) {
+                const float inv = 1.f / l_run;
+                float *dst = p.out + (row0 + l16) * D + dim0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < kDpl; j += 4)
+                        *(f32x4_t *)(dst + i * kDpl + j) =
+                            f32x4_t{acc[j][i] * inv, acc[j + 1][i] * inv, acc[j + 2][i] * inv,
+                                    acc[j + 3][i] * inv};
+            }
+            return;
+        }
+        // Partial record of piece s + item: acc [rec_heads][D], then the
+        // running max [rec_heads], then the sum [rec_heads].
+        float *rec = rec_base + (size_t)(s + item) * rec_stride;
+        if (live) {
+            float *dst = rec + l16 * D + dim0;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                pw[i] = INT8 ? (sc[i] == -INFINITY ? 0.f : pr[i] * vsc[i]) : pr[i];
-            *(f32x4_t *)&lds_p[wave][l16][4 * lg] = pw;
-            if (lg == 0) lds_alpha[wave][l16] = alpha;
-        }
-        wave_lds_sync();
-        // O += P V with fp32 FMAs; this lane owns dims 8*vc..8*vc+7 of token rows vr*kVLoads+j.
-        float pw[GT][L::kVLoads];
 #pragma unroll
-        for (int h = 0; h < GT; ++h) {
-            const float a = lds_alpha[wave][h];
-#pragma unroll
-            for (int j = 0; j < L::kVLoads; ++j) pw[h][j] = lds_p[wave][h][vr * L::kVLoads + j];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] *= a;
-        }
-        // Rows past the context end (last tile only) are replaced by zeros.
-        const int last_row = t_end - 1 - t0;                 // uniform
-        const bool partial = last_row < kTile - 1;
-#pragma unroll
-        for (int j = 0; j < L::kVLoads; ++j) {
-            typename L::VReg vr_j = r.v[j];
-            if (partial && vr * L::kVLoads + j > last_row) vr_j = typename L::VReg{};
-            float vf[8];
-            if constexpr (INT8) {
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    vf[b] = i8_at(vr_j.x, b);
-                    vf[4 + b] = i8_at(vr_j.y, b);
-                }
-            } else {
-                vf[0] = bf16_lo(vr_j.x); vf[1] = bf16_hi(vr_j.x);
-                vf[2] = bf16_lo(vr_j.y); vf[3] = bf16_hi(vr_j.y);
-                vf[4] = bf16_lo(vr_j.z); vf[5] = bf16_hi(vr_j.z);
-                vf[6] = bf16_lo(vr_j.w); vf[7] = bf16_hi(vr_j.w);
+                for (int j = 0; j < kDpl; j += 4)
+                    *(f32x4_t *)(dst + i * kDpl + j) =
+                        f32x4_t{acc[j][i], acc[j + 1][i], acc[j + 2][i], acc[j + 3][i]};
+            if (lg == 0) {
+                rec[p.rec_heads * D + l16] = m_run;
+                rec[p.rec_heads * D + p.rec_heads + l16] = l_run;
             }
-#pragma unroll
-            for (int h = 0; h < GT; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw[h][j], vf[e], acc[h][e]);
         }
     };
 
-    // Register pipeline of kStages tile buffers: while the wave processes one
-    // tile, the loads of its next kStages-1 tiles are in flight.  The scheduling
-    // barriers keep each prefetch issued before the processing of the current
-    // tile starts.  The loop runs whole rounds of kStages tiles (one back edge,
-    // no early exit), so the set of pending loads at its head is the same on
-    // entry and on every iteration; the last 0..kStages-1 tiles, already in
-    // flight, are processed after it.  Prefetches past the end re-load the last
-    // tile (a cache hit), which keeps every load unconditional.
-    constexpr int kStages = 3;
-    if (n_tiles > 0) {
-        TileRegs<D, INT8> buf[kStages];
-        auto tile_of = [&](int k) __attribute__((always_inline)) { return min(k, n_tiles - 1); };
-        // One pipeline step on buffer I (a compile-time index): prefetch tile
-        // k + kStages - 1 into the buffer freed by the previous step, then
-        // process tile k.
-        auto step = [&](auto I, int k) __attribute__((always_inline)) {
-            constexpr int i = decltype(I)::value;
-            load_tile(buf[(i + kStages - 1) % kStages], tile_of(k + kStages - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            compute_tile(buf[i], k);
-        };
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
-        static_assert(kStages == 3, "three explicit steps below");
-        load_tile(buf[0], tile_of(0));
-        __builtin_amdgcn_sched_barrier(0);
-        load_tile(buf[1], tile_of(1));
-        __builtin_amdgcn_sched_barrier(0);
-        const int rounds = n_tiles / kStages;
-        for (int rd = 0; rd < rounds; ++rd) {
-            step(I0{}, rd * kStages);
-            step(I1{}, rd * kStages + 1);
-            step(I2{}, rd * kStages + 2);
-        }
-        const int rem = n_tiles - rounds * kStages;
-        if (rem > 0) compute_tile(buf[0], rounds * kStages);
-        if (rem > 1) compute_tile(buf[1], rounds * kStages + 1);
-    }
-
-    // Finish inside the wave: the four score-lane groups hold partial sums, the
-    // V token rows hold partial accumulators over different tokens.
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    // ---- Items of this workgroup (at most one when balanced). ----
+    for (int item = blockIdx.x; item < items.n; item += gridDim.x) {
+        const int lo = items.lo(item);
+        const int hi = items.lo(item + 1);
+        // Find the sequence holding tile `lo`: running inclusive scan of the
+        // per-sequence tile counts, one chunk of kThreads sequences at a time.
+        int base = 0;
+        for (int c0 = 0;; c0 += kThreads) {
+            const int s = c0 + threadIdx.x;
+            const int n = s < S ? tiles_of(ctx_of(s)) : 0;
+            int incl = n;
 #pragma unroll
-    for (int off = L::kLanesPerRow; off < 64; off <<= 1)
-#pragma unroll
-        for (int h = 0; h < GT; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
-    wave_lds_sync();
-    if (lane < GT) {
-        lds_ml[wave][0][lane] = m_run;
-        lds_ml[wave][1][lane] = l_run;
-    }
-    wave_lds_sync();
-    if (vr == 0) {
-#pragma unroll
-        for (int h = 0; h < GT; ++h) {
-            if (h >= n_heads) continue;                      // uniform; keeps the loop unrollable
-            const int64_t row = (int64_t)s * Hq + h_base + h;
-            const float lsum = lds_ml[wave][1][h];
-            f32x4_t o0, o1;
-            if (single) {
-                const float inv = lsum > 0.f ? 1.f / lsum : 0.f;   // lsum == 0 only for ctx == 0
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    o0[e] = acc[h][e] * inv;
-                    o1[e] = acc[h][4 + e] * inv;
-                }
-                float *dst = p.out + row * D + vc * 8;
-                *(f32x4_t *)dst = o0;
-                *(f32x4_t *)(dst + 4) = o1;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    o0[e] = acc[h][e];
-                    o1[e] = acc[h][4 + e];
-                }
-                const int64_t pr = row * p.max_splits + split;
-                float *dst = p.part_acc + pr * D + vc * 8;
-                *(f32x4_t *)dst = o0;
-                *(f32x4_t *)(dst + 4) = o1;
-                if (vc == 0) {
-                    p.part_ml[2 * pr] = lds_ml[wave][0][h];
-                    p.part_ml[2 * pr + 1] = lsum;
-                }
+            for (int off = 1; off < 64; off <<= 1) {
+                const int t = __shfl_up(incl, off);
+                if (lane >= off) incl += t;
             }
+            if (lane == 63) lds_red[wave] = incl;
+            __syncthreads();
+            int before = base, chunk_total = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                before += w < wave ? lds_red[w] : 0;
+                chunk_total += lds_red[w];
+            }
+            incl += before;
+            if (s < S && incl - n <= lo && lo < incl) {
+                lds_found[0] = s;
+                lds_found[1] = incl - n;
+            }
+            __syncthreads();
+            base += chunk_total;
+            if (base > lo) break;   // uniform: every thread has the same base
+            __syncthreads();        // lds_red is rewritten by the next chunk
+        }
+        int s = lds_found[0];
+        int seg = lds_found[1];     // first tile of sequence s in the list
+        __syncthreads();            // lds_found may be rewritten by the next item
+        if (!active) continue;
+        for (int x = lo; x < hi; ++s) {
+            const int ctx = ctx_of(s);
+            const int nt = tiles_of(ctx);
+            const int end = min(hi, seg + nt);
+            const int first = items.of(seg), last = items.of(seg + nt - 1);
+            if (x == seg && unit == 0 && lane == 0) {   // the piece that starts the sequence
+                p.seg_items[2 * s] = first;
+                p.seg_items[2 * s + 1] = last;
+            }
+            process(s, ctx, x - seg, end - seg, first, last, item);
+            x = end;
+            seg += nt;
         }
     }
 }
 
-// Merge the partitions of one (sequence, query head): weights 2^(m_p - M) l_p,
-// partitions visited in index order.
+struct MergeParams {
+    const float *part;
+    const int32_t *seg_items;
+    float *out;
+    int num_q_heads;
+    int group;
+    int n_chunks;
+    int rec_heads;
+    int max_pieces;
+};
+
+// Merge the partial records of one (sequence, query head) row whose sequence
+// was split over several items: M = max_p m_p, w_p = 2^(m_p - M),
+// out = sum_p w_p acc_p / sum_p w_p l_p.  Wave w takes pieces w, w + 4, ...
+// in index order; the four wave results are then combined in wave order, so
+// the result does not depend on timing.
 template <int D>
-__global__ __launch_bounds__(64) void pa_reduce_kernel(const ReduceParams p) {
-    constexpr int kPer = D / 64;
-    const int row = blockIdx.x;                 // s * Hq + h
+__global__ __launch_bounds__(kThreads) void pa_merge_kernel(const MergeParams p) {
+    constexpr int kPer = D / 64;   // dims per lane
+    __shared__ float lds_m[kWaves], lds_l[kWaves];
+    __shared__ __attribute__((aligned(16))) float lds_acc[kWaves][D];
+    const int row = blockIdx.x;    // s * Hq + h
     const int s = row / p.num_q_heads;
-    const int lane = threadIdx.x;
-    const int ctx = p.context_lens[s];
-    const int n = (ctx + p.split_tokens - 1) / p.split_tokens;
-    const float *ml = p.part_ml + (int64_t)row * p.max_splits * 2;
-    const float *pa = p.part_acc + (int64_t)row * p.max_splits * D;
+    const int h = row - s * p.num_q_heads;
+    const int first = p.seg_items[2 * s], last = p.seg_items[2 * s + 1];
+    if (first == last) return;     // whole sequence: written by the decode kernel
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int g = h / p.group, hg = h - g * p.group;
+    const int unit = g * p.n_chunks + hg / kHeads;
+    const int hh = hg % kHeads;
+    const size_t rec_floats = (size_t)p.rec_heads * (D + 2);
+    const float *rec0 = p.part + ((size_t)(unit / kWaves) * p.max_pieces * kWaves + unit % kWaves) * rec_floats;
+    const size_t stride = (size_t)kWaves * rec_floats;
+    const int m_off = p.rec_heads * D + hh, l_off = p.rec_heads * D + p.rec_heads + hh;
+    const int a_off = hh * D + lane * kPer;
     float M = -INFINITY;
-    for (int i = 0; i < n; ++i) M = fmaxf(M, ml[2 * i]);
-    float Lsum = 0.f;
-    float A[kPer];
+    for (int j = first + wave; j <= last; j += kWaves) M = fmaxf(M, rec0[(size_t)(s + j) * stride + m_off]);
+    float L = 0.f, a[kPer];
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) A[e] = 0.f;
-    for (int i = 0; i < n; ++i) {
-        const float f = __builtin_amdgcn_exp2f(ml[2 * i] - M);
-        Lsum = fmaf(f, ml[2 * i + 1], Lsum);
+    for (int e = 0; e < kPer; ++e) a[e] = 0.f;
+    for (int j = first + wave; j <= last; j += kWaves) {
+        const float *r = rec0 + (size_t)(s + j) * stride;
+        const float f = __builtin_amdgcn_exp2f(r[m_off] - M);
+        L = fmaf(f, r[l_off], L);
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) A[e] = fmaf(f, pa[(int64_t)i * D + lane * kPer + e], A[e]);
+        for (int e = 0; e < kPer; ++e) a[e] = fmaf(f, r[a_off + e], a[e]);
+    }
+    if (lane == 0) {
+        lds_m[wave] = M;
+        lds_l[wave] = L;
     }
 #pragma unroll
-    for (int e = 0; e < kPer; ++e)
-        p.out[(int64_t)row * D + lane * kPer + e] = Lsum > 0.f ? A[e] / Lsum : 0.f;
+    for (int e = 0; e < kPer; ++e) lds_acc[wave][lane * kPer + e] = a[e];
+    __syncthreads();
+    if (wave != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) Mt = fmaxf(Mt, lds_m[w]);
+    float Lt = 0.f, o[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(lds_m[w] - Mt);   // 0 for a wave without pieces
+        Lt = fmaf(f, lds_l[w], Lt);
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) o[e] = fmaf(f, lds_acc[w][lane * kPer + e], o[e]);
+    }
+    const float inv = 1.f / Lt;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) p.out[(size_t)row * D + lane * kPer + e] = o[e] * inv;
 }
 
 // ----------------------------------------------------------------------------
 // Host side: validation, plan, dispatch.
 
 struct Plan {
-    int split_tokens;
-    int max_splits;
-    int chunk_heads;   // template GT
     int n_chunks;
+    int units;
+    int groups;       // unit groups = gridDim.y
+    int item_tiles;   // 0 = balanced
+    int max_pieces;   // partial records per (unit group, wave)
+    int rec_heads;
     int log2_bs;
+    int max_ctx;
 };
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -513,6 +704,7 @@ int ilog2(int x) {
     return r;
 }
 
+// Shape checks and the device-independent plan.
 int make_plan(const pa_shape *sh, Plan *pl) {
     if (!sh) return PA_ERR_NULL;
     if (sh->num_seqs < 0 || sh->num_q_heads <= 0 || sh->num_kv_heads <= 0 ||
@@ -527,58 +719,63 @@ int make_plan(const pa_shape *sh, Plan *pl) {
     const int64_t max_ctx = (int64_t)sh->max_blocks_per_seq * sh->block_size;
     if (max_ctx > (int64_t)1 << 30) return PA_ERR_SHAPE;
     const int group = sh->num_q_heads / sh->num_kv_heads;
-    int gt = 1;
-    while (gt < group && gt < kMaxChunkHeads) gt <<= 1;
-    pl->chunk_heads = gt;
-    pl->n_chunks = (group + gt - 1) / gt;
+    pl->n_chunks = (group + kHeads - 1) / kHeads;
+    pl->units = sh->num_kv_heads * pl->n_chunks;
+    pl->groups = (pl->units + kWaves - 1) / kWaves;
+    pl->rec_heads = group < kHeads ? group : kHeads;
     pl->log2_bs = ilog2(sh->block_size);
-    int T = sh->split_tokens;
-    if (T == 0) T = 512;            // default partition; one partition if the context is shorter
-    // A partition may span at most kMaxPartitionBlocks blocks (its ids fit one wave).
-    const int64_t t_cap = (int64_t)(kMaxPartitionBlocks - 1) * sh->block_size / kTile * kTile;
-    if (T > t_cap) T = (int)t_cap;
-    if ((int64_t)T >= max_ctx) {
-        pl->split_tokens = (int)((max_ctx + kTile - 1) / kTile * kTile);
-        pl->max_splits = 1;
-    } else {
-        pl->split_tokens = T;
-        pl->max_splits = (int)((max_ctx + T - 1) / T);
-    }
-    if (pl->max_splits > 65535 || sh->num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+    pl->max_ctx = (int)max_ctx;
+    // Upper bound of the work-list length (every sequence at max_ctx).
+    const int64_t t_max = (int64_t)sh->num_seqs * ((max_ctx + kTile - 1) / kTile);
+    if (t_max >= ((int64_t)1 << 31) || pl->groups > 65535) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)sh->num_seqs * sh->num_q_heads >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
+    pl->item_tiles = sh->split_tokens / kTile;
+    const int64_t items = pl->item_tiles ? (t_max + pl->item_tiles - 1) / pl->item_tiles : kMaxItems;
+    const int64_t pieces = (int64_t)sh->num_seqs + items;
+    if (pieces * pl->groups * kWaves * pl->rec_heads * (sh->head_dim + 2) >= ((int64_t)1 << 40))
+        return PA_ERR_UNSUPPORTED;
+    pl->max_pieces = (int)pieces;
     return PA_OK;
 }
 
-size_t workspace_for(const pa_shape *sh, const Plan &pl) {
-    if (pl.max_splits <= 1) return 0;
-    const size_t rows = (size_t)sh->num_seqs * sh->num_q_heads * pl.max_splits;
-    const size_t acc = (rows * sh->head_dim * sizeof(float) + 255) & ~(size_t)255;
-    return acc + rows * 2 * sizeof(float);
+// Workgroups of the decode kernel the current device holds at once (queried
+// once per device and kernel).
+int device_capacity(int head_dim, bool int8) {
+    constexpr int kMaxDev = 64;
+    static int cache[kMaxDev][4];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+    const int slot = (head_dim == 128 ? 2 : 0) + (int8 ? 1 : 0);
+    int &c = cache[dev][slot];
+    if (c > 0) return c;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 0;
+    int per_cu = 0;
+    hipError_t e;
+    if (head_dim == 128)
+        e = int8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pa_decode_kernel<128, true>, kThreads, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pa_decode_kernel<128, false>, kThreads, 0);
+    else
+        e = int8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pa_decode_kernel<64, true>, kThreads, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pa_decode_kernel<64, false>, kThreads, 0);
+    if (e != hipSuccess || per_cu <= 0) per_cu = 1;
+    c = cus * per_cu;
+    return c;
 }
 
-template <int D, bool INT8>
-int launch_decode_d(const DecodeParams &prm, const Plan &pl, int S, int Hkv, hipStream_t st) {
-    dim3 grid((Hkv * pl.n_chunks + kWaves - 1) / kWaves, pl.max_splits, S);
-    dim3 block(kThreads);
-    switch (pl.chunk_heads) {
-        case 1: hipLaunchKernelGGL((pa_decode_kernel<D, 1, INT8>), grid, block, 0, st, prm); break;
-        case 2: hipLaunchKernelGGL((pa_decode_kernel<D, 2, INT8>), grid, block, 0, st, prm); break;
-        case 4: hipLaunchKernelGGL((pa_decode_kernel<D, 4, INT8>), grid, block, 0, st, prm); break;
-        case 8: hipLaunchKernelGGL((pa_decode_kernel<D, 8, INT8>), grid, block, 0, st, prm); break;
-        case 16: hipLaunchKernelGGL((pa_decode_kernel<D, 16, INT8>), grid, block, 0, st, prm); break;
-        default: return PA_ERR_UNSUPPORTED;
-    }
-    if (pl.max_splits > 1) {
-        ReduceParams rp;
-        rp.context_lens = prm.context_lens;
-        rp.part_acc = prm.part_acc;
-        rp.part_ml = prm.part_ml;
-        rp.out = prm.out;
-        rp.num_q_heads = prm.num_q_heads;
-        rp.split_tokens = pl.split_tokens;
-        rp.max_splits = pl.max_splits;
-        hipLaunchKernelGGL((pa_reduce_kernel<D>), dim3(S * prm.num_q_heads), dim3(64), 0, st, rp);
-    }
-    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+struct WsLayout {
+    size_t seg_offset;
+    size_t total;
+};
+
+WsLayout workspace_layout(const pa_shape *sh, const Plan &pl) {
+    WsLayout w;
+    const size_t rec_floats = (size_t)pl.rec_heads * (sh->head_dim + 2);
+    const size_t part_bytes = (size_t)pl.groups * pl.max_pieces * kWaves * rec_floats * sizeof(float);
+    w.seg_offset = (part_bytes + 255) & ~(size_t)255;
+    w.total = w.seg_offset + (((size_t)sh->num_seqs * 2 * sizeof(int32_t) + 255) & ~(size_t)255);
+    return w;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -593,11 +790,16 @@ int decode_common(bool int8, const void *q, const void *k, const void *v, const 
     if (!q || !k || !v || !bt || !cl || !out) return PA_ERR_NULL;
     if (int8 && (!ks || !vs)) return PA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PA_ERR_ALIGNMENT;
-    const size_t need = workspace_for(sh, pl);
-    if (need > 0 && (!ws || ws_bytes < need)) return PA_ERR_WORKSPACE;
-    if (need > 0 && !aligned16(ws)) return PA_ERR_ALIGNMENT;
+    const WsLayout wl = workspace_layout(sh, pl);
+    if (!ws || ws_bytes < wl.total) return PA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return PA_ERR_ALIGNMENT;
+    const int cap = device_capacity(sh->head_dim, int8);
+    if (cap <= 0) return PA_ERR_LAUNCH;
+    int wgs = cap / pl.groups;
+    if (wgs < 1) wgs = 1;
+    if (wgs > kMaxItems) wgs = kMaxItems;
 
-    DecodeParams prm;
+    Params prm;
     prm.q = (const uint16_t *)q;
     prm.k = k;
     prm.v = v;
@@ -606,25 +808,43 @@ int decode_common(bool int8, const void *q, const void *k, const void *v, const 
     prm.block_tables = bt;
     prm.context_lens = cl;
     prm.out = out;
-    const size_t rows = (size_t)sh->num_seqs * sh->num_q_heads * pl.max_splits;
-    const size_t acc_bytes = (rows * sh->head_dim * sizeof(float) + 255) & ~(size_t)255;
-    prm.part_acc = need ? (float *)ws : nullptr;
-    prm.part_ml = need ? (float *)((char *)ws + acc_bytes) : nullptr;
+    prm.part = (float *)ws;
+    prm.seg_items = (int32_t *)((char *)ws + wl.seg_offset);
     prm.scale_log2 = scale * kLog2e;
+    prm.num_seqs = sh->num_seqs;
     prm.num_q_heads = sh->num_q_heads;
     prm.num_kv_heads = sh->num_kv_heads;
     prm.group = sh->num_q_heads / sh->num_kv_heads;
     prm.n_chunks = pl.n_chunks;
+    prm.units = pl.units;
+    prm.rec_heads = pl.rec_heads;
     prm.max_blocks_per_seq = sh->max_blocks_per_seq;
+    prm.max_ctx = pl.max_ctx;
     prm.log2_block_size = pl.log2_bs;
-    prm.split_tokens = pl.split_tokens;
-    prm.max_splits = pl.max_splits;
+    prm.item_tiles = pl.item_tiles;
+    prm.max_pieces = pl.max_pieces;
+    MergeParams mp;
+    mp.part = prm.part;
+    mp.seg_items = prm.seg_items;
+    mp.out = out;
+    mp.num_q_heads = sh->num_q_heads;
+    mp.group = prm.group;
+    mp.n_chunks = pl.n_chunks;
+    mp.rec_heads = pl.rec_heads;
+    mp.max_pieces = pl.max_pieces;
+    const dim3 grid(wgs, pl.groups), block(kThreads);
+    const dim3 mgrid((unsigned)((int64_t)sh->num_seqs * sh->num_q_heads));
     hipStream_t st = (hipStream_t)stream;
-    if (sh->head_dim == 128)
-        return int8 ? launch_decode_d<128, true>(prm, pl, sh->num_seqs, sh->num_kv_heads, st)
-                    : launch_decode_d<128, false>(prm, pl, sh->num_seqs, sh->num_kv_heads, st);
-    return int8 ? launch_decode_d<64, true>(prm, pl, sh->num_seqs, sh->num_kv_heads, st)
-                : launch_decode_d<64, false>(prm, pl, sh->num_seqs, sh->num_kv_heads, st);
+    if (sh->head_dim == 128) {
+        if (int8) hipLaunchKernelGGL((pa_decode_kernel<128, true>), grid, block, 0, st, prm);
+        else hipLaunchKernelGGL((pa_decode_kernel<128, false>), grid, block, 0, st, prm);
+        hipLaunchKernelGGL((pa_merge_kernel<128>), mgrid, block, 0, st, mp);
+    } else {
+        if (int8) hipLaunchKernelGGL((pa_decode_kernel<64, true>), grid, block, 0, st, prm);
+        else hipLaunchKernelGGL((pa_decode_kernel<64, false>), grid, block, 0, st, prm);
+        hipLaunchKernelGGL((pa_merge_kernel<64>), mgrid, block, 0, st, mp);
+    }
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -635,15 +855,15 @@ int paged_attn_plan(const pa_shape *shape, int32_t *split_tokens, int32_t *max_s
     Plan pl;
     int rc = make_plan(shape, &pl);
     if (rc != PA_OK) return rc;
-    if (split_tokens) *split_tokens = pl.split_tokens;
-    if (max_splits) *max_splits = pl.max_splits;
+    if (split_tokens) *split_tokens = pl.item_tiles * kTile;
+    if (max_splits) *max_splits = pl.max_pieces - shape->num_seqs;
     return PA_OK;
 }
 
 size_t paged_attn_workspace_bytes(const pa_shape *shape) {
     Plan pl;
     if (make_plan(shape, &pl) != PA_OK) return 0;
-    return workspace_for(shape, pl);
+    return workspace_layout(shape, pl).total;
 }
 
 int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
@@ -668,9 +888,9 @@ const char *paged_attn_strerror(int code) {
         case PA_OK: return "ok";
         case PA_ERR_NULL: return "a required pointer is NULL";
         case PA_ERR_SHAPE: return "invalid shape";
-        case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size or grid size";
+        case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size or problem size";
         case PA_ERR_WORKSPACE: return "workspace missing or too small";
-        case PA_ERR_LAUNCH: return "kernel launch failed";
+        case PA_ERR_LAUNCH: return "kernel launch failed or no usable device";
         case PA_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
         default: return "unknown error";
     }

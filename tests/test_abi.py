@@ -83,19 +83,29 @@ def test_misaligned_pointers():
         assert call(shape(), **{name: bad}) == B.PA_ERR_ALIGNMENT, name
 
 
-def test_workspace_required_when_split():
-    sh = shape(split_tokens=64)           # 256 max tokens -> 4 partitions
-    assert B.plan(sh) == (64, 4)
+def test_workspace_always_required():
+    # Partial results of split sequences and their counters live in the workspace.
+    for st in (0, 64):
+        sh = shape(split_tokens=st)
+        need = B.workspace_bytes(sh)
+        assert need > 0
+        assert call(sh) == B.PA_ERR_WORKSPACE
+        assert call(sh, ws=FAKE, ws_n=need - 1) == B.PA_ERR_WORKSPACE
+
+
+def test_plan_fixed_items():
+    sh = shape(split_tokens=64)           # 4 sequences x 16 tiles in items of 4 tiles
+    assert B.plan(sh) == (64, 16)
     need = B.workspace_bytes(sh)
-    assert need >= 4 * 8 * 4 * (64 + 2) * 4
-    assert call(sh) == B.PA_ERR_WORKSPACE
-    assert call(sh, ws=FAKE, ws_n=need - 1) == B.PA_ERR_WORKSPACE
+    # records: 1 unit group x (S + items) pieces x 4 waves x G heads x (D + 2) floats, + counters
+    expect = ((1 * (4 + 16) * 4 * 4 * (64 + 2) * 4 + 255) // 256) * 256 + 256
+    assert need == expect, (need, expect)
 
 
-def test_single_partition_needs_no_workspace():
-    sh = shape()                          # 256 max tokens <= default partition
-    assert B.plan(sh) == (256, 1)
-    assert B.workspace_bytes(sh) == 0
+def test_plan_balanced_is_device_independent():
+    sh = shape()
+    assert B.plan(sh) == (0, 4096)
+    assert B.workspace_bytes(sh) == ((1 * (4 + 4096) * 4 * 4 * 66 * 4 + 255) // 256) * 256 + 256
 
 
 def test_zero_sequences_is_a_no_op():
@@ -105,5 +115,6 @@ def test_zero_sequences_is_a_no_op():
 def test_plan_long_context():
     sh = shape(num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128,
                max_blocks_per_seq=8192, num_blocks=32768, split_tokens=512)
-    assert B.plan(sh) == (512, 256)
-    assert B.workspace_bytes(sh) == ((4 * 32 * 256 * 128 * 4 + 255) // 256) * 256 + 4 * 32 * 256 * 8
+    assert B.plan(sh) == (512, 4 * 131072 // 512)
+    pieces = 4 + 1024
+    assert B.workspace_bytes(sh) == ((2 * pieces * 4 * 4 * 130 * 4 + 255) // 256) * 256 + 256

@@ -100,11 +100,13 @@ def test_gqa_mapping_constant_values():
     for g in range(4):
         v["v_cache"][:, :, g, :] = float(g + 1)
     out = run(v).cpu()
-    # fp32 sum(p*c)/sum(p) rounds, so not bit-exact; a wrong head->kv-head map
-    # (h % G instead of h / G) is off by at least 1.
+    # Not bit-exact: the softmax weights enter the PV product as a bf16 pair
+    # (high part + remainder, exact to 2^-17 relative) and sum(p*c)/sum(p) is
+    # rounded in fp32, so the result is c within a few 2^-17 c.  A wrong
+    # head->kv-head map (h % G instead of h / G) is off by at least 1.
     for h in range(16):
         assert torch.allclose(out[:, h], torch.full_like(out[:, h], float(h // 4 + 1)),
-                              rtol=0, atol=1e-5), h
+                              rtol=0, atol=1e-4), h
 
 
 def test_uniform_keys_mean_of_values():
