@@ -3,19 +3,22 @@
 
 A step is one decode of the whole batch: every sequence's single query token
 attends over its paged context (all layers of the workload), through the
-C-ABI library -- the main kernel plus, when the context is partitioned, the
-reduction kernel.  Inputs are seeded, synthetic and resident in HBM before
-timing starts.  Each timed step is preceded (outside the timed events) by a
-2 GiB device READ that evicts the KV cache from the 256 MB MALL and the L2s
-with clean lines, so the KV bytes really come from HBM.  (A write-based
-flush would leave the MALL full of dirty lines whose write-back then
-competes with the timed kernel.)
+C-ABI library -- per layer one paged_attn_decode call, i.e. the decode kernel
+and the merge kernel of split sequences.  Inputs are seeded, synthetic and
+resident in HBM before timing starts.  Each timed step is preceded (outside
+the timed events) by a 2 GiB device READ that evicts the KV cache from the
+256 MB MALL and the L2s with clean lines, so the KV bytes really come from
+HBM.  (A write-based flush would leave the MALL full of dirty lines whose
+write-back then competes with the timed kernel.)
 
-Prints ONE JSON line.  `value` is decode tokens/s (sequences decoded per
-second: each step produces one token per sequence); `roofline` relates the
-algorithmic bytes of one step to its measured duration against the 8 TB/s
-HBM peak; `cpu_baseline` is the fp64 oracle timed on the host's cores on a
-bounded sample of the same workload.
+Prints ONE JSON line.  `value` is decode tokens/s (each step produces one
+token per sequence); `roofline` relates the algorithmic bytes of one decode
+call to its measured duration (HIP events on the launch stream) against the
+8 TB/s HBM peak; `traffic` is the HBM bytes per call that rocprofv3 counters
+measured for this kernel source (null if the source changed since);
+`hbm_read_probe_gbps` is what a plain coalesced read of the same number of
+bytes achieves on this device; `cpu_baseline` is the fp64 oracle timed on the
+host's cores on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload llama3_8b]
 """
@@ -35,6 +38,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
 METRIC = ("decode attention tokens/s and achieved KV-read HBM GB/s (% of peak), "
           "Llama-3-8B shape")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -44,14 +48,46 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--split-tokens", type=int, default=None,
-                    help="context partition size (default: the workload's, else the library's)")
+                    help="work item length in tokens (default: the workload's; 0 = balanced)")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the read-probe ceiling")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON with measured HBM bytes per decode call (from rocprofv3 counters)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after timing, copy this many bytes 3x with the probe copy kernel "
+                         "(reference for hardware byte counters)")
     return ap.parse_args()
+
+
+def event_ms(stream, fn, reps, before=None):
+    """Per-rep durations (ms) of fn() between HIP events recorded on `stream`."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        if before is not None:
+            before()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def measured_traffic(workload: str):
+    """Bytes per decode call from the committed counter summary, if it was
+    taken on the current kernel source."""
+    from paged_kv_cache_393_amd import rocprof_summary as R
+
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("workload") != workload or rec.get("source_sha256") != R.source_sha256():
+        return None
+    return rec.get("bytes_per_call")
 
 
 def main() -> int:
@@ -59,7 +95,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the decode path has no multi-GPU leg in this build.", file=sys.stderr)
+              "this decode path has no multi-GPU leg: every box here has one GPU.", file=sys.stderr)
         return 2
 
     import torch
@@ -67,6 +103,7 @@ def main() -> int:
     from paged_kv_cache_393_amd import accounting as A
     from paged_kv_cache_393_amd import binding as B
     from paged_kv_cache_393_amd import inputs as I
+    from paged_kv_cache_393_amd import probe as P
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -84,7 +121,7 @@ def main() -> int:
     L = wl.num_layers
     layers = [I.layer_views(inp, l) for l in range(L)]
     shape = B.shape_of(layers[0]["q"], layers[0]["k_cache"], layers[0]["block_tables"], split)
-    plan_split, plan_parts = B.plan(shape)
+    plan_split, plan_items = B.plan(shape)
     workspace = B.alloc_workspace(shape, dev)
     outs = [torch.empty(v["q"].shape, dtype=torch.float32, device=dev) for v in layers]
     stream = torch.cuda.current_stream()
@@ -101,42 +138,47 @@ def main() -> int:
         if flush_buf is not None:
             flush_buf.amax()      # a read of 2 GiB: clean eviction of MALL and L2
 
-    for i in range(args.warmup):
+    for _ in range(args.warmup):
         evict()
         step()
-    torch.cuda.synchronize()
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    for i in range(args.steps):
-        evict()
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
+    ms = event_ms(stream, step, args.steps, before=evict)
     wall = time.perf_counter() - w0
-    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_sorted = sorted(ms)
     ms_mean = statistics.fmean(ms)
     pct = lambda q: ms_sorted[min(len(ms_sorted) - 1, int(q * len(ms_sorted)))]
+    print(f"[bench] {args.steps} timed steps done", file=sys.stderr, flush=True)
 
     ctx = inp["context_lens"].cpu().tolist()
     S = wl.num_seqs
-    step_bytes = L * A.decode_bytes(ctx, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                    wl.block_size, wl.kv_dtype)
+    call_bytes = A.decode_bytes(ctx, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                wl.block_size, wl.kv_dtype)
+    step_bytes = L * call_bytes
     kv_bytes = L * sum(ctx) * (A.kv_bytes_per_token(1, wl.num_kv_heads, wl.head_dim,
                                                      1 if wl.kv_dtype == "int8" else 2)
                                + (2 * wl.num_kv_heads * 4 if wl.kv_dtype == "int8" else 0))
     flops = L * A.decode_flops(ctx, wl.num_q_heads, wl.head_dim)
     t_s = ms_mean / 1e3
     gbps = step_bytes / t_s / 1e9
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        tr = json.load(open(args.traffic))
-        if tr.get("workload") == wl.name:
-            traffic = tr.get("bytes_per_call")
+
+    probe_gbps = None
+    if not args.no_probe:
+        nbytes = (call_bytes // 16) * 16
+        pbuf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        pbuf.fill_(1)
+        sink = torch.zeros(256, dtype=torch.int32, device=dev)
+        pms = event_ms(stream, lambda: P.read(pbuf, sink, stream), 20, before=evict)
+        probe_gbps = nbytes / (statistics.median(pms) / 1e3) / 1e9
+        del pbuf
+
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            P.copy(src, dst, stream)
+        torch.cuda.synchronize()
+        del src, dst
 
     record = {
         "metric": METRIC,
@@ -157,7 +199,7 @@ def main() -> int:
             "head_dim": wl.head_dim, "block_size": wl.block_size, "layers": L,
             "context_tokens": sum(ctx), "ctx_min": min(ctx), "ctx_max": max(ctx),
             "num_blocks": inp["num_blocks"], "kv_dtype": wl.kv_dtype,
-            "split_tokens": plan_split, "partitions": plan_parts,
+            "split_tokens": plan_split, "max_items": plan_items,
             "cache_evict_between_steps": "2 GiB read" if flush_buf is not None else None,
         },
         "kv_gbps": kv_bytes / t_s / 1e9,
@@ -165,16 +207,18 @@ def main() -> int:
         "ms_p10": pct(0.10), "ms_median": pct(0.50), "ms_p90": pct(0.90),
         "wall_ms_per_step_incl_evict": wall / args.steps * 1e3,
         "tflops": flops / t_s / 1e12,
+        "hbm_read_probe_gbps": probe_gbps,
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode_kernel (one launch per layer; split sequences merged in-kernel)",
+            "kernel": "paged_attn_decode call: pa_decode_kernel + pa_merge_kernel",
             "achieved": gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": gbps / HBM_PEAK_GBPS,
-            "traffic": traffic,
-            "algorithmic_bytes_per_step": step_bytes,
-            "launches_per_step": L,
+            "traffic": measured_traffic(wl.name),
+            "algorithmic_bytes_per_call": call_bytes,
+            "calls_per_step": L,
+            "ms_per_call": ms_mean / L,
         },
         "cpu_baseline": None,
     }
@@ -187,7 +231,9 @@ def main() -> int:
 
 
 def cpu_baseline(wl, views0, out0, ctx, n_layers, budget_s):
-    """fp64 oracle on a bounded sample of layer 0, scaled to the whole step by token count."""
+    """fp64 oracle on a bounded sample of layer 0, scaled to the whole step by
+    context-token count.  The sample is a prefix of the batch sized to about
+    budget_s of work; small samples are timed several times (median)."""
     import numpy as np
 
     import oracle
@@ -202,23 +248,30 @@ def cpu_baseline(wl, views0, out0, ctx, n_layers, budget_s):
         qb = I.bf16_bits(sub["q"])
         bt = sub["block_tables"].numpy()
         cl = sub["context_lens"].numpy()
-        t = time.perf_counter()
         if "k_scales" in sub:
-            ref = oracle.paged_decode_int8(qb, sub["k_cache"].numpy(), sub["v_cache"].numpy(),
-                                           sub["k_scales"].numpy(), sub["v_scales"].numpy(),
-                                           bt, cl, sub["scale"])
+            args = (qb, sub["k_cache"].numpy(), sub["v_cache"].numpy(), sub["k_scales"].numpy(),
+                    sub["v_scales"].numpy(), bt, cl, sub["scale"])
+            fn = oracle.paged_decode_int8
         else:
-            ref = oracle.paged_decode_bf16(qb, I.bf16_bits(sub["k_cache"]),
-                                           I.bf16_bits(sub["v_cache"]), bt, cl, sub["scale"])
-        return time.perf_counter() - t, ref
+            args = (qb, I.bf16_bits(sub["k_cache"]), I.bf16_bits(sub["v_cache"]), bt, cl,
+                    sub["scale"])
+            fn = oracle.paged_decode_bf16
+        t = time.perf_counter()
+        ref = fn(*args)
+        return time.perf_counter() - t, ref, args, fn
 
-    order = list(range(len(ctx)))
-    t1, _ = run(order[:1])
+    t1, _, _, _ = run([0])
     per_token = t1 / max(1, ctx[0])
     avg = sum(ctx) / len(ctx)
     n = max(1, min(len(ctx), int(budget_s / max(per_token * avg, 1e-9))))
-    ids = order[:n]
-    t_sample, ref = run(ids)
+    ids = list(range(n))
+    t_first, ref, args, fn = run(ids)
+    times = [t_first]
+    while sum(times) < min(budget_s, 3.0) and len(times) < 25:
+        t = time.perf_counter()
+        fn(*args)
+        times.append(time.perf_counter() - t)
+    t_sample = statistics.median(times)
     got = out0[ids].double().cpu().numpy()
     sample_tokens = sum(ctx[i] for i in ids)
     t_full = t_sample * (sum(ctx) / sample_tokens) * n_layers
@@ -228,8 +281,8 @@ def cpu_baseline(wl, views0, out0, ctx, n_layers, budget_s):
         "cores": threads,
         "kind": "oracle",
         "sample": (f"{n} of {len(ctx)} sequences of layer 0 of {n_layers} "
-                   f"({sample_tokens} of {sum(ctx)} context tokens), {t_sample:.2f}s, "
-                   "scaled to the full step by context-token count"),
+                   f"({sample_tokens} of {sum(ctx)} context tokens), median of {len(times)} runs "
+                   f"of {t_sample:.3f}s, scaled to the full step by context-token count"),
         "parity_max_abs_vs_gpu": float(np.abs(got - ref).max()),
     }
 

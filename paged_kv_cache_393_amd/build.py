@@ -10,8 +10,13 @@ import sys
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(_HERE)
-SOURCES = [os.path.join(_HERE, "csrc", "paged_attn.hip")]
-LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+# (source, output) of every HIP library: the decode path and the bench's
+# measurement kernels.
+LIBS = [
+    (os.path.join(_HERE, "csrc", "paged_attn.hip"), os.path.join(_HERE, "libpagedattn.so")),
+    (os.path.join(_HERE, "csrc", "pa_probe.hip"), os.path.join(_HERE, "libpaprobe.so")),
+]
+LIB_PATH = LIBS[0][1]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -28,19 +33,26 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + SOURCES + ["-o", tmp]
+def _compile(source: str, out: str, verbose: bool) -> str:
+    tmp = out + ".tmp"
+    cmd = [hipcc()] + HIPCC_FLAGS + [source, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
+        raise RuntimeError(f"hipcc failed ({r.returncode}) on {source}:\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP library for gfx950; returns the decode library's path."""
+    for source, out in LIBS:
+        _compile(source, out, verbose)
     return LIB_PATH
 
 

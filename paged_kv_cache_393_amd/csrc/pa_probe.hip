@@ -1,0 +1,84 @@
+// pa_probe.hip -- measurement support for the decode bench (gfx950).
+//
+// Two plain kernels with a known number of HBM bytes, used to put the decode
+// kernel's bandwidth in context:
+//   * pa_probe_read: streams a buffer once with 16-byte loads (the practical
+//     read ceiling of the device for a perfectly coalesced stream);
+//   * pa_probe_copy: copies a buffer (reads N and writes N bytes), the
+//     reference against which hardware fetch/write byte counters are scaled.
+// Neither is part of the decode path.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+// Grid-stride read with two independent 16-B loads in flight per iteration;
+// the XOR of everything read is stored only if it equals an unlikely value,
+// which keeps the loads alive without writing.
+__global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4_t *__restrict__ p, int64_t n16,
+                                                              uint32_t *__restrict__ sink) {
+    uint32_t acc = 0;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; i + stride < n16; i += 2 * stride) {
+        const u32x4_t a = __builtin_nontemporal_load(p + i);
+        const u32x4_t b = __builtin_nontemporal_load(p + i + stride);
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
+    }
+    for (; i < n16; i += stride) {
+        const u32x4_t a = p[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    if (acc == 0x9e3779b9u) sink[blockIdx.x & 255] = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void probe_copy_kernel(const u32x4_t *__restrict__ src,
+                                                              u32x4_t *__restrict__ dst, int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+int grid_for(int64_t n16) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 0;
+    int64_t g = (int64_t)cus * 8;   // 8 workgroups per compute unit
+    const int64_t need = (n16 + kThreads - 1) / kThreads;
+    return (int)(g < need ? g : (need > 0 ? need : 1));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int pa_probe_read(const void *buf, int64_t bytes, void *sink, void *stream) {
+    if (!buf || !sink) return PA_PROBE_ERR_ARG;
+    if (bytes <= 0 || bytes % 16 != 0 || !aligned16(buf)) return PA_PROBE_ERR_ARG;
+    const int grid = grid_for(bytes / 16);
+    if (grid <= 0) return PA_PROBE_ERR_LAUNCH;
+    hipLaunchKernelGGL(probe_read_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const u32x4_t *)buf, bytes / 16, (uint32_t *)sink);
+    return hipGetLastError() == hipSuccess ? PA_PROBE_OK : PA_PROBE_ERR_LAUNCH;
+}
+
+int pa_probe_copy(const void *src, void *dst, int64_t bytes, void *stream) {
+    if (!src || !dst) return PA_PROBE_ERR_ARG;
+    if (bytes <= 0 || bytes % 16 != 0 || !aligned16(src) || !aligned16(dst)) return PA_PROBE_ERR_ARG;
+    const int grid = grid_for(bytes / 16);
+    if (grid <= 0) return PA_PROBE_ERR_LAUNCH;
+    hipLaunchKernelGGL(probe_copy_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const u32x4_t *)src, (u32x4_t *)dst, bytes / 16);
+    return hipGetLastError() == hipSuccess ? PA_PROBE_OK : PA_PROBE_ERR_LAUNCH;
+}
+
+}  // extern "C"
