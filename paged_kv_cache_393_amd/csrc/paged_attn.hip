@@ -72,7 +72,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // Tuning knobs (compile-time): tiles in flight per wave, and the minimum
 // number of waves per SIMD the register allocation must allow.
 #ifndef PA_STAGES
-#define PA_STAGES 3
+#define PA_STAGES 2
 #endif
 #ifndef PA_WAVES_PER_EU
 #define PA_WAVES_PER_EU 2
@@ -85,6 +85,7 @@ constexpr int kHeads = 16;          // query heads per unit (MFMA columns)
 constexpr int kWindow = 128;        // block ids held in registers (two per lane)
 constexpr int kMinItemTiles = 4;    // shortest balanced item
 constexpr int kMaxItems = 4096;     // balanced items per unit group (>= workgroups launched)
+constexpr int kLdsSeqs = 2048;      // sequences whose tile prefix and length are kept in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 // Word 3 of a raw (unformatted, stride 0) buffer resource on CDNA3/CDNA4.
 constexpr int kRsrcFlags = 0x00020000;
@@ -233,6 +234,8 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
     constexpr int kDpl = L::kDpl;
     static_assert(L::kKLoads >= 1, "head_dim");
 
+    __shared__ int lds_incl[kLdsSeqs];   // inclusive prefix of tiles per sequence
+    __shared__ int lds_ctx[kLdsSeqs];    // context length per sequence
     __shared__ int lds_red[kWaves];
     __shared__ int lds_found[2];
     __shared__ __attribute__((aligned(16))) float lds_sc[kWaves][2 * kTile];
@@ -250,18 +253,38 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
         return min(max(p.context_lens[s], 0), p.max_ctx);
     };
 
-    // ---- Work list length (the host checked that it fits in int). ----
-    int local = 0;
-    for (int s = threadIdx.x; s < S; s += kThreads) local += tiles_of(ctx_of(s));
+    // ---- Tiles per sequence: the list length T (the host checked that it
+    // fits in int) and, for batches of up to kLdsSeqs, the inclusive prefix
+    // and the context lengths in LDS. ----
+    const bool in_lds = S <= kLdsSeqs;
+    int T = 0;
+    for (int c0 = 0; c0 < S; c0 += kThreads) {
+        const int s = c0 + threadIdx.x;
+        const int ctx = s < S ? ctx_of(s) : 0;
+        const int n = s < S ? tiles_of(ctx) : 0;
+        int incl = n;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) local += __shfl_xor(local, off);
-    if (lane == 0) lds_red[wave] = local;
-    __syncthreads();
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+        }
+        if (lane == 63) lds_red[wave] = incl;
+        __syncthreads();
+        int before = T, chunk_total = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            before += w < wave ? lds_red[w] : 0;
+            chunk_total += lds_red[w];
+        }
+        if (in_lds && s < S) {
+            lds_incl[s] = incl + before;
+            lds_ctx[s] = ctx;
+        }
+        __syncthreads();
+        T += chunk_total;
+    }
     Items items;
-    items.T = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) items.T += lds_red[w];
-    __syncthreads();
+    items.T = T;
     items.fixed = p.item_tiles;
     items.n = p.item_tiles ? (items.T + p.item_tiles - 1) / p.item_tiles
                            : min((int)gridDim.x, (items.T + kMinItemTiles - 1) / kMinItemTiles);
@@ -293,9 +316,36 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
         v_off[i] = (int)((uint32_t)(4 * lg + i) * rb32 + (uint32_t)(l16 * L::kVBytes));
     const int s_off = (int)(((uint32_t)l16 * (uint32_t)Hkv + (uint32_t)g) * 4u);
 
-    // One piece: tiles [ta, tb) of sequence s for this wave's unit.  Items
-    // `first` .. `last` are those that hold the sequence; `item` holds this piece.
-    auto process = [&](int s, int ctx, int ta, int tb, int first, int last, int item)
+    // Per-piece operands: the query heads (B operand of S = K Q^T; zero for
+    // padding heads) and the block ids of the piece as a register window of
+    // kWindow entries (lane i holds ids first + i and first + 64 + i).
+    struct Meta {
+        bf16x4_t q[L::kSteps];
+        int w0, w1, first;
+    };
+    auto load_window = [&](Meta &m, const int32_t *table, int blk_first, int blk_end)
+        __attribute__((always_inline)) {
+        m.first = blk_first;
+        m.w0 = (blk_first + lane < blk_end) ? table[blk_first + lane] : 0;
+        m.w1 = (blk_first + 64 + lane < blk_end) ? table[blk_first + 64 + lane] : 0;
+    };
+    // Meta of the piece of sequence s holding tokens [t_begin, t_end).
+    auto load_meta = [&](Meta &m, int s, int t_begin, int t_end) __attribute__((always_inline)) {
+        const uint16_t *qrow = p.q + ((int64_t)s * Hq + h_base + (live ? l16 : 0)) * D;
+#pragma unroll
+        for (int st = 0; st < L::kSteps; ++st) {
+            u32x2_t w = *(const u32x2_t *)(qrow + L::step_dim(st, lg));
+            if (!live) w = u32x2_t{0u, 0u};
+            m.q[st] = __builtin_bit_cast(bf16x4_t, w);
+        }
+        load_window(m, p.block_tables + (int64_t)s * p.max_blocks_per_seq, t_begin >> bs_log2,
+                    ((t_end - 1) >> bs_log2) + 1);
+    };
+
+    // One piece: tiles [ta, tb) of sequence s for this wave's unit, with its
+    // operands in `mt`.  Items `first` .. `last` are those that hold the
+    // sequence; `item` holds this piece.
+    auto process = [&](int s, int ctx, int ta, int tb, int first, int last, int item, Meta &mt)
         __attribute__((always_inline)) {
         const int64_t row0 = (int64_t)s * Hq + h_base;   // output row of head column 0
         if (ctx == 0) {   // empty context: the output row is zero (always one whole piece)
@@ -309,43 +359,21 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
         const int t_begin = ta * kTile;
         const int t_end = min(ctx, tb * kTile);
         const int n_tiles = tb - ta;
+        const bf16x4_t(&qop)[L::kSteps] = mt.q;
 
-        // Query operand (B of S = K Q^T): head l16 of the unit, zero for padding heads.
-        bf16x4_t qop[L::kSteps];
-        {
-            const uint16_t *qrow = p.q + (row0 + (live ? l16 : 0)) * D;
-#pragma unroll
-            for (int st = 0; st < L::kSteps; ++st) {
-                u32x2_t w = *(const u32x2_t *)(qrow + L::step_dim(st, lg));
-                if (!live) w = u32x2_t{0u, 0u};
-                qop[st] = __builtin_bit_cast(bf16x4_t, w);
-            }
-        }
-
-        // Block ids of the piece as a register window of kWindow entries (lane
-        // i holds ids win_first + i and win_first + 64 + i), refilled when a
-        // tile leaves it, so the tile loop makes no dependent memory access
-        // unless a piece spans more than kWindow blocks.
+        // The window is refilled when a tile leaves it, so the tile loop makes
+        // no dependent memory access unless a piece spans more than kWindow
+        // blocks.
         const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
         const int blk_end = ((t_end - 1) >> bs_log2) + 1;
-        int win_first = t_begin >> bs_log2;
-        int win0 = 0, win1 = 0;
-        auto fill_window = [&]() __attribute__((always_inline)) {
-            win0 = (win_first + lane < blk_end) ? table[win_first + lane] : 0;
-            win1 = (win_first + 64 + lane < blk_end) ? table[win_first + 64 + lane] : 0;
-        };
-        fill_window();
         // Token-slot index phys * block_size + slot of the first token of tile `tile` (uniform).
         auto tile_slot = [&](int tile) __attribute__((always_inline)) -> int64_t {
             const int t0 = t_begin + tile * kTile;
             const int blk = t0 >> bs_log2;
-            if (blk - win_first >= kWindow) {
-                win_first = blk;
-                fill_window();
-            }
-            const int idx = blk - win_first;
-            const int phys = idx < 64 ? __builtin_amdgcn_readlane(win0, idx)
-                                      : __builtin_amdgcn_readlane(win1, idx - 64);
+            if (blk - mt.first >= kWindow) load_window(mt, table, blk, blk_end);
+            const int idx = blk - mt.first;
+            const int phys = idx < 64 ? __builtin_amdgcn_readlane(mt.w0, idx)
+                                      : __builtin_amdgcn_readlane(mt.w1, idx - 64);
             return ((int64_t)phys << bs_log2) + (t0 & bs_mask);
         };
 
@@ -559,42 +587,64 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
     for (int item = blockIdx.x; item < items.n; item += gridDim.x) {
         const int lo = items.lo(item);
         const int hi = items.lo(item + 1);
-        // Find the sequence holding tile `lo`: running inclusive scan of the
-        // per-sequence tile counts, one chunk of kThreads sequences at a time.
-        int base = 0;
-        for (int c0 = 0;; c0 += kThreads) {
-            const int s = c0 + threadIdx.x;
-            const int n = s < S ? tiles_of(ctx_of(s)) : 0;
-            int incl = n;
+        // The sequence s holding tile `lo`, and its first tile seg.
+        int s, seg;
+        if (in_lds) {
+            if (!active) continue;
+            // Two-level 64-way search for the first s with incl[s] > lo.
+            const int bk = (S + 63) >> 6;   // <= 32
+            const uint64_t m1 = __ballot(lds_incl[min(S - 1, (lane + 1) * bk - 1)] > lo);
+            const int f = __builtin_ctzll(m1);
+            const int i2 = min(S - 1, f * bk + lane);
+            const uint64_t m2 = __ballot(lane < bk && lds_incl[i2] > lo);
+            s = f * bk + __builtin_ctzll(m2);
+            seg = s > 0 ? __builtin_amdgcn_readfirstlane(lds_incl[s - 1]) : 0;
+        } else {
+            // Running inclusive scan of the per-sequence tile counts, one chunk
+            // of kThreads sequences at a time (the whole workgroup).
+            int base = 0;
+            for (int c0 = 0;; c0 += kThreads) {
+                const int sc = c0 + threadIdx.x;
+                const int n = sc < S ? tiles_of(ctx_of(sc)) : 0;
+                int incl = n;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int t = __shfl_up(incl, off);
-                if (lane >= off) incl += t;
-            }
-            if (lane == 63) lds_red[wave] = incl;
-            __syncthreads();
-            int before = base, chunk_total = 0;
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int t = __shfl_up(incl, off);
+                    if (lane >= off) incl += t;
+                }
+                if (lane == 63) lds_red[wave] = incl;
+                __syncthreads();
+                int before = base, chunk_total = 0;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                before += w < wave ? lds_red[w] : 0;
-                chunk_total += lds_red[w];
+                for (int w = 0; w < kWaves; ++w) {
+                    before += w < wave ? lds_red[w] : 0;
+                    chunk_total += lds_red[w];
+                }
+                incl += before;
+                if (sc < S && incl - n <= lo && lo < incl) {
+                    lds_found[0] = sc;
+                    lds_found[1] = incl - n;
+                }
+                __syncthreads();
+                base += chunk_total;
+                if (base > lo) break;   // uniform: every thread has the same base
+                __syncthreads();        // lds_red is rewritten by the next chunk
             }
-            incl += before;
-            if (s < S && incl - n <= lo && lo < incl) {
-                lds_found[0] = s;
-                lds_found[1] = incl - n;
-            }
-            __syncthreads();
-            base += chunk_total;
-            if (base > lo) break;   // uniform: every thread has the same base
-            __syncthreads();        // lds_red is rewritten by the next chunk
+            s = lds_found[0];
+            seg = lds_found[1];
+            __syncthreads();            // lds_found may be rewritten by the next item
+            if (!active) continue;
         }
-        int s = lds_found[0];
-        int seg = lds_found[1];     // first tile of sequence s in the list
-        __syncthreads();            // lds_found may be rewritten by the next item
-        if (!active) continue;
+        auto seq_ctx = [&](int sq) __attribute__((always_inline)) -> int {
+            return in_lds ? __builtin_amdgcn_readfirstlane(lds_ctx[sq]) : ctx_of(sq);
+        };
+        // Pieces of the item: the operands of the next piece are loaded
+        // before the current one streams, so a piece starts without waiting
+        // for its query and block ids.
+        Meta mc, mn;
+        int ctx = seq_ctx(s);
+        if (ctx > 0) load_meta(mc, s, (lo - seg) * kTile, min(ctx, (hi - seg) * kTile));
         for (int x = lo; x < hi; ++s) {
-            const int ctx = ctx_of(s);
             const int nt = tiles_of(ctx);
             const int end = min(hi, seg + nt);
             const int first = items.of(seg), last = items.of(seg + nt - 1);
@@ -602,7 +652,11 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
                 p.seg_items[2 * s] = first;
                 p.seg_items[2 * s + 1] = last;
             }
-            process(s, ctx, x - seg, end - seg, first, last, item);
+            const int ctx_next = end < hi ? seq_ctx(s + 1) : 0;
+            if (ctx_next > 0) load_meta(mn, s + 1, 0, min(ctx_next, (hi - end) * kTile));
+            process(s, ctx, x - seg, end - seg, first, last, item, mc);
+            if (ctx_next > 0) mc = mn;   // (an empty next sequence needs none)
+            ctx = ctx_next;
             x = end;
             seg += nt;
         }
@@ -623,11 +677,13 @@ struct MergeParams {
 // Merge the partial records of one (sequence, query head) row whose sequence
 // was split over several items: M = max_p m_p, w_p = 2^(m_p - M),
 // out = sum_p w_p acc_p / sum_p w_p l_p.  Wave w takes pieces w, w + 4, ...
-// in index order; the four wave results are then combined in wave order, so
-// the result does not depend on timing.
+// in index order and merges them online (running max, rescaled sums), four
+// pieces' loads in flight at a time; the four wave results are then combined
+// in wave order, so the result does not depend on timing.
 template <int D>
 __global__ __launch_bounds__(kThreads) void pa_merge_kernel(const MergeParams p) {
     constexpr int kPer = D / 64;   // dims per lane
+    constexpr int kUnroll = 4;     // pieces loaded together
     __shared__ float lds_m[kWaves], lds_l[kWaves];
     __shared__ __attribute__((aligned(16))) float lds_acc[kWaves][D];
     const int row = blockIdx.x;    // s * Hq + h
@@ -644,17 +700,32 @@ __global__ __launch_bounds__(kThreads) void pa_merge_kernel(const MergeParams p)
     const size_t stride = (size_t)kWaves * rec_floats;
     const int m_off = p.rec_heads * D + hh, l_off = p.rec_heads * D + p.rec_heads + hh;
     const int a_off = hh * D + lane * kPer;
-    float M = -INFINITY;
-    for (int j = first + wave; j <= last; j += kWaves) M = fmaxf(M, rec0[(size_t)(s + j) * stride + m_off]);
-    float L = 0.f, a[kPer];
+    float M = -INFINITY, L = 0.f, a[kPer];
 #pragma unroll
     for (int e = 0; e < kPer; ++e) a[e] = 0.f;
-    for (int j = first + wave; j <= last; j += kWaves) {
-        const float *r = rec0 + (size_t)(s + j) * stride;
-        const float f = __builtin_amdgcn_exp2f(r[m_off] - M);
-        L = fmaf(f, r[l_off], L);
+    for (int j0 = first + wave; j0 <= last; j0 += kUnroll * kWaves) {
+        float mj[kUnroll], lj[kUnroll], aj[kUnroll][kPer];
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) a[e] = fmaf(f, r[a_off + e], a[e]);
+        for (int u = 0; u < kUnroll; ++u) {
+            const int j = j0 + u * kWaves;
+            const bool ok = j <= last;
+            const float *r = rec0 + (size_t)(s + (ok ? j : first)) * stride;
+            mj[u] = ok ? r[m_off] : -INFINITY;
+            lj[u] = r[l_off];
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) aj[u][e] = r[a_off + e];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (mj[u] == -INFINITY) continue;   // past the last piece
+            const float mn = fmaxf(M, mj[u]);
+            const float c = __builtin_amdgcn_exp2f(M - mn);   // 0 while M is -inf
+            const float f = __builtin_amdgcn_exp2f(mj[u] - mn);
+            L = fmaf(f, lj[u], L * c);
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) a[e] = fmaf(f, aj[u][e], a[e] * c);
+            M = mn;
+        }
     }
     if (lane == 0) {
         lds_m[wave] = M;

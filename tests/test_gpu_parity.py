@@ -168,6 +168,28 @@ def test_split_vs_unsplit_and_reproducible():
     assert_parity(whole, ref, "unsplit")
 
 
+def test_workspace_reused_across_calls_and_shapes():
+    # One workspace serves a sequence of calls of different shapes and item
+    # sizes (no state carries over between calls): each result is
+    # bit-identical to a run with a fresh workspace.
+    note("workspace reuse")
+    cases = [C.make_case(5, 32, 8, 128, 16, ctx=(3000, 17, 0, 900, 1), seed=40, device=DEV)[1],
+             C.make_case(3, 8, 2, 64, 16, ctx=(250, 1000, 33), seed=41, device=DEV)[1],
+             C.make_case(4, 16, 2, 128, 256, ctx=(5000, 257, 4096, 2), seed=42, kv_dtype="int8",
+                         device=DEV)[1]]
+    splits = (0, 16, 512)
+    fresh = {(i, st): run(v, st).clone() for i, v in enumerate(cases) for st in splits}
+    need = max(B.workspace_bytes(B.shape_of(v["q"], v["k_cache"], v["block_tables"], st))
+               for v in cases for st in splits)
+    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device=DEV)   # garbage-filled
+    for rep in range(2):
+        for i, v in enumerate(cases):
+            for st in splits:
+                got = B.decode_views(v, split_tokens=st, workspace=ws)
+                torch.cuda.synchronize()
+                assert torch.equal(got.view(torch.int32), fresh[(i, st)].view(torch.int32)), (rep, i, st)
+
+
 def test_large_scores_stable():
     note("large scores")
     _, v = C.make_case(2, 8, 2, 128, 16, ctx=(600, 31), seed=37, device=DEV)
