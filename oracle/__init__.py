@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for PagedAttention decode -- TEST INFRASTRUCTURE ONLY.
+"""fp64 CPU oracle for PagedAttention decode and the KV write path -- TEST
+INFRASTRUCTURE ONLY.
 
 Only the test suite, the smoke check and the bench's ``cpu_baseline`` leg may
 import this package.  It shares no code with the HIP library or with the
@@ -8,7 +9,9 @@ arrays through ctypes.
 
 Every function here cites the passage it follows in ``oracle.c``'s header:
 the ybb.press page "LLM 推理 KV Cache 内存管理深度工程实践" sections 2.2
-(paged attention forward), 6.1 (INT8 KV quantization) and 6.2 (GQA sharing),
+(paged attention forward), 2.1 (BlockTable.append_slot: a token's global
+slot address block * block_size + offset), 6.1 (INT8 KV quantization) and 6.2
+(GQA sharing),
 and the t6page "KV cache" page, section "PagedAttention 的算子" (softmax after
 merging all blocks).
 
@@ -61,6 +64,11 @@ class OracleLib:
         lib.oracle_paged_decode_int8.restype = i32
         lib.oracle_quantize_int8_rows.argtypes = [P, i64, i32, P, P]
         lib.oracle_quantize_int8_rows.restype = None
+        lib.oracle_kv_write_bf16.argtypes = [P, P, P, i32, i32, i32, i64, i64, P, P, i32, i64]
+        lib.oracle_kv_write_bf16.restype = i32
+        lib.oracle_kv_write_int8.argtypes = [P, P, P, i32, i32, i32, i64, i64, P, P, P, P, i32,
+                                             i64]
+        lib.oracle_kv_write_int8.restype = i32
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i32
         lib.oracle_set_num_threads.argtypes = [i32]
@@ -180,3 +188,62 @@ def quantize_int8_rows(x, lib: "OracleLib | None" = None) -> tuple[np.ndarray, n
     L = lib.lib if lib is not None else _load()
     L.oracle_quantize_int8_rows(_ptr(x), rows, D, _ptr(codes), _ptr(scales))
     return codes, scales
+
+
+def slot_of(block_table_row, pos: int, block_size: int) -> int:
+    """Global slot address of logical token `pos` of a sequence whose logical
+    blocks map to block_table_row (ybb.press page, section 2.1: append_slot
+    hands out last_block * block_size + used_slots)."""
+    return int(block_table_row[pos // block_size]) * block_size + pos % block_size
+
+
+def _write_args(key_bits, value_bits, slots):
+    key_bits = _c(key_bits, np.uint16)
+    value_bits = _c(value_bits, np.uint16)
+    slots = _c(slots, np.int32)
+    if key_bits.ndim != 3 or value_bits.shape != key_bits.shape or slots.shape != key_bits.shape[:1]:
+        raise ValueError("key / value must be [T, Hkv, D] and slots [T]")
+    return key_bits, value_bits, slots
+
+
+def kv_write_bf16(key_bits, value_bits, slots, k_cache_bits, v_cache_bits,
+                  lib: "OracleLib | None" = None):
+    """(k_cache, v_cache) after storing token t's rows at slot slots[t] (copies;
+    the inputs are not modified).  bf16 as raw uint16 bits; caches
+    [NB, BS, Hkv, D]; a negative slot writes nothing."""
+    key_bits, value_bits, slots = _write_args(key_bits, value_bits, slots)
+    kc = np.array(_c(k_cache_bits, np.uint16), copy=True)
+    vc = np.array(_c(v_cache_bits, np.uint16), copy=True)
+    T, Hkv, D = key_bits.shape
+    NB, BS, Hkv2, D2 = kc.shape
+    if (Hkv2, D2) != (Hkv, D) or vc.shape != kc.shape:
+        raise ValueError("cache shape disagrees with key / value")
+    L = lib.lib if lib is not None else _load()
+    rc = L.oracle_kv_write_bf16(_ptr(key_bits), _ptr(value_bits), _ptr(slots), T, Hkv, D,
+                                Hkv * D, Hkv * D, _ptr(kc), _ptr(vc), BS, NB)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return kc, vc
+
+
+def kv_write_int8(key_bits, value_bits, slots, k_codes, v_codes, k_scales, v_scales,
+                  lib: "OracleLib | None" = None):
+    """(k_codes, v_codes, k_scales, v_scales) after quantizing and storing token
+    t's rows at slot slots[t] (copies).  Codes int8 [NB, BS, Hkv, D], scales
+    fp32 [NB, BS, Hkv]."""
+    key_bits, value_bits, slots = _write_args(key_bits, value_bits, slots)
+    kc = np.array(_c(k_codes, np.int8), copy=True)
+    vc = np.array(_c(v_codes, np.int8), copy=True)
+    ks = np.array(_c(k_scales, np.float32), copy=True)
+    vs = np.array(_c(v_scales, np.float32), copy=True)
+    T, Hkv, D = key_bits.shape
+    NB, BS, Hkv2, D2 = kc.shape
+    if (Hkv2, D2) != (Hkv, D) or vc.shape != kc.shape or ks.shape != (NB, BS, Hkv) or \
+            vs.shape != ks.shape:
+        raise ValueError("cache / scale shapes disagree with key / value")
+    L = lib.lib if lib is not None else _load()
+    rc = L.oracle_kv_write_int8(_ptr(key_bits), _ptr(value_bits), _ptr(slots), T, Hkv, D,
+                                Hkv * D, Hkv * D, _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs), BS, NB)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return kc, vc, ks, vs

@@ -1,5 +1,6 @@
 /*
- * oracle.c -- plain, slow, fp64 CPU reference for PagedAttention decode.
+ * oracle.c -- plain, slow, fp64 CPU reference for PagedAttention decode and
+ * for the KV write path that fills the paged cache (at the end of this file).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * bench's cpu_baseline leg may load this library.  It shares no code, header,
@@ -232,4 +233,101 @@ void oracle_quantize_int8_rows(const float *x, int64_t rows, int D, int8_t *code
             codes[r * D + i] = (int8_t)c;
         }
     }
+}
+
+/*
+ * KV write path: each new token's key and value rows are stored at the token
+ * slot the block table handed out for it.  The ybb.press page, section 2.1
+ * (BlockTable.append_slot), gives a token's global slot address as
+ * block * BS + offset (offset = slots already used in that block); the cache
+ * position is therefore block = slot / BS, offset = slot % BS, and token t's
+ * row for kv head g lands at cache[block, offset, g, :], in K and in V alike.
+ * A negative slot marks a token with no slot (append_slot returned None, or a
+ * padding token): nothing is written for it.
+ *
+ * key / value: bf16 bits; token t's row for kv head g starts at element
+ * t * key_stride + g * D (resp. value_stride).  slots: int32 [T].
+ * Checked before anything is written: every slot < NB * BS, and no slot
+ * appears twice (two tokens cannot own one slot).  Returns 0 or a negative
+ * code (the caches are then untouched).
+ */
+static int check_slots(const int32_t *slots, int T, int BS, int64_t NB)
+{
+    const int64_t n_slots = NB * (int64_t)BS;
+    int64_t n_valid = 0;
+    for (int t = 0; t < T; ++t) {
+        if (slots[t] >= 0 && (int64_t)slots[t] >= n_slots) return ORC_ERR_TABLE;
+        if (slots[t] >= 0) ++n_valid;
+    }
+    if (n_valid == 0) return ORC_OK;
+    unsigned char *seen = (unsigned char *)calloc((size_t)n_slots, 1);
+    if (!seen) return ORC_ERR_NOMEM;
+    int rc = ORC_OK;
+    for (int t = 0; t < T && rc == ORC_OK; ++t) {
+        if (slots[t] < 0) continue;
+        if (seen[slots[t]]) rc = ORC_ERR_ARG;
+        seen[slots[t]] = 1;
+    }
+    free(seen);
+    return rc;
+}
+
+int oracle_kv_write_bf16(const uint16_t *key, const uint16_t *value, const int32_t *slots,
+                         int T, int Hkv, int D, int64_t key_stride, int64_t value_stride,
+                         uint16_t *k_cache, uint16_t *v_cache, int BS, int64_t NB)
+{
+    if (T < 0 || Hkv <= 0 || D <= 0 || BS <= 0 || NB < 0) return ORC_ERR_ARG;
+    if (T > 0 && (!key || !value || !slots || !k_cache || !v_cache)) return ORC_ERR_ARG;
+    int rc = check_slots(slots, T, BS, NB);
+    if (rc != ORC_OK) return rc;
+    for (int t = 0; t < T; ++t) {
+        if (slots[t] < 0) continue;
+        const int64_t block = slots[t] / BS;
+        const int64_t offset = slots[t] % BS;
+        for (int g = 0; g < Hkv; ++g) {
+            const int64_t dst = ((block * BS + offset) * Hkv + g) * (int64_t)D;
+            for (int i = 0; i < D; ++i) {
+                k_cache[dst + i] = key[t * key_stride + (int64_t)g * D + i];
+                v_cache[dst + i] = value[t * value_stride + (int64_t)g * D + i];
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * int8 KV write path: as oracle_kv_write_bf16, but each (token, kv head) row
+ * is quantized on the way in with the section 6.1 recipe of the same page
+ * (oracle_quantize_int8_rows on the row widened exactly from bf16 to fp32);
+ * the codes go to the int8 caches [NB, BS, Hkv, D] and the row's scale to
+ * k_scales / v_scales [NB, BS, Hkv] at the same (block, offset, g).
+ */
+int oracle_kv_write_int8(const uint16_t *key, const uint16_t *value, const int32_t *slots,
+                         int T, int Hkv, int D, int64_t key_stride, int64_t value_stride,
+                         int8_t *k_cache, int8_t *v_cache, float *k_scales, float *v_scales,
+                         int BS, int64_t NB)
+{
+    if (T < 0 || Hkv <= 0 || D <= 0 || BS <= 0 || NB < 0) return ORC_ERR_ARG;
+    if (T > 0 && (!key || !value || !slots || !k_cache || !v_cache || !k_scales || !v_scales))
+        return ORC_ERR_ARG;
+    int rc = check_slots(slots, T, BS, NB);
+    if (rc != ORC_OK) return rc;
+    float *row = (float *)malloc(sizeof(float) * (size_t)D);
+    if (!row) return ORC_ERR_NOMEM;
+    for (int t = 0; t < T; ++t) {
+        if (slots[t] < 0) continue;
+        const int64_t block = slots[t] / BS;
+        const int64_t offset = slots[t] % BS;
+        for (int g = 0; g < Hkv; ++g) {
+            const int64_t cell = (block * BS + offset) * Hkv + g;
+            for (int i = 0; i < D; ++i)
+                row[i] = (float)bf16_bits_to_double(key[t * key_stride + (int64_t)g * D + i]);
+            oracle_quantize_int8_rows(row, 1, D, k_cache + cell * D, k_scales + cell);
+            for (int i = 0; i < D; ++i)
+                row[i] = (float)bf16_bits_to_double(value[t * value_stride + (int64_t)g * D + i]);
+            oracle_quantize_int8_rows(row, 1, D, v_cache + cell * D, v_scales + cell);
+        }
+    }
+    free(row);
+    return ORC_OK;
 }

@@ -22,6 +22,11 @@ Workloads (names say what they are; shapes follow the pages):
     [1024, 8192], K/V int8 with one fp32 scale per (token, kv head) from
     N(0,1) source data.
 
+New tokens for the KV write path (``make_new_tokens``, ``draw_slots``): key
+and value rows fp32 N(0, 1) rounded to bf16, and distinct destination slots
+drawn as a seeded random permutation of the pool's slots, optionally with a
+seeded fraction of tokens given no slot (-1).
+
 Recipe (the same for every workload):
   * context lengths: integer-uniform in [lo, hi] inclusive from a CPU
     ``torch.Generator`` seeded with the workload seed (or the fixed list);
@@ -239,6 +244,38 @@ def select_sequences(views: dict, seq_ids: Sequence[int], block_size: int) -> di
         out["k_scales"] = views["k_scales"].index_select(0, idx).cpu()
         out["v_scales"] = views["v_scales"].index_select(0, idx).cpu()
     return out
+
+
+def make_new_tokens(num_tokens: int, num_kv_heads: int, head_dim: int, seed: int,
+                    device="cpu", token_stride: Optional[int] = None):
+    """(key, value) bf16 [T, Hkv, d] for T new tokens: fp32 N(0, 1) rounded to bf16.
+
+    With token_stride (elements, >= Hkv * d) the rows are views into a wider
+    buffer, as when K and V are slices of a fused projection output."""
+    device = torch.device(device)
+    row = num_kv_heads * head_dim
+    stride = token_stride or row
+    if stride < row:
+        raise ValueError("token_stride smaller than a token's row")
+    gen = torch.Generator(device=device).manual_seed(seed * 104729 + 3)
+    buf = torch.empty((2, max(num_tokens, 1), stride), dtype=torch.bfloat16, device=device)
+    _fill_normal_bf16(buf, gen)
+    key = buf[0, :num_tokens, :row].unflatten(-1, (num_kv_heads, head_dim))
+    value = buf[1, :num_tokens, :row].unflatten(-1, (num_kv_heads, head_dim))
+    return key, value
+
+
+def draw_slots(num_tokens: int, num_slots: int, seed: int, pad_fraction: float = 0.0):
+    """int32 [T]: distinct token slots drawn at random from [0, num_slots), a
+    seeded fraction of them replaced by -1 (tokens without a slot)."""
+    if num_tokens > num_slots:
+        raise ValueError("more tokens than slots")
+    g = torch.Generator().manual_seed(seed * 15485863 + 11)
+    slots = torch.randperm(num_slots, generator=g)[:num_tokens].to(torch.int32)
+    if pad_fraction > 0 and num_tokens > 0:
+        pad = torch.rand(num_tokens, generator=g) < pad_fraction
+        slots[pad] = -1
+    return slots
 
 
 def bf16_bits(t: torch.Tensor):

@@ -34,6 +34,19 @@ MUTANTS = {
     "quant_divisor_128": ("float s = amax / 127.0f;", "float s = amax / 128.0f;"),
     "quant_truncates": ("nearbyintf(xr[i] / s)", "truncf(xr[i] / s)"),
     "max_not_subtracted_in_exp": ("double e = exp(scores[t] - m);", "double e = exp(scores[t] - 2.0 * m);"),
+    "write_block_mod": ("const int64_t block = slots[t] / BS;", "const int64_t block = slots[t] % BS;"),
+    "write_offset_div": ("const int64_t offset = slots[t] % BS;", "const int64_t offset = slots[t] / BS;"),
+    "write_key_into_v": ("v_cache[dst + i] = value[", "v_cache[dst + i] = key["),
+    "write_head_major": ("const int64_t dst = ((block * BS + offset) * Hkv + g) * (int64_t)D;",
+                         "const int64_t dst = ((block * Hkv + g) * BS + offset) * (int64_t)D;"),
+    "write_head_ignored": ("k_cache[dst + i] = key[t * key_stride + (int64_t)g * D + i];",
+                           "k_cache[dst + i] = key[t * key_stride + i];"),
+    "int8_write_cell_ignores_head": ("const int64_t cell = (block * BS + offset) * Hkv + g;",
+                                     "const int64_t cell = (block * BS + offset) * Hkv;"),
+    "int8_write_v_from_key": ("row[i] = (float)bf16_bits_to_double(value[",
+                              "row[i] = (float)bf16_bits_to_double(key["),
+    "int8_write_v_scale_into_k": ("v_cache + cell * D, v_scales + cell);",
+                                  "v_cache + cell * D, k_scales + cell);"),
 }
 
 PIN_FUNCS = [
@@ -48,6 +61,11 @@ PIN_FUNCS = [
     "test_quantizer_closed_form_properties",
     "test_int8_matches_bf16_on_lossless_values",
     "test_generator_int8_synthesis_matches_oracle_quantizer",
+    "test_write_then_decode_matches_sdpa_on_appended_context",
+    "test_write_places_rows_at_flat_slot_and_leaves_the_rest",
+    "test_write_rejects_out_of_range_and_duplicate_slots",
+    "test_int8_write_of_lossless_rows_is_exact_per_head",
+    "test_int8_write_error_bound_and_decode_against_dequantized_sdpa",
 ]
 
 RUNNER = r"""

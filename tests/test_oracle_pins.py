@@ -226,3 +226,131 @@ def test_generator_int8_synthesis_matches_oracle_quantizer():
     c1, s1 = I.synth_int8_rows(x)
     c2, s2 = oracle.quantize_int8_rows(x.numpy())
     assert np.array_equal(c1.numpy(), c2) and np.array_equal(s1.numpy(), s2)
+
+
+# ---------------------------------------------------------------------------
+# KV write path (ybb.press page, section 2.1: a token's slot address is
+# block * block_size + offset; section 6.1: int8 quantization on the way in).
+
+
+def _append_case(ctx, Hq=8, Hkv=2, D=64, bs=16, seed=31, kv_dtype="bf16"):
+    """A case whose tables already cover ctx + 1 tokens per sequence, with the
+    new token's K/V rows and the slot append_slot would hand out for it."""
+    full = tuple(c + 1 for c in ctx)
+    NB = sum((c + bs - 1) // bs for c in full) + 3
+    _, v = C.make_case(len(ctx), Hq, Hkv, D, bs, ctx=full, NB=NB, seed=seed, kv_dtype=kv_dtype)
+    key, value = I.make_new_tokens(len(ctx), Hkv, D, seed=seed)
+    bt = v["block_tables"].numpy()
+    slots = np.array([oracle.slot_of(bt[s], c, bs) for s, c in enumerate(ctx)], dtype=np.int32)
+    return v, key, value, slots
+
+
+def test_write_then_decode_matches_sdpa_on_appended_context():
+    # Storing the new token at its slot and decoding over ctx + 1 tokens must
+    # equal plain attention over [the old context ; the new token] -- this ties
+    # the slot split (block = slot / bs, offset = slot % bs), the K/V and head
+    # placement of the write to the decode's block-table reading.
+    ctx = (0, 15, 16, 31, 47, 100)
+    bs = 16
+    v, key, value, slots = _append_case(ctx, bs=bs)
+    kc, vc = oracle.kv_write_bf16(I.bf16_bits(key), I.bf16_bits(value), slots,
+                                  I.bf16_bits(v["k_cache"]), I.bf16_bits(v["v_cache"]))
+    w = dict(v, k_cache=torch.from_numpy(kc.view(np.int16)).view(torch.bfloat16),
+             v_cache=torch.from_numpy(vc.view(np.int16)).view(torch.bfloat16))
+    out = C.oracle_out(w)
+    q = v["q"].to(torch.float64)
+    for s, c in enumerate(ctx):
+        K, V = C.gathered(v, bs, s)               # old cache, first c + 1 tokens
+        K = np.concatenate([K[:, :c], key[s].double().numpy()[:, None]], axis=1)
+        V = np.concatenate([V[:, :c], value[s].double().numpy()[:, None]], axis=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[s][None, :, None, :], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+            scale=float(np.float32(v["scale"])), enable_gqa=True)[0, :, 0, :].numpy()
+        assert np.allclose(out[s], ref, rtol=0, atol=1e-12), s
+
+
+def test_write_places_rows_at_flat_slot_and_leaves_the_rest():
+    # The [NB, bs, Hkv, D] cache seen as [NB * bs, Hkv, D] rows is indexed by
+    # the slot address directly; slots of -1 write nothing; every other row is
+    # bit-identical to before.
+    NB, bs, Hkv, D, T = 6, 16, 4, 64, 40
+    gen = torch.Generator().manual_seed(32)
+    kc0 = torch.randn(NB, bs, Hkv, D, generator=gen).to(torch.bfloat16)
+    vc0 = torch.randn(NB, bs, Hkv, D, generator=gen).to(torch.bfloat16)
+    key, value = I.make_new_tokens(T, Hkv, D, seed=32)
+    slots = I.draw_slots(T, NB * bs, seed=32, pad_fraction=0.25).numpy()
+    assert (slots < 0).any() and (slots >= 0).any()
+    kc, vc = oracle.kv_write_bf16(I.bf16_bits(key), I.bf16_bits(value), slots,
+                                  I.bf16_bits(kc0), I.bf16_bits(vc0))
+    kflat, vflat = kc.reshape(NB * bs, Hkv, D), vc.reshape(NB * bs, Hkv, D)
+    k0, v0 = I.bf16_bits(kc0).reshape(NB * bs, Hkv, D), I.bf16_bits(vc0).reshape(NB * bs, Hkv, D)
+    kb, vb = I.bf16_bits(key), I.bf16_bits(value)
+    hit = np.zeros(NB * bs, dtype=bool)
+    for t, sl in enumerate(slots):
+        if sl >= 0:
+            assert np.array_equal(kflat[sl], kb[t]) and np.array_equal(vflat[sl], vb[t])
+            hit[sl] = True
+    assert np.array_equal(kflat[~hit], k0[~hit]) and np.array_equal(vflat[~hit], v0[~hit])
+
+
+def test_write_rejects_out_of_range_and_duplicate_slots():
+    NB, bs, Hkv, D = 2, 16, 1, 64
+    key, value = I.make_new_tokens(2, Hkv, D, seed=33)
+    z = np.zeros((NB, bs, Hkv, D), dtype=np.uint16)
+    for bad in ([0, NB * bs], [5, 5]):
+        with pytest.raises(ValueError):
+            oracle.kv_write_bf16(I.bf16_bits(key), I.bf16_bits(value),
+                                 np.array(bad, dtype=np.int32), z, z)
+
+
+def _lossless_rows(T, Hkv, D, seed):
+    """bf16 rows k * 2^-(5+g) (integer |k| <= 127, row maximum 127): exact in
+    bf16, they quantize to exactly (k, 2^-(5+g)) -- a different scale per head."""
+    gen = torch.Generator().manual_seed(seed)
+    k = torch.randint(-127, 128, (T, Hkv, D), generator=gen, dtype=torch.int64)
+    k[..., seed % D] = 127 if seed % 2 else -127
+    mult = torch.tensor([2.0 ** -(5 + g) for g in range(Hkv)], dtype=torch.float64)
+    return k, (k.double() * mult[None, :, None]).to(torch.bfloat16), mult
+
+
+def test_int8_write_of_lossless_rows_is_exact_per_head():
+    NB, bs, Hkv, D, T = 5, 16, 4, 128, 30
+    kk, key, mult = _lossless_rows(T, Hkv, D, seed=34)
+    vk, value, _ = _lossless_rows(T, Hkv, D, seed=35)
+    value = value * 2                       # V rows: scales 2^-(4+g), not K's
+    slots = I.draw_slots(T, NB * bs, seed=34).numpy()
+    z8 = np.zeros((NB, bs, Hkv, D), dtype=np.int8)
+    zs = np.full((NB, bs, Hkv), -1.0, dtype=np.float32)
+    kc, vc, ks, vs = oracle.kv_write_int8(I.bf16_bits(key), I.bf16_bits(value), slots,
+                                          z8, z8, zs, zs)
+    kc, vc = kc.reshape(NB * bs, Hkv, D), vc.reshape(NB * bs, Hkv, D)
+    ks, vs = ks.reshape(NB * bs, Hkv), vs.reshape(NB * bs, Hkv)
+    for t, sl in enumerate(slots):
+        assert np.array_equal(kc[sl], kk[t].numpy().astype(np.int8))
+        assert np.array_equal(vc[sl], vk[t].numpy().astype(np.int8))
+        assert np.array_equal(ks[sl], mult.numpy().astype(np.float32))
+        assert np.array_equal(vs[sl], 2 * mult.numpy().astype(np.float32))
+    untouched = np.setdiff1d(np.arange(NB * bs), slots)
+    assert np.all(ks[untouched] == -1.0) and np.all(kc[untouched] == 0)
+
+
+def test_int8_write_error_bound_and_decode_against_dequantized_sdpa():
+    # Random rows: codes in [-127, 127], each row's largest code is +-127, the
+    # dequantized value is within half a step of the source; decoding the
+    # written cache equals plain attention over the dequantized rows.
+    ctx = (1, 16, 33, 64)
+    bs = 16
+    v, key, value, slots = _append_case(ctx, D=128, seed=36, kv_dtype="int8")
+    kc, vc, ks, vs = oracle.kv_write_int8(
+        I.bf16_bits(key), I.bf16_bits(value), slots, v["k_cache"].numpy(), v["v_cache"].numpy(),
+        v["k_scales"].numpy(), v["v_scales"].numpy())
+    Hkv = key.shape[1]
+    for src, codes, scales in ((key, kc, ks), (value, vc, vs)):
+        c = codes.reshape(-1, Hkv, 128)[slots].astype(np.float64)
+        sc = scales.reshape(-1, Hkv)[slots].astype(np.float64)
+        assert np.all(np.abs(c).max(axis=-1) == 127)
+        err = np.abs(src.double().numpy() - c * sc[..., None])
+        assert np.all(err <= sc[..., None] * (0.5 + 1e-5))
+    w = dict(v, k_cache=torch.from_numpy(kc), v_cache=torch.from_numpy(vc),
+             k_scales=torch.from_numpy(ks), v_scales=torch.from_numpy(vs))
+    assert np.allclose(C.oracle_out(w), C.sdpa_reference(w, bs), rtol=0, atol=1e-12)
