@@ -21,6 +21,11 @@ bytes achieves on this device; `cpu_baseline` is the fp64 oracle timed on the
 host's cores on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload llama3_8b]
+
+With --workload kv_write_llama3_8b (or kv_write_int8_llama3_8b) it times the
+KV write path instead -- one paged_kv_write call per step, storing a
+16384-token prefill chunk into the paged cache -- and prints the same kind of
+line for it.
 """
 from __future__ import annotations
 
@@ -76,16 +81,17 @@ def event_ms(stream, fn, reps, before=None):
     return [a.elapsed_time(b) for a, b in ev]
 
 
-def measured_traffic(workload: str):
-    """Bytes per decode call from the committed counter summary, if it was
-    taken on the current kernel source."""
+def measured_traffic(workload: str, operation: str = "decode"):
+    """Bytes per call from the committed counter summary, if it was taken on
+    the current source of the operation's kernels."""
     from paged_kv_cache_393_amd import rocprof_summary as R
 
     path = os.path.join(PROFILES, f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("workload") != workload or rec.get("source_sha256") != R.source_sha256():
+    src = R.OPERATIONS[operation][1]
+    if rec.get("workload") != workload or rec.get("source_sha256") != R.source_sha256(src):
         return None
     return rec.get("bytes_per_call")
 
@@ -109,6 +115,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     B.load()   # fails loudly if the HIP library is missing
+    if args.workload in I.WRITE_WORKLOADS:
+        return bench_write(args)
     wl = I.WORKLOADS[args.workload]
     split = wl.split_tokens if args.split_tokens is None else args.split_tokens
     dev = torch.device("cuda:0")
@@ -228,6 +236,135 @@ def main() -> int:
 
     print(json.dumps(record), flush=True)
     return 0
+
+
+def bench_write(args) -> int:
+    """The KV write path on its own: one paged_kv_write(_int8) call per step."""
+    import torch
+
+    from paged_kv_cache_393_amd import accounting as A
+    from paged_kv_cache_393_amd import binding as B
+    from paged_kv_cache_393_amd import inputs as I
+    from paged_kv_cache_393_amd import probe as P
+
+    ww = I.WRITE_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = I.make_write_inputs(ww, dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    print(f"[bench] inputs for {ww.name} ready", file=sys.stderr, flush=True)
+
+    def step():
+        B.kv_write_inputs(inp, stream=stream)
+
+    flush_buf = None if args.no_flush else torch.ones((2 << 30) // 4, dtype=torch.float32,
+                                                       device=dev)
+
+    def evict():
+        if flush_buf is not None:
+            flush_buf.amax()
+
+    for _ in range(args.warmup):
+        evict()
+        step()
+    torch.cuda.synchronize()
+    ms = event_ms(stream, step, args.steps, before=evict)
+    ms_sorted = sorted(ms)
+    ms_mean = statistics.fmean(ms)
+    pct = lambda q: ms_sorted[min(len(ms_sorted) - 1, int(q * len(ms_sorted)))]
+    print(f"[bench] {args.steps} timed steps done", file=sys.stderr, flush=True)
+    T = ww.num_tokens
+    written = int((inp["slots"] >= 0).sum())
+    nbytes = A.write_bytes(T, written, ww.num_kv_heads, ww.head_dim, ww.kv_dtype)
+    t_s = ms_mean / 1e3
+    gbps = nbytes / t_s / 1e9
+
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            P.copy(src, dst, stream)
+        torch.cuda.synchronize()
+        del src, dst
+
+    record = {
+        "metric": "KV write path tokens/s and achieved HBM GB/s (% of peak), Llama-3-8B shape",
+        "value": T / t_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_mean,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": ww.kv_dtype,
+        "data": "synthetic (seeded N(0,1) bf16 K/V rows, random distinct slots)",
+        "config": {
+            "workload": ww.name, "num_tokens": T, "num_kv_heads": ww.num_kv_heads,
+            "head_dim": ww.head_dim, "block_size": ww.block_size, "num_blocks": ww.num_blocks,
+            "kv_dtype": ww.kv_dtype, "tokens_written": written,
+            "cache_evict_between_steps": "2 GiB read" if flush_buf is not None else None,
+        },
+        "pct_of_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
+        "ms_p10": pct(0.10), "ms_median": pct(0.50), "ms_p90": pct(0.90),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kv_write_kernel",
+            "achieved": gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS,
+            "traffic": measured_traffic(ww.name, "write"),
+            "algorithmic_bytes_per_call": nbytes,
+            "calls_per_step": 1,
+            "ms_per_call": ms_mean,
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_write(ww, inp),
+    }
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+def cpu_baseline_write(ww, inp):
+    """The oracle's write on the whole workload (host copies of the same
+    inputs), median of repeated runs, and whether it matches the GPU bytes."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_cache_393_amd import inputs as I
+
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    kb, vb = I.bf16_bits(inp["key"]), I.bf16_bits(inp["value"])
+    sl = inp["slots"].cpu().numpy()
+    if ww.kv_dtype == "bf16":
+        z = np.zeros(tuple(inp["k_cache"].shape), dtype=np.uint16)
+        fn = lambda: oracle.kv_write_bf16(kb, vb, sl, z, z)
+        got = (I.bf16_bits(inp["k_cache"]), I.bf16_bits(inp["v_cache"]))
+    else:
+        z = np.zeros(tuple(inp["k_cache"].shape), dtype=np.int8)
+        zs = np.zeros(tuple(inp["k_scales"].shape), dtype=np.float32)
+        fn = lambda: oracle.kv_write_int8(kb, vb, sl, z, z, zs, zs)
+        got = tuple(inp[k].cpu().numpy() for k in ("k_cache", "v_cache", "k_scales", "v_scales"))
+    times = []
+    ref = None
+    while sum(times) < 3.0 and len(times) < 25:
+        t = time.perf_counter()
+        ref = fn()
+        times.append(time.perf_counter() - t)
+    t_med = statistics.median(times)
+    same = all(np.array_equal(a.view(np.uint8), b.view(np.uint8)) for a, b in zip(got, ref))
+    return {
+        "value": ww.num_tokens / t_med,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"the whole workload ({ww.num_tokens} tokens), one thread, median of "
+                   f"{len(times)} runs of {t_med:.3f}s (the copy into fresh arrays included)"),
+        "bit_identical_to_gpu": bool(same),
+    }
 
 
 def cpu_baseline(wl, views0, out0, ctx, n_layers, budget_s):

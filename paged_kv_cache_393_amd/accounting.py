@@ -40,3 +40,19 @@ def decode_bytes(context_lens: Iterable[int], num_q_heads: int, num_kv_heads: in
 def decode_flops(context_lens: Iterable[int], num_q_heads: int, head_dim: int) -> int:
     """QK and PV multiply-adds (2 flops each) over every (query head, context token)."""
     return 4 * head_dim * num_q_heads * sum(int(c) for c in context_lens)
+
+
+def write_bytes(num_tokens: int, num_written: int, num_kv_heads: int, head_dim: int,
+                kv_dtype: str = "bf16") -> int:
+    """Algorithmic bytes of one KV write call: the slot of every token, the K
+    and V rows (bf16) of the tokens that have a slot, and what lands in the
+    cache -- the same rows in bf16, or int8 codes plus one fp32 scale per row."""
+    rows = 2 * num_written * num_kv_heads           # K and V rows moved
+    read = num_tokens * 4 + rows * head_dim * 2
+    if kv_dtype == "bf16":
+        written = rows * head_dim * 2
+    elif kv_dtype == "int8":
+        written = rows * (head_dim + 4)
+    else:
+        raise ValueError(kv_dtype)
+    return read + written

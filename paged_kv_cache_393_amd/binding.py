@@ -17,6 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "paged_attn.h")
+WRITE_HEADER = os.path.join(os.path.dirname(_HERE), "include", "paged_kv_write.h")
 
 PA_OK = 0
 PA_ERR_NULL = -1
@@ -31,6 +32,12 @@ class PaShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
         "max_blocks_per_seq", "num_blocks", "split_tokens")]
+
+
+class PaWriteShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_tokens", "num_kv_heads", "head_dim", "block_size", "num_blocks", "key_stride",
+        "value_stride")]
 
 
 class PagedAttnError(RuntimeError):
@@ -61,6 +68,11 @@ def load() -> ctypes.CDLL:
     lib.paged_attn_decode_int8.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, SP, P,
                                            ctypes.c_size_t, P]
     lib.paged_attn_decode_int8.restype = ctypes.c_int
+    WP = ctypes.POINTER(PaWriteShape)
+    lib.paged_kv_write.argtypes = [P, P, P, P, P, WP, P]
+    lib.paged_kv_write.restype = ctypes.c_int
+    lib.paged_kv_write_int8.argtypes = [P, P, P, P, P, P, P, WP, P]
+    lib.paged_kv_write_int8.restype = ctypes.c_int
     lib.paged_attn_strerror.argtypes = [ctypes.c_int]
     lib.paged_attn_strerror.restype = ctypes.c_char_p
     lib.paged_attn_abi_version.argtypes = []
@@ -70,10 +82,13 @@ def load() -> ctypes.CDLL:
 
 
 def header_functions() -> list:
-    """Names of the functions include/paged_attn.h declares."""
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(paged_attn_\w+)\s*\(", text)))
+    """Names of the functions the library's headers (include/paged_attn.h,
+    include/paged_kv_write.h) declare."""
+    names = set()
+    for h in (HEADER, WRITE_HEADER):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b((?:paged_attn|paged_kv)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def strerror(code: int) -> str:
@@ -198,3 +213,73 @@ def decode_views(views: dict, out=None, split_tokens: int = 0, workspace=None, s
     return decode(views["q"], views["k_cache"], views["v_cache"], views["block_tables"],
                   views["context_lens"], views["scale"], out=out, split_tokens=split_tokens,
                   workspace=workspace, stream=stream)
+
+
+def write_shape(key, k_cache, num_blocks=None) -> PaWriteShape:
+    """Shape record of a write of `key` [T, Hkv, d] (rows may be strided) into `k_cache`."""
+    T, Hkv, D = key.shape
+    NB, bs, Hkv2, D2 = k_cache.shape
+    if (Hkv2, D2) != (Hkv, D):
+        raise ValueError("key and cache disagree on kv heads / head_dim")
+    return PaWriteShape(T, Hkv, D, bs, NB if num_blocks is None else num_blocks, 0, 0)
+
+
+def _validate_write(key, value, slot_mapping, k_cache, v_cache, kv_dtype):
+    for name, t in (("key", key), ("value", value), ("slot_mapping", slot_mapping),
+                    ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    for name, t in (("key", key), ("value", value)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3:
+            raise TypeError(f"{name} must be bf16 [T, Hkv, d]")
+        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError(f"{name}: each token's [Hkv, d] rows must be contiguous")
+    if value.shape != key.shape:
+        raise ValueError("key and value shapes differ")
+    if slot_mapping.dtype != torch.int32 or tuple(slot_mapping.shape) != (key.shape[0],):
+        raise TypeError("slot_mapping must be int32 [T]")
+    if not slot_mapping.is_contiguous() or not k_cache.is_contiguous() or \
+            not v_cache.is_contiguous():
+        raise ValueError("slot_mapping and the caches must be contiguous")
+    if k_cache.dtype != kv_dtype or v_cache.dtype != kv_dtype or k_cache.shape != v_cache.shape:
+        raise TypeError(f"caches must be two {kv_dtype} tensors of one shape")
+
+
+def _write_shape_strided(key, value, k_cache):
+    sh = write_shape(key, k_cache)
+    sh.key_stride = key.stride(0) if key.shape[0] > 1 else 0
+    sh.value_stride = value.stride(0) if value.shape[0] > 1 else 0
+    return sh
+
+
+def kv_write(key, value, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """paged_kv_write: store token t's K/V rows at slot slot_mapping[t] (bf16 cache)."""
+    _validate_write(key, value, slot_mapping, k_cache, v_cache, torch.bfloat16)
+    sh = _write_shape_strided(key, value, k_cache)
+    _check(load().paged_kv_write(_ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(k_cache),
+                                 _ptr(v_cache), ctypes.byref(sh), _stream_handle(stream)))
+
+
+def kv_write_int8(key, value, slot_mapping, k_cache, v_cache, k_scales, v_scales,
+                  stream=None) -> None:
+    """paged_kv_write_int8: quantize token t's K/V rows and store them at slot_mapping[t]."""
+    _validate_write(key, value, slot_mapping, k_cache, v_cache, torch.int8)
+    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be a contiguous fp32 device tensor")
+        if tuple(t.shape) != tuple(k_cache.shape[:3]):
+            raise ValueError(f"{name} must be [num_blocks, block_size, num_kv_heads]")
+    sh = _write_shape_strided(key, value, k_cache)
+    _check(load().paged_kv_write_int8(_ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(k_cache),
+                                      _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+                                      ctypes.byref(sh), _stream_handle(stream)))
+
+
+def kv_write_inputs(inp: dict, stream=None) -> None:
+    """Run the write of a make_write_inputs() dict (bf16 or int8 cache)."""
+    if "k_scales" in inp:
+        kv_write_int8(inp["key"], inp["value"], inp["slots"], inp["k_cache"], inp["v_cache"],
+                      inp["k_scales"], inp["v_scales"], stream=stream)
+    else:
+        kv_write(inp["key"], inp["value"], inp["slots"], inp["k_cache"], inp["v_cache"],
+                 stream=stream)

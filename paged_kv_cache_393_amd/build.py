@@ -10,11 +10,12 @@ import sys
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(_HERE)
-# (source, output) of every HIP library: the decode path and the bench's
-# measurement kernels.
+# (sources, output) of every HIP library: the paged KV cache library (decode
+# and the KV write path) and the bench's measurement kernels.
 LIBS = [
-    (os.path.join(_HERE, "csrc", "paged_attn.hip"), os.path.join(_HERE, "libpagedattn.so")),
-    (os.path.join(_HERE, "csrc", "pa_probe.hip"), os.path.join(_HERE, "libpaprobe.so")),
+    ([os.path.join(_HERE, "csrc", "paged_attn.hip"), os.path.join(_HERE, "csrc", "kv_write.hip")],
+     os.path.join(_HERE, "libpagedattn.so")),
+    ([os.path.join(_HERE, "csrc", "pa_probe.hip")], os.path.join(_HERE, "libpaprobe.so")),
 ]
 LIB_PATH = LIBS[0][1]
 ARCH = "gfx950"
@@ -33,16 +34,16 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def _compile(source: str, out: str, verbose: bool) -> str:
+def _compile(sources: list, out: str, verbose: bool) -> str:
     tmp = out + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + [source, "-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + list(sources) + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}) on {source}:\n{msgs}")
+        raise RuntimeError(f"hipcc failed ({r.returncode}) on {sources}:\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
     os.replace(tmp, out)
@@ -51,8 +52,8 @@ def _compile(source: str, out: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     """Compile every HIP library for gfx950; returns the decode library's path."""
-    for source, out in LIBS:
-        _compile(source, out, verbose)
+    for sources, out in LIBS:
+        _compile(sources, out, verbose)
     return LIB_PATH
 
 

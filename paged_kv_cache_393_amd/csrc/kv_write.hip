@@ -1,0 +1,176 @@
+// kv_write.hip -- the KV write path for gfx950 (CDNA4) behind the C-ABI of
+// include/paged_kv_write.h: the new tokens' key and value rows are stored at
+// the token slots the block tables handed out (ybb.press page "LLM 推理 KV
+// Cache 内存管理深度工程实践", section 2.1: slot = block * block_size +
+// offset), optionally quantized to int8 on the way in (same page, 6.1).
+//
+// The work is pure data movement (plus, for int8, a per-row max and a
+// division per element), so the kernel is shaped for HBM: one group of
+// head_dim/8 lanes owns one (token, kv head) row and moves it with one 16-byte
+// load and one store per lane for K and the same for V.  The rows of one token
+// are adjacent in the input and, since the cache is [blocks, block_size, kv
+// heads, head_dim], also adjacent at the destination (row slot * Hkv + g), so
+// every wave reads and writes whole 64..256-byte runs.
+//
+// int8: the row's |x| maximum is reduced across the lane group with xor
+// shuffles; scale = max / 127 and code = x / scale use IEEE fp32 division
+// (correctly rounded) and round-half-to-even (v_rndne_f32), clamped to
+// [-127, 127].  These are the same fp32 operations in the same order as the
+// page's tensor recipe, so codes and scales are bit-reproducible.
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "paged_kv_write.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+struct WriteParams {
+    const uint16_t *key;
+    const uint16_t *value;
+    const int32_t *slots;
+    void *k_cache;
+    void *v_cache;
+    float *k_scales;
+    float *v_scales;
+    int64_t key_stride;    // elements
+    int64_t value_stride;  // elements
+    int64_t n_slots;       // num_blocks * block_size
+    uint32_t rows;         // num_tokens * num_kv_heads
+    uint32_t hkv;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Quantizes one lane's 8 values of a row whose lanes form a group of L
+// (consecutive lanes); returns the 8 codes packed little-endian and the row's
+// scale (the same in every lane of the group).
+template <int L>
+__device__ __forceinline__ uint2 quantize8(const uint4 w, float &scale_out) {
+    float x[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                  bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+    for (int m = 1; m < L; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, L));
+    const float s = amax / 127.0f;
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float c = 0.0f;
+        if (s != 0.0f) c = fminf(fmaxf(__builtin_rintf(x[i] / s), -127.0f), 127.0f);
+        const uint32_t byte = (uint32_t)(int32_t)c & 0xffu;
+        packed[i / 4] |= byte << (8 * (i % 4));
+    }
+    scale_out = s;
+    return make_uint2(packed[0], packed[1]);
+}
+
+template <int D, bool INT8>
+__global__ __launch_bounds__(kThreads) void kv_write_kernel(WriteParams p) {
+    constexpr int L = D / 8;                    // lanes per row, 8 bf16 (16 B) each
+    constexpr int kRowsPerGroup = kThreads / L;
+    const int lane = threadIdx.x % L;
+    const uint32_t row = blockIdx.x * (uint32_t)kRowsPerGroup + threadIdx.x / L;
+    // Every lane of a row's group takes the same exits, so the shuffles in
+    // quantize8 only ever involve lanes that are all active.
+    if (row >= p.rows) return;
+    const uint32_t t = row / p.hkv;
+    const uint32_t g = row - t * p.hkv;
+    const int32_t slot = p.slots[t];
+    if (slot < 0 || (int64_t)slot >= p.n_slots) return;
+
+    const uint4 kw = *reinterpret_cast<const uint4 *>(p.key + (int64_t)t * p.key_stride +
+                                                      g * D + lane * 8);
+    const uint4 vw = *reinterpret_cast<const uint4 *>(p.value + (int64_t)t * p.value_stride +
+                                                      g * D + lane * 8);
+    const int64_t cell = (int64_t)slot * p.hkv + g;   // (block, offset, g) row of the cache
+    if constexpr (!INT8) {
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.k_cache) + cell * D + lane * 8) = kw;
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.v_cache) + cell * D + lane * 8) = vw;
+    } else {
+        float ks, vs;
+        const uint2 kc = quantize8<L>(kw, ks);
+        const uint2 vc = quantize8<L>(vw, vs);
+        *reinterpret_cast<uint2 *>(static_cast<int8_t *>(p.k_cache) + cell * D + lane * 8) = kc;
+        *reinterpret_cast<uint2 *>(static_cast<int8_t *>(p.v_cache) + cell * D + lane * 8) = vc;
+        if (lane == 0) {
+            p.k_scales[cell] = ks;
+            p.v_scales[cell] = vs;
+        }
+    }
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int write_common(const void *key, const void *value, const int32_t *slots, void *kc, void *vc,
+                 float *ks, float *vs, const pa_write_shape *sh, void *stream, bool int8) {
+    if (!sh) return PA_ERR_NULL;
+    if (sh->num_tokens < 0 || sh->num_kv_heads < 1 || sh->block_size < 1 || sh->num_blocks < 1 ||
+        sh->key_stride < 0 || sh->value_stride < 0)
+        return PA_ERR_SHAPE;
+    if (sh->head_dim != 64 && sh->head_dim != 128) return PA_ERR_UNSUPPORTED;
+    const int64_t row = (int64_t)sh->num_kv_heads * sh->head_dim;
+    const int64_t kst = sh->key_stride ? sh->key_stride : row;
+    const int64_t vst = sh->value_stride ? sh->value_stride : row;
+    if (kst < row || vst < row) return PA_ERR_SHAPE;
+    const int64_t rows = (int64_t)sh->num_tokens * sh->num_kv_heads;
+    if (rows >= ((int64_t)1 << 27)) return PA_ERR_UNSUPPORTED;
+    if (rows == 0) return PA_OK;   // nothing to store; the pointers are not looked at
+    if (!key || !value || !slots || !kc || !vc) return PA_ERR_NULL;
+    if (int8 && (!ks || !vs)) return PA_ERR_NULL;
+    if (!aligned(key, 16) || !aligned(value, 16) || kst % 8 || vst % 8) return PA_ERR_ALIGNMENT;
+    if (int8 ? (!aligned(kc, 8) || !aligned(vc, 8) || !aligned(ks, 4) || !aligned(vs, 4))
+             : (!aligned(kc, 16) || !aligned(vc, 16)))
+        return PA_ERR_ALIGNMENT;
+
+    WriteParams p;
+    p.key = static_cast<const uint16_t *>(key);
+    p.value = static_cast<const uint16_t *>(value);
+    p.slots = slots;
+    p.k_cache = kc;
+    p.v_cache = vc;
+    p.k_scales = ks;
+    p.v_scales = vs;
+    p.key_stride = kst;
+    p.value_stride = vst;
+    p.n_slots = (int64_t)sh->num_blocks * sh->block_size;
+    p.rows = (uint32_t)rows;
+    p.hkv = (uint32_t)sh->num_kv_heads;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int rows_per_group = kThreads / (sh->head_dim / 8);
+    const dim3 grid((unsigned)((rows + rows_per_group - 1) / rows_per_group));
+    const dim3 block(kThreads);
+    if (sh->head_dim == 128) {
+        if (int8) hipLaunchKernelGGL((kv_write_kernel<128, true>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((kv_write_kernel<128, false>), grid, block, 0, st, p);
+    } else {
+        if (int8) hipLaunchKernelGGL((kv_write_kernel<64, true>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((kv_write_kernel<64, false>), grid, block, 0, st, p);
+    }
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_kv_write(const void *key, const void *value, const int32_t *slot_mapping,
+                   void *k_cache, void *v_cache, const pa_write_shape *shape, void *stream) {
+    return write_common(key, value, slot_mapping, k_cache, v_cache, nullptr, nullptr, shape,
+                        stream, false);
+}
+
+int paged_kv_write_int8(const void *key, const void *value, const int32_t *slot_mapping,
+                        int8_t *k_cache, int8_t *v_cache, float *k_scales, float *v_scales,
+                        const pa_write_shape *shape, void *stream) {
+    return write_common(key, value, slot_mapping, k_cache, v_cache, k_scales, v_scales, shape,
+                        stream, true);
+}
+
+}  // extern "C"

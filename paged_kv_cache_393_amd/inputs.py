@@ -278,6 +278,52 @@ def draw_slots(num_tokens: int, num_slots: int, seed: int, pad_fraction: float =
     return slots
 
 
+@dataclasses.dataclass(frozen=True)
+class WriteWorkload:
+    """A KV write: num_tokens new tokens stored into a pool of num_blocks blocks."""
+    name: str
+    num_tokens: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    seed: int
+    kv_dtype: str = "bf16"
+    pad_fraction: float = 0.0
+
+
+WRITE_WORKLOADS = {
+    # A 16384-token prefill chunk of one Llama-3-8B-shaped layer (8 kv heads,
+    # d 128, block_size 16) filling a 1024-block pool: every slot written once,
+    # in a random order of slots.
+    "kv_write_llama3_8b": WriteWorkload("kv_write_llama3_8b", 16384, 8, 128, 16, 1024, seed=6),
+    "kv_write_int8_llama3_8b": WriteWorkload("kv_write_int8_llama3_8b", 16384, 8, 128, 16, 1024,
+                                             seed=7, kv_dtype="int8"),
+}
+
+
+def make_write_inputs(ww: WriteWorkload, device="cpu") -> dict:
+    """key / value bf16 [T, Hkv, d], slots int32 [T] (a seeded random choice of
+    distinct pool slots) and the destination caches (bf16 zeros, or int8 zeros
+    with zero scales) of a write workload."""
+    device = torch.device(device)
+    key, value = make_new_tokens(ww.num_tokens, ww.num_kv_heads, ww.head_dim, ww.seed, device)
+    slots = draw_slots(ww.num_tokens, ww.num_blocks * ww.block_size, ww.seed, ww.pad_fraction)
+    shape = (ww.num_blocks, ww.block_size, ww.num_kv_heads, ww.head_dim)
+    out = {"workload": ww, "key": key, "value": value, "slots": slots.to(device)}
+    if ww.kv_dtype == "bf16":
+        out["k_cache"] = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        out["v_cache"] = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+    elif ww.kv_dtype == "int8":
+        out["k_cache"] = torch.zeros(shape, dtype=torch.int8, device=device)
+        out["v_cache"] = torch.zeros(shape, dtype=torch.int8, device=device)
+        out["k_scales"] = torch.zeros(shape[:3], dtype=torch.float32, device=device)
+        out["v_scales"] = torch.zeros(shape[:3], dtype=torch.float32, device=device)
+    else:
+        raise ValueError(f"unknown kv dtype {ww.kv_dtype}")
+    return out
+
+
 def bf16_bits(t: torch.Tensor):
     """Raw uint16 bit patterns (numpy) of a bf16 tensor."""
     import numpy as np

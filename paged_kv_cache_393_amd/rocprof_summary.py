@@ -3,11 +3,13 @@
     # kernel durations (rocprofv3 --kernel-trace --stats --output-format csv)
     python -m paged_kv_cache_393_amd.rocprof_summary stats OUTDIR --out FILE --command "..."
 
-    # HBM traffic per decode call from two counter runs (FETCH_SIZE, then
-    # WRITE_SIZE) of a bench run that also copied --copy-bytes bytes with the
-    # probe copy kernel, whose counter readings scale the decode kernels'
+    # HBM traffic per call of an operation (decode, or the KV write) from two
+    # counter runs (FETCH_SIZE, then WRITE_SIZE) of a bench run that also
+    # copied --copy-bytes bytes with the probe copy kernel, whose counter
+    # readings calibrate those of the operation's kernels
     python -m paged_kv_cache_393_amd.rocprof_summary traffic --fetch DIR1 --write DIR2 \\
-        --copy-bytes N --workload NAME --out FILE --command "..." --command "..."
+        --copy-bytes N --workload NAME --operation decode|write --out FILE \\
+        --command "..." --command "..."
 
 Only reads the CSV files rocprofv3 wrote; nothing here touches the GPU.
 """
@@ -24,7 +26,14 @@ import sys
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(_HERE, "csrc", "paged_attn.hip")
-KERNELS = ("pa_decode_kernel", "pa_merge_kernel", "probe_copy_kernel", "probe_read_kernel")
+WRITE_SOURCE = os.path.join(_HERE, "csrc", "kv_write.hip")
+KERNELS = ("pa_decode_kernel", "pa_merge_kernel", "kv_write_kernel", "probe_copy_kernel",
+           "probe_read_kernel")
+# The kernels of each timed operation and the source file they are built from.
+OPERATIONS = {
+    "decode": (("pa_decode_kernel", "pa_merge_kernel"), KERNEL_SOURCE),
+    "write": (("kv_write_kernel",), WRITE_SOURCE),
+}
 
 
 def source_sha256(path: str = KERNEL_SOURCE) -> str:
@@ -74,7 +83,8 @@ def cmd_stats(a) -> int:
     for r in rows:
         lines.append(f"{short_name(r['kernel']):<28} {r['calls']:>6} {r['avg_ns'] / 1e3:>9.2f} "
                      f"{r['min_ns'] / 1e3:>9.2f} {r['max_ns'] / 1e3:>9.2f} {r['pct']:>6.2f}")
-    lines += ["", f"decode kernel source sha256: {source_sha256()}"]
+    kernels, src = OPERATIONS[a.operation]
+    lines += ["", f"{os.path.basename(src)} sha256: {source_sha256(src)}"]
     text = "\n".join(lines) + "\n"
     with open(a.out, "w") as f:
         f.write(text)
@@ -91,7 +101,8 @@ def cmd_traffic(a) -> int:
     sw = a.copy_bytes / (copy_w * 1024.0)
     per_kernel = {}
     total = 0.0
-    for k in ("pa_decode_kernel", "pa_merge_kernel"):
+    kernels, src = OPERATIONS[a.operation]
+    for k in kernels:
         fk = fetch.get(k, {}).get("FETCH_SIZE", 0.0)
         wk = write.get(k, {}).get("WRITE_SIZE", 0.0)
         b = fk * 1024.0 * sf + wk * 1024.0 * sw
@@ -99,7 +110,8 @@ def cmd_traffic(a) -> int:
         total += b
     rec = {
         "workload": a.workload,
-        "source_sha256": source_sha256(),
+        "source": os.path.basename(src),
+        "source_sha256": source_sha256(src),
         "copy_calibration": {"bytes": a.copy_bytes, "fetch_kib": copy_f, "write_kib": copy_w,
                              "fetch_scale": sf, "write_scale": sw},
         "kernels": per_kernel,
@@ -121,6 +133,7 @@ def main(argv=None) -> int:
     s.add_argument("--out", required=True)
     s.add_argument("--command", required=True)
     s.add_argument("--title", default="")
+    s.add_argument("--operation", choices=sorted(OPERATIONS), default="decode")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -128,6 +141,7 @@ def main(argv=None) -> int:
     t.add_argument("--workload", required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--command", action="append", default=[])
+    t.add_argument("--operation", choices=sorted(OPERATIONS), default="decode")
     a = ap.parse_args(argv)
     return cmd_stats(a) if a.what == "stats" else cmd_traffic(a)
 
