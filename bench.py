@@ -280,6 +280,16 @@ def bench_write(args) -> int:
     t_s = ms_mean / 1e3
     gbps = nbytes / t_s / 1e9
 
+    copy_gbps = None
+    if not args.no_probe:
+        # a plain copy moving the same number of bytes (half read, half written)
+        half = (nbytes // 2 // 16) * 16
+        src = torch.ones(half // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        pms = event_ms(stream, lambda: P.copy(src, dst, stream), 20, before=evict)
+        copy_gbps = 2 * half / (statistics.median(pms) / 1e3) / 1e9
+        del src, dst
+
     if args.copy_bytes > 0:
         src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -309,6 +319,7 @@ def bench_write(args) -> int:
         },
         "pct_of_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
         "ms_p10": pct(0.10), "ms_median": pct(0.50), "ms_p90": pct(0.90),
+        "hbm_copy_probe_gbps": copy_gbps,
         "roofline": {
             "bound": "hbm",
             "kernel": "kv_write_kernel",

@@ -12,11 +12,12 @@
 // heads, head_dim], also adjacent at the destination (row slot * Hkv + g), so
 // every wave reads and writes whole 64..256-byte runs.
 //
-// int8: the row's |x| maximum is reduced across the lane group with xor
-// shuffles; scale = max / 127 and code = x / scale use IEEE fp32 division
-// (correctly rounded) and round-half-to-even (v_rndne_f32), clamped to
-// [-127, 127].  These are the same fp32 operations in the same order as the
-// page's tensor recipe, so codes and scales are bit-reproducible.
+// int8: the row's |x| maximum is reduced across the lane group with DPP lane
+// moves; scale = max / 127 (IEEE fp32 division) and code = x / scale
+// rounded half to even (v_rndne_f32), clamped to [-127, 127] -- the page's
+// tensor recipe in fp32.  The quotient is formed by a reciprocal multiply
+// where that provably rounds to the same code, by the IEEE division elsewhere
+// (see quantize8), so codes and scales are exactly those of the recipe.
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -46,9 +47,39 @@ struct WriteParams {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// A DPP lane move inside each 16-lane row (kCtrl: a gfx9 dpp_ctrl value).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+// Maximum over each aligned group of L lanes (8 or 16), left in every lane
+// of the group, without LDS: quad permutations xor 1 and xor 2 give the max of
+// each quad, the half-row mirror (lane i <-> 7 - i) joins the two quads of an
+// 8-lane half, the row mirror (lane i <-> 15 - i) the two halves of a row.
+// Every move reads a lane of the same group.
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(L == 8 || L == 16, "groups of 8 or 16 lanes");
+    v = fmaxf(v, dpp_move<0xB1>(v));     // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_move<0x4E>(v));     // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_move<0x141>(v));    // row_half_mirror
+    if constexpr (L == 16) v = fmaxf(v, dpp_move<0x140>(v));   // row_mirror
+    return v;
+}
+
 // Quantizes one lane's 8 values of a row whose lanes form a group of L
 // (consecutive lanes); returns the 8 codes packed little-endian and the row's
 // scale (the same in every lane of the group).
+//
+// code = rint(x / s) needs only the integer the quotient rounds to.  With
+// r = rcp(s) (v_rcp_f32, within 1 ulp) the product x * r is within
+// 127 * 3 * 2^-24 < 2^-15 of the correctly rounded quotient (|x| <= amax, so
+// |x / s| <= 127 * (1 + 2^-23)).  Unless the product lies within 2^-12 of a
+// half-integer, both round to the same integer.  Lanes where it does (about
+// 1e-4 of the values) and rows whose scale is too small for a finite
+// reciprocal take the IEEE division instead, so every code is exactly
+// rint(x / s).
 template <int L>
 __device__ __forceinline__ uint2 quantize8(const uint4 w, float &scale_out) {
     float x[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
@@ -56,14 +87,18 @@ __device__ __forceinline__ uint2 quantize8(const uint4 w, float &scale_out) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-#pragma unroll
-    for (int m = 1; m < L; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, L));
+    amax = group_max<L>(amax);
     const float s = amax / 127.0f;
+    const bool fast_row = amax >= 0x1p-96f;
+    const float r = __builtin_amdgcn_rcpf(s);
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+        float q = x[i] * r;
+        const float frac = q - floorf(q);
+        if (!fast_row || fabsf(frac - 0.5f) < 0x1p-12f) q = x[i] / s;
         float c = 0.0f;
-        if (s != 0.0f) c = fminf(fmaxf(__builtin_rintf(x[i] / s), -127.0f), 127.0f);
+        if (s != 0.0f) c = fminf(fmaxf(__builtin_rintf(q), -127.0f), 127.0f);
         const uint32_t byte = (uint32_t)(int32_t)c & 0xffu;
         packed[i / 4] |= byte << (8 * (i % 4));
     }
@@ -77,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(WriteParams p) {
     constexpr int kRowsPerGroup = kThreads / L;
     const int lane = threadIdx.x % L;
     const uint32_t row = blockIdx.x * (uint32_t)kRowsPerGroup + threadIdx.x / L;
-    // Every lane of a row's group takes the same exits, so the shuffles in
+    // Every lane of a row's group takes the same exits, so the lane moves in
     // quantize8 only ever involve lanes that are all active.
     if (row >= p.rows) return;
     const uint32_t t = row / p.hkv;

@@ -208,3 +208,56 @@ def test_full_size_write_workload_bit_exact(name):
         assert np.array_equal(inp["v_cache"].cpu().numpy(), rv)
         assert np.array_equal(inp["k_scales"].cpu().numpy(), rks)
         assert np.array_equal(inp["v_scales"].cpu().numpy(), rvs)
+
+
+def _dense_bf16_rows(amaxes, D):
+    """Rows of D bf16 values: for each row maximum a, element 0 is a and the
+    others run through EVERY bf16 value x with a/512 <= |x| <= a (both signs),
+    so every quotient x / (a / 127) that can round to a non-zero code occurs."""
+    allbf = (np.arange(0, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    rows = []
+    for a in amaxes:
+        xs = allbf[(allbf <= a) & (allbf >= a / 512)]
+        xs = np.concatenate([xs, -xs])
+        for start in range(0, xs.size, D - 1):
+            chunk = xs[start:start + D - 1]
+            row = np.zeros(D, dtype=np.float32)
+            row[0] = a
+            row[1:1 + chunk.size] = chunk
+            rows.append(row)
+    return torch.from_numpy(np.stack(rows)).to(torch.bfloat16)
+
+
+def test_int8_write_every_bf16_value_for_many_scales():
+    # The kernel forms x / scale by a reciprocal multiply where that provably
+    # gives the same rounded code and by IEEE division near half-integers;
+    # over all bf16 inputs of 48 rows maxima (powers of two, whose quotients
+    # hit half-integers exactly, and random ones) the codes must be the
+    # oracle's, which always divides.
+    note("int8 write exhaustive bf16 quotients")
+    gen = torch.Generator().manual_seed(215)
+    pow2 = [2.0 ** e for e in range(-20, 21, 4)]
+    rand = (torch.rand(37, generator=gen, dtype=torch.float64) * 60 - 30).exp2().tolist()
+    amaxes = [float(torch.tensor(a).to(torch.bfloat16)) for a in pow2 + rand]
+    D, Hkv = 128, 1
+    rows = _dense_bf16_rows(amaxes, D)
+    T = rows.shape[0]
+    key = rows.reshape(T, Hkv, D).to(DEV)
+    value = (-rows).flip(0).reshape(T, Hkv, D).contiguous().to(DEV)
+    NB, bs = (T + 15) // 16, 16
+    slots = torch.randperm(NB * bs, generator=gen)[:T].to(torch.int32)
+    kc = torch.zeros(NB, bs, Hkv, D, dtype=torch.int8, device=DEV)
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros(NB, bs, Hkv, dtype=torch.float32, device=DEV)
+    vs = torch.zeros_like(ks)
+    B.kv_write_int8(key, value, slots.to(DEV), kc, vc, ks, vs)
+    torch.cuda.synchronize()
+    z8 = np.zeros((NB, bs, Hkv, D), dtype=np.int8)
+    zs = np.zeros((NB, bs, Hkv), dtype=np.float32)
+    rk, rv, rks, rvs = oracle.kv_write_int8(I.bf16_bits(key), I.bf16_bits(value), slots.numpy(),
+                                            z8, z8, zs, zs)
+    for got, ref, what in ((kc, rk, "k codes"), (vc, rv, "v codes"), (ks, rks, "k scales"),
+                           (vs, rvs, "v scales")):
+        g = got.cpu().numpy()
+        assert np.array_equal(g.view(np.uint8), ref.view(np.uint8)), \
+            f"{what}: {int((g != ref).sum())} of {g.size} differ"
