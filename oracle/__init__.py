@@ -10,8 +10,8 @@ arrays through ctypes.
 Every function here cites the passage it follows in ``oracle.c``'s header:
 the ybb.press page "LLM 推理 KV Cache 内存管理深度工程实践" sections 2.2
 (paged attention forward), 2.1 (BlockTable.append_slot: a token's global
-slot address block * block_size + offset), 6.1 (INT8 KV quantization) and 6.2
-(GQA sharing),
+slot address block * block_size + offset), 6.1 (INT8 KV quantization, and the
+cast of the cache to FP8 E4M3) and 6.2 (GQA sharing),
 and the t6page "KV cache" page, section "PagedAttention 的算子" (softmax after
 merging all blocks).
 
@@ -69,6 +69,15 @@ class OracleLib:
         lib.oracle_kv_write_int8.argtypes = [P, P, P, i32, i32, i32, i64, i64, P, P, P, P, i32,
                                              i64]
         lib.oracle_kv_write_int8.restype = i32
+        lib.oracle_paged_decode_fp8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                                i64, ctypes.c_float, P]
+        lib.oracle_paged_decode_fp8.restype = i32
+        lib.oracle_kv_write_fp8.argtypes = [P, P, P, i32, i32, i32, i64, i64, P, P, i32, i64]
+        lib.oracle_kv_write_fp8.restype = i32
+        lib.oracle_fp8_e4m3_decode_array.argtypes = [P, i64, P]
+        lib.oracle_fp8_e4m3_decode_array.restype = None
+        lib.oracle_fp8_e4m3_encode_array.argtypes = [P, i64, P]
+        lib.oracle_fp8_e4m3_encode_array.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i32
         lib.oracle_set_num_threads.argtypes = [i32]
@@ -178,6 +187,44 @@ def paged_decode_int8(q_bits, k_codes, v_codes, k_scales, v_scales, block_tables
     return out
 
 
+def paged_decode_fp8(q_bits, k_codes, v_codes, block_tables, context_lens, scale,
+                     lib: "OracleLib | None" = None) -> np.ndarray:
+    """out[s,h,:] (float64) for an FP8 E4M3 cache given as uint8 codes."""
+    q_bits = _c(q_bits, np.uint16)
+    k_codes = _c(k_codes, np.uint8)
+    v_codes = _c(v_codes, np.uint8)
+    bt = _c(block_tables, np.int32)
+    cl = _c(context_lens, np.int32)
+    if v_codes.shape != k_codes.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    S, Hq, Hkv, D, BS, MB, NB = _check_shapes(q_bits, k_codes, bt, cl)
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    L = lib.lib if lib is not None else _load()
+    rc = L.oracle_paged_decode_fp8(_ptr(q_bits), _ptr(k_codes), _ptr(v_codes), _ptr(bt), _ptr(cl),
+                                   S, Hq, Hkv, D, BS, MB, NB, ctypes.c_float(scale), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return out
+
+
+def fp8_e4m3_decode(codes, lib: "OracleLib | None" = None) -> np.ndarray:
+    """float64 values of E4M3 codes (uint8, any shape)."""
+    codes = _c(codes, np.uint8)
+    out = np.zeros(codes.shape, dtype=np.float64)
+    L = lib.lib if lib is not None else _load()
+    L.oracle_fp8_e4m3_decode_array(_ptr(codes), codes.size, _ptr(out))
+    return out
+
+
+def fp8_e4m3_encode(x, lib: "OracleLib | None" = None) -> np.ndarray:
+    """uint8 E4M3 codes of float64 values x (any shape): the cast to float8_e4m3fn."""
+    x = _c(x, np.float64)
+    out = np.zeros(x.shape, dtype=np.uint8)
+    L = lib.lib if lib is not None else _load()
+    L.oracle_fp8_e4m3_encode_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
 def quantize_int8_rows(x, lib: "OracleLib | None" = None) -> tuple[np.ndarray, np.ndarray]:
     """(codes int8 [..., D], scales fp32 [...]) for fp32 rows x [..., D]."""
     x = _c(x, np.float32)
@@ -247,3 +294,21 @@ def kv_write_int8(key_bits, value_bits, slots, k_codes, v_codes, k_scales, v_sca
     if rc != 0:
         raise ValueError(f"oracle rejected the inputs (code {rc})")
     return kc, vc, ks, vs
+
+
+def kv_write_fp8(key_bits, value_bits, slots, k_codes, v_codes, lib: "OracleLib | None" = None):
+    """(k_codes, v_codes) after casting token t's rows to FP8 E4M3 and storing
+    them at slot slots[t] (copies).  Codes uint8 [NB, BS, Hkv, D]."""
+    key_bits, value_bits, slots = _write_args(key_bits, value_bits, slots)
+    kc = np.array(_c(k_codes, np.uint8), copy=True)
+    vc = np.array(_c(v_codes, np.uint8), copy=True)
+    T, Hkv, D = key_bits.shape
+    NB, BS, Hkv2, D2 = kc.shape
+    if (Hkv2, D2) != (Hkv, D) or vc.shape != kc.shape:
+        raise ValueError("cache shape disagrees with key / value")
+    L = lib.lib if lib is not None else _load()
+    rc = L.oracle_kv_write_fp8(_ptr(key_bits), _ptr(value_bits), _ptr(slots), T, Hkv, D,
+                               Hkv * D, Hkv * D, _ptr(kc), _ptr(vc), BS, NB)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return kc, vc

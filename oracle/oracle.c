@@ -34,7 +34,9 @@
  *     G consecutive query heads shares one KV head (read as g = h / G).
  *   - same ybb.press page, section 6.1 (INT8 KV): symmetric quantization with
  *     scale = amax(|x|) / 127 over the head dimension; the int8 entry point
- *     dequantizes k_t = code * scale before the definition above.
+ *     dequantizes k_t = code * scale before the definition above.  The same
+ *     section casts the cache to FP8 E4M3 (float8_e4m3fn) with no scale; the
+ *     fp8 entry point decodes each code exactly before the definition above.
  *
  * Precision: every input is widened exactly to double (bf16 -> double and
  * int8 -> double are exact; the fp32 scale is taken as double(scale_f32)).
@@ -82,11 +84,70 @@ void oracle_set_num_threads(int n)
 }
 
 /* Element kinds of the KV cache. */
-enum { KV_BF16 = 0, KV_INT8 = 1 };
+enum { KV_BF16 = 0, KV_INT8 = 1, KV_FP8 = 2 };
+
+/*
+ * FP8 E4M3 (the OCP "FN" variant that torch.float8_e4m3fn names; the ybb.press
+ * page, section 6.1, casts the cache to it for inference): 1 sign bit, 4
+ * exponent bits with bias 7, 3 mantissa bits, no infinities, and NaN only for
+ * exponent and mantissa all ones (codes 0x7F and 0xFF).  Exponent field 0 holds
+ * the subnormals m * 2^-9.  Decoded exactly to double.
+ */
+double oracle_fp8_e4m3_to_double(uint8_t code)
+{
+    const int sign = code >> 7;
+    const int e = (code >> 3) & 15;
+    const int m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/*
+ * The code of x after the cast to E4M3: the nearest finite E4M3 value, ties
+ * to the even code (mantissa LSB 0).  A magnitude that rounds past the largest
+ * finite value 448 (i.e. above the midpoint 464 between 448 and the next step
+ * 480, which is the NaN pattern), an infinity and a NaN give the NaN code with
+ * x's sign -- the conversion torch's cast performs.  Found by comparing x with
+ * every finite code, so no bit tricks are involved.
+ */
+uint8_t oracle_fp8_e4m3_from_double(double x)
+{
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    if (isnan(x) || isinf(x)) return (uint8_t)(sign | 0x7F);
+    const double a = fabs(x);
+    if (a > 464.0) return (uint8_t)(sign | 0x7F);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {            /* non-negative finite codes */
+        const double d = fabs(oracle_fp8_e4m3_to_double((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* Array forms of the two conversions above (for the tests). */
+void oracle_fp8_e4m3_decode_array(const uint8_t *codes, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_fp8_e4m3_to_double(codes[i]);
+}
+
+void oracle_fp8_e4m3_encode_array(const double *x, int64_t n, uint8_t *codes)
+{
+    for (int64_t i = 0; i < n; ++i) codes[i] = oracle_fp8_e4m3_from_double(x[i]);
+}
 
 typedef struct {
     int kind;
-    const void *k;          /* [NB, BS, Hkv, D] bf16 bits or int8 codes */
+    const void *k;          /* [NB, BS, Hkv, D] bf16 bits, int8 codes or fp8 codes */
     const void *v;
     const float *k_scales;  /* [NB, BS, Hkv], int8 only */
     const float *v_scales;
@@ -100,6 +161,9 @@ static double kv_elem(const kv_src *src, int which_v, int64_t b, int r, int g, i
     if (src->kind == KV_BF16) {
         const uint16_t *base = (const uint16_t *)(which_v ? src->v : src->k);
         return bf16_bits_to_double(base[slot * D + i]);
+    } else if (src->kind == KV_FP8) {
+        const uint8_t *base = (const uint8_t *)(which_v ? src->v : src->k);
+        return oracle_fp8_e4m3_to_double(base[slot * D + i]);
     } else {
         const int8_t *base = (const int8_t *)(which_v ? src->v : src->k);
         const float *sc = which_v ? src->v_scales : src->k_scales;
@@ -205,6 +269,21 @@ int oracle_paged_decode_int8(const uint16_t *q, const int8_t *k_cache, const int
                              float scale, double *out)
 {
     kv_src src = {KV_INT8, k_cache, v_cache, k_scales, v_scales};
+    return decode_common(q, &src, block_tables, context_lens, S, Hq, Hkv, D, BS, MB, NB, scale, out);
+}
+
+/*
+ * FP8 E4M3 KV cache (ybb.press page, section 6.1: the cache cast to
+ * float8_e4m3fn, no scale): k_cache / v_cache hold codes [NB, BS, Hkv, D],
+ * each decoded exactly by oracle_fp8_e4m3_to_double.  The rest as in the bf16
+ * entry point.
+ */
+int oracle_paged_decode_fp8(const uint16_t *q, const uint8_t *k_cache, const uint8_t *v_cache,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            int S, int Hq, int Hkv, int D, int BS, int MB, int64_t NB,
+                            float scale, double *out)
+{
+    kv_src src = {KV_FP8, k_cache, v_cache, NULL, NULL};
     return decode_common(q, &src, block_tables, context_lens, S, Hq, Hkv, D, BS, MB, NB, scale, out);
 }
 
@@ -329,5 +408,35 @@ int oracle_kv_write_int8(const uint16_t *key, const uint16_t *value, const int32
         }
     }
     free(row);
+    return ORC_OK;
+}
+
+/*
+ * FP8 KV write path: as oracle_kv_write_bf16, each element of the token's
+ * bf16 K / V rows cast to its E4M3 code (oracle_fp8_e4m3_from_double; the
+ * bf16 value widens exactly) and stored at the same cache position.
+ */
+int oracle_kv_write_fp8(const uint16_t *key, const uint16_t *value, const int32_t *slots,
+                        int T, int Hkv, int D, int64_t key_stride, int64_t value_stride,
+                        uint8_t *k_cache, uint8_t *v_cache, int BS, int64_t NB)
+{
+    if (T < 0 || Hkv <= 0 || D <= 0 || BS <= 0 || NB < 0) return ORC_ERR_ARG;
+    if (T > 0 && (!key || !value || !slots || !k_cache || !v_cache)) return ORC_ERR_ARG;
+    int rc = check_slots(slots, T, BS, NB);
+    if (rc != ORC_OK) return rc;
+    for (int t = 0; t < T; ++t) {
+        if (slots[t] < 0) continue;
+        const int64_t block = slots[t] / BS;
+        const int64_t offset = slots[t] % BS;
+        for (int g = 0; g < Hkv; ++g) {
+            const int64_t dst = ((block * BS + offset) * Hkv + g) * (int64_t)D;
+            for (int i = 0; i < D; ++i) {
+                k_cache[dst + i] = oracle_fp8_e4m3_from_double(
+                    bf16_bits_to_double(key[t * key_stride + (int64_t)g * D + i]));
+                v_cache[dst + i] = oracle_fp8_e4m3_from_double(
+                    bf16_bits_to_double(value[t * value_stride + (int64_t)g * D + i]));
+            }
+        }
+    }
     return ORC_OK;
 }

@@ -21,6 +21,7 @@ Workloads (names say what they are; shapes follow the pages):
   * ``int8_llama3_8b``: 32/8/128, block_size 16, batch 128, contexts uniform in
     [1024, 8192], K/V int8 with one fp32 scale per (token, kv head) from
     N(0,1) source data.
+  * ``fp8_llama3_8b``: the same shapes with the K/V cache in FP8 E4M3.
 
 New tokens for the KV write path (``make_new_tokens``, ``draw_slots``): key
 and value rows fp32 N(0, 1) rounded to bf16, and distinct destination slots
@@ -36,6 +37,8 @@ Recipe (the same for every workload):
     sequence's last block are 0;
   * q, K, V: fp32 N(0, 1) from a generator on the target device seeded with
     the workload seed, rounded to bf16 (round-to-nearest-even);
+  * fp8 cache: fp32 N(0, 1) cast to float8_e4m3fn by torch (the cast of the
+    ybb.press page, section 6.1), no scale;
   * int8 cache: fp32 N(0, 1) source rows of head_dim, one row per (token slot,
     kv head), turned into codes and scales by the symmetric amax/127 recipe
     of the ybb.press page, section 6.1 (round half to even, zero rows get
@@ -65,7 +68,7 @@ class Workload:
     num_blocks: Optional[int] = None           # None: exactly what the contexts need
     max_blocks_per_seq: Optional[int] = None   # None: ceil(max possible ctx / block_size)
     num_layers: int = 1                        # > 1: layered [2, L, NB, bs, Hkv, d] cache
-    kv_dtype: str = "bf16"                     # "bf16" or "int8"
+    kv_dtype: str = "bf16"                     # "bf16", "int8" or "fp8"
     split_tokens: int = 0                      # 0: let the library choose
 
     @property
@@ -89,6 +92,8 @@ WORKLOADS = {
                               ctx_range=(2048, 32768), num_layers=4),
     "int8_llama3_8b": Workload("int8_llama3_8b", 128, 32, 8, 128, 16, seed=5,
                                ctx_range=(1024, 8192), kv_dtype="int8"),
+    "fp8_llama3_8b": Workload("fp8_llama3_8b", 128, 32, 8, 128, 16, seed=9,
+                              ctx_range=(1024, 8192), kv_dtype="fp8"),
 }
 
 
@@ -136,6 +141,14 @@ def _fill_normal_bf16(t: torch.Tensor, gen: torch.Generator, chunk_elems: int = 
                                             dtype=torch.float32).to(torch.bfloat16)
 
 
+def _fill_normal_fp8(t: torch.Tensor, gen: torch.Generator, chunk_elems: int = 1 << 27):
+    flat = t.view(-1)
+    for start in range(0, flat.numel(), chunk_elems):
+        n = min(chunk_elems, flat.numel() - start)
+        flat[start:start + n] = torch.randn(n, generator=gen, device=t.device,
+                                            dtype=torch.float32).to(torch.float8_e4m3fn)
+
+
 def synth_int8_rows(x: torch.Tensor):
     """Codes + scales for fp32 rows x [..., d] by the symmetric amax/127 recipe."""
     amax = x.abs().amax(dim=-1)
@@ -164,7 +177,8 @@ def make_inputs(wl: Workload, device="cpu") -> dict:
 
     Keys: ``q`` bf16 [L, S, Hq, d] (L = num_layers), ``block_tables`` int32
     [S, MB], ``context_lens`` int32 [S], ``num_blocks``, ``scale`` (python
-    float, 1/sqrt(d)), and either ``kv`` bf16 [2, L, NB, bs, Hkv, d] or
+    float, 1/sqrt(d)), and either ``kv`` bf16 (or float8_e4m3fn) [2, L, NB,
+    bs, Hkv, d] or
     ``kv_codes`` int8 [2, L, NB, bs, Hkv, d] + ``kv_scales`` fp32
     [2, L, NB, bs, Hkv].  Use :func:`layer_views` for per-layer tensors.
     """
@@ -195,6 +209,10 @@ def make_inputs(wl: Workload, device="cpu") -> dict:
         _fill_int8(codes, scales, gen)
         out["kv_codes"] = codes
         out["kv_scales"] = scales
+    elif wl.kv_dtype == "fp8":
+        kv = torch.empty(shape, dtype=torch.float8_e4m3fn, device=device)
+        _fill_normal_fp8(kv, gen)
+        out["kv"] = kv
     else:
         raise ValueError(f"unknown kv dtype {wl.kv_dtype}")
     return out
@@ -299,6 +317,8 @@ WRITE_WORKLOADS = {
     "kv_write_llama3_8b": WriteWorkload("kv_write_llama3_8b", 16384, 8, 128, 16, 1024, seed=6),
     "kv_write_int8_llama3_8b": WriteWorkload("kv_write_int8_llama3_8b", 16384, 8, 128, 16, 1024,
                                              seed=7, kv_dtype="int8"),
+    "kv_write_fp8_llama3_8b": WriteWorkload("kv_write_fp8_llama3_8b", 16384, 8, 128, 16, 1024,
+                                            seed=8, kv_dtype="fp8"),
 }
 
 
@@ -314,6 +334,9 @@ def make_write_inputs(ww: WriteWorkload, device="cpu") -> dict:
     if ww.kv_dtype == "bf16":
         out["k_cache"] = torch.zeros(shape, dtype=torch.bfloat16, device=device)
         out["v_cache"] = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+    elif ww.kv_dtype == "fp8":
+        out["k_cache"] = torch.zeros(shape, dtype=torch.float8_e4m3fn, device=device)
+        out["v_cache"] = torch.zeros(shape, dtype=torch.float8_e4m3fn, device=device)
     elif ww.kv_dtype == "int8":
         out["k_cache"] = torch.zeros(shape, dtype=torch.int8, device=device)
         out["v_cache"] = torch.zeros(shape, dtype=torch.int8, device=device)

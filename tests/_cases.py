@@ -30,6 +30,9 @@ def oracle_out(views) -> np.ndarray:
     q = I.bf16_bits(views["q"])
     bt = views["block_tables"].cpu().numpy()
     cl = views["context_lens"].cpu().numpy()
+    if views["k_cache"].dtype == torch.float8_e4m3fn:
+        return oracle.paged_decode_fp8(q, fp8_codes(views["k_cache"]), fp8_codes(views["v_cache"]),
+                                       bt, cl, views["scale"])
     if "k_scales" in views:
         return oracle.paged_decode_int8(q, views["k_cache"].cpu().numpy(),
                                         views["v_cache"].cpu().numpy(),
@@ -37,6 +40,11 @@ def oracle_out(views) -> np.ndarray:
                                         views["v_scales"].cpu().numpy(), bt, cl, views["scale"])
     return oracle.paged_decode_bf16(q, I.bf16_bits(views["k_cache"]), I.bf16_bits(views["v_cache"]),
                                     bt, cl, views["scale"])
+
+
+def fp8_codes(t: torch.Tensor) -> np.ndarray:
+    """uint8 codes (numpy) of a float8_e4m3fn tensor."""
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy()
 
 
 def used_blocks(views, bs):
@@ -58,6 +66,8 @@ def poison(views, bs, value=float("nan"), table_pad=-1):
     ctx = views["context_lens"].cpu().tolist()
     int8 = kc.dtype == torch.int8
     fill = -128 if int8 else value
+    if kc.dtype == torch.float8_e4m3fn:
+        fill = float("nan")
     bt_cpu = bt.cpu()
     for s, c in enumerate(ctx):
         n = (c + bs - 1) // bs

@@ -47,6 +47,17 @@ MUTANTS = {
                               "row[i] = (float)bf16_bits_to_double(key["),
     "int8_write_v_scale_into_k": ("v_cache + cell * D, v_scales + cell);",
                                   "v_cache + cell * D, k_scales + cell);"),
+    "fp8_exponent_bias_8": ("v = ldexp(1.0 + m / 8.0, e - 7);", "v = ldexp(1.0 + m / 8.0, e - 8);"),
+    "fp8_subnormal_as_normal": ("v = ldexp((double)m, -9);", "v = ldexp(1.0 + m / 8.0, -7);"),
+    "fp8_ties_to_odd": ("(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
+    "fp8_saturates": ("if (a > 464.0) return (uint8_t)(sign | 0x7F);",
+                      "if (a > 464.0) return (uint8_t)(sign | 0x7E);"),
+    "fp8_nan_loses_sign": ("if (isnan(x) || isinf(x)) return (uint8_t)(sign | 0x7F);",
+                           "if (isnan(x) || isinf(x)) return (uint8_t)0x7F;"),
+    "fp8_cache_read_as_integers": ("return oracle_fp8_e4m3_to_double(base[slot * D + i]);",
+                                   "return (double)base[slot * D + i];"),
+    "fp8_write_value_from_key": ("v_cache[dst + i] = oracle_fp8_e4m3_from_double(\n                    bf16_bits_to_double(value[",
+                                 "v_cache[dst + i] = oracle_fp8_e4m3_from_double(\n                    bf16_bits_to_double(key["),
 }
 
 PIN_FUNCS = [
@@ -66,6 +77,11 @@ PIN_FUNCS = [
     "test_write_rejects_out_of_range_and_duplicate_slots",
     "test_int8_write_of_lossless_rows_is_exact_per_head",
     "test_int8_write_error_bound_and_decode_against_dequantized_sdpa",
+    "test_fp8_decode_of_every_code_matches_torch",
+    "test_fp8_cast_of_every_bf16_matches_torch",
+    "test_fp8_decode_matches_sdpa_on_decoded_cache",
+    "test_fp8_matches_bf16_on_the_same_values",
+    "test_fp8_write_then_decode_matches_sdpa_on_appended_context",
 ]
 
 RUNNER = r"""

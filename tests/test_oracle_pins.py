@@ -354,3 +354,69 @@ def test_int8_write_error_bound_and_decode_against_dequantized_sdpa():
     w = dict(v, k_cache=torch.from_numpy(kc), v_cache=torch.from_numpy(vc),
              k_scales=torch.from_numpy(ks), v_scales=torch.from_numpy(vs))
     assert np.allclose(C.oracle_out(w), C.sdpa_reference(w, bs), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 KV cache (ybb.press page, section 6.1: the cache cast to
+# float8_e4m3fn).  torch's float8_e4m3fn type is an independent library
+# implementation of the same format and cast.
+
+
+def test_fp8_decode_of_every_code_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.fp8_e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 2      # 0x7F and 0xFF
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))   # -0 is 0x80
+    assert ours[0x7E] == 448.0 and ours[1] == 2.0 ** -9 and ours[8] == 2.0 ** -6
+
+
+def test_fp8_cast_of_every_bf16_matches_torch():
+    # Every bf16 bit pattern (finite, subnormal, +-inf, NaN): our cast must give
+    # torch's code, including ties to even, the subnormal range and the NaN
+    # code for magnitudes past 464 and for infinities.
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    ref = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = oracle.fp8_e4m3_encode(x.to(torch.float64).numpy())
+    bad = np.nonzero(ours != ref)[0]
+    assert bad.size == 0, [(hex(int(bits[i])), int(ours[i]), int(ref[i])) for i in bad[:8]]
+
+
+def test_fp8_decode_matches_sdpa_on_decoded_cache():
+    _, v = C.make_case(3, 8, 2, 128, 16, ctx=(64, 3, 129), seed=41, kv_dtype="fp8")
+    assert np.allclose(C.oracle_out(v), C.sdpa_reference(v, 16), rtol=0, atol=1e-12)
+
+
+def test_fp8_matches_bf16_on_the_same_values():
+    # Every finite E4M3 value is exact in bf16: a bf16 cache holding the decoded
+    # codes must give bit for bit the same output as the fp8 entry point.
+    _, v8 = C.make_case(2, 4, 2, 64, 16, ctx=(23, 40), seed=42, kv_dtype="fp8")
+    vb = dict(v8, k_cache=v8["k_cache"].to(torch.bfloat16), v_cache=v8["v_cache"].to(torch.bfloat16))
+    assert np.array_equal(C.oracle_out(v8), C.oracle_out(vb))
+
+
+def test_fp8_write_then_decode_matches_sdpa_on_appended_context():
+    # The new token, cast to E4M3 and stored at its slot, then decode over
+    # ctx + 1 tokens == plain attention over [old context ; cast new token].
+    ctx = (0, 15, 16, 100)
+    bs = 16
+    v, key, value, slots = _append_case(ctx, bs=bs, seed=43, kv_dtype="fp8")
+    kc, vc = oracle.kv_write_fp8(I.bf16_bits(key), I.bf16_bits(value), slots,
+                                 C.fp8_codes(v["k_cache"]), C.fp8_codes(v["v_cache"]))
+    w = dict(v, k_cache=torch.from_numpy(kc).view(torch.float8_e4m3fn),
+             v_cache=torch.from_numpy(vc).view(torch.float8_e4m3fn))
+    out = C.oracle_out(w)
+    q = v["q"].to(torch.float64)
+    for s, c in enumerate(ctx):
+        K, V = C.gathered(v, bs, s)
+        kn = key[s].to(torch.float8_e4m3fn).to(torch.float64).numpy()[:, None]
+        vn = value[s].to(torch.float8_e4m3fn).to(torch.float64).numpy()[:, None]
+        K = np.concatenate([K[:, :c], kn], axis=1)
+        V = np.concatenate([V[:, :c], vn], axis=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[s][None, :, None, :], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+            scale=float(np.float32(v["scale"])), enable_gqa=True)[0, :, 0, :].numpy()
+        assert np.allclose(out[s], ref, rtol=0, atol=1e-12), s
