@@ -22,7 +22,7 @@ host's cores on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload llama3_8b]
 
-With --workload kv_write_llama3_8b (or kv_write_int8_llama3_8b) it times the
+With --workload kv_write_llama3_8b (or kv_write_int8_ / kv_write_fp8_llama3_8b) it times the
 KV write path instead -- one paged_kv_write call per step, storing a
 16384-token prefill chunk into the paged cache -- and prints the same kind of
 line for it.
@@ -164,7 +164,7 @@ def main() -> int:
                                 wl.block_size, wl.kv_dtype)
     step_bytes = L * call_bytes
     kv_bytes = L * sum(ctx) * (A.kv_bytes_per_token(1, wl.num_kv_heads, wl.head_dim,
-                                                     1 if wl.kv_dtype == "int8" else 2)
+                                                     2 if wl.kv_dtype == "bf16" else 1)
                                + (2 * wl.num_kv_heads * 4 if wl.kv_dtype == "int8" else 0))
     flops = L * A.decode_flops(ctx, wl.num_q_heads, wl.head_dim)
     t_s = ms_mean / 1e3
@@ -239,7 +239,7 @@ def main() -> int:
 
 
 def bench_write(args) -> int:
-    """The KV write path on its own: one paged_kv_write(_int8) call per step."""
+    """The KV write path on its own: one paged_kv_write(_int8 / _fp8) call per step."""
     import torch
 
     from paged_kv_cache_393_amd import accounting as A
@@ -338,43 +338,59 @@ def bench_write(args) -> int:
     return 0
 
 
-def cpu_baseline_write(ww, inp):
-    """The oracle's write on the whole workload (host copies of the same
-    inputs), median of repeated runs, and whether it matches the GPU bytes."""
+def cpu_baseline_write(ww, inp, budget_s=3.0):
+    """The oracle's write on a prefix of the workload's tokens sized to about
+    budget_s per run (host copies of the same inputs; the whole workload when
+    it fits), median of repeated runs scaled to all tokens, and whether the
+    sampled tokens' cache rows match the GPU's bytes."""
     import numpy as np
+    import torch
 
     import oracle
     from paged_kv_cache_393_amd import inputs as I
 
     if not os.path.exists(oracle.LIB_PATH):
         oracle.build()
-    kb, vb = I.bf16_bits(inp["key"]), I.bf16_bits(inp["value"])
-    sl = inp["slots"].cpu().numpy()
+    kb_all, vb_all = I.bf16_bits(inp["key"]), I.bf16_bits(inp["value"])
+    sl_all = inp["slots"].cpu().numpy()
+    shape = tuple(inp["k_cache"].shape)
+    rows = lambda a: a.reshape(shape[0] * shape[1], *a.shape[2:])
     if ww.kv_dtype == "bf16":
-        z = np.zeros(tuple(inp["k_cache"].shape), dtype=np.uint16)
-        fn = lambda: oracle.kv_write_bf16(kb, vb, sl, z, z)
+        z = np.zeros(shape, dtype=np.uint16)
+        run = lambda n: oracle.kv_write_bf16(kb_all[:n], vb_all[:n], sl_all[:n], z, z)
         got = (I.bf16_bits(inp["k_cache"]), I.bf16_bits(inp["v_cache"]))
+    elif ww.kv_dtype == "fp8":
+        z = np.zeros(shape, dtype=np.uint8)
+        run = lambda n: oracle.kv_write_fp8(kb_all[:n], vb_all[:n], sl_all[:n], z, z)
+        got = tuple(inp[k].view(torch.uint8).cpu().numpy() for k in ("k_cache", "v_cache"))
     else:
-        z = np.zeros(tuple(inp["k_cache"].shape), dtype=np.int8)
+        z = np.zeros(shape, dtype=np.int8)
         zs = np.zeros(tuple(inp["k_scales"].shape), dtype=np.float32)
-        fn = lambda: oracle.kv_write_int8(kb, vb, sl, z, z, zs, zs)
+        run = lambda n: oracle.kv_write_int8(kb_all[:n], vb_all[:n], sl_all[:n], z, z, zs, zs)
         got = tuple(inp[k].cpu().numpy() for k in ("k_cache", "v_cache", "k_scales", "v_scales"))
-    times = []
-    ref = None
-    while sum(times) < 3.0 and len(times) < 25:
+    T = ww.num_tokens
+    t = time.perf_counter()
+    run(min(T, 256))
+    per_tok = (time.perf_counter() - t) / min(T, 256)
+    n = max(256, min(T, int(budget_s / max(per_tok, 1e-12))))
+    times, ref = [], None
+    while sum(times) < budget_s and len(times) < 25:
         t = time.perf_counter()
-        ref = fn()
+        ref = run(n)
         times.append(time.perf_counter() - t)
     t_med = statistics.median(times)
-    same = all(np.array_equal(a.view(np.uint8), b.view(np.uint8)) for a, b in zip(got, ref))
+    written = sl_all[:n][sl_all[:n] >= 0]
+    same = all(np.array_equal(rows(a)[written].view(np.uint8), rows(b)[written].view(np.uint8))
+               for a, b in zip(got, ref))
     return {
-        "value": ww.num_tokens / t_med,
+        "value": n / t_med,
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"the whole workload ({ww.num_tokens} tokens), one thread, median of "
-                   f"{len(times)} runs of {t_med:.3f}s (the copy into fresh arrays included)"),
-        "bit_identical_to_gpu": bool(same),
+        "sample": (f"the first {n} of {T} tokens, one thread, median of {len(times)} runs of "
+                   f"{t_med:.3f}s (the copy of the caches into fresh arrays included), "
+                   f"tokens/s of the sample"),
+        "bit_identical_to_gpu_on_sample": bool(same),
     }
 
 
@@ -383,6 +399,7 @@ def cpu_baseline(wl, views0, out0, ctx, n_layers, budget_s):
     context-token count.  The sample is a prefix of the batch sized to about
     budget_s of work; small samples are timed several times (median)."""
     import numpy as np
+    import torch
 
     import oracle
     from paged_kv_cache_393_amd import inputs as I
@@ -396,7 +413,11 @@ def cpu_baseline(wl, views0, out0, ctx, n_layers, budget_s):
         qb = I.bf16_bits(sub["q"])
         bt = sub["block_tables"].numpy()
         cl = sub["context_lens"].numpy()
-        if "k_scales" in sub:
+        if sub["k_cache"].dtype == torch.float8_e4m3fn:
+            args = (qb, sub["k_cache"].view(torch.uint8).numpy(),
+                    sub["v_cache"].view(torch.uint8).numpy(), bt, cl, sub["scale"])
+            fn = oracle.paged_decode_fp8
+        elif "k_scales" in sub:
             args = (qb, sub["k_cache"].numpy(), sub["v_cache"].numpy(), sub["k_scales"].numpy(),
                     sub["v_scales"].numpy(), bt, cl, sub["scale"])
             fn = oracle.paged_decode_int8

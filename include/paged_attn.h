@@ -121,6 +121,21 @@ int paged_attn_decode_int8(const void *q, const int8_t *k_cache, const int8_t *v
                            float *out, const pa_shape *shape, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/*
+ * FP8 E4M3 KV cache: each element is a float8_e4m3fn code (OCP E4M3 "FN": 1
+ * sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, NaN = codes
+ * 0x7F / 0xFF, largest finite 448), the cast of the cache that the ybb.press
+ * page, section 6.1, gives for inference; there is no scale.
+ *   k_cache, v_cache  uint8 codes [num_blocks, block_size, num_kv_heads, head_dim]
+ * Each code is decoded exactly (every E4M3 value is a bf16 value) inside the
+ * kernel; everything else as paged_attn_decode.  A NaN code in a token the
+ * context reads makes that sequence's output NaN, as the definition says.
+ */
+int paged_attn_decode_fp8(const void *q, const uint8_t *k_cache, const uint8_t *v_cache,
+                          const int32_t *block_tables, const int32_t *context_lens, float scale,
+                          float *out, const pa_shape *shape, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Static description of an error code; never NULL. */
 const char *paged_attn_strerror(int code);
 

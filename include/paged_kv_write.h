@@ -1,7 +1,8 @@
 /*
  * paged_kv_write.h -- C-ABI of the KV write path of the MI355X (gfx950)
  * paged KV cache library: storing the new tokens' keys and values into the
- * paged cache that paged_attn_decode reads.
+ * paged cache that the paged_attn_decode entry points read (bf16, int8 or
+ * FP8 E4M3).
  *
  * The operation: token t of the call owns the global token slot
  * slot_mapping[t], the address that BlockTable.append_slot hands out on the
@@ -76,6 +77,18 @@ int paged_kv_write(const void *key, const void *value, const int32_t *slot_mappi
 int paged_kv_write_int8(const void *key, const void *value, const int32_t *slot_mapping,
                         int8_t *k_cache, int8_t *v_cache, float *k_scales, float *v_scales,
                         const pa_write_shape *shape, void *stream);
+
+/*
+ * FP8 E4M3 cache: each element is cast to its float8_e4m3fn code (the cast of
+ * the same page, section 6.1, as torch performs it): round to nearest even,
+ * subnormals kept, a magnitude past 464 (beyond the largest finite value 448),
+ * an infinity or a NaN gives the NaN code with the value's sign (0x7F / 0xFF).
+ * No scale.  k_cache / v_cache: uint8 codes [num_blocks, block_size,
+ * num_kv_heads, head_dim], 8-byte aligned.  One kernel launch.
+ */
+int paged_kv_write_fp8(const void *key, const void *value, const int32_t *slot_mapping,
+                       uint8_t *k_cache, uint8_t *v_cache, const pa_write_shape *shape,
+                       void *stream);
 
 #ifdef __cplusplus
 }

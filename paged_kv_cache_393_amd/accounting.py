@@ -28,6 +28,8 @@ def decode_bytes(context_lens: Iterable[int], num_q_heads: int, num_kv_heads: in
         kv = tokens * kv_bytes_per_token(1, num_kv_heads, head_dim, 2)
     elif kv_dtype == "int8":
         kv = tokens * (kv_bytes_per_token(1, num_kv_heads, head_dim, 1) + 2 * num_kv_heads * 4)
+    elif kv_dtype == "fp8":
+        kv = tokens * kv_bytes_per_token(1, num_kv_heads, head_dim, 1)
     else:
         raise ValueError(kv_dtype)
     S = len(ctx)
@@ -46,13 +48,16 @@ def write_bytes(num_tokens: int, num_written: int, num_kv_heads: int, head_dim: 
                 kv_dtype: str = "bf16") -> int:
     """Algorithmic bytes of one KV write call: the slot of every token, the K
     and V rows (bf16) of the tokens that have a slot, and what lands in the
-    cache -- the same rows in bf16, or int8 codes plus one fp32 scale per row."""
+    cache -- the same rows in bf16, int8 codes plus one fp32 scale per row, or
+    FP8 codes."""
     rows = 2 * num_written * num_kv_heads           # K and V rows moved
     read = num_tokens * 4 + rows * head_dim * 2
     if kv_dtype == "bf16":
         written = rows * head_dim * 2
     elif kv_dtype == "int8":
         written = rows * (head_dim + 4)
+    elif kv_dtype == "fp8":
+        written = rows * head_dim
     else:
         raise ValueError(kv_dtype)
     return read + written

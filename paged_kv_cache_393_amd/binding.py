@@ -73,6 +73,11 @@ def load() -> ctypes.CDLL:
     lib.paged_kv_write.restype = ctypes.c_int
     lib.paged_kv_write_int8.argtypes = [P, P, P, P, P, P, P, WP, P]
     lib.paged_kv_write_int8.restype = ctypes.c_int
+    lib.paged_attn_decode_fp8.argtypes = [P, P, P, P, P, ctypes.c_float, P, SP, P,
+                                          ctypes.c_size_t, P]
+    lib.paged_attn_decode_fp8.restype = ctypes.c_int
+    lib.paged_kv_write_fp8.argtypes = [P, P, P, P, P, WP, P]
+    lib.paged_kv_write_fp8.restype = ctypes.c_int
     lib.paged_attn_strerror.argtypes = [ctypes.c_int]
     lib.paged_attn_strerror.restype = ctypes.c_char_p
     lib.paged_attn_abi_version.argtypes = []
@@ -203,8 +208,35 @@ def decode_int8(q, k_cache, v_cache, k_scales, v_scales, block_tables, context_l
     return out
 
 
+FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)
+
+
+def decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale: float, out=None,
+               split_tokens: int = 0, workspace=None, stream=None) -> torch.Tensor:
+    """out fp32 [S, Hq, D] = paged_attn_decode_fp8(...): the cache holds FP8 E4M3
+    codes (a float8_e4m3fn or uint8 tensor)."""
+    if k_cache.dtype not in FP8_DTYPES or v_cache.dtype != k_cache.dtype:
+        raise TypeError("fp8 cache must be float8_e4m3fn (or uint8 codes)")
+    _validate(q, k_cache, v_cache, block_tables, context_lens, k_cache.dtype)
+    shape = shape_of(q, k_cache, block_tables, split_tokens)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(shape, q.device)
+    rc = load().paged_attn_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                      _ptr(context_lens), ctypes.c_float(scale), _ptr(out),
+                                      ctypes.byref(shape), _ptr(workspace),
+                                      ctypes.c_size_t(workspace.numel()), _stream_handle(stream))
+    _check(rc)
+    return out
+
+
 def decode_views(views: dict, out=None, split_tokens: int = 0, workspace=None, stream=None):
     """Decode one layer given the per-layer views of the input generator."""
+    if views["k_cache"].dtype in FP8_DTYPES:
+        return decode_fp8(views["q"], views["k_cache"], views["v_cache"], views["block_tables"],
+                          views["context_lens"], views["scale"], out=out,
+                          split_tokens=split_tokens, workspace=workspace, stream=stream)
     if "k_scales" in views:
         return decode_int8(views["q"], views["k_cache"], views["v_cache"], views["k_scales"],
                            views["v_scales"], views["block_tables"], views["context_lens"],
@@ -275,8 +307,23 @@ def kv_write_int8(key, value, slot_mapping, k_cache, v_cache, k_scales, v_scales
                                       ctypes.byref(sh), _stream_handle(stream)))
 
 
+def kv_write_fp8(key, value, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """paged_kv_write_fp8: cast token t's K/V rows to FP8 E4M3 and store them at
+    slot_mapping[t] (cache: float8_e4m3fn or uint8 codes)."""
+    if k_cache.dtype not in FP8_DTYPES:
+        raise TypeError("fp8 cache must be float8_e4m3fn (or uint8 codes)")
+    _validate_write(key, value, slot_mapping, k_cache, v_cache, k_cache.dtype)
+    sh = _write_shape_strided(key, value, k_cache)
+    _check(load().paged_kv_write_fp8(_ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(k_cache),
+                                     _ptr(v_cache), ctypes.byref(sh), _stream_handle(stream)))
+
+
 def kv_write_inputs(inp: dict, stream=None) -> None:
-    """Run the write of a make_write_inputs() dict (bf16 or int8 cache)."""
+    """Run the write of a make_write_inputs() dict (bf16, int8 or fp8 cache)."""
+    if inp["k_cache"].dtype in FP8_DTYPES:
+        kv_write_fp8(inp["key"], inp["value"], inp["slots"], inp["k_cache"], inp["v_cache"],
+                     stream=stream)
+        return
     if "k_scales" in inp:
         kv_write_int8(inp["key"], inp["value"], inp["slots"], inp["k_cache"], inp["v_cache"],
                       inp["k_scales"], inp["v_scales"], stream=stream)

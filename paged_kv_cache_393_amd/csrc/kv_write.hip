@@ -2,7 +2,8 @@
 // include/paged_kv_write.h: the new tokens' key and value rows are stored at
 // the token slots the block tables handed out (ybb.press page "LLM 推理 KV
 // Cache 内存管理深度工程实践", section 2.1: slot = block * block_size +
-// offset), optionally quantized to int8 on the way in (same page, 6.1).
+// offset), optionally quantized to int8 or cast to FP8 E4M3 on the way in
+// (same page, 6.1).
 //
 // The work is pure data movement (plus, for int8, a per-row max and a
 // division per element), so the kernel is shaped for HBM: one group of
@@ -106,7 +107,32 @@ __device__ __forceinline__ uint2 quantize8(const uint4 w, float &scale_out) {
     return make_uint2(packed[0], packed[1]);
 }
 
-template <int D, bool INT8>
+// Casts one lane's 8 bf16 values to FP8 E4M3 codes (packed little-endian).
+// v_cvt_pk_fp8_f32 rounds to nearest even, keeps subnormals and turns
+// magnitudes past 464 into the NaN code with the value's sign -- the cast of
+// torch's float8_e4m3fn -- except that it gives 0xFF for every NaN input; a
+// NaN is therefore first replaced by the infinity of its sign, which converts
+// to the NaN code of that sign.
+__device__ __forceinline__ float nan_to_signed_inf(float x) {
+    return __builtin_isnan(x) ? __builtin_copysignf(__builtin_inff(), x) : x;
+}
+
+__device__ __forceinline__ uint2 cast_fp8x8(const uint4 w) {
+    float x[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                  bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = nan_to_signed_inf(x[i]);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], hi, true);
+    return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+// Element kinds of the cache written.
+enum WriteKind : int { kWriteBf16 = 0, kWriteInt8 = 1, kWriteFp8 = 2 };
+
+template <int D, int KIND>
 __global__ __launch_bounds__(kThreads) void kv_write_kernel(WriteParams p) {
     constexpr int L = D / 8;                    // lanes per row, 8 bf16 (16 B) each
     constexpr int kRowsPerGroup = kThreads / L;
@@ -125,9 +151,12 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(WriteParams p) {
     const uint4 vw = *reinterpret_cast<const uint4 *>(p.value + (int64_t)t * p.value_stride +
                                                       g * D + lane * 8);
     const int64_t cell = (int64_t)slot * p.hkv + g;   // (block, offset, g) row of the cache
-    if constexpr (!INT8) {
+    if constexpr (KIND == kWriteBf16) {
         *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.k_cache) + cell * D + lane * 8) = kw;
         *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.v_cache) + cell * D + lane * 8) = vw;
+    } else if constexpr (KIND == kWriteFp8) {
+        *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(p.k_cache) + cell * D + lane * 8) = cast_fp8x8(kw);
+        *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(p.v_cache) + cell * D + lane * 8) = cast_fp8x8(vw);
     } else {
         float ks, vs;
         const uint2 kc = quantize8<L>(kw, ks);
@@ -144,7 +173,8 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(WriteParams p) {
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int write_common(const void *key, const void *value, const int32_t *slots, void *kc, void *vc,
-                 float *ks, float *vs, const pa_write_shape *sh, void *stream, bool int8) {
+                 float *ks, float *vs, const pa_write_shape *sh, void *stream, int kind) {
+    const bool int8 = kind == kWriteInt8;
     if (!sh) return PA_ERR_NULL;
     if (sh->num_tokens < 0 || sh->num_kv_heads < 1 || sh->block_size < 1 || sh->num_blocks < 1 ||
         sh->key_stride < 0 || sh->value_stride < 0)
@@ -160,9 +190,10 @@ int write_common(const void *key, const void *value, const int32_t *slots, void 
     if (!key || !value || !slots || !kc || !vc) return PA_ERR_NULL;
     if (int8 && (!ks || !vs)) return PA_ERR_NULL;
     if (!aligned(key, 16) || !aligned(value, 16) || kst % 8 || vst % 8) return PA_ERR_ALIGNMENT;
-    if (int8 ? (!aligned(kc, 8) || !aligned(vc, 8) || !aligned(ks, 4) || !aligned(vs, 4))
-             : (!aligned(kc, 16) || !aligned(vc, 16)))
+    if (kind == kWriteBf16 ? (!aligned(kc, 16) || !aligned(vc, 16))
+                           : (!aligned(kc, 8) || !aligned(vc, 8)))
         return PA_ERR_ALIGNMENT;
+    if (int8 && (!aligned(ks, 4) || !aligned(vs, 4))) return PA_ERR_ALIGNMENT;
 
     WriteParams p;
     p.key = static_cast<const uint16_t *>(key);
@@ -182,11 +213,13 @@ int write_common(const void *key, const void *value, const int32_t *slots, void 
     const dim3 grid((unsigned)((rows + rows_per_group - 1) / rows_per_group));
     const dim3 block(kThreads);
     if (sh->head_dim == 128) {
-        if (int8) hipLaunchKernelGGL((kv_write_kernel<128, true>), grid, block, 0, st, p);
-        else hipLaunchKernelGGL((kv_write_kernel<128, false>), grid, block, 0, st, p);
+        if (kind == kWriteInt8) hipLaunchKernelGGL((kv_write_kernel<128, kWriteInt8>), grid, block, 0, st, p);
+        else if (kind == kWriteFp8) hipLaunchKernelGGL((kv_write_kernel<128, kWriteFp8>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((kv_write_kernel<128, kWriteBf16>), grid, block, 0, st, p);
     } else {
-        if (int8) hipLaunchKernelGGL((kv_write_kernel<64, true>), grid, block, 0, st, p);
-        else hipLaunchKernelGGL((kv_write_kernel<64, false>), grid, block, 0, st, p);
+        if (kind == kWriteInt8) hipLaunchKernelGGL((kv_write_kernel<64, kWriteInt8>), grid, block, 0, st, p);
+        else if (kind == kWriteFp8) hipLaunchKernelGGL((kv_write_kernel<64, kWriteFp8>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((kv_write_kernel<64, kWriteBf16>), grid, block, 0, st, p);
     }
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
@@ -198,14 +231,21 @@ extern "C" {
 int paged_kv_write(const void *key, const void *value, const int32_t *slot_mapping,
                    void *k_cache, void *v_cache, const pa_write_shape *shape, void *stream) {
     return write_common(key, value, slot_mapping, k_cache, v_cache, nullptr, nullptr, shape,
-                        stream, false);
+                        stream, kWriteBf16);
+}
+
+int paged_kv_write_fp8(const void *key, const void *value, const int32_t *slot_mapping,
+                       uint8_t *k_cache, uint8_t *v_cache, const pa_write_shape *shape,
+                       void *stream) {
+    return write_common(key, value, slot_mapping, k_cache, v_cache, nullptr, nullptr, shape,
+                        stream, kWriteFp8);
 }
 
 int paged_kv_write_int8(const void *key, const void *value, const int32_t *slot_mapping,
                         int8_t *k_cache, int8_t *v_cache, float *k_scales, float *v_scales,
                         const pa_write_shape *shape, void *stream) {
     return write_common(key, value, slot_mapping, k_cache, v_cache, k_scales, v_scales, shape,
-                        stream, true);
+                        stream, kWriteInt8);
 }
 
 }  // extern "C"

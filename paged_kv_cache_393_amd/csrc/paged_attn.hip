@@ -7,7 +7,8 @@
 // scale * q.k and one exact softmax over the whole context (ybb.press page
 // "LLM 推理 KV Cache 内存管理深度工程实践", sections 2.2 and 6.2; t6page
 // "KV cache" page, section "PagedAttention 的算子").  The int8 variant
-// dequantizes code * per-(slot, kv head) scale (same ybb.press page, 6.1).
+// dequantizes code * per-(slot, kv head) scale, the fp8 variant reads the
+// cache cast to FP8 E4M3 (both: same ybb.press page, 6.1).
 //
 // Work decomposition.  A "unit" is (kv head, chunk of <= 16 query heads of
 // its group); one wave serves one unit.  A workgroup holds four waves for four
@@ -87,12 +88,14 @@ constexpr int kMinItemTiles = 4;    // shortest balanced item
 constexpr int kMaxItems = 4096;     // balanced items per unit group (>= workgroups launched)
 constexpr int kLdsSeqs = 2048;      // sequences whose tile prefix and length are kept in LDS
 constexpr float kLog2e = 1.4426950408889634f;
+// Element kinds of the KV cache.
+enum KvKind : int { kBf16 = 0, kInt8 = 1, kFp8 = 2 };
 // Word 3 of a raw (unformatted, stride 0) buffer resource on CDNA3/CDNA4.
 constexpr int kRsrcFlags = 0x00020000;
 
 struct Params {
     const uint16_t *q;       // bf16 [S, Hq, D]
-    const void *k;           // [NB, bs, Hkv, D] bf16 or int8
+    const void *k;           // [NB, bs, Hkv, D] bf16, int8 or fp8 (E4M3)
     const void *v;
     const float *k_scales;   // [NB, bs, Hkv] (int8 only)
     const float *v_scales;
@@ -136,6 +139,19 @@ __device__ __forceinline__ bf16x4_t i8x4_to_bf16x4(uint32_t w) {
                                                 pack_hi16(i8_at(w, 2), i8_at(w, 3))});
 }
 
+// Two FP8 E4M3 codes (bytes 2*hi, 2*hi + 1 of w) -> their bf16 pair, low half
+// first.  Exact: every E4M3 value (subnormals and NaN included) is a bf16
+// value, and the scale operand is 1.
+template <bool kHi>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+}
+
+// Four FP8 E4M3 codes -> four bf16 (exact).
+__device__ __forceinline__ bf16x4_t fp8x4_to_bf16x4(uint32_t w) {
+    return __builtin_bit_cast(bf16x4_t, u32x2_t{fp8x2_to_bf16x2<false>(w), fp8x2_to_bf16x2<true>(w)});
+}
+
 // Order this wave's LDS writes before its following LDS reads (other lanes'
 // data); LDS requests of one wave complete in order.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -177,9 +193,9 @@ struct Items {
     }
 };
 
-template <int D, bool INT8>
+template <int D, int KV>
 struct Layout {
-    static constexpr int kElem = INT8 ? 1 : 2;                 // bytes per cache element
+    static constexpr int kElem = KV == kBf16 ? 2 : 1;          // bytes per cache element
     static constexpr int kKElemsPerLoad = 16 / kElem;          // K dims per 16-B load
     static constexpr int kKLoads = D / (4 * kKElemsPerLoad);   // 16-B K loads per lane per tile
     static constexpr int kSteps = D / 16;                      // QK MFMA k-steps (4 dims x 4 groups)
@@ -195,9 +211,9 @@ struct Layout {
     }
 };
 
-template <int D, bool INT8>
+template <int D, int KV>
 struct TileRegs {
-    using L = Layout<D, INT8>;
+    using L = Layout<D, KV>;
     u32x4_t k[L::kKLoads];
     typename L::VReg v[4];   // token rows 4*(l/16) + i
     float ks;                // int8: K scale of token row l%16
@@ -212,13 +228,19 @@ __device__ __forceinline__ uint32_t vword(const VR &r, int w) {
 }
 
 // A operand of PV block j: element j of the four token rows, as bf16x4.
-template <int D, bool INT8>
-__device__ __forceinline__ bf16x4_t v_operand(const typename Layout<D, INT8>::VReg (&v)[4], int j) {
+template <int D, int KV>
+__device__ __forceinline__ bf16x4_t v_operand(const typename Layout<D, KV>::VReg (&v)[4], int j) {
     u32x2_t r;
-    if constexpr (INT8) {
+    if constexpr (KV == kInt8) {
         const int w = j >> 2, b = j & 3;
         r.x = pack_hi16(i8_at(vword(v[0], w), b), i8_at(vword(v[1], w), b));
         r.y = pack_hi16(i8_at(vword(v[2], w), b), i8_at(vword(v[3], w), b));
+    } else if constexpr (KV == kFp8) {
+        // Byte b of rows (0, 1) and of rows (2, 3) side by side, then converted.
+        const int w = j >> 2, b = j & 3;
+        const uint32_t sel = (uint32_t)b | ((uint32_t)(4 + b) << 8) | 0x0c0c0000u;
+        r.x = fp8x2_to_bf16x2<false>(__builtin_amdgcn_perm(vword(v[1], w), vword(v[0], w), sel));
+        r.y = fp8x2_to_bf16x2<false>(__builtin_amdgcn_perm(vword(v[3], w), vword(v[2], w), sel));
     } else {
         const int w = j >> 1;
         const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
@@ -228,9 +250,10 @@ __device__ __forceinline__ bf16x4_t v_operand(const typename Layout<D, INT8>::VR
     return __builtin_bit_cast(bf16x4_t, r);
 }
 
-template <int D, bool INT8>
+template <int D, int KV>
 __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(const Params p) {
-    using L = Layout<D, INT8>;
+    constexpr bool INT8 = KV == kInt8;
+    using L = Layout<D, KV>;
     constexpr int kDpl = L::kDpl;
     static_assert(L::kKLoads >= 1, "head_dim");
 
@@ -382,7 +405,7 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
         // A tile never crosses a block (block_size is a multiple of 16); rows
         // at or past the context end fall outside the range and read as 0
         // without touching memory.
-        auto load_tile = [&](TileRegs<D, INT8> &r, int tile) __attribute__((always_inline)) {
+        auto load_tile = [&](TileRegs<D, KV> &r, int tile) __attribute__((always_inline)) {
             const int64_t slot0 = tile_slot(tile);
             const int rows = min(kTile, t_end - (t_begin + tile * kTile));
             const int range = rows * (int)rb32;
@@ -422,7 +445,7 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
 #pragma unroll
         for (int j = 0; j < kDpl; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        auto compute_tile = [&](TileRegs<D, INT8> &r, int tile) __attribute__((always_inline)) {
+        auto compute_tile = [&](TileRegs<D, KV> &r, int tile) __attribute__((always_inline)) {
             const int t0 = t_begin + tile * kTile;
             if constexpr (INT8) {
                 wave_lds_sync();
@@ -436,8 +459,10 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
                 const int m = st / L::kStepsPerLoad;
                 const int sub = st % L::kStepsPerLoad;
                 bf16x4_t a;
-                if constexpr (INT8) {
+                if constexpr (KV == kInt8) {
                     a = i8x4_to_bf16x4(r.k[m][sub]);
+                } else if constexpr (KV == kFp8) {
+                    a = fp8x4_to_bf16x4(r.k[m][sub]);
                 } else {
                     u32x2_t w = sub == 0 ? u32x2_t{r.k[m].x, r.k[m].y} : u32x2_t{r.k[m].z, r.k[m].w};
                     a = __builtin_bit_cast(bf16x4_t, w);
@@ -505,7 +530,7 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
             }
 #pragma unroll
             for (int j = 0; j < kDpl; ++j) {
-                const bf16x4_t a = v_operand<D, INT8>(r.v, j);
+                const bf16x4_t a = v_operand<D, KV>(r.v, j);
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bhi, acc[j], 0, 0, 0);
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, blo, acc[j], 0, 0, 0);
             }
@@ -523,7 +548,7 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
         constexpr int kStages = PA_STAGES;
         static_assert(kStages >= 2 && kStages <= 6, "pipeline depth");
         {
-            TileRegs<D, INT8> buf[kStages];
+            TileRegs<D, KV> buf[kStages];
             auto tile_of = [&](int k) __attribute__((always_inline)) { return min(k, n_tiles - 1); };
             static_for<0, kStages - 1>([&](auto I) __attribute__((always_inline)) {
                 load_tile(buf[decltype(I)::value], tile_of(decltype(I)::value));
@@ -811,12 +836,17 @@ int make_plan(const pa_shape *sh, Plan *pl) {
 
 // Workgroups of the decode kernel the current device holds at once (queried
 // once per device and kernel).
-int device_capacity(int head_dim, bool int8) {
+template <int D, int KV>
+hipError_t blocks_per_cu(int *n) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, pa_decode_kernel<D, KV>, kThreads, 0);
+}
+
+int device_capacity(int head_dim, int kind) {
     constexpr int kMaxDev = 64;
-    static int cache[kMaxDev][4];
+    static int cache[kMaxDev][6];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
-    const int slot = (head_dim == 128 ? 2 : 0) + (int8 ? 1 : 0);
+    const int slot = (head_dim == 128 ? 3 : 0) + kind;
     int &c = cache[dev][slot];
     if (c > 0) return c;
     int cus = 0;
@@ -824,12 +854,14 @@ int device_capacity(int head_dim, bool int8) {
         return 0;
     int per_cu = 0;
     hipError_t e;
-    if (head_dim == 128)
-        e = int8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pa_decode_kernel<128, true>, kThreads, 0)
-                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pa_decode_kernel<128, false>, kThreads, 0);
-    else
-        e = int8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pa_decode_kernel<64, true>, kThreads, 0)
-                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pa_decode_kernel<64, false>, kThreads, 0);
+    switch (slot) {
+        case 0: e = blocks_per_cu<64, kBf16>(&per_cu); break;
+        case 1: e = blocks_per_cu<64, kInt8>(&per_cu); break;
+        case 2: e = blocks_per_cu<64, kFp8>(&per_cu); break;
+        case 3: e = blocks_per_cu<128, kBf16>(&per_cu); break;
+        case 4: e = blocks_per_cu<128, kInt8>(&per_cu); break;
+        default: e = blocks_per_cu<128, kFp8>(&per_cu); break;
+    }
     if (e != hipSuccess || per_cu <= 0) per_cu = 1;
     c = cus * per_cu;
     return c;
@@ -851,9 +883,10 @@ WsLayout workspace_layout(const pa_shape *sh, const Plan &pl) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-int decode_common(bool int8, const void *q, const void *k, const void *v, const float *ks,
+int decode_common(int kind, const void *q, const void *k, const void *v, const float *ks,
                   const float *vs, const int32_t *bt, const int32_t *cl, float scale, float *out,
                   const pa_shape *sh, void *ws, size_t ws_bytes, void *stream) {
+    const bool int8 = kind == kInt8;
     Plan pl;
     int rc = make_plan(sh, &pl);
     if (rc != PA_OK) return rc;
@@ -864,7 +897,7 @@ int decode_common(bool int8, const void *q, const void *k, const void *v, const 
     const WsLayout wl = workspace_layout(sh, pl);
     if (!ws || ws_bytes < wl.total) return PA_ERR_WORKSPACE;
     if (!aligned16(ws)) return PA_ERR_ALIGNMENT;
-    const int cap = device_capacity(sh->head_dim, int8);
+    const int cap = device_capacity(sh->head_dim, kind);
     if (cap <= 0) return PA_ERR_LAUNCH;
     int wgs = cap / pl.groups;
     if (wgs < 1) wgs = 1;
@@ -907,12 +940,14 @@ int decode_common(bool int8, const void *q, const void *k, const void *v, const 
     const dim3 mgrid((unsigned)((int64_t)sh->num_seqs * sh->num_q_heads));
     hipStream_t st = (hipStream_t)stream;
     if (sh->head_dim == 128) {
-        if (int8) hipLaunchKernelGGL((pa_decode_kernel<128, true>), grid, block, 0, st, prm);
-        else hipLaunchKernelGGL((pa_decode_kernel<128, false>), grid, block, 0, st, prm);
+        if (kind == kInt8) hipLaunchKernelGGL((pa_decode_kernel<128, kInt8>), grid, block, 0, st, prm);
+        else if (kind == kFp8) hipLaunchKernelGGL((pa_decode_kernel<128, kFp8>), grid, block, 0, st, prm);
+        else hipLaunchKernelGGL((pa_decode_kernel<128, kBf16>), grid, block, 0, st, prm);
         hipLaunchKernelGGL((pa_merge_kernel<128>), mgrid, block, 0, st, mp);
     } else {
-        if (int8) hipLaunchKernelGGL((pa_decode_kernel<64, true>), grid, block, 0, st, prm);
-        else hipLaunchKernelGGL((pa_decode_kernel<64, false>), grid, block, 0, st, prm);
+        if (kind == kInt8) hipLaunchKernelGGL((pa_decode_kernel<64, kInt8>), grid, block, 0, st, prm);
+        else if (kind == kFp8) hipLaunchKernelGGL((pa_decode_kernel<64, kFp8>), grid, block, 0, st, prm);
+        else hipLaunchKernelGGL((pa_decode_kernel<64, kBf16>), grid, block, 0, st, prm);
         hipLaunchKernelGGL((pa_merge_kernel<64>), mgrid, block, 0, st, mp);
     }
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
@@ -941,7 +976,15 @@ int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *block_tables, const int32_t *context_lens, float scale,
                       float *out, const pa_shape *shape, void *workspace, size_t workspace_bytes,
                       void *stream) {
-    return decode_common(false, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,
+    return decode_common(kBf16, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,
+                         scale, out, shape, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_decode_fp8(const void *q, const uint8_t *k_cache, const uint8_t *v_cache,
+                          const int32_t *block_tables, const int32_t *context_lens, float scale,
+                          float *out, const pa_shape *shape, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    return decode_common(kFp8, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,
                          scale, out, shape, workspace, workspace_bytes, stream);
 }
 
@@ -950,7 +993,7 @@ int paged_attn_decode_int8(const void *q, const int8_t *k_cache, const int8_t *v
                            const int32_t *block_tables, const int32_t *context_lens, float scale,
                            float *out, const pa_shape *shape, void *workspace,
                            size_t workspace_bytes, void *stream) {
-    return decode_common(true, q, k_cache, v_cache, k_scales, v_scales, block_tables,
+    return decode_common(kInt8, q, k_cache, v_cache, k_scales, v_scales, block_tables,
                          context_lens, scale, out, shape, workspace, workspace_bytes, stream);
 }
 

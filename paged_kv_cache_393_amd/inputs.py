@@ -254,10 +254,15 @@ def select_sequences(views: dict, seq_ids: Sequence[int], block_size: int) -> di
     if not phys:
         phys = [0]
     idx = torch.tensor(phys, dtype=torch.int64, device=views["k_cache"].device)
+
+    def pick(t):   # float8 tensors are gathered as their bytes
+        if t.dtype == torch.float8_e4m3fn:
+            return t.view(torch.uint8).index_select(0, idx).cpu().view(torch.float8_e4m3fn)
+        return t.index_select(0, idx).cpu()
+
     out = {"q": views["q"][seq_ids].cpu(), "block_tables": new_tables, "context_lens": ctx,
-           "scale": views["scale"],
-           "k_cache": views["k_cache"].index_select(0, idx).cpu(),
-           "v_cache": views["v_cache"].index_select(0, idx).cpu()}
+           "scale": views["scale"], "k_cache": pick(views["k_cache"]),
+           "v_cache": pick(views["v_cache"])}
     if "k_scales" in views:
         out["k_scales"] = views["k_scales"].index_select(0, idx).cpu()
         out["v_scales"] = views["v_scales"].index_select(0, idx).cpu()

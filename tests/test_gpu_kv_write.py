@@ -261,3 +261,103 @@ def test_int8_write_every_bf16_value_for_many_scales():
         g = got.cpu().numpy()
         assert np.array_equal(g.view(np.uint8), ref.view(np.uint8)), \
             f"{what}: {int((g != ref).sum())} of {g.size} differ"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hkv", [1, 3, 8])
+@pytest.mark.parametrize("T", [0, 1, 37, 300])
+def test_fp8_write_bit_exact(D, Hkv, T):
+    note(f"fp8 write D={D} Hkv={Hkv} T={T}")
+    bs = 16
+    NB = max(1, (T + bs - 1) // bs) + 3
+    check_fp8_write(T, Hkv, D, bs, NB, seed=300 + T + D + Hkv)
+
+
+def check_fp8_write(T, Hkv, D, bs, NB, seed, pad=0.2, token_stride=None, key=None, value=None,
+                    slots=None):
+    gen = torch.Generator().manual_seed(seed)
+    kc = torch.randint(0, 256, (NB, bs, Hkv, D), generator=gen, dtype=torch.int32).to(torch.uint8)
+    vc = torch.randint(0, 256, (NB, bs, Hkv, D), generator=gen, dtype=torch.int32).to(torch.uint8)
+    if key is None:
+        key, value = I.make_new_tokens(T, Hkv, D, seed=seed, device=DEV, token_stride=token_stride)
+    if slots is None:
+        slots = I.draw_slots(T, NB * bs, seed=seed, pad_fraction=pad)
+    g_kc = kc.to(DEV).view(torch.float8_e4m3fn)
+    g_vc = vc.to(DEV).view(torch.float8_e4m3fn)
+    B.kv_write_fp8(key, value, slots.to(DEV), g_kc, g_vc)
+    torch.cuda.synchronize()
+    # the kernel skips slots past the pool (a caller error the oracle rejects):
+    # for the oracle they are tokens without a slot
+    sl = slots.numpy().copy()
+    sl[sl >= NB * bs] = -1
+    rk, rv = oracle.kv_write_fp8(I.bf16_bits(key), I.bf16_bits(value), sl, kc.numpy(), vc.numpy())
+    gk, gv = C.fp8_codes(g_kc), C.fp8_codes(g_vc)
+    assert np.array_equal(gk, rk), f"k codes: {int((gk != rk).sum())} differ"
+    assert np.array_equal(gv, rv), f"v codes: {int((gv != rv).sum())} differ"
+
+
+def test_fp8_write_every_bf16_value():
+    # All 65536 bf16 bit patterns (zeros, subnormals, the 448/464 boundary,
+    # infinities, NaNs of both signs) go through the kernel's cast: every code
+    # must be the oracle's, i.e. torch's float8_e4m3fn cast.
+    note("fp8 write exhaustive bf16")
+    D, Hkv = 128, 1
+    T = 65536 // D
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    key = bits.reshape(T, Hkv, D).to(DEV)
+    value = bits.flip(0).reshape(T, Hkv, D).contiguous().to(DEV)
+    NB, bs = T // 16, 16
+    slots = torch.randperm(NB * bs, generator=torch.Generator().manual_seed(301)).to(torch.int32)
+    check_fp8_write(T, Hkv, D, bs, NB, seed=301, key=key, value=value, slots=slots)
+
+
+def test_fp8_write_strided_and_out_of_range():
+    note("fp8 write strided / out of range")
+    check_fp8_write(77, 8, 128, 16, 10, seed=302, token_stride=(32 + 16) * 128)
+    NB, bs = 4, 16
+    key, value = I.make_new_tokens(4, 2, 64, seed=303, device=DEV)
+    slots = torch.tensor([3, NB * bs, -1, 0], dtype=torch.int32)
+    check_fp8_write(4, 2, 64, bs, NB, seed=303, key=key, value=value, slots=slots)
+
+
+def test_fp8_write_then_decode():
+    note("fp8 write then decode")
+    ctx = (0, 15, 16, 100, 511, 2000)
+    bs, Hq, Hkv, D = 16, 32, 8, 128
+    full = tuple(c + 1 for c in ctx)
+    NB = sum((c + bs - 1) // bs for c in full) + 2
+    _, v = C.make_case(len(ctx), Hq, Hkv, D, bs, ctx=full, NB=NB, seed=304, kv_dtype="fp8",
+                       device=DEV)
+    key, value = I.make_new_tokens(len(ctx), Hkv, D, seed=304, device=DEV)
+    bt = v["block_tables"].cpu().numpy()
+    slots = np.array([oracle.slot_of(bt[s], c, bs) for s, c in enumerate(ctx)], dtype=np.int32)
+    host = {k: (t.cpu() if torch.is_tensor(t) else t) for k, t in v.items()}
+    B.kv_write_fp8(key, value, torch.from_numpy(slots).to(DEV), v["k_cache"], v["v_cache"])
+    rk, rv = oracle.kv_write_fp8(I.bf16_bits(key), I.bf16_bits(value), slots,
+                                 C.fp8_codes(host["k_cache"]), C.fp8_codes(host["v_cache"]))
+    host["k_cache"] = torch.from_numpy(rk).view(torch.float8_e4m3fn)
+    host["v_cache"] = torch.from_numpy(rv).view(torch.float8_e4m3fn)
+    out = B.decode_views(v)
+    torch.cuda.synchronize()
+    assert_parity(out, C.oracle_out(host), "fp8 write+decode")
+
+
+def test_full_size_fp8_write_workload_sampled():
+    # The bench's fp8 write workload at full size, same launch as the bench;
+    # the oracle checks a seeded sample of 2048 tokens (all their heads).
+    note("full-size fp8 write workload")
+    ww = I.WRITE_WORKLOADS["kv_write_fp8_llama3_8b"]
+    inp = I.make_write_inputs(ww, DEV)
+    B.kv_write_inputs(inp)
+    torch.cuda.synchronize()
+    pick = torch.randperm(ww.num_tokens, generator=torch.Generator().manual_seed(305))[:2048]
+    slots = inp["slots"].cpu()[pick].numpy()
+    kb, vb = I.bf16_bits(inp["key"].cpu()[pick]), I.bf16_bits(inp["value"].cpu()[pick])
+    shape = tuple(inp["k_cache"].shape)
+    z = np.zeros(shape, dtype=np.uint8)
+    rk, rv = oracle.kv_write_fp8(kb, vb, slots, z, z)
+    gk = C.fp8_codes(inp["k_cache"]).reshape(-1, ww.num_kv_heads, ww.head_dim)
+    gv = C.fp8_codes(inp["v_cache"]).reshape(-1, ww.num_kv_heads, ww.head_dim)
+    rk = rk.reshape(-1, ww.num_kv_heads, ww.head_dim)
+    rv = rv.reshape(-1, ww.num_kv_heads, ww.head_dim)
+    assert np.array_equal(gk[slots], rk[slots]) and np.array_equal(gv[slots], rv[slots])

@@ -59,7 +59,7 @@ def test_tiny_workload_all_partitions():
 EDGE_CTX = (0, 1, 15, 16, 17, 511, 512, 513)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 2), (16, 2), (32, 1)])
 @pytest.mark.parametrize("bs", [16, 32, 256])
@@ -118,7 +118,7 @@ def test_uniform_keys_mean_of_values():
         assert_parity(run(v, st), ref, f"uniform split={st}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
 def test_poisoned_padding_bit_identical(kv):
     note(f"poison {kv}")
     for bs in (16, 256):
@@ -218,10 +218,49 @@ def test_int8_lossless_values_match_bf16_path():
     assert_parity(run(vi), ref, "int8")
 
 
+def test_fp8_path_matches_bf16_path_on_the_same_values():
+    # Every E4M3 value is a bf16 value and the kernel decodes the codes
+    # exactly, so an fp8 cache and a bf16 cache holding the decoded values give
+    # the same result up to fp32 summation order: the two layouts feed the QK
+    # products' dims to the matrix cores in a different order (16 vs 8
+    # elements per 16-byte load).
+    note("fp8 vs bf16 same values")
+    for bs, ctx in ((16, (100, 513, 40, 1)), (256, (3000, 257, 16))):
+        NB = sum((c + bs - 1) // bs for c in ctx) + 2
+        _, v8 = C.make_case(len(ctx), 32, 8, 128, bs, ctx=ctx, NB=NB, seed=39, kv_dtype="fp8",
+                            device=DEV)
+        vb = dict(v8, k_cache=v8["k_cache"].to(torch.bfloat16),
+                  v_cache=v8["v_cache"].to(torch.bfloat16))
+        ref = C.oracle_out(v8)
+        for st in (0, 64):
+            a, b = run(v8, st).clone(), run(vb, st)
+            assert float((a - b).abs().max()) <= 1e-5, (bs, st)
+            assert_parity(a, ref, f"fp8 bs={bs} split={st}")
+            assert_parity(b, ref, f"bf16 bs={bs} split={st}")
+
+
+def test_fp8_nan_code_reaches_only_its_output_elements():
+    # A NaN code in V at one valid (token, kv head, dim) makes exactly that dim
+    # of that kv head's query heads NaN (as in the definition); every other
+    # output element keeps its bits.
+    note("fp8 nan locality")
+    _, v = C.make_case(2, 8, 2, 64, 16, ctx=(40, 70), seed=44, kv_dtype="fp8", device=DEV)
+    clean = run(v).clone()
+    b = int(v["block_tables"][1, 1])
+    v["v_cache"].view(torch.uint8)[b, 3, 1, 10] = 0x7F      # token 19 of sequence 1
+    got = run(v)
+    nan = torch.isnan(got)
+    expect = torch.zeros_like(nan)
+    expect[1, 4:8, 10] = True                               # heads 4..7 use kv head 1
+    assert torch.equal(nan, expect)
+    assert torch.equal(got[~expect].view(torch.int32), clean[~expect].view(torch.int32))
+
+
 # Full-size workloads in the launch configuration the bench times; the oracle
 # checks a seeded sample of sequences (all of their heads, all of their tokens).
 FULL = [("tiny", None, 0), ("llama3_8b", (0, 17, 63), 0), ("long_context", (2,), 0),
-        ("nano_vllm_70b", (5, 30), 0), ("int8_llama3_8b", (0, 64, 127), 0)]
+        ("nano_vllm_70b", (5, 30), 0), ("int8_llama3_8b", (0, 64, 127), 0),
+        ("fp8_llama3_8b", (0, 64, 127), 0)]
 
 
 @pytest.mark.parametrize("name,sample,layer", FULL)
