@@ -11,7 +11,10 @@ Every function here cites the passage it follows in ``oracle.c``'s header:
 the ybb.press page "LLM 推理 KV Cache 内存管理深度工程实践" sections 2.2
 (paged attention forward), 2.1 (BlockTable.append_slot: a token's global
 slot address block * block_size + offset), 6.1 (INT8 KV quantization, and the
-cast of the cache to FP8 E4M3) and 6.2 (GQA sharing),
+cast of the cache to FP8 E4M3) and 6.2 (GQA sharing), the blog.hotdry.top page
+"KV缓存内存布局优化：分页策略、量化压缩与动态驱逐的工程实践", section
+"PagedEviction 块级驱逐机制" (token importance ||V||/||K||, lowest-mean full
+block evicted),
 and the t6page "KV cache" page, section "PagedAttention 的算子" (softmax after
 merging all blocks).
 
@@ -78,6 +81,14 @@ class OracleLib:
         lib.oracle_fp8_e4m3_decode_array.restype = None
         lib.oracle_fp8_e4m3_encode_array.argtypes = [P, i64, P]
         lib.oracle_fp8_e4m3_encode_array.restype = None
+        for name, cache_args in (("oracle_token_scores_bf16", [P, P]),
+                                 ("oracle_token_scores_int8", [P, P, P, P]),
+                                 ("oracle_token_scores_fp8", [P, P])):
+            fn = getattr(lib, name)
+            fn.argtypes = cache_args + [P, P, P, i32, i32, i32, i32, i32, i64, P, i64]
+            fn.restype = i32
+        lib.oracle_evict_lowest_block.argtypes = [P, i64, P, P, P, P, i32, i32, i32]
+        lib.oracle_evict_lowest_block.restype = i32
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i32
         lib.oracle_set_num_threads.argtypes = [i32]
@@ -312,3 +323,60 @@ def kv_write_fp8(key_bits, value_bits, slots, k_codes, v_codes, lib: "OracleLib 
     if rc != 0:
         raise ValueError(f"oracle rejected the inputs (code {rc})")
     return kc, vc
+
+
+def token_scores(views, token_begin=None, score_stride=None, lib: "OracleLib | None" = None):
+    """PagedEviction importances ||V_t|| / ||K_t|| (float64 [S, score_stride],
+    NaN where not computed) for per-layer views (bf16, int8 or fp8 cache)."""
+    import torch
+
+    bt = _c(views["block_tables"].cpu().numpy(), np.int32)
+    cl = _c(views["context_lens"].cpu().numpy(), np.int32)
+    kc, vc = views["k_cache"].cpu(), views["v_cache"].cpu()
+    NB, BS, Hkv, D = kc.shape
+    S, MB = bt.shape
+    stride = score_stride or MB * BS
+    out = np.full((S, stride), np.nan, dtype=np.float64)
+    tb = None if token_begin is None else _c(np.asarray(token_begin), np.int32)
+    tbp = _ptr(tb) if tb is not None else None
+    L = lib.lib if lib is not None else _load()
+    if kc.dtype == torch.float8_e4m3fn:
+        k8 = _c(kc.view(torch.uint8).numpy(), np.uint8)
+        v8 = _c(vc.view(torch.uint8).numpy(), np.uint8)
+        rc = L.oracle_token_scores_fp8(_ptr(k8), _ptr(v8), _ptr(bt), tbp, _ptr(cl), S, Hkv, D, BS,
+                                       MB, NB, _ptr(out), stride)
+    elif "k_scales" in views:
+        k8 = _c(kc.numpy(), np.int8)
+        v8 = _c(vc.numpy(), np.int8)
+        ks = _c(views["k_scales"].cpu().numpy(), np.float32)
+        vs = _c(views["v_scales"].cpu().numpy(), np.float32)
+        rc = L.oracle_token_scores_int8(_ptr(k8), _ptr(v8), _ptr(ks), _ptr(vs), _ptr(bt), tbp,
+                                        _ptr(cl), S, Hkv, D, BS, MB, NB, _ptr(out), stride)
+    else:
+        kb = _c(kc.contiguous().view(torch.int16).numpy().view(np.uint16), np.uint16)
+        vb = _c(vc.contiguous().view(torch.int16).numpy().view(np.uint16), np.uint16)
+        rc = L.oracle_token_scores_bf16(_ptr(kb), _ptr(vb), _ptr(bt), tbp, _ptr(cl), S, Hkv, D, BS,
+                                        MB, NB, _ptr(out), stride)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return out
+
+
+def evict_lowest_block(scores, block_tables, context_lens, evict_mask, block_size,
+                       lib: "OracleLib | None" = None):
+    """Decode-phase PagedEviction on copies: returns (scores, block_tables,
+    context_lens, evicted) after evicting, for every masked sequence, its full
+    block of lowest mean importance.  scores: float32 [S, stride]."""
+    as_i32 = lambda a: np.asarray(a, dtype=np.int32) if isinstance(a, (list, tuple)) else a
+    sc = np.array(_c(scores, np.float32), copy=True)
+    bt = np.array(_c(block_tables, np.int32), copy=True)
+    cl = np.array(_c(as_i32(context_lens), np.int32), copy=True)
+    mask = _c(np.asarray(evict_mask, dtype=np.int32), np.int32)
+    S, MB = bt.shape
+    ev = np.zeros(S, dtype=np.int32)
+    L = lib.lib if lib is not None else _load()
+    rc = L.oracle_evict_lowest_block(_ptr(sc), sc.shape[1], _ptr(bt), _ptr(cl), _ptr(mask), _ptr(ev),
+                                     S, MB, block_size)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return sc, bt, cl, ev

@@ -1,6 +1,7 @@
 /*
- * oracle.c -- plain, slow, fp64 CPU reference for PagedAttention decode and
- * for the KV write path that fills the paged cache (at the end of this file).
+ * oracle.c -- plain, slow, fp64 CPU reference for PagedAttention decode, for
+ * the KV write path that fills the paged cache, and for PagedEviction's token
+ * importance and block eviction (the last two at the end of this file).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * bench's cpu_baseline leg may load this library.  It shares no code, header,
@@ -437,6 +438,146 @@ int oracle_kv_write_fp8(const uint16_t *key, const uint16_t *value, const int32_
                     bf16_bits_to_double(value[t * value_stride + (int64_t)g * D + i]));
             }
         }
+    }
+    return ORC_OK;
+}
+
+/*
+ * PagedEviction, token importance (page "KV缓存内存布局优化：分页策略、量化压缩
+ * 与动态驱逐的工程实践", section "PagedEviction 块级驱逐机制"): a token's
+ * importance is the ratio of the L2 norms of its value and key,
+ * S_t = ||V_t||_2 / ||K_t||_2, where K_t and V_t are the token's whole rows in
+ * the layer's cache (all kv heads, all dims), dequantized like the decode
+ * entry points.  For every sequence s, tokens t in [token_begin[s],
+ * context_lens[s]) (token_begin NULL: from 0) get scores[s * score_stride + t]
+ * = S_t in double; other entries are left alone.  Norms and ratio in double.
+ */
+static int token_scores_common(const kv_src *src, const int32_t *block_tables,
+                               const int32_t *token_begin, const int32_t *context_lens,
+                               int S, int Hkv, int D, int BS, int MB, int64_t NB,
+                               double *scores, int64_t score_stride)
+{
+    if (!src->k || !src->v || !block_tables || !context_lens || !scores) return ORC_ERR_ARG;
+    if (S < 0 || Hkv <= 0 || D <= 0 || BS <= 0 || MB < 0 || NB < 0) return ORC_ERR_ARG;
+    if (src->kind == KV_INT8 && (!src->k_scales || !src->v_scales)) return ORC_ERR_ARG;
+    for (int s = 0; s < S; ++s) {
+        int n = context_lens[s];
+        int b0 = token_begin ? token_begin[s] : 0;
+        if (n < 0 || (int64_t)n > (int64_t)MB * BS || (int64_t)n > score_stride) return ORC_ERR_TABLE;
+        if (b0 < 0) return ORC_ERR_ARG;
+        int nblk = (n + BS - 1) / BS;
+        for (int j = 0; j < nblk; ++j) {
+            int32_t b = block_tables[(int64_t)s * MB + j];
+            if (b < 0 || (int64_t)b >= NB) return ORC_ERR_TABLE;
+        }
+    }
+    for (int s = 0; s < S; ++s) {
+        const int n = context_lens[s];
+        for (int t = token_begin ? token_begin[s] : 0; t < n; ++t) {
+            const int64_t b = block_tables[(int64_t)s * MB + t / BS];
+            const int r = t % BS;
+            double kk = 0.0, vv = 0.0;
+            for (int g = 0; g < Hkv; ++g) {
+                for (int i = 0; i < D; ++i) {
+                    const double kx = kv_elem(src, 0, b, r, g, i, BS, Hkv, D);
+                    const double vx = kv_elem(src, 1, b, r, g, i, BS, Hkv, D);
+                    kk += kx * kx;
+                    vv += vx * vx;
+                }
+            }
+            scores[(int64_t)s * score_stride + t] = sqrt(vv) / sqrt(kk);
+        }
+    }
+    return ORC_OK;
+}
+
+int oracle_token_scores_bf16(const uint16_t *k_cache, const uint16_t *v_cache,
+                             const int32_t *block_tables, const int32_t *token_begin,
+                             const int32_t *context_lens, int S, int Hkv, int D, int BS, int MB,
+                             int64_t NB, double *scores, int64_t score_stride)
+{
+    kv_src src = {KV_BF16, k_cache, v_cache, NULL, NULL};
+    return token_scores_common(&src, block_tables, token_begin, context_lens, S, Hkv, D, BS, MB,
+                               NB, scores, score_stride);
+}
+
+int oracle_token_scores_int8(const int8_t *k_cache, const int8_t *v_cache, const float *k_scales,
+                             const float *v_scales, const int32_t *block_tables,
+                             const int32_t *token_begin, const int32_t *context_lens, int S,
+                             int Hkv, int D, int BS, int MB, int64_t NB, double *scores,
+                             int64_t score_stride)
+{
+    kv_src src = {KV_INT8, k_cache, v_cache, k_scales, v_scales};
+    return token_scores_common(&src, block_tables, token_begin, context_lens, S, Hkv, D, BS, MB,
+                               NB, scores, score_stride);
+}
+
+int oracle_token_scores_fp8(const uint8_t *k_cache, const uint8_t *v_cache,
+                            const int32_t *block_tables, const int32_t *token_begin,
+                            const int32_t *context_lens, int S, int Hkv, int D, int BS, int MB,
+                            int64_t NB, double *scores, int64_t score_stride)
+{
+    kv_src src = {KV_FP8, k_cache, v_cache, NULL, NULL};
+    return token_scores_common(&src, block_tables, token_begin, context_lens, S, Hkv, D, BS, MB,
+                               NB, scores, score_stride);
+}
+
+/*
+ * PagedEviction, decode-phase block eviction (same page and section: when
+ * the newest block fills, the mean importance of every existing full block is
+ * evaluated and the full block with the lowest mean is evicted whole).
+ *
+ * For each sequence s with evict_mask[s] != 0 and at least one full block
+ * (n_full = context_lens[s] / BS):
+ *   - the mean of full block j is (sum of its BS token scores, added in token
+ *     order in double) / BS, from the fp32 scores given (the importances the
+ *     caller holds, so that both sides take the decision from the same bits);
+ *   - the victim is the block with the smallest mean, the lowest j among
+ *     equal means; NaN means are never chosen unless every mean is NaN (then
+ *     block 0);
+ *   - the victim leaves the table: entries j+1 .. nblk-1 move down by one and
+ *     entry nblk-1 becomes -1; the scores of the tokens after the victim move
+ *     down by BS (the last BS positions of the old context keep their old
+ *     values); context_lens[s] -= BS; evicted[s] = the victim's physical block.
+ * Otherwise evicted[s] = -1 and nothing changes.  Tables, lengths and scores
+ * are updated in place.
+ */
+int oracle_evict_lowest_block(float *scores, int64_t score_stride, int32_t *block_tables,
+                              int32_t *context_lens, const int32_t *evict_mask, int32_t *evicted,
+                              int S, int MB, int BS)
+{
+    if (!scores || !block_tables || !context_lens || !evict_mask || !evicted) return ORC_ERR_ARG;
+    if (S < 0 || MB <= 0 || BS <= 0) return ORC_ERR_ARG;
+    for (int s = 0; s < S; ++s) {
+        const int n = context_lens[s];
+        if (n < 0 || (int64_t)n > (int64_t)MB * BS || (int64_t)n > score_stride) return ORC_ERR_TABLE;
+    }
+    for (int s = 0; s < S; ++s) {
+        evicted[s] = -1;
+        const int n = context_lens[s];
+        const int n_full = n / BS;
+        if (!evict_mask[s] || n_full == 0) continue;
+        float *sc = scores + (int64_t)s * score_stride;
+        int victim = -1;
+        double best = 0.0;
+        for (int j = 0; j < n_full; ++j) {
+            double sum = 0.0;
+            for (int r = 0; r < BS; ++r) sum += (double)sc[(int64_t)j * BS + r];
+            const double mean = sum / BS;
+            if (isnan(mean)) continue;
+            if (victim < 0 || mean < best) {
+                victim = j;
+                best = mean;
+            }
+        }
+        if (victim < 0) victim = 0;
+        int32_t *row = block_tables + (int64_t)s * MB;
+        const int nblk = (n + BS - 1) / BS;
+        evicted[s] = row[victim];
+        for (int j = victim; j + 1 < nblk; ++j) row[j] = row[j + 1];
+        row[nblk - 1] = -1;
+        for (int t = victim * BS; t + BS < n; ++t) sc[t] = sc[t + BS];
+        context_lens[s] = n - BS;
     }
     return ORC_OK;
 }

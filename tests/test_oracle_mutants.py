@@ -58,6 +58,22 @@ MUTANTS = {
                                    "return (double)base[slot * D + i];"),
     "fp8_write_value_from_key": ("v_cache[dst + i] = oracle_fp8_e4m3_from_double(\n                    bf16_bits_to_double(value[",
                                  "v_cache[dst + i] = oracle_fp8_e4m3_from_double(\n                    bf16_bits_to_double(key["),
+    "score_ratio_inverted": ("scores[(int64_t)s * score_stride + t] = sqrt(vv) / sqrt(kk);",
+                             "scores[(int64_t)s * score_stride + t] = sqrt(kk) / sqrt(vv);"),
+    "score_without_sqrt": ("scores[(int64_t)s * score_stride + t] = sqrt(vv) / sqrt(kk);",
+                           "scores[(int64_t)s * score_stride + t] = vv / kk;"),
+    "score_first_head_only": ("double kk = 0.0, vv = 0.0;\n            for (int g = 0; g < Hkv; ++g) {",
+                              "double kk = 0.0, vv = 0.0;\n            for (int g = 0; g < 1; ++g) {"),
+    "score_ignores_begin": ("for (int t = token_begin ? token_begin[s] : 0; t < n; ++t) {",
+                            "for (int t = 0; t < n; ++t) {"),
+    "evict_argmax": ("if (victim < 0 || mean < best) {", "if (victim < 0 || mean > best) {"),
+    "evict_ties_to_last": ("if (victim < 0 || mean < best) {", "if (victim < 0 || mean <= best) {"),
+    "evict_nan_candidate": ("            if (isnan(mean)) continue;\n", ""),
+    "evict_partial_block_candidate": ("const int n_full = n / BS;", "const int n_full = (n + BS - 1) / BS;"),
+    "evict_table_not_shifted": ("for (int j = victim; j + 1 < nblk; ++j) row[j] = row[j + 1];",
+                                "for (int j = victim + 1; j + 1 < nblk; ++j) row[j] = row[j + 1];"),
+    "evict_scores_not_shifted": ("for (int t = victim * BS; t + BS < n; ++t) sc[t] = sc[t + BS];", ""),
+    "evict_context_kept": ("context_lens[s] = n - BS;", "context_lens[s] = n;"),
 }
 
 PIN_FUNCS = [
@@ -82,6 +98,13 @@ PIN_FUNCS = [
     "test_fp8_decode_matches_sdpa_on_decoded_cache",
     "test_fp8_matches_bf16_on_the_same_values",
     "test_fp8_write_then_decode_matches_sdpa_on_appended_context",
+    "test_token_scores_closed_form_on_constant_rows",
+    "test_token_scores_match_norms_all_kinds",
+    "test_token_scores_scale_with_v_and_inversely_with_k",
+    "test_evict_removes_the_lowest_mean_full_block",
+    "test_evict_ties_take_the_lowest_block_and_nan_is_never_chosen",
+    "test_evict_masked_and_short_sequences_are_untouched",
+    "test_decode_after_eviction_equals_attention_without_the_block",
 ]
 
 RUNNER = r"""
