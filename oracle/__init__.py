@@ -85,9 +85,9 @@ class OracleLib:
                                  ("oracle_token_scores_int8", [P, P, P, P]),
                                  ("oracle_token_scores_fp8", [P, P])):
             fn = getattr(lib, name)
-            fn.argtypes = cache_args + [P, P, P, i32, i32, i32, i32, i32, i64, P, i64]
+            fn.argtypes = cache_args + [P, P, P, i32, i32, i32, i32, i32, i64, P]
             fn.restype = i32
-        lib.oracle_evict_lowest_block.argtypes = [P, i64, P, P, P, P, i32, i32, i32]
+        lib.oracle_evict_lowest_block.argtypes = [P, P, P, P, P, i32, i32, i32, i64]
         lib.oracle_evict_lowest_block.restype = i32
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i32
@@ -325,9 +325,10 @@ def kv_write_fp8(key_bits, value_bits, slots, k_codes, v_codes, lib: "OracleLib 
     return kc, vc
 
 
-def token_scores(views, token_begin=None, score_stride=None, lib: "OracleLib | None" = None):
-    """PagedEviction importances ||V_t|| / ||K_t|| (float64 [S, score_stride],
-    NaN where not computed) for per-layer views (bf16, int8 or fp8 cache)."""
+def token_scores(views, token_begin=None, lib: "OracleLib | None" = None):
+    """PagedEviction importances ||V_t|| / ||K_t|| kept per token slot:
+    float64 [NB, BS] (NaN where no scored token lives) for per-layer views
+    (bf16, int8 or fp8 cache)."""
     import torch
 
     bt = _c(views["block_tables"].cpu().numpy(), np.int32)
@@ -335,8 +336,7 @@ def token_scores(views, token_begin=None, score_stride=None, lib: "OracleLib | N
     kc, vc = views["k_cache"].cpu(), views["v_cache"].cpu()
     NB, BS, Hkv, D = kc.shape
     S, MB = bt.shape
-    stride = score_stride or MB * BS
-    out = np.full((S, stride), np.nan, dtype=np.float64)
+    out = np.full((NB, BS), np.nan, dtype=np.float64)
     tb = None if token_begin is None else _c(np.asarray(token_begin), np.int32)
     tbp = _ptr(tb) if tb is not None else None
     L = lib.lib if lib is not None else _load()
@@ -344,39 +344,40 @@ def token_scores(views, token_begin=None, score_stride=None, lib: "OracleLib | N
         k8 = _c(kc.view(torch.uint8).numpy(), np.uint8)
         v8 = _c(vc.view(torch.uint8).numpy(), np.uint8)
         rc = L.oracle_token_scores_fp8(_ptr(k8), _ptr(v8), _ptr(bt), tbp, _ptr(cl), S, Hkv, D, BS,
-                                       MB, NB, _ptr(out), stride)
+                                       MB, NB, _ptr(out))
     elif "k_scales" in views:
         k8 = _c(kc.numpy(), np.int8)
         v8 = _c(vc.numpy(), np.int8)
         ks = _c(views["k_scales"].cpu().numpy(), np.float32)
         vs = _c(views["v_scales"].cpu().numpy(), np.float32)
         rc = L.oracle_token_scores_int8(_ptr(k8), _ptr(v8), _ptr(ks), _ptr(vs), _ptr(bt), tbp,
-                                        _ptr(cl), S, Hkv, D, BS, MB, NB, _ptr(out), stride)
+                                        _ptr(cl), S, Hkv, D, BS, MB, NB, _ptr(out))
     else:
         kb = _c(kc.contiguous().view(torch.int16).numpy().view(np.uint16), np.uint16)
         vb = _c(vc.contiguous().view(torch.int16).numpy().view(np.uint16), np.uint16)
         rc = L.oracle_token_scores_bf16(_ptr(kb), _ptr(vb), _ptr(bt), tbp, _ptr(cl), S, Hkv, D, BS,
-                                        MB, NB, _ptr(out), stride)
+                                        MB, NB, _ptr(out))
     if rc != 0:
         raise ValueError(f"oracle rejected the inputs (code {rc})")
     return out
 
 
-def evict_lowest_block(scores, block_tables, context_lens, evict_mask, block_size,
+def evict_lowest_block(scores, block_tables, context_lens, evict_mask,
                        lib: "OracleLib | None" = None):
-    """Decode-phase PagedEviction on copies: returns (scores, block_tables,
+    """Decode-phase PagedEviction on copies: returns (block_tables,
     context_lens, evicted) after evicting, for every masked sequence, its full
-    block of lowest mean importance.  scores: float32 [S, stride]."""
+    block of lowest mean importance.  scores: float32 per-slot [NB, BS]."""
     as_i32 = lambda a: np.asarray(a, dtype=np.int32) if isinstance(a, (list, tuple)) else a
-    sc = np.array(_c(scores, np.float32), copy=True)
-    bt = np.array(_c(block_tables, np.int32), copy=True)
+    sc = _c(scores, np.float32)
+    NB, BS = sc.shape
+    bt = np.array(_c(as_i32(block_tables), np.int32), copy=True)
     cl = np.array(_c(as_i32(context_lens), np.int32), copy=True)
     mask = _c(np.asarray(evict_mask, dtype=np.int32), np.int32)
     S, MB = bt.shape
     ev = np.zeros(S, dtype=np.int32)
     L = lib.lib if lib is not None else _load()
-    rc = L.oracle_evict_lowest_block(_ptr(sc), sc.shape[1], _ptr(bt), _ptr(cl), _ptr(mask), _ptr(ev),
-                                     S, MB, block_size)
+    rc = L.oracle_evict_lowest_block(_ptr(sc), _ptr(bt), _ptr(cl), _ptr(mask), _ptr(ev), S, MB,
+                                     BS, NB)
     if rc != 0:
         raise ValueError(f"oracle rejected the inputs (code {rc})")
-    return sc, bt, cl, ev
+    return bt, cl, ev

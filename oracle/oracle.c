@@ -448,14 +448,15 @@ int oracle_kv_write_fp8(const uint16_t *key, const uint16_t *value, const int32_
  * importance is the ratio of the L2 norms of its value and key,
  * S_t = ||V_t||_2 / ||K_t||_2, where K_t and V_t are the token's whole rows in
  * the layer's cache (all kv heads, all dims), dequantized like the decode
- * entry points.  For every sequence s, tokens t in [token_begin[s],
- * context_lens[s]) (token_begin NULL: from 0) get scores[s * score_stride + t]
- * = S_t in double; other entries are left alone.  Norms and ratio in double.
+ * entry points.  The score is kept with the token's slot, like its K/V:
+ * scores[b * BS + r] for the token in physical block b, slot r.  For every
+ * sequence s, tokens t in [token_begin[s], context_lens[s]) (token_begin
+ * NULL: from 0) are scored; other entries are left alone.  Norms and ratio in
+ * double.
  */
 static int token_scores_common(const kv_src *src, const int32_t *block_tables,
                                const int32_t *token_begin, const int32_t *context_lens,
-                               int S, int Hkv, int D, int BS, int MB, int64_t NB,
-                               double *scores, int64_t score_stride)
+                               int S, int Hkv, int D, int BS, int MB, int64_t NB, double *scores)
 {
     if (!src->k || !src->v || !block_tables || !context_lens || !scores) return ORC_ERR_ARG;
     if (S < 0 || Hkv <= 0 || D <= 0 || BS <= 0 || MB < 0 || NB < 0) return ORC_ERR_ARG;
@@ -463,7 +464,7 @@ static int token_scores_common(const kv_src *src, const int32_t *block_tables,
     for (int s = 0; s < S; ++s) {
         int n = context_lens[s];
         int b0 = token_begin ? token_begin[s] : 0;
-        if (n < 0 || (int64_t)n > (int64_t)MB * BS || (int64_t)n > score_stride) return ORC_ERR_TABLE;
+        if (n < 0 || (int64_t)n > (int64_t)MB * BS) return ORC_ERR_TABLE;
         if (b0 < 0) return ORC_ERR_ARG;
         int nblk = (n + BS - 1) / BS;
         for (int j = 0; j < nblk; ++j) {
@@ -485,7 +486,7 @@ static int token_scores_common(const kv_src *src, const int32_t *block_tables,
                     vv += vx * vx;
                 }
             }
-            scores[(int64_t)s * score_stride + t] = sqrt(vv) / sqrt(kk);
+            scores[b * BS + r] = sqrt(vv) / sqrt(kk);
         }
     }
     return ORC_OK;
@@ -494,32 +495,31 @@ static int token_scores_common(const kv_src *src, const int32_t *block_tables,
 int oracle_token_scores_bf16(const uint16_t *k_cache, const uint16_t *v_cache,
                              const int32_t *block_tables, const int32_t *token_begin,
                              const int32_t *context_lens, int S, int Hkv, int D, int BS, int MB,
-                             int64_t NB, double *scores, int64_t score_stride)
+                             int64_t NB, double *scores)
 {
     kv_src src = {KV_BF16, k_cache, v_cache, NULL, NULL};
     return token_scores_common(&src, block_tables, token_begin, context_lens, S, Hkv, D, BS, MB,
-                               NB, scores, score_stride);
+                               NB, scores);
 }
 
 int oracle_token_scores_int8(const int8_t *k_cache, const int8_t *v_cache, const float *k_scales,
                              const float *v_scales, const int32_t *block_tables,
                              const int32_t *token_begin, const int32_t *context_lens, int S,
-                             int Hkv, int D, int BS, int MB, int64_t NB, double *scores,
-                             int64_t score_stride)
+                             int Hkv, int D, int BS, int MB, int64_t NB, double *scores)
 {
     kv_src src = {KV_INT8, k_cache, v_cache, k_scales, v_scales};
     return token_scores_common(&src, block_tables, token_begin, context_lens, S, Hkv, D, BS, MB,
-                               NB, scores, score_stride);
+                               NB, scores);
 }
 
 int oracle_token_scores_fp8(const uint8_t *k_cache, const uint8_t *v_cache,
                             const int32_t *block_tables, const int32_t *token_begin,
                             const int32_t *context_lens, int S, int Hkv, int D, int BS, int MB,
-                            int64_t NB, double *scores, int64_t score_stride)
+                            int64_t NB, double *scores)
 {
     kv_src src = {KV_FP8, k_cache, v_cache, NULL, NULL};
     return token_scores_common(&src, block_tables, token_begin, context_lens, S, Hkv, D, BS, MB,
-                               NB, scores, score_stride);
+                               NB, scores);
 }
 
 /*
@@ -529,40 +529,46 @@ int oracle_token_scores_fp8(const uint8_t *k_cache, const uint8_t *v_cache,
  *
  * For each sequence s with evict_mask[s] != 0 and at least one full block
  * (n_full = context_lens[s] / BS):
- *   - the mean of full block j is (sum of its BS token scores, added in token
- *     order in double) / BS, from the fp32 scores given (the importances the
- *     caller holds, so that both sides take the decision from the same bits);
+ *   - the mean of full block j (physical block b = block_tables[s][j]) is
+ *     (sum of its BS slot scores scores[b * BS + r], added in slot order in
+ *     double) / BS, from the fp32 scores given (the importances the caller
+ *     holds, so that both sides take the decision from the same bits);
  *   - the victim is the block with the smallest mean, the lowest j among
  *     equal means; NaN means are never chosen unless every mean is NaN (then
  *     block 0);
  *   - the victim leaves the table: entries j+1 .. nblk-1 move down by one and
- *     entry nblk-1 becomes -1; the scores of the tokens after the victim move
- *     down by BS (the last BS positions of the old context keep their old
- *     values); context_lens[s] -= BS; evicted[s] = the victim's physical block.
- * Otherwise evicted[s] = -1 and nothing changes.  Tables, lengths and scores
- * are updated in place.
+ *     entry nblk-1 becomes -1; context_lens[s] -= BS; evicted[s] = the
+ *     victim's physical block (free for reuse; its scores stay with it).
+ * Otherwise evicted[s] = -1 and nothing changes.  Tables and lengths are
+ * updated in place.
  */
-int oracle_evict_lowest_block(float *scores, int64_t score_stride, int32_t *block_tables,
-                              int32_t *context_lens, const int32_t *evict_mask, int32_t *evicted,
-                              int S, int MB, int BS)
+int oracle_evict_lowest_block(const float *scores, int32_t *block_tables, int32_t *context_lens,
+                              const int32_t *evict_mask, int32_t *evicted, int S, int MB, int BS,
+                              int64_t NB)
 {
     if (!scores || !block_tables || !context_lens || !evict_mask || !evicted) return ORC_ERR_ARG;
-    if (S < 0 || MB <= 0 || BS <= 0) return ORC_ERR_ARG;
+    if (S < 0 || MB <= 0 || BS <= 0 || NB < 0) return ORC_ERR_ARG;
     for (int s = 0; s < S; ++s) {
         const int n = context_lens[s];
-        if (n < 0 || (int64_t)n > (int64_t)MB * BS || (int64_t)n > score_stride) return ORC_ERR_TABLE;
+        if (n < 0 || (int64_t)n > (int64_t)MB * BS) return ORC_ERR_TABLE;
+        if (!evict_mask[s]) continue;
+        for (int j = 0; j < (n + BS - 1) / BS; ++j) {
+            int32_t b = block_tables[(int64_t)s * MB + j];
+            if (b < 0 || (int64_t)b >= NB) return ORC_ERR_TABLE;
+        }
     }
     for (int s = 0; s < S; ++s) {
         evicted[s] = -1;
         const int n = context_lens[s];
         const int n_full = n / BS;
         if (!evict_mask[s] || n_full == 0) continue;
-        float *sc = scores + (int64_t)s * score_stride;
+        int32_t *row = block_tables + (int64_t)s * MB;
         int victim = -1;
         double best = 0.0;
         for (int j = 0; j < n_full; ++j) {
+            const float *blk = scores + (int64_t)row[j] * BS;
             double sum = 0.0;
-            for (int r = 0; r < BS; ++r) sum += (double)sc[(int64_t)j * BS + r];
+            for (int r = 0; r < BS; ++r) sum += (double)blk[r];
             const double mean = sum / BS;
             if (isnan(mean)) continue;
             if (victim < 0 || mean < best) {
@@ -571,12 +577,10 @@ int oracle_evict_lowest_block(float *scores, int64_t score_stride, int32_t *bloc
             }
         }
         if (victim < 0) victim = 0;
-        int32_t *row = block_tables + (int64_t)s * MB;
         const int nblk = (n + BS - 1) / BS;
         evicted[s] = row[victim];
         for (int j = victim; j + 1 < nblk; ++j) row[j] = row[j + 1];
         row[nblk - 1] = -1;
-        for (int t = victim * BS; t + BS < n; ++t) sc[t] = sc[t + BS];
         context_lens[s] = n - BS;
     }
     return ORC_OK;

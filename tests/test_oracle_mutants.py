@@ -58,10 +58,13 @@ MUTANTS = {
                                    "return (double)base[slot * D + i];"),
     "fp8_write_value_from_key": ("v_cache[dst + i] = oracle_fp8_e4m3_from_double(\n                    bf16_bits_to_double(value[",
                                  "v_cache[dst + i] = oracle_fp8_e4m3_from_double(\n                    bf16_bits_to_double(key["),
-    "score_ratio_inverted": ("scores[(int64_t)s * score_stride + t] = sqrt(vv) / sqrt(kk);",
-                             "scores[(int64_t)s * score_stride + t] = sqrt(kk) / sqrt(vv);"),
-    "score_without_sqrt": ("scores[(int64_t)s * score_stride + t] = sqrt(vv) / sqrt(kk);",
-                           "scores[(int64_t)s * score_stride + t] = vv / kk;"),
+    "score_ratio_inverted": ("scores[b * BS + r] = sqrt(vv) / sqrt(kk);",
+                             "scores[b * BS + r] = sqrt(kk) / sqrt(vv);"),
+    "score_without_sqrt": ("scores[b * BS + r] = sqrt(vv) / sqrt(kk);", "scores[b * BS + r] = vv / kk;"),
+    "score_at_logical_position": ("scores[b * BS + r] = sqrt(vv) / sqrt(kk);",
+                                  "scores[(int64_t)s * MB * BS + t] = sqrt(vv) / sqrt(kk);"),
+    "evict_mean_of_logical_slots": ("const float *blk = scores + (int64_t)row[j] * BS;",
+                                    "const float *blk = scores + (int64_t)j * BS;"),
     "score_first_head_only": ("double kk = 0.0, vv = 0.0;\n            for (int g = 0; g < Hkv; ++g) {",
                               "double kk = 0.0, vv = 0.0;\n            for (int g = 0; g < 1; ++g) {"),
     "score_ignores_begin": ("for (int t = token_begin ? token_begin[s] : 0; t < n; ++t) {",
@@ -72,7 +75,6 @@ MUTANTS = {
     "evict_partial_block_candidate": ("const int n_full = n / BS;", "const int n_full = (n + BS - 1) / BS;"),
     "evict_table_not_shifted": ("for (int j = victim; j + 1 < nblk; ++j) row[j] = row[j + 1];",
                                 "for (int j = victim + 1; j + 1 < nblk; ++j) row[j] = row[j + 1];"),
-    "evict_scores_not_shifted": ("for (int t = victim * BS; t + BS < n; ++t) sc[t] = sc[t + BS];", ""),
     "evict_context_kept": ("context_lens[s] = n - BS;", "context_lens[s] = n;"),
 }
 

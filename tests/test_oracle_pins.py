@@ -432,20 +432,31 @@ def _filled_views(kv="bf16", ctx=(37, 64, 5), seed=51, Hkv=2, D=64, bs=16):
     return C.make_case(len(ctx), 4, Hkv, D, bs, ctx=ctx, seed=seed, kv_dtype=kv)[1]
 
 
+def _slot_of_tokens(v, s, bs):
+    """(physical block, slot) of every token of sequence s."""
+    n = int(v["context_lens"][s])
+    t = np.arange(n)
+    return v["block_tables"].numpy()[s][t // bs], t % bs
+
+
 def test_token_scores_closed_form_on_constant_rows():
-    # Every K element 0.5 and every V element 2.0: ||V|| / ||K|| = 4 exactly.
+    # Every K element 0.5 and every V element 2.0: ||V|| / ||K|| = 4 exactly,
+    # at each token's slot and nowhere else.
     v = _filled_views()
     v["k_cache"].fill_(0.5)
     v["v_cache"].fill_(2.0)
     sc = oracle.token_scores(v)
-    for s, n in enumerate(v["context_lens"].tolist()):
-        assert np.all(sc[s, :n] == 4.0) and np.all(np.isnan(sc[s, n:]))
+    hit = np.zeros(sc.shape, dtype=bool)
+    for s in range(3):
+        b, r = _slot_of_tokens(v, s, 16)
+        hit[b, r] = True
+    assert np.all(sc[hit] == 4.0) and np.all(np.isnan(sc[~hit]))
 
 
 @pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
 def test_token_scores_match_norms_of_gathered_rows(kv):
     # Brute force: rows gathered by numpy indexing, norms by torch over all kv
-    # heads and dims of each token.
+    # heads and dims of each token; scores read back at the tokens' slots.
     v = _filled_views(kv=kv, ctx=(37, 64, 5, 0), seed=52, Hkv=3)
     begin = np.array([0, 20, 5, 0], dtype=np.int32)
     sc = oracle.token_scores(v, token_begin=begin)
@@ -456,9 +467,10 @@ def test_token_scores_match_norms_of_gathered_rows(kv):
         nk = torch.linalg.vector_norm(torch.from_numpy(K), dim=(0, 2))
         nv = torch.linalg.vector_norm(torch.from_numpy(V), dim=(0, 2))
         ref = (nv / nk).numpy()
-        b = begin[s]
-        assert np.allclose(sc[s, b:n], ref[b:], rtol=1e-12, atol=0)
-        assert np.all(np.isnan(sc[s, :b]))
+        b, r = _slot_of_tokens(v, s, 16)
+        got = sc[b, r]
+        assert np.allclose(got[begin[s]:], ref[begin[s]:], rtol=1e-12, atol=0)
+        assert np.all(np.isnan(got[:begin[s]]))
 
 
 def test_token_scores_match_norms_all_kinds():
@@ -475,53 +487,54 @@ def test_token_scores_scale_with_v_and_inversely_with_k():
     assert np.array_equal(oracle.token_scores(w), base / 4, equal_nan=True)
 
 
-def _block_scores(means, bs, extra=0, seed=0):
-    """fp32 token scores [1, len(means)*bs + extra] whose full blocks have the
-    given means exactly (block j: mean + symmetric +-2^-8 offsets)."""
+def _pool_scores(means, bs, NB, order, seed=0, tail=0):
+    """fp32 per-slot scores [NB, bs]: logical block j of the table `order` has
+    mean means[j] exactly (+-2^-8 offsets in a random arrangement); a partial
+    block after them gets `tail` tokens of score -100 (lowest of all)."""
     rng = np.random.default_rng(seed)
-    rows = []
-    for m in means:
-        off = rng.permutation(np.repeat([2.0 ** -8, -2.0 ** -8], bs // 2))
-        rows.append(m + off)
-    tail = np.full(extra, -100.0)                           # partial block: lowest of all
-    return np.concatenate(rows + [tail]).astype(np.float32)[None, :]
+    sc = np.full((NB, bs), 7.0, dtype=np.float32)
+    for j, m in enumerate(means):
+        sc[order[j]] = m + rng.permutation(np.repeat([2.0 ** -8, -2.0 ** -8], bs // 2))
+    if tail:
+        sc[order[len(means)], :tail] = -100.0
+    return sc
 
 
 def test_evict_removes_the_lowest_mean_full_block():
-    bs = 16
+    bs, NB = 16, 12
     means = [3.0, 1.5, 0.25, 2.0, 0.75]
-    sc = _block_scores(means, bs, extra=5)
-    n = sc.shape[1]
-    row = np.array([[40, 41, 42, 43, 44, 45, 99, 99]], dtype=np.int32)
-    out_sc, bt, cl, ev = oracle.evict_lowest_block(sc, row, [n], [1], bs)
-    assert ev[0] == 42 and cl[0] == n - bs
-    assert np.array_equal(bt[0], [40, 41, 43, 44, 45, -1, 99, 99])
-    assert np.array_equal(out_sc[0, :n - bs], np.delete(sc[0], np.s_[2 * bs:3 * bs]))
+    row = [9, 4, 7, 0, 11, 3]                              # 5 full blocks + 1 partial
+    sc = _pool_scores(means, bs, NB, row, tail=5)
+    n = 5 * bs + 5
+    table = np.array([row + [99, 99]], dtype=np.int32)
+    bt, cl, ev = oracle.evict_lowest_block(sc, table, [n], [1])
+    assert ev[0] == 7 and cl[0] == n - bs
+    assert np.array_equal(bt[0], np.delete(table[0], 2)[:5].tolist() + [-1, 99, 99])
     # the partial last block (lowest scores of all) was never a candidate
 
 
 def test_evict_ties_take_the_lowest_block_and_nan_is_never_chosen():
-    bs = 16
-    sc = _block_scores([2.0, 1.0, 3.0, 1.0], bs)
-    _, bt, _, ev = oracle.evict_lowest_block(sc, np.array([[7, 8, 9, 10]], np.int32), [64], [1], bs)
-    assert ev[0] == 8 and np.array_equal(bt[0], [7, 9, 10, -1])
-    sc[0, 5] = np.nan                                       # block 0's mean becomes NaN
-    sc[0, 16:32] = 5.0
-    _, _, _, ev = oracle.evict_lowest_block(sc, np.array([[7, 8, 9, 10]], np.int32), [64], [1], bs)
-    assert ev[0] == 10                                      # means: NaN, 5, 3, 1
-    allnan = np.full((1, 32), np.nan, np.float32)
-    _, _, _, ev = oracle.evict_lowest_block(allnan, np.array([[3, 4]], np.int32), [32], [1], bs)
+    bs, NB = 16, 6
+    row = [2, 5, 1, 4]
+    sc = _pool_scores([2.0, 1.0, 3.0, 1.0], bs, NB, row)
+    bt, _, ev = oracle.evict_lowest_block(sc, np.array([row], np.int32), [64], [1])
+    assert ev[0] == 5 and np.array_equal(bt[0], [2, 1, 4, -1])
+    sc[2, 5] = np.nan                                       # block 0's mean becomes NaN
+    sc[5] = 5.0
+    _, _, ev = oracle.evict_lowest_block(sc, np.array([row], np.int32), [64], [1])
+    assert ev[0] == 4                                       # means: NaN, 5, 3, 1
+    allnan = np.full((NB, bs), np.nan, np.float32)
+    _, _, ev = oracle.evict_lowest_block(allnan, np.array([[3, 0]], np.int32), [32], [1])
     assert ev[0] == 3
 
 
 def test_evict_masked_and_short_sequences_are_untouched():
-    bs = 16
-    sc = _block_scores([1.0, 2.0], bs, extra=3)
-    sc2 = np.concatenate([sc, sc])
+    bs, NB = 16, 8
+    sc = _pool_scores([1.0, 2.0], bs, NB, [1, 2, 3], tail=3)
     bt = np.array([[1, 2, 3], [4, 5, 6]], np.int32)
-    out_sc, out_bt, cl, ev = oracle.evict_lowest_block(sc2, bt, [35, 15], [0, 1], bs)
+    out_bt, cl, ev = oracle.evict_lowest_block(sc, bt, [35, 15], [0, 1])
     assert np.array_equal(ev, [-1, -1]) and np.array_equal(cl, [35, 15])
-    assert np.array_equal(out_bt, bt) and np.array_equal(out_sc, sc2)
+    assert np.array_equal(out_bt, bt)
 
 
 def test_decode_after_eviction_equals_attention_without_the_block():
@@ -532,7 +545,7 @@ def test_decode_after_eviction_equals_attention_without_the_block():
     _, v = C.make_case(3, 8, 2, 64, bs, ctx=ctx, seed=54)
     sc = oracle.token_scores(v).astype(np.float32)
     bt0 = v["block_tables"].numpy()
-    out_sc, bt, cl, ev = oracle.evict_lowest_block(sc, bt0, np.array(ctx, np.int32), [1, 1, 1], bs)
+    bt, cl, ev = oracle.evict_lowest_block(sc, bt0, np.array(ctx, np.int32), [1, 1, 1])
     w = dict(v, block_tables=torch.from_numpy(bt), context_lens=torch.from_numpy(cl))
     out = C.oracle_out(w)
     q = v["q"].to(torch.float64)
@@ -545,5 +558,5 @@ def test_decode_after_eviction_equals_attention_without_the_block():
             torch.from_numpy(V[:, keep])[None], scale=float(np.float32(v["scale"])),
             enable_gqa=True)[0, :, 0, :].numpy()
         assert np.allclose(out[s], ref, rtol=0, atol=1e-12), s
-        full_means = [sc[s, j * bs:(j + 1) * bs].astype(np.float64).mean() for j in range(n // bs)]
+        full_means = [sc[bt0[s][j]].astype(np.float64).mean() for j in range(n // bs)]
         assert victim == int(np.argmin(full_means))
