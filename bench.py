@@ -25,7 +25,8 @@ host's cores on a bounded sample of the same workload.
 With --workload kv_write_llama3_8b (or kv_write_int8_ / kv_write_fp8_llama3_8b) it times the
 KV write path instead -- one paged_kv_write call per step, storing a
 16384-token prefill chunk into the paged cache -- and prints the same kind of
-line for it.
+line for it; with --workload scores_<decode workload> (e.g. scores_llama3_8b)
+it times PagedEviction's token scoring over that workload's whole cache.
 """
 from __future__ import annotations
 
@@ -117,6 +118,8 @@ def main() -> int:
     B.load()   # fails loudly if the HIP library is missing
     if args.workload in I.WRITE_WORKLOADS:
         return bench_write(args)
+    if args.workload.startswith("scores_"):
+        return bench_scores(args)
     wl = I.WORKLOADS[args.workload]
     split = wl.split_tokens if args.split_tokens is None else args.split_tokens
     dev = torch.device("cuda:0")
@@ -336,6 +339,142 @@ def bench_write(args) -> int:
     }
     print(json.dumps(record), flush=True)
     return 0
+
+
+def bench_scores(args) -> int:
+    """PagedEviction scoring on its own: one paged_kv_token_scores call per step
+    over every token of a decode workload's cache (scores_<workload>)."""
+    import torch
+
+    from paged_kv_cache_393_amd import accounting as A
+    from paged_kv_cache_393_amd import binding as B
+    from paged_kv_cache_393_amd import inputs as I
+    from paged_kv_cache_393_amd import probe as P
+
+    wl = I.WORKLOADS[args.workload[len("scores_"):]]
+    if wl.num_layers != 1:
+        raise SystemExit("scoring bench takes a single-layer workload")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = I.make_inputs(wl, dev)
+    v = I.layer_views(inp, 0)
+    scores = torch.zeros(tuple(v["k_cache"].shape[:2]), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    print(f"[bench] inputs for scores of {wl.name} ready", file=sys.stderr, flush=True)
+
+    def step():
+        B.token_scores(v, scores=scores, stream=stream)
+
+    flush_buf = None if args.no_flush else torch.ones((2 << 30) // 4, dtype=torch.float32,
+                                                       device=dev)
+
+    def evict():
+        if flush_buf is not None:
+            flush_buf.amax()
+
+    for _ in range(args.warmup):
+        evict()
+        step()
+    torch.cuda.synchronize()
+    ms = event_ms(stream, step, args.steps, before=evict)
+    ms_sorted = sorted(ms)
+    ms_mean = statistics.fmean(ms)
+    pct = lambda q: ms_sorted[min(len(ms_sorted) - 1, int(q * len(ms_sorted)))]
+    print(f"[bench] {args.steps} timed steps done", file=sys.stderr, flush=True)
+    ctx = inp["context_lens"].cpu().tolist()
+    nbytes = A.score_bytes(ctx, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.kv_dtype)
+    t_s = ms_mean / 1e3
+    gbps = nbytes / t_s / 1e9
+    probe_gbps = None
+    if not args.no_probe:
+        nb = (nbytes // 16) * 16
+        pbuf = torch.empty(nb, dtype=torch.uint8, device=dev)
+        pbuf.fill_(1)
+        sink = torch.zeros(256, dtype=torch.int32, device=dev)
+        pms = event_ms(stream, lambda: P.read(pbuf, sink, stream), 20, before=evict)
+        probe_gbps = nb / (statistics.median(pms) / 1e3) / 1e9
+        del pbuf
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            P.copy(src, dst, stream)
+        torch.cuda.synchronize()
+        del src, dst
+    name = "scores_" + wl.name
+    record = {
+        "metric": "PagedEviction token-importance scoring tokens/s and achieved HBM GB/s "
+                  "(% of peak), Llama-3-8B shape",
+        "value": sum(ctx) / t_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_mean,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype,
+        "data": "synthetic (seeded N(0,1) K/V, shuffled block pool)",
+        "config": {"workload": name, "num_seqs": wl.num_seqs, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "block_size": wl.block_size,
+                   "context_tokens": sum(ctx), "kv_dtype": wl.kv_dtype,
+                   "cache_evict_between_steps": "2 GiB read" if flush_buf is not None else None},
+        "pct_of_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
+        "ms_p10": pct(0.10), "ms_median": pct(0.50), "ms_p90": pct(0.90),
+        "hbm_read_probe_gbps": probe_gbps,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "token_scores_kernel",
+            "achieved": gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS,
+            "traffic": measured_traffic(name, "scores"),
+            "algorithmic_bytes_per_call": nbytes,
+            "calls_per_step": 1,
+            "ms_per_call": ms_mean,
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_scores(v, ctx),
+    }
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+def cpu_baseline_scores(views, ctx, budget_s=3.0):
+    """The oracle's scoring on the first sequences (about budget_s per run),
+    median of repeated runs, scaled to tokens/s; and its largest relative
+    difference from the GPU's scores on that sample."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_cache_393_amd import inputs as I
+
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    S = len(ctx)
+    t = time.perf_counter()
+    host = I.select_sequences(views, [0], views["k_cache"].shape[1])
+    oracle.token_scores(host)
+    per_tok = (time.perf_counter() - t) / max(1, ctx[0])
+    n = max(1, min(S, int(budget_s / max(per_tok * sum(ctx) / S, 1e-12))))
+    sub = I.select_sequences(views, list(range(n)), views["k_cache"].shape[1])
+    times, ref = [], None
+    while sum(times) < budget_s and len(times) < 25:
+        t = time.perf_counter()
+        ref = oracle.token_scores(sub)
+        times.append(time.perf_counter() - t)
+    t_med = statistics.median(times)
+    tokens = sum(ctx[:n])
+    return {
+        "value": tokens / t_med,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"the first {n} of {S} sequences ({tokens} tokens), one thread, median of "
+                  f"{len(times)} runs of {t_med:.3f}s",
+    }
 
 
 def cpu_baseline_write(ww, inp, budget_s=3.0):

@@ -337,7 +337,7 @@ def token_scores(views, token_begin=None, lib: "OracleLib | None" = None):
     NB, BS, Hkv, D = kc.shape
     S, MB = bt.shape
     out = np.full((NB, BS), np.nan, dtype=np.float64)
-    tb = None if token_begin is None else _c(np.asarray(token_begin), np.int32)
+    tb = None if token_begin is None else _c(np.asarray(token_begin, dtype=np.int32), np.int32)
     tbp = _ptr(tb) if tb is not None else None
     L = lib.lib if lib is not None else _load()
     if kc.dtype == torch.float8_e4m3fn:

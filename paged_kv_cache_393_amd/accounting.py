@@ -61,3 +61,18 @@ def write_bytes(num_tokens: int, num_written: int, num_kv_heads: int, head_dim: 
     else:
         raise ValueError(kv_dtype)
     return read + written
+
+
+def score_bytes(context_lens: Iterable[int], num_kv_heads: int, head_dim: int, block_size: int,
+                kv_dtype: str = "bf16") -> int:
+    """Algorithmic bytes of one PagedEviction scoring call over whole contexts:
+    every token's K and V rows (plus int8 scales), its fp32 score, the valid
+    block-table entries and the context lengths."""
+    ctx = [int(c) for c in context_lens]
+    tokens = sum(ctx)
+    elem = 2 if kv_dtype == "bf16" else 1
+    per_token = 2 * num_kv_heads * head_dim * elem + 4
+    if kv_dtype == "int8":
+        per_token += 2 * num_kv_heads * 4
+    tables = sum((c + block_size - 1) // block_size for c in ctx) * 4
+    return tokens * per_token + tables + 4 * len(ctx)

@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "paged_attn.h")
 WRITE_HEADER = os.path.join(os.path.dirname(_HERE), "include", "paged_kv_write.h")
+EVICT_HEADER = os.path.join(os.path.dirname(_HERE), "include", "paged_kv_evict.h")
 
 PA_OK = 0
 PA_ERR_NULL = -1
@@ -38,6 +39,11 @@ class PaWriteShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tokens", "num_kv_heads", "head_dim", "block_size", "num_blocks", "key_stride",
         "value_stride")]
+
+
+class PaScoreShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_kv_heads", "head_dim", "block_size", "max_blocks_per_seq", "num_blocks")]
 
 
 class PagedAttnError(RuntimeError):
@@ -78,6 +84,15 @@ def load() -> ctypes.CDLL:
     lib.paged_attn_decode_fp8.restype = ctypes.c_int
     lib.paged_kv_write_fp8.argtypes = [P, P, P, P, P, WP, P]
     lib.paged_kv_write_fp8.restype = ctypes.c_int
+    CP = ctypes.POINTER(PaScoreShape)
+    lib.paged_kv_token_scores.argtypes = [P, P, P, P, P, P, CP, P]
+    lib.paged_kv_token_scores.restype = ctypes.c_int
+    lib.paged_kv_token_scores_int8.argtypes = [P, P, P, P, P, P, P, P, CP, P]
+    lib.paged_kv_token_scores_int8.restype = ctypes.c_int
+    lib.paged_kv_token_scores_fp8.argtypes = [P, P, P, P, P, P, CP, P]
+    lib.paged_kv_token_scores_fp8.restype = ctypes.c_int
+    lib.paged_kv_evict_lowest_block.argtypes = [P, P, P, P, P, CP, P]
+    lib.paged_kv_evict_lowest_block.restype = ctypes.c_int
     lib.paged_attn_strerror.argtypes = [ctypes.c_int]
     lib.paged_attn_strerror.restype = ctypes.c_char_p
     lib.paged_attn_abi_version.argtypes = []
@@ -88,9 +103,9 @@ def load() -> ctypes.CDLL:
 
 def header_functions() -> list:
     """Names of the functions the library's headers (include/paged_attn.h,
-    include/paged_kv_write.h) declare."""
+    include/paged_kv_write.h, include/paged_kv_evict.h) declare."""
     names = set()
-    for h in (HEADER, WRITE_HEADER):
+    for h in (HEADER, WRITE_HEADER, EVICT_HEADER):
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
         names.update(re.findall(r"\b((?:paged_attn|paged_kv)_\w+)\s*\(", text))
     return sorted(names)
@@ -330,3 +345,70 @@ def kv_write_inputs(inp: dict, stream=None) -> None:
     else:
         kv_write(inp["key"], inp["value"], inp["slots"], inp["k_cache"], inp["v_cache"],
                  stream=stream)
+
+
+def score_shape(k_cache, block_tables) -> PaScoreShape:
+    NB, bs, Hkv, D = k_cache.shape
+    S, MB = block_tables.shape
+    return PaScoreShape(S, Hkv, D, bs, MB, NB)
+
+
+def token_scores(views: dict, scores=None, token_begin=None, stream=None) -> torch.Tensor:
+    """PagedEviction importances ||V|| / ||K|| of the tokens of per-layer views
+    (bf16, int8 or fp8 cache), stored per token slot: fp32 [num_blocks,
+    block_size].  A new `scores` tensor is filled with NaN first; slots of no
+    scored token keep what `scores` held."""
+    kc, vc = views["k_cache"], views["v_cache"]
+    bt, cl = views["block_tables"], views["context_lens"]
+    for name, t in (("k_cache", kc), ("v_cache", vc), ("block_tables", bt), ("context_lens", cl)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if bt.dtype != torch.int32 or cl.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    NB, bs = kc.shape[0], kc.shape[1]
+    if scores is None:
+        scores = torch.full((NB, bs), float("nan"), dtype=torch.float32, device=kc.device)
+    if scores.dtype != torch.float32 or tuple(scores.shape) != (NB, bs) or not scores.is_contiguous():
+        raise ValueError("scores must be contiguous fp32 [num_blocks, block_size]")
+    if token_begin is not None and (token_begin.dtype != torch.int32 or not token_begin.is_cuda):
+        raise TypeError("token_begin must be an int32 device tensor")
+    sh = score_shape(kc, bt)
+    L = load()
+    tb = _ptr(token_begin)
+    if kc.dtype in FP8_DTYPES:
+        rc = L.paged_kv_token_scores_fp8(_ptr(kc), _ptr(vc), _ptr(bt), tb, _ptr(cl), _ptr(scores),
+                                         ctypes.byref(sh), _stream_handle(stream))
+    elif "k_scales" in views:
+        rc = L.paged_kv_token_scores_int8(_ptr(kc), _ptr(vc), _ptr(views["k_scales"]),
+                                          _ptr(views["v_scales"]), _ptr(bt), tb, _ptr(cl),
+                                          _ptr(scores), ctypes.byref(sh), _stream_handle(stream))
+    else:
+        if kc.dtype != torch.bfloat16:
+            raise TypeError("cache must be bf16, int8 (with scales) or fp8")
+        rc = L.paged_kv_token_scores(_ptr(kc), _ptr(vc), _ptr(bt), tb, _ptr(cl), _ptr(scores),
+                                     ctypes.byref(sh), _stream_handle(stream))
+    _check(rc)
+    return scores
+
+
+def evict_lowest_block(scores, block_tables, context_lens, evict_mask, evicted=None,
+                       stream=None) -> torch.Tensor:
+    """paged_kv_evict_lowest_block: for every masked sequence evict its full
+    block of lowest mean importance (block_tables and context_lens updated in
+    place); returns evicted int32 [S] (the freed physical block, or -1)."""
+    S, MB = block_tables.shape
+    NB, bs = scores.shape
+    for name, t, dt in (("scores", scores, torch.float32), ("block_tables", block_tables, torch.int32),
+                        ("context_lens", context_lens, torch.int32),
+                        ("evict_mask", evict_mask, torch.int32)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != dt:
+            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    if tuple(context_lens.shape) != (S,) or tuple(evict_mask.shape) != (S,):
+        raise ValueError("context_lens and evict_mask must be [S]")
+    if evicted is None:
+        evicted = torch.empty(S, dtype=torch.int32, device=scores.device)
+    sh = PaScoreShape(S, 1, 64, bs, MB, NB)     # heads / head_dim are not used here
+    _check(load().paged_kv_evict_lowest_block(_ptr(scores), _ptr(block_tables), _ptr(context_lens),
+                                              _ptr(evict_mask), _ptr(evicted), ctypes.byref(sh),
+                                              _stream_handle(stream)))
+    return evicted

@@ -8,7 +8,9 @@ from paged_kv_cache_393_amd import binding as B
 
 DECLARED = {"paged_attn_plan", "paged_attn_workspace_bytes", "paged_attn_decode",
             "paged_attn_decode_int8", "paged_attn_strerror", "paged_attn_abi_version",
-            "paged_kv_write", "paged_kv_write_int8", "paged_attn_decode_fp8", "paged_kv_write_fp8"}
+            "paged_kv_write", "paged_kv_write_int8", "paged_attn_decode_fp8", "paged_kv_write_fp8",
+            "paged_kv_token_scores", "paged_kv_token_scores_int8", "paged_kv_token_scores_fp8",
+            "paged_kv_evict_lowest_block"}
 
 
 def lib():
@@ -227,3 +229,52 @@ def test_fp8_write_argument_errors():
 def test_write_zero_tokens_is_a_no_op():
     assert wcall(wshape(num_tokens=0)) == B.PA_OK
     assert wcall_int8(wshape(num_tokens=0)) == B.PA_OK
+
+
+# ---- PagedEviction (include/paged_kv_evict.h) ----
+
+def sshape(**kw):
+    base = dict(num_seqs=2, num_kv_heads=2, head_dim=128, block_size=16, max_blocks_per_seq=8,
+                num_blocks=16)
+    base.update(kw)
+    return B.PaScoreShape(*[base[n] for n, _ in B.PaScoreShape._fields_])
+
+
+def scall(sh, k=FAKE, v=FAKE, bt=FAKE, tb=None, cl=FAKE, sc=FAKE):
+    return lib().paged_kv_token_scores(k, v, bt, tb, cl, sc, ctypes.byref(sh), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_seqs=-1), B.PA_ERR_SHAPE),
+    (dict(num_kv_heads=0), B.PA_ERR_SHAPE),
+    (dict(block_size=0), B.PA_ERR_SHAPE),
+    (dict(max_blocks_per_seq=0), B.PA_ERR_SHAPE),
+    (dict(num_blocks=0), B.PA_ERR_SHAPE),
+    (dict(head_dim=96), B.PA_ERR_UNSUPPORTED),
+    (dict(block_size=8192), B.PA_ERR_UNSUPPORTED),
+    (dict(num_seqs=70000), B.PA_ERR_UNSUPPORTED),
+])
+def test_score_shape_errors(kw, code):
+    assert scall(sshape(**kw)) == code
+    L = lib()
+    assert L.paged_kv_evict_lowest_block(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(sshape(**kw)),
+                                         None) == code
+
+
+def test_score_and_evict_null_alignment_and_empty():
+    L = lib()
+    for name in ("k", "v", "bt", "cl", "sc"):
+        assert scall(sshape(), **{name: ctypes.c_void_p(0)}) == B.PA_ERR_NULL, name
+    assert scall(sshape(), k=ctypes.c_void_p(0x100008)) == B.PA_ERR_ALIGNMENT
+    assert scall(sshape(), sc=ctypes.c_void_p(0x100002)) == B.PA_ERR_ALIGNMENT
+    assert L.paged_kv_token_scores_int8(FAKE, FAKE, None, FAKE, FAKE, None, FAKE, FAKE,
+                                        ctypes.byref(sshape()), None) == B.PA_ERR_NULL
+    assert L.paged_kv_token_scores_fp8(FAKE, ctypes.c_void_p(0x100004), FAKE, None, FAKE, FAKE,
+                                       ctypes.byref(sshape()), None) == B.PA_ERR_ALIGNMENT
+    assert scall(sshape(num_seqs=0), k=None, v=None, bt=None, cl=None, sc=None) == B.PA_OK
+    for i in range(5):
+        args = [FAKE] * 5
+        args[i] = None
+        assert L.paged_kv_evict_lowest_block(*args, ctypes.byref(sshape()), None) == B.PA_ERR_NULL
+    assert L.paged_kv_evict_lowest_block(None, None, None, None, None,
+                                         ctypes.byref(sshape(num_seqs=0)), None) == B.PA_OK
