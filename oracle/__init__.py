@@ -14,7 +14,10 @@ slot address block * block_size + offset), 6.1 (INT8 KV quantization, and the
 cast of the cache to FP8 E4M3) and 6.2 (GQA sharing), the blog.hotdry.top page
 "KV缓存内存布局优化：分页策略、量化压缩与动态驱逐的工程实践", section
 "PagedEviction 块级驱逐机制" (token importance ||V||/||K||, lowest-mean full
-block evicted),
+block evicted), the ybb.press page's section 7.3 and the t6page page's
+section "Chunked prefill：让 prefill 不阻塞 decode" (a prompt's prefill in
+512-token chunks, each chunk's queries attending causally over the paged
+cache),
 and the t6page "KV cache" page, section "PagedAttention 的算子" (softmax after
 merging all blocks).
 
@@ -89,6 +92,9 @@ class OracleLib:
             fn.restype = i32
         lib.oracle_evict_lowest_block.argtypes = [P, P, P, P, P, i32, i32, i32, i64]
         lib.oracle_evict_lowest_block.restype = i32
+        lib.oracle_paged_prefill_bf16.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                                  i64, ctypes.c_float, P]
+        lib.oracle_paged_prefill_bf16.restype = i32
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i32
         lib.oracle_set_num_threads.argtypes = [i32]
@@ -381,3 +387,30 @@ def evict_lowest_block(scores, block_tables, context_lens, evict_mask,
     if rc != 0:
         raise ValueError(f"oracle rejected the inputs (code {rc})")
     return bt, cl, ev
+
+
+def paged_prefill_bf16(q_bits, k_bits, v_bits, block_tables, context_lens, q_offsets, scale,
+                       lib: "OracleLib | None" = None) -> np.ndarray:
+    """out [q_offsets[-1], Hq, D] (float64): chunked-prefill attention, every
+    sequence's last n_q context tokens as causal queries (bf16 cache)."""
+    as_i32 = lambda a: np.asarray(a, dtype=np.int32) if isinstance(a, (list, tuple)) else a
+    q_bits = _c(q_bits, np.uint16)
+    k_bits = _c(k_bits, np.uint16)
+    v_bits = _c(v_bits, np.uint16)
+    bt = _c(block_tables, np.int32)
+    cl = _c(as_i32(context_lens), np.int32)
+    qo = _c(as_i32(q_offsets), np.int32)
+    Nq, Hq, D = q_bits.shape
+    NB, BS, Hkv, D2 = k_bits.shape
+    S, MB = bt.shape
+    if D2 != D or v_bits.shape != k_bits.shape or cl.shape != (S,) or qo.shape != (S + 1,) or \
+            int(qo[-1]) != Nq:
+        raise ValueError("shapes disagree")
+    out = np.zeros((Nq, Hq, D), dtype=np.float64)
+    L = lib.lib if lib is not None else _load()
+    rc = L.oracle_paged_prefill_bf16(_ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(bt), _ptr(cl),
+                                     _ptr(qo), S, Hq, Hkv, D, BS, MB, NB, ctypes.c_float(scale),
+                                     _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return out

@@ -585,3 +585,91 @@ int oracle_evict_lowest_block(const float *scores, int32_t *block_tables, int32_
     }
     return ORC_OK;
 }
+
+/*
+ * Paged chunked-prefill attention (ybb.press page, section 7.3: a long prompt's
+ * prefill is cut into 512-token chunks that run alongside the decodes; the t6page
+ * "KV cache" page, section "Chunked prefill：让 prefill 不阻塞 decode": one batch =
+ * one prefill chunk + all decodes).  Every sequence s brings n_q = q_offsets[s+1] - q_offsets[s]
+ * query tokens: the LAST n_q tokens of its context (their K/V already stored,
+ * n_q <= context_lens[s]).  Query i of s sits at position
+ * p = context_lens[s] - n_q + i and attends causally: to tokens 0 .. p of its
+ * sequence, through the block table, with the decode definition (scores
+ * scale * q.k, one softmax, weighted V; GQA g = h / G).  n_q = 1 is a decode.
+ * q: bf16 [q_offsets[S], Hq, D]; out: double [q_offsets[S], Hq, D].
+ */
+static void attend_prefix(const double *qd, const kv_src *src, const int32_t *table_row, int n,
+                          int g, int Hkv, int D, int BS, double sc, double *scores, double *o)
+{
+    for (int i = 0; i < D; ++i) o[i] = 0.0;
+    if (n == 0) return;
+    double m = -INFINITY;
+    for (int t = 0; t < n; ++t) {
+        const int64_t b = table_row[t / BS];
+        const int r = t % BS;
+        double dot = 0.0;
+        for (int i = 0; i < D; ++i) dot += qd[i] * kv_elem(src, 0, b, r, g, i, BS, Hkv, D);
+        scores[t] = sc * dot;
+        if (scores[t] > m) m = scores[t];
+    }
+    double denom = 0.0;
+    for (int t = 0; t < n; ++t) {
+        const int64_t b = table_row[t / BS];
+        const int r = t % BS;
+        const double e = exp(scores[t] - m);
+        denom += e;
+        for (int i = 0; i < D; ++i) o[i] += e * kv_elem(src, 1, b, r, g, i, BS, Hkv, D);
+    }
+    for (int i = 0; i < D; ++i) o[i] /= denom;
+}
+
+int oracle_paged_prefill_bf16(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                              const int32_t *block_tables, const int32_t *context_lens,
+                              const int32_t *q_offsets, int S, int Hq, int Hkv, int D, int BS,
+                              int MB, int64_t NB, float scale, double *out)
+{
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !q_offsets || !out)
+        return ORC_ERR_ARG;
+    if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || MB < 0 || NB < 0 || Hq % Hkv)
+        return ORC_ERR_ARG;
+    if (q_offsets[0] != 0) return ORC_ERR_ARG;
+    for (int s = 0; s < S; ++s) {
+        const int n = context_lens[s];
+        const int nq = q_offsets[s + 1] - q_offsets[s];
+        if (nq < 0 || nq > n) return ORC_ERR_ARG;
+        if (n < 0 || (int64_t)n > (int64_t)MB * BS) return ORC_ERR_TABLE;
+        for (int j = 0; j < (n + BS - 1) / BS; ++j) {
+            int32_t b = block_tables[(int64_t)s * MB + j];
+            if (b < 0 || (int64_t)b >= NB) return ORC_ERR_TABLE;
+        }
+    }
+    kv_src src = {KV_BF16, k_cache, v_cache, NULL, NULL};
+    const int G = Hq / Hkv;
+    const int64_t rows = (int64_t)q_offsets[S] * Hq;
+    int err = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t row = 0; row < rows; ++row) {
+        const int64_t qi = row / Hq;          /* query token index over the batch */
+        const int h = (int)(row % Hq);
+        int s = 0;
+        while (q_offsets[s + 1] <= qi) ++s;
+        const int nq = q_offsets[s + 1] - q_offsets[s];
+        const int i = (int)(qi - q_offsets[s]);
+        const int p = context_lens[s] - nq + i;            /* the query's position */
+        double *scores = (double *)malloc(sizeof(double) * (size_t)(p + 1));
+        double *qd = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!scores || !qd) {
+            free(scores);
+            free(qd);
+#pragma omp atomic write
+            err = ORC_ERR_NOMEM;
+            continue;
+        }
+        for (int x = 0; x < D; ++x) qd[x] = bf16_bits_to_double(q[row * D + x]);
+        attend_prefix(qd, &src, block_tables + (int64_t)s * MB, p + 1, h / G, Hkv, D, BS,
+                      (double)scale, scores, out + row * D);
+        free(scores);
+        free(qd);
+    }
+    return err;
+}

@@ -76,6 +76,13 @@ MUTANTS = {
     "evict_table_not_shifted": ("for (int j = victim; j + 1 < nblk; ++j) row[j] = row[j + 1];",
                                 "for (int j = victim + 1; j + 1 < nblk; ++j) row[j] = row[j + 1];"),
     "evict_context_kept": ("context_lens[s] = n - BS;", "context_lens[s] = n;"),
+    "prefill_position_from_chunk_start": ("const int p = context_lens[s] - nq + i;", "const int p = i;"),
+    "prefill_excludes_itself": ("block_tables + (int64_t)s * MB, p + 1, h / G,",
+                                "block_tables + (int64_t)s * MB, p, h / G,"),
+    "prefill_head_mod": ("block_tables + (int64_t)s * MB, p + 1, h / G,",
+                         "block_tables + (int64_t)s * MB, p + 1, h % Hkv,"),
+    "prefill_k_as_v": ("const double e = exp(scores[t] - m);\n        denom += e;\n        for (int i = 0; i < D; ++i) o[i] += e * kv_elem(src, 1,",
+                       "const double e = exp(scores[t] - m);\n        denom += e;\n        for (int i = 0; i < D; ++i) o[i] += e * kv_elem(src, 0,"),
 }
 
 PIN_FUNCS = [
@@ -107,6 +114,10 @@ PIN_FUNCS = [
     "test_evict_ties_take_the_lowest_block_and_nan_is_never_chosen",
     "test_evict_masked_and_short_sequences_are_untouched",
     "test_decode_after_eviction_equals_attention_without_the_block",
+    "test_prefill_single_query_is_the_decode",
+    "test_prefill_whole_prompt_matches_causal_sdpa",
+    "test_prefill_chunk_after_a_cached_prefix_matches_masked_sdpa",
+    "test_prefill_is_causal",
 ]
 
 RUNNER = r"""

@@ -560,3 +560,84 @@ def test_decode_after_eviction_equals_attention_without_the_block():
         assert np.allclose(out[s], ref, rtol=0, atol=1e-12), s
         full_means = [sc[bt0[s][j]].astype(np.float64).mean() for j in range(n // bs)]
         assert victim == int(np.argmin(full_means))
+
+
+# ---------------------------------------------------------------------------
+# Paged chunked prefill (ybb.press page, section 7.3; t6page "KV cache" page,
+# section "Chunked prefill：让 prefill 不阻塞 decode"): every sequence's last
+# n_q context tokens are queries attending causally over the paged cache.
+
+
+def _prefill_case(ctx, nq, Hq=8, Hkv=2, D=64, bs=16, seed=61):
+    _, v = C.make_case(len(ctx), Hq, Hkv, D, bs, ctx=ctx, seed=seed)
+    q_off = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    gen = torch.Generator().manual_seed(seed + 1)
+    q = torch.randn(int(q_off[-1]), Hq, D, generator=gen).to(torch.bfloat16)
+    return v, q, q_off
+
+
+def _prefill_oracle(v, q, q_off):
+    return oracle.paged_prefill_bf16(I.bf16_bits(q), I.bf16_bits(v["k_cache"]),
+                                     I.bf16_bits(v["v_cache"]), v["block_tables"].numpy(),
+                                     v["context_lens"].numpy(), q_off, v["scale"])
+
+
+def _sdpa_masked(v, q, q_off, bs):
+    """Brute force: gathered K/V and torch SDPA with an explicit boolean mask
+    allowing token t for the query at position p iff t <= p."""
+    out = []
+    for s, n in enumerate(v["context_lens"].tolist()):
+        nq = int(q_off[s + 1] - q_off[s])
+        if nq == 0:
+            continue
+        K, V = C.gathered(v, bs, s)                         # [Hkv, n, D]
+        pos = n - nq + np.arange(nq)
+        allow = torch.from_numpy(np.arange(n)[None, :] <= pos[:, None])   # [nq, n]
+        qs = q[q_off[s]:q_off[s + 1]].to(torch.float64).permute(1, 0, 2)  # [Hq, nq, D]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qs[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None], attn_mask=allow,
+            scale=float(np.float32(v["scale"])), enable_gqa=True)
+        out.append(o[0].permute(1, 0, 2).numpy())
+    return np.concatenate(out)
+
+
+def test_prefill_single_query_is_the_decode():
+    ctx = (1, 17, 100, 250)
+    v, q, q_off = _prefill_case(ctx, [1, 1, 1, 1])
+    got = _prefill_oracle(v, q, q_off)
+    dec = C.oracle_out(dict(v, q=q))
+    assert np.array_equal(got, dec)
+
+
+def test_prefill_whole_prompt_matches_causal_sdpa():
+    # n_q = ctx (no cached prefix): plain causal attention.
+    ctx = (40, 77, 16)
+    v, q, q_off = _prefill_case(ctx, list(ctx), seed=62)
+    got = _prefill_oracle(v, q, q_off)
+    for s, n in enumerate(ctx):
+        K, V = C.gathered(v, 16, s)
+        qs = q[q_off[s]:q_off[s + 1]].to(torch.float64).permute(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qs[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None], is_causal=True,
+            scale=float(np.float32(v["scale"])), enable_gqa=True)[0].permute(1, 0, 2).numpy()
+        assert np.allclose(got[q_off[s]:q_off[s + 1]], ref, rtol=0, atol=1e-12), s
+
+
+def test_prefill_chunk_after_a_cached_prefix_matches_masked_sdpa():
+    ctx = (600, 100, 35, 512)
+    nq = [88, 100, 1, 512]
+    v, q, q_off = _prefill_case(ctx, nq, Hq=16, Hkv=2, seed=63)
+    assert np.allclose(_prefill_oracle(v, q, q_off), _sdpa_masked(v, q, q_off, 16),
+                       rtol=0, atol=1e-12)
+
+
+def test_prefill_is_causal():
+    # Changing the K/V of the last token changes only the last query's output.
+    ctx = (50,)
+    v, q, q_off = _prefill_case(ctx, [20], seed=64)
+    base = _prefill_oracle(v, q, q_off)
+    b = int(v["block_tables"][0, 49 // 16])
+    v["k_cache"][b, 49 % 16] = 3.0
+    v["v_cache"][b, 49 % 16] = -2.0
+    got = _prefill_oracle(v, q, q_off)
+    assert np.array_equal(got[:19], base[:19]) and not np.array_equal(got[19], base[19])
