@@ -26,7 +26,10 @@ With --workload kv_write_llama3_8b (or kv_write_int8_ / kv_write_fp8_llama3_8b) 
 KV write path instead -- one paged_kv_write call per step, storing a
 16384-token prefill chunk into the paged cache -- and prints the same kind of
 line for it; with --workload scores_<decode workload> (e.g. scores_llama3_8b)
-it times PagedEviction's token scoring over that workload's whole cache.
+it times PagedEviction's token scoring over that workload's whole cache; with
+--workload prefill_llama3_8b it times chunked-prefill attention (the eight
+512-token chunks of a 4096-token prompt in one call) against the bf16
+matrix-core peak.
 """
 from __future__ import annotations
 
@@ -120,6 +123,8 @@ def main() -> int:
         return bench_write(args)
     if args.workload.startswith("scores_"):
         return bench_scores(args)
+    if args.workload in I.PREFILL_WORKLOADS:
+        return bench_prefill(args)
     wl = I.WORKLOADS[args.workload]
     split = wl.split_tokens if args.split_tokens is None else args.split_tokens
     dev = torch.device("cuda:0")
@@ -440,6 +445,126 @@ def bench_scores(args) -> int:
     }
     print(json.dumps(record), flush=True)
     return 0
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak, published
+
+
+def bench_prefill(args) -> int:
+    """Chunked-prefill attention on its own: one paged_attn_prefill call per step."""
+    import torch
+
+    from paged_kv_cache_393_amd import accounting as A
+    from paged_kv_cache_393_amd import binding as B
+    from paged_kv_cache_393_amd import inputs as I
+
+    pw = I.PREFILL_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    v = I.make_prefill_inputs(pw, dev)
+    out = torch.empty(v["q"].shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    print(f"[bench] inputs for {pw.name} ready", file=sys.stderr, flush=True)
+
+    def step():
+        B.prefill(v["q"], v["k_cache"], v["v_cache"], v["block_tables"], v["context_lens"],
+                  v["q_offsets"], v["scale"], v["max_q_len"], out=out, stream=stream)
+
+    flush_buf = None if args.no_flush else torch.ones((2 << 30) // 4, dtype=torch.float32,
+                                                       device=dev)
+
+    def evict():
+        if flush_buf is not None:
+            flush_buf.amax()
+
+    for _ in range(args.warmup):
+        evict()
+        step()
+    torch.cuda.synchronize()
+    ms = event_ms(stream, step, args.steps, before=evict)
+    ms_sorted = sorted(ms)
+    ms_mean = statistics.fmean(ms)
+    pct = lambda q: ms_sorted[min(len(ms_sorted) - 1, int(q * len(ms_sorted)))]
+    print(f"[bench] {args.steps} timed steps done", file=sys.stderr, flush=True)
+    flops = A.prefill_flops(pw.ctx, pw.n_q, pw.num_q_heads, pw.head_dim)
+    nbytes = A.prefill_bytes(pw.ctx, pw.n_q, pw.num_q_heads, pw.num_kv_heads, pw.head_dim,
+                             pw.block_size)
+    t_s = ms_mean / 1e3
+    tflops = flops / t_s / 1e12
+    record = {
+        "metric": "chunked-prefill attention query tokens/s and achieved bf16 matrix-core "
+                  "TFLOP/s (% of peak), Llama-3-8B shape",
+        "value": sum(pw.n_q) / t_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_mean,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/K/V, shuffled block pool)",
+        "config": {"workload": pw.name, "context_lens": list(pw.ctx), "query_tokens": list(pw.n_q),
+                   "num_q_heads": pw.num_q_heads, "num_kv_heads": pw.num_kv_heads,
+                   "head_dim": pw.head_dim, "block_size": pw.block_size,
+                   "cache_evict_between_steps": "2 GiB read" if flush_buf is not None else None},
+        "ms_p10": pct(0.10), "ms_median": pct(0.50), "ms_p90": pct(0.90),
+        "hbm_gbps": nbytes / t_s / 1e9,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "pa_prefill_kernel",
+            "achieved": tflops,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": measured_traffic(pw.name, "prefill"),
+            "algorithmic_flops_per_call": flops,
+            "algorithmic_bytes_per_call": nbytes,
+            "calls_per_step": 1,
+            "ms_per_call": ms_mean,
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_prefill(pw, v, out, flops),
+    }
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+def cpu_baseline_prefill(pw, v, out, flops_total):
+    """The oracle on the first (shortest) chunk of the batch, median of repeated
+    runs up to about 3 s, scaled to the whole call by flop count; and its
+    largest difference from the GPU output on that chunk."""
+    import numpy as np
+
+    import oracle
+    from paged_kv_cache_393_amd import accounting as A
+    from paged_kv_cache_393_amd import inputs as I
+
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    sub = I.select_sequences(v, [0], pw.block_size)
+    nq = pw.n_q[0]
+    q0 = v["q"][:nq].cpu()
+    args = (I.bf16_bits(q0), I.bf16_bits(sub["k_cache"]), I.bf16_bits(sub["v_cache"]),
+            sub["block_tables"].numpy(), sub["context_lens"].numpy(), [0, nq], sub["scale"])
+    times, ref = [], None
+    while sum(times) < 3.0 and len(times) < 25:
+        t = time.perf_counter()
+        ref = oracle.paged_prefill_bf16(*args)
+        times.append(time.perf_counter() - t)
+    t_med = statistics.median(times)
+    f0 = A.prefill_flops(pw.ctx[:1], pw.n_q[:1], pw.num_q_heads, pw.head_dim)
+    t_full = t_med * flops_total / f0
+    return {
+        "value": sum(pw.n_q) / t_full,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"chunk 0 ({nq} queries over {pw.ctx[0]} tokens), median of {len(times)} runs "
+                   f"of {t_med:.3f}s, scaled to the whole call by flop count"),
+        "parity_max_abs_vs_gpu": float(np.abs(out[:nq].double().cpu().numpy() - ref).max()),
+    }
 
 
 def cpu_baseline_scores(views, ctx, budget_s=3.0):

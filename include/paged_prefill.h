@@ -1,0 +1,71 @@
+/*
+ * paged_prefill.h -- C-ABI of paged chunked-prefill attention in the MI355X
+ * (gfx950) paged KV cache library.
+ *
+ * The operation (ybb.press page "LLM 推理 KV Cache 内存管理深度工程实践", section
+ * 7.3: a long prompt's prefill is cut into 512-token chunks run between the
+ * decodes; t6page "KV cache" page, section "Chunked prefill：让 prefill 不阻塞
+ * decode": one batch = one prefill chunk + all decodes).  Every sequence s
+ * brings n_q[s] = q_offsets[s+1] - q_offsets[s] query tokens: the LAST n_q[s]
+ * tokens of its context, whose K/V are already in the paged cache (written
+ * with paged_kv_write).  Query i of s is at position
+ * p = context_lens[s] - n_q[s] + i and attends causally to tokens 0 .. p of
+ * its sequence through the block table, with the decode definition: scores
+ * scale * q.k, one softmax, weighted V, G = Hq/Hkv consecutive query heads per
+ * kv head.  n_q = 1 is a decode, so one call can carry a prefill chunk and
+ * decodes together.
+ *
+ * Layouts (row-major; all pointers are DEVICE memory owned by the caller):
+ *   q             bf16 [q_offsets[S], Hq, head_dim]  (sequence s: rows q_offsets[s] ..)
+ *   k_cache, v_cache  bf16 [num_blocks, block_size, Hkv, head_dim]
+ *   block_tables  int32 [S, max_blocks_per_seq];  context_lens int32 [S]
+ *   q_offsets     int32 [S + 1], q_offsets[0] = 0, non-decreasing
+ *   out           fp32 [q_offsets[S], Hq, head_dim]
+ *
+ * Ownership and state: the library allocates nothing and keeps no state; one
+ * kernel launch, asynchronous on `stream` (a hipStream_t; NULL = the null
+ * stream).  Errors: PA_OK or a negative PA_ERR_* code of paged_attn.h,
+ * detected on the host before the launch (out untouched then).  Not checked
+ * (device data): n_q[s] <= max_q_len, n_q[s] <= context_lens[s] <=
+ * max_blocks_per_seq * block_size, valid block ids for every block a context
+ * uses.  Slots past each context end are never read.
+ */
+#ifndef PAGED_PREFILL_H
+#define PAGED_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "paged_attn.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pa_prefill_shape {
+    int32_t num_seqs;           /* S >= 0 (0 is a no-op) */
+    int32_t num_q_heads;        /* Hq >= 1, a multiple of Hkv */
+    int32_t num_kv_heads;       /* Hkv >= 1 */
+    int32_t head_dim;           /* 64 or 128 */
+    int32_t block_size;         /* a power of two, 16 .. 4096 */
+    int32_t max_blocks_per_seq; /* >= 1 */
+    int32_t num_blocks;         /* >= 1 */
+    int32_t max_q_len;          /* >= 1: no sequence brings more query tokens */
+} pa_prefill_shape;
+
+/*
+ * Chunked-prefill attention over a bf16 cache.  Matrix cores compute the
+ * scores and the weighted values; the softmax weights enter the second product
+ * as a bf16 high part plus a bf16 remainder (exact to 2^-17 relative);
+ * accumulation is fp32.
+ */
+int paged_attn_prefill(const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, const int32_t *context_lens,
+                       const int32_t *q_offsets, float scale, float *out,
+                       const pa_prefill_shape *shape, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_PREFILL_H */

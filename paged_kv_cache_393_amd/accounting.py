@@ -76,3 +76,27 @@ def score_bytes(context_lens: Iterable[int], num_kv_heads: int, head_dim: int, b
         per_token += 2 * num_kv_heads * 4
     tables = sum((c + block_size - 1) // block_size for c in ctx) * 4
     return tokens * per_token + tables + 4 * len(ctx)
+
+
+def prefill_flops(context_lens: Iterable[int], n_q: Iterable[int], num_q_heads: int,
+                  head_dim: int) -> int:
+    """QK and PV multiply-adds (2 flops each) of causal chunked prefill: the
+    query at position p of a sequence attends to p + 1 tokens."""
+    total = 0
+    for c, nq in zip(context_lens, n_q):
+        c, nq = int(c), int(nq)
+        # sum over positions p = c - nq .. c - 1 of (p + 1)
+        total += nq * (2 * c - nq + 1) // 2
+    return 4 * head_dim * num_q_heads * total
+
+
+def prefill_bytes(context_lens: Iterable[int], n_q: Iterable[int], num_q_heads: int,
+                  num_kv_heads: int, head_dim: int, block_size: int) -> int:
+    """Bytes one chunked-prefill call must move at least once: each context's
+    K and V, the queries (bf16) and outputs (fp32), the table entries."""
+    ctx = [int(c) for c in context_lens]
+    nq = [int(n) for n in n_q]
+    kv = sum(ctx) * 2 * num_kv_heads * head_dim * 2
+    qo = sum(nq) * num_q_heads * head_dim * (2 + 4)
+    tables = sum((c + block_size - 1) // block_size for c in ctx) * 4
+    return kv + qo + tables + 8 * len(ctx) + 4

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "paged_attn.h")
 WRITE_HEADER = os.path.join(os.path.dirname(_HERE), "include", "paged_kv_write.h")
 EVICT_HEADER = os.path.join(os.path.dirname(_HERE), "include", "paged_kv_evict.h")
+PREFILL_HEADER = os.path.join(os.path.dirname(_HERE), "include", "paged_prefill.h")
 
 PA_OK = 0
 PA_ERR_NULL = -1
@@ -44,6 +45,12 @@ class PaWriteShape(ctypes.Structure):
 class PaScoreShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_seqs", "num_kv_heads", "head_dim", "block_size", "max_blocks_per_seq", "num_blocks")]
+
+
+class PaPrefillShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size", "max_blocks_per_seq",
+        "num_blocks", "max_q_len")]
 
 
 class PagedAttnError(RuntimeError):
@@ -93,6 +100,9 @@ def load() -> ctypes.CDLL:
     lib.paged_kv_token_scores_fp8.restype = ctypes.c_int
     lib.paged_kv_evict_lowest_block.argtypes = [P, P, P, P, P, CP, P]
     lib.paged_kv_evict_lowest_block.restype = ctypes.c_int
+    lib.paged_attn_prefill.argtypes = [P, P, P, P, P, P, ctypes.c_float, P,
+                                       ctypes.POINTER(PaPrefillShape), P]
+    lib.paged_attn_prefill.restype = ctypes.c_int
     lib.paged_attn_strerror.argtypes = [ctypes.c_int]
     lib.paged_attn_strerror.restype = ctypes.c_char_p
     lib.paged_attn_abi_version.argtypes = []
@@ -103,9 +113,10 @@ def load() -> ctypes.CDLL:
 
 def header_functions() -> list:
     """Names of the functions the library's headers (include/paged_attn.h,
-    include/paged_kv_write.h, include/paged_kv_evict.h) declare."""
+    include/paged_kv_write.h, include/paged_kv_evict.h, include/paged_prefill.h)
+    declare."""
     names = set()
-    for h in (HEADER, WRITE_HEADER, EVICT_HEADER):
+    for h in (HEADER, WRITE_HEADER, EVICT_HEADER, PREFILL_HEADER):
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
         names.update(re.findall(r"\b((?:paged_attn|paged_kv)_\w+)\s*\(", text))
     return sorted(names)
@@ -412,3 +423,34 @@ def evict_lowest_block(scores, block_tables, context_lens, evict_mask, evicted=N
                                               _ptr(evict_mask), _ptr(evicted), ctypes.byref(sh),
                                               _stream_handle(stream)))
     return evicted
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, q_offsets, scale: float,
+            max_q_len: int, out=None, stream=None) -> torch.Tensor:
+    """out fp32 [q_offsets[-1], Hq, D] = paged_attn_prefill(...): every sequence's
+    last (q_offsets[s+1] - q_offsets[s]) context tokens attend causally over
+    the paged bf16 cache.  max_q_len bounds the query tokens of any sequence."""
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_tables", block_tables), ("context_lens", context_lens),
+                    ("q_offsets", q_offsets)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise TypeError("q and the cache must be bf16")
+    if k_cache.shape != v_cache.shape or q.shape[2] != k_cache.shape[3]:
+        raise ValueError("q / cache shapes disagree")
+    for name, t in (("block_tables", block_tables), ("context_lens", context_lens),
+                    ("q_offsets", q_offsets)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    S, MB = block_tables.shape
+    if tuple(q_offsets.shape) != (S + 1,) or tuple(context_lens.shape) != (S,):
+        raise ValueError("q_offsets must be [S + 1] and context_lens [S]")
+    NB, bs, Hkv, D = k_cache.shape
+    sh = PaPrefillShape(S, q.shape[1], Hkv, D, bs, MB, NB, int(max_q_len))
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _check(load().paged_attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                     _ptr(context_lens), _ptr(q_offsets), ctypes.c_float(scale),
+                                     _ptr(out), ctypes.byref(sh), _stream_handle(stream)))
+    return out

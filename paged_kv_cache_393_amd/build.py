@@ -11,10 +11,11 @@ import sys
 _HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(_HERE)
 # (sources, output) of every HIP library: the paged KV cache library (decode,
-# the KV write path, PagedEviction) and the bench's measurement kernels.
+# the KV write path, PagedEviction, chunked prefill) and the bench's
+# measurement kernels.
 LIBS = [
     ([os.path.join(_HERE, "csrc", "paged_attn.hip"), os.path.join(_HERE, "csrc", "kv_write.hip"),
-      os.path.join(_HERE, "csrc", "kv_evict.hip")],
+      os.path.join(_HERE, "csrc", "kv_evict.hip"), os.path.join(_HERE, "csrc", "paged_prefill.hip")],
      os.path.join(_HERE, "libpagedattn.so")),
     ([os.path.join(_HERE, "csrc", "pa_probe.hip")], os.path.join(_HERE, "libpaprobe.so")),
 ]

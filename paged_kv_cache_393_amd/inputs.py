@@ -302,6 +302,47 @@ def draw_slots(num_tokens: int, num_slots: int, seed: int, pad_fraction: float =
 
 
 @dataclasses.dataclass(frozen=True)
+class PrefillWorkload:
+    """Chunked prefill: sequence s has context ctx[s] whose last n_q[s] tokens
+    are the chunk's queries (their K/V already in the cache)."""
+    name: str
+    ctx: tuple
+    n_q: tuple
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    seed: int
+
+
+PREFILL_WORKLOADS = {
+    # The eight 512-token chunks of a 4096-token prompt of one Llama-3-8B-shaped
+    # layer (32 q / 8 kv heads, d 128, block_size 16) in one batch: chunk k
+    # attends over 512 (k + 1) tokens.
+    "prefill_llama3_8b": PrefillWorkload("prefill_llama3_8b", tuple(512 * (k + 1) for k in range(8)),
+                                         (512,) * 8, 32, 8, 128, 16, seed=10),
+}
+
+
+def make_prefill_inputs(pw: PrefillWorkload, device="cpu") -> dict:
+    """Cache, tables and lengths as make_inputs (seeded, shuffled pool), plus
+    the chunk queries q bf16 [sum n_q, Hq, d] (fp32 N(0,1) rounded) and
+    q_offsets int32 [S + 1]."""
+    wl = Workload(pw.name, len(pw.ctx), pw.num_q_heads, pw.num_kv_heads, pw.head_dim,
+                  pw.block_size, seed=pw.seed, ctx_fixed=pw.ctx)
+    inp = make_inputs(wl, device)
+    views = layer_views(inp, 0)
+    nq = torch.tensor((0,) + tuple(pw.n_q), dtype=torch.int64)
+    q_off = torch.cumsum(nq, 0).to(torch.int32)
+    gen = torch.Generator(device=torch.device(device)).manual_seed(pw.seed * 31 + 7)
+    q = torch.empty((int(q_off[-1]), pw.num_q_heads, pw.head_dim), dtype=torch.bfloat16,
+                    device=device)
+    _fill_normal_bf16(q, gen)
+    views.update(q=q, q_offsets=q_off.to(device), max_q_len=max(pw.n_q))
+    return views
+
+
+@dataclasses.dataclass(frozen=True)
 class WriteWorkload:
     """A KV write: num_tokens new tokens stored into a pool of num_blocks blocks."""
     name: str

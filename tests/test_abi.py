@@ -10,7 +10,7 @@ DECLARED = {"paged_attn_plan", "paged_attn_workspace_bytes", "paged_attn_decode"
             "paged_attn_decode_int8", "paged_attn_strerror", "paged_attn_abi_version",
             "paged_kv_write", "paged_kv_write_int8", "paged_attn_decode_fp8", "paged_kv_write_fp8",
             "paged_kv_token_scores", "paged_kv_token_scores_int8", "paged_kv_token_scores_fp8",
-            "paged_kv_evict_lowest_block"}
+            "paged_kv_evict_lowest_block", "paged_attn_prefill"}
 
 
 def lib():
@@ -278,3 +278,38 @@ def test_score_and_evict_null_alignment_and_empty():
         assert L.paged_kv_evict_lowest_block(*args, ctypes.byref(sshape()), None) == B.PA_ERR_NULL
     assert L.paged_kv_evict_lowest_block(None, None, None, None, None,
                                          ctypes.byref(sshape(num_seqs=0)), None) == B.PA_OK
+
+
+# ---- chunked prefill (include/paged_prefill.h) ----
+
+def pshape(**kw):
+    base = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                max_blocks_per_seq=8, num_blocks=16, max_q_len=64)
+    base.update(kw)
+    return B.PaPrefillShape(*[base[n] for n, _ in B.PaPrefillShape._fields_])
+
+
+def pcall(sh, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qo=FAKE, out=FAKE):
+    return lib().paged_attn_prefill(q, k, v, bt, cl, qo, ctypes.c_float(0.1), out,
+                                    ctypes.byref(sh), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_seqs=-1), B.PA_ERR_SHAPE),
+    (dict(num_q_heads=6, num_kv_heads=4), B.PA_ERR_SHAPE),
+    (dict(max_q_len=0), B.PA_ERR_SHAPE),
+    (dict(num_blocks=0), B.PA_ERR_SHAPE),
+    (dict(head_dim=96), B.PA_ERR_UNSUPPORTED),
+    (dict(block_size=8), B.PA_ERR_UNSUPPORTED),
+    (dict(block_size=48), B.PA_ERR_UNSUPPORTED),
+])
+def test_prefill_shape_errors(kw, code):
+    assert pcall(pshape(**kw)) == code
+
+
+def test_prefill_null_alignment_and_empty():
+    for name in ("q", "k", "v", "bt", "cl", "qo", "out"):
+        assert pcall(pshape(), **{name: ctypes.c_void_p(0)}) == B.PA_ERR_NULL, name
+    for name in ("q", "k", "v", "out"):
+        assert pcall(pshape(), **{name: ctypes.c_void_p(0x100008)}) == B.PA_ERR_ALIGNMENT, name
+    assert pcall(pshape(num_seqs=0), q=None, k=None) == B.PA_OK
