@@ -85,6 +85,23 @@ def event_ms(stream, fn, reps, before=None):
     return [a.elapsed_time(b) for a, b in ev]
 
 
+def copy_for_counters(args, dev, stream) -> None:
+    """After timing: copy --copy-bytes bytes three times with the probe copy
+    kernel, the reference that scales hardware byte counters."""
+    if args.copy_bytes <= 0:
+        return
+    import torch
+
+    from paged_kv_cache_393_amd import probe as P
+
+    src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        P.copy(src, dst, stream)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def measured_traffic(workload: str, operation: str = "decode"):
     """Bytes per call from the committed counter summary, if it was taken on
     the current source of the operation's kernels."""
@@ -188,13 +205,7 @@ def main() -> int:
         probe_gbps = nbytes / (statistics.median(pms) / 1e3) / 1e9
         del pbuf
 
-    if args.copy_bytes > 0:
-        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            P.copy(src, dst, stream)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_for_counters(args, dev, stream)
 
     record = {
         "metric": METRIC,
@@ -298,13 +309,7 @@ def bench_write(args) -> int:
         copy_gbps = 2 * half / (statistics.median(pms) / 1e3) / 1e9
         del src, dst
 
-    if args.copy_bytes > 0:
-        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            P.copy(src, dst, stream)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_for_counters(args, dev, stream)
 
     record = {
         "metric": "KV write path tokens/s and achieved HBM GB/s (% of peak), Llama-3-8B shape",
@@ -400,13 +405,7 @@ def bench_scores(args) -> int:
         pms = event_ms(stream, lambda: P.read(pbuf, sink, stream), 20, before=evict)
         probe_gbps = nb / (statistics.median(pms) / 1e3) / 1e9
         del pbuf
-    if args.copy_bytes > 0:
-        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            P.copy(src, dst, stream)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_for_counters(args, dev, stream)
     name = "scores_" + wl.name
     record = {
         "metric": "PagedEviction token-importance scoring tokens/s and achieved HBM GB/s "
@@ -492,6 +491,7 @@ def bench_prefill(args) -> int:
                              pw.block_size)
     t_s = ms_mean / 1e3
     tflops = flops / t_s / 1e12
+    copy_for_counters(args, dev, stream)
     record = {
         "metric": "chunked-prefill attention query tokens/s and achieved bf16 matrix-core "
                   "TFLOP/s (% of peak), Llama-3-8B shape",

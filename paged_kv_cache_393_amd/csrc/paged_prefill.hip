@@ -54,10 +54,15 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #ifndef PF_WAVES_PER_EU
 #define PF_WAVES_PER_EU 2
 #endif
+// Column blocks per wave (2 fits two waves per SIMD; more registers per wave
+// cost the occupancy that hides the loads' latency).
+#ifndef PF_NC
+#define PF_NC 2
+#endif
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kNc = 2;                     // MFMA column blocks (16 rows each) per wave
+constexpr int kNc = PF_NC;                 // MFMA column blocks (16 rows each) per wave
 constexpr int kRowsPerWave = 16 * kNc;
 constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
 constexpr int kTileTokens = 32;
@@ -101,7 +106,11 @@ template <int D>
 __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(const PrefillParams p) {
     constexpr int kSteps = D / 32;    // QK k-steps of 32 dims
     constexpr int kDpl = D / 16;      // V dims per lane chunk = PV output blocks
-    const int s = blockIdx.z;
+    // Workgroups are dispatched in blockIdx order: take the last sequences and
+    // the last row tiles (the longest causal spans in a chunk batch) first,
+    // so that the short ones fill in at the end.
+    const int s = gridDim.z - 1 - blockIdx.z;
+    const int bx = gridDim.x - 1 - blockIdx.x;
     const int g = blockIdx.y;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -111,7 +120,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int q0 = p.q_offsets[s];
     const int nq = p.q_offsets[s + 1] - q0;
     const int R = nq * G;
-    const int row0 = blockIdx.x * kRowsPerGroup + wave * kRowsPerWave;
+    const int row0 = bx * kRowsPerGroup + wave * kRowsPerWave;
     if (row0 >= R) return;            // (no barrier below)
     const int ctx = p.context_lens[s];
     const int Hq = p.num_q_heads;
@@ -150,6 +159,11 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) pmax = max(pmax, __shfl_xor(pmax, off));
     const int n_tiles = pmax / kTileTokens + 1;
+    int pmin = pos[0];
+#pragma unroll
+    for (int cb = 1; cb < kNc; ++cb) pmin = min(pmin, pos[cb]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) pmin = min(pmin, __shfl_xor(pmin, off));
 
     f32x4_t acc[kDpl][kNc];
 #pragma unroll
@@ -203,11 +217,19 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
             }
             float sc[8];
             float mx = -INFINITY;
+            if (t0 + kTileTokens - 1 <= pmin) {   // every token of the tile is visible
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = t0 + 16 * (e >> 2) + 4 * hgrp + (e & 3);
-                sc[e] = t <= pos[cb] ? sacc[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
-                mx = fmaxf(mx, sc[e]);
+                for (int e = 0; e < 8; ++e) {
+                    sc[e] = sacc[e >> 2][e & 3] * p.scale_log2;
+                    mx = fmaxf(mx, sc[e]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int t = t0 + 16 * (e >> 2) + 4 * hgrp + (e & 3);
+                    sc[e] = t <= pos[cb] ? sacc[e >> 2][e & 3] * p.scale_log2 : -INFINITY;
+                    mx = fmaxf(mx, sc[e]);
+                }
             }
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -235,7 +257,10 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
             pop[cb] = __builtin_bit_cast(bf16x8_t, pw);
             pop_lo[cb] = __builtin_bit_cast(bf16x8_t, pl);
         }
-        if (__ballot(alpha[0] != 1.f || alpha[kNc - 1] != 1.f)) {
+        bool moved = false;
+#pragma unroll
+        for (int cb = 0; cb < kNc; ++cb) moved = moved || alpha[cb] != 1.f;
+        if (__ballot(moved)) {
 #pragma unroll
             for (int j = 0; j < kDpl; ++j)
 #pragma unroll
