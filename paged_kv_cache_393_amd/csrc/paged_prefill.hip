@@ -65,8 +65,11 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #define PF_XCD_MAP 1
 #endif
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+#ifndef PF_WAVES
+#define PF_WAVES 8
+#endif
+constexpr int kWaves = PF_WAVES;           // waves per workgroup (rows share each staged tile)
+constexpr int kThreads = 64 * kWaves;
 constexpr int kNc = PF_NC;                 // MFMA column blocks (16 rows each) per wave
 constexpr int kRowsPerWave = 16 * kNc;
 constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
@@ -105,7 +108,8 @@ struct TileLds {
     static constexpr int kChunks = D / 8;
     static constexpr int kRowBytes = D * 2;
     static constexpr int kBytes = kLdsTokens * kRowBytes;            // one tensor
-    static constexpr int kChunksPerThread = kLdsTokens * kChunks / kThreads;
+    static constexpr int kTotalChunks = kLdsTokens * kChunks;       // one tensor
+    static constexpr int kChunksPerThread = (kTotalChunks + kThreads - 1) / kThreads;
     __device__ static int offset(int row, int chunk) {
         return row * kRowBytes + ((chunk ^ (row % kChunks)) * 16);
     }
@@ -200,14 +204,21 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int n_tiles = wg_pmax / kLdsTokens + 1;      // the workgroup's LDS tiles (uniform)
     const int my_steps = pmax / kTileTokens + 1;       // this wave's compute steps
 
-    // This thread's share of a tile's loads: chunk c of rows r0 + 16 j.
-    const int ld_row0 = (int)threadIdx.x / TL::kChunks;
+    // This thread's share of a tile's loads: flat chunks threadIdx.x + j * kThreads
+    // (row = flat / chunks per row, chunk = flat % chunks per row).
     const int ld_chunk = (int)threadIdx.x % TL::kChunks;
     u32x4_t pre_k[kCpt], pre_v[kCpt];
+    auto ld_ok = [&](int j) __attribute__((always_inline)) {
+        return TL::kTotalChunks % kThreads == 0 || (int)threadIdx.x + j * kThreads < TL::kTotalChunks;
+    };
+    auto ld_row = [&](int j) __attribute__((always_inline)) {
+        return ((int)threadIdx.x + j * kThreads) / TL::kChunks;
+    };
     auto load_tile = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kCpt; ++j) {
-            const int row = ld_row0 + j * (kThreads / TL::kChunks);   // 0 .. kLdsTokens-1
+            if (!ld_ok(j)) continue;
+            const int row = ld_row(j);                                // 0 .. kLdsTokens-1
             const int tb = t0 + (row & ~15);                          // the row's 16-token half
             const int rows = min(16, max(0, ctx - tb));
             const int phys = rows > 0 ? table[tb >> bs_log2] : 0;
@@ -224,7 +235,8 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kCpt; ++j) {
-            const int row = ld_row0 + j * (kThreads / TL::kChunks);
+            if (!ld_ok(j)) continue;
+            const int row = ld_row(j);
             const int o = TL::offset(row, ld_chunk);
             *(u32x4_t *)(&lds_kv[buf][0][o]) = pre_k[j];
             *(u32x4_t *)(&lds_kv[buf][1][o]) = pre_v[j];
