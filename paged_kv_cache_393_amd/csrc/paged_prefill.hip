@@ -13,28 +13,26 @@
 // and k-elements 8*(l/16) .. +7; C lane l holding column l%16, rows 4*(l/16)+i).
 //
 // A "row" is a (query token, query head of the kv head's group) pair.  One
-// workgroup takes 128 rows of one (sequence, kv head); each of its 4 waves
+// workgroup takes 256 rows of one (sequence, kv head); each of its 8 waves
 // owns 32 rows as two MFMA column blocks.  The workgroup streams the context
-// in 32-token tiles through the block table: each thread loads 64 B of the
-// next tile into registers (buffer loads whose range is each 16-token half's
-// valid rows, so nothing past the context end is touched) while the current
-// tile is computed from LDS, then stores them to the other LDS buffer (one
-// barrier per tile; rows XOR-swizzled so the operand reads are conflict free):
-//   * S^T = K Q^T per 16-token half: K rows (tokens) are the A operand, 16 B
-//     per lane from LDS; the wave's query rows are the B operand, held in
-//     registers for the whole context.
+// in 32-token tiles through the block table with direct-to-LDS buffer loads
+// (whose range is each 16-token half's valid rows, so nothing past the
+// context end is touched), double-buffered, one barrier per tile:
+//   * S^T = K Q^T: K tokens are the A operand, 16 B per lane from LDS; the
+//     wave's query rows are the B operand, held in registers throughout.
 //   * causal mask and online softmax in the accumulator registers: lane l
-//     holds column (row) l%16 and tokens 4*(l/16) + j of each half.
+//     holds column (row) l%16 and tokens 16 h + 4*(l/16) + i of half h.
 //   * O^T += V^T P^T: the 8 weights a lane holds ARE its B-operand k-elements,
-//     under the token order e -> 16*(e/4) + 4*(l/16) + e%4; the A operand is
-//     built from V with the same order: each lane loads, for those 8 tokens,
-//     the contiguous dims chunk (l%16)*(D/16) .., and output block j takes
-//     element j of each token's chunk (row m = dim m*(D/16) + j).  The weights
-//     enter as a bf16 high part plus a bf16 remainder (two products), exact
-//     to 2^-17 relative: a single bf16 rounding (2^-9) of the weights alone
-//     exceeds a 2e-3 absolute bar on short contexts.
-// Tokens past a column's position get weight 0; the accumulators leave lane l
-// with row l%16 and the 4*(D/16) contiguous dims from 4*(D/16)*(l/16).
+//     under the token order e -> 16*(e/4) + 4*(l/16) + e%4; the A operand
+//     (16 dims x those 8 tokens) comes straight from the token-major V tile
+//     through LDS transpose reads.  The weights enter as a bf16 high part
+//     plus a bf16 remainder (two products), exact to 2^-17 relative: a single
+//     bf16 rounding (2^-9) of the weights alone exceeds a 2e-3 absolute bar
+//     on short contexts.
+// Software pipeline: on this chip a wave co-issues vector instructions with
+// its own in-flight matrix instructions (not with another wave's), so one
+// iteration runs the softmax of tile i between the MFMAs of the scores of
+// tile i+1 and the weighted sum of tile i-1.
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -52,34 +50,24 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 #ifndef PF_WAVES_PER_EU
 #define PF_WAVES_PER_EU 2
-#endif
-// Column blocks per wave (2 fits two waves per SIMD; more registers per wave
-// cost the occupancy that hides the loads' latency).
-#ifndef PF_NC
-#define PF_NC 2
 #endif
 #ifndef PF_XCD_MAP
 #define PF_XCD_MAP 1
 #endif
 
-#ifndef PF_WAVES
-#define PF_WAVES 8
-#endif
-constexpr int kWaves = PF_WAVES;           // waves per workgroup (rows share each staged tile)
+constexpr int kWaves = 8;                  // waves per workgroup (rows share each staged tile)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kNc = PF_NC;                 // MFMA column blocks (16 rows each) per wave
+constexpr int kNc = 2;                     // MFMA column blocks (16 rows each) per wave
 constexpr int kRowsPerWave = 16 * kNc;
 constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
-constexpr int kTileTokens = 32;           // tokens per compute step (two 16-token MFMA halves)
-#ifndef PF_LDS_TOKENS
-#define PF_LDS_TOKENS 32
-#endif
-constexpr int kLdsTokens = PF_LDS_TOKENS;  // tokens per LDS-staged tile (compute steps of 32)
+constexpr int kTileTokens = 32;            // tokens per staged tile and step (two 16-token halves)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRsrcFlags = 0x00020000;     // word 3 of a raw buffer resource on CDNA3/CDNA4
+constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0) alone (gfx9 field layout)
 
 struct PrefillParams {
     const uint16_t *q;
@@ -89,7 +77,8 @@ struct PrefillParams {
     const int32_t *context_lens;
     const int32_t *q_offsets;
     float *out;
-    float scale_log2;
+    float scale_log2;        // |scale| log2(e)
+    uint32_t q_sign;         // 0x80008000 when scale < 0: q is negated on load
     int num_q_heads;
     int num_kv_heads;
     int group;
@@ -99,31 +88,53 @@ struct PrefillParams {
     int tiles_x;             // row tiles per (sequence, kv head)
 };
 
-// LDS staging of one kLdsTokens-token K/V tile of a kv head: row r (token t0 + r) is
-// D*2 bytes = D/8 chunks of 16 B; chunk c of row r sits at position
-// c ^ (r % (D/8)) so that the operand reads below (16 rows at one chunk, or
-// one row at 16 chunks) touch distinct banks.
+// LDS staging of one 32-token tile of one kv head's K or V (D*2 bytes a
+// token, 16-B chunks of 8 dims).  Each layout makes its operand reads
+// bank-conflict free and lets a 1-KB piece of the tile arrive as one
+// direct-to-LDS load of 16 B a lane.
+//   K: per 16-token half, chunk-major: chunk c of token r at
+//      (r / 16) * 16 * chunks + c * 16 + r % 16 (16-B units) -- the scores
+//      read 16 tokens at one chunk, 256 contiguous bytes.
+//   V: token-major, chunk c of token r at r * chunks + (c ^ f(r)), f(r) even
+//      -- a transpose read takes 8 B (4 dims) of 16 tokens; f spreads the
+//      16 tokens' 32-B dim ranges over distinct banks, 8 tokens a pass.
 template <int D>
 struct TileLds {
     static constexpr int kChunks = D / 8;
     static constexpr int kRowBytes = D * 2;
-    static constexpr int kBytes = kLdsTokens * kRowBytes;            // one tensor
-    static constexpr int kTotalChunks = kLdsTokens * kChunks;       // one tensor
-    static constexpr int kChunksPerThread = (kTotalChunks + kThreads - 1) / kThreads;
-    __device__ static int offset(int row, int chunk) {
-        return row * kRowBytes + ((chunk ^ (row % kChunks)) * 16);
+    static constexpr int kBytes = kTileTokens * kRowBytes;            // one tensor
+    static constexpr int kRowsPerBankSpan = 256 / kRowBytes;          // tokens in 256 B (one pass of banks)
+    __device__ static int k_offset(int row, int chunk) {
+        return (row >> 4) * (kChunks * 256) + chunk * 256 + (row & 15) * 16;
     }
+    __device__ static int v_swz(int row) { return 2 * ((row / kRowsPerBankSpan) % (kChunks / 2)); }
+    __device__ static int v_offset(int row, int chunk) { return row * kRowBytes + ((chunk ^ v_swz(row)) * 16); }
 };
+
+// Max over the four lane groups (lanes l, l^16, l^32, l^48) with two VALU
+// lane swaps: the upper and lower 32 lanes, then the odd and even 16-lane rows.
+__device__ __forceinline__ float group_max(float x) {
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(const PrefillParams p) {
     constexpr int kSteps = D / 32;    // QK k-steps of 32 dims
-    constexpr int kDpl = D / 16;      // V dims per lane = PV output blocks
+    constexpr int kDpl = D / 16;      // PV output blocks of 16 dims
     using TL = TileLds<D>;
-    constexpr int kCpt = TL::kChunksPerThread;
-    // [buffer][K, V] tiles, double-buffered: the next tile is loaded into
-    // registers while the current one is computed from LDS.
-    __shared__ __attribute__((aligned(16))) char lds_kv[2][2][TL::kBytes];
+    // A tile of one tensor is loaded as 1-KB pieces, one direct-to-LDS load
+    // of 16 B per lane each, within one 16-token half: the piece's
+    // block-table entry, and its buffer resource, are wave-uniform.
+    constexpr int kPieces = TL::kBytes / 1024;
+    constexpr int kRowsPerPiece = 64 / TL::kChunks;      // V pieces: whole tokens
+    constexpr int kPiecesPerWave = (2 * kPieces + kWaves - 1) / kWaves;
+    static_assert(TL::kBytes % 1024 == 0 && 16 % kRowsPerPiece == 0 && TL::kChunks % 4 == 0,
+                  "pieces within one half");
+    __shared__ __attribute__((aligned(1024))) char lds_k[2][TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_v[2][TL::kBytes];
     __shared__ int lds_pmax[kWaves];
 
 #if PF_XCD_MAP
@@ -143,7 +154,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int bx = gridDim.x - 1 - blockIdx.x;
     const int g = blockIdx.y;
 #endif
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int hgrp = lane >> 4;       // lane group: k-elements / accumulator rows
     const int l16 = lane & 15;
@@ -163,6 +174,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
     const int bs_log2 = p.log2_block_size;
     const int bs_mask = (1 << bs_log2) - 1;
+    const float c = p.scale_log2;      // |scale| log2(e); a negative scale negates q
 
     // Columns of this lane: row r = row0 + 16 cb + l16 -> query token r / G,
     // head g*G + r % G, position ctx - nq + r / G.  Columns past R compute
@@ -180,7 +192,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         const uint16_t *qrow = p.q + ((int64_t)(q0 + i) * Hq + g * G + hh) * D;
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) {
-            u32x4_t w = *(const u32x4_t *)(qrow + 32 * st + 8 * hgrp);
+            u32x4_t w = *(const u32x4_t *)(qrow + 32 * st + 8 * hgrp) ^ p.q_sign;
             if (!colv[cb]) w = u32x4_t{0u, 0u, 0u, 0u};
             qop[cb][st] = __builtin_bit_cast(bf16x8_t, w);
         }
@@ -196,51 +208,98 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         pmax = max(pmax, __shfl_xor(pmax, off));
         pmin = min(pmin, __shfl_xor(pmin, off));
     }
+    pmax = __builtin_amdgcn_readfirstlane(pmax);      // wave-uniform after the reduction
+    pmin = __builtin_amdgcn_readfirstlane(pmin);
     if (lane == 0) lds_pmax[wave] = wave_live ? pmax : -1;
     __syncthreads();
     int wg_pmax = lds_pmax[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) wg_pmax = max(wg_pmax, lds_pmax[w]);
-    const int n_tiles = wg_pmax / kLdsTokens + 1;      // the workgroup's LDS tiles (uniform)
-    const int my_steps = pmax / kTileTokens + 1;       // this wave's compute steps
+    const int n_tiles = wg_pmax / kTileTokens + 1;     // the workgroup's tiles (uniform)
+    const int my_steps = pmax / kTileTokens + 1;       // this wave's tiles
 
-    // This thread's share of a tile's loads: flat chunks threadIdx.x + j * kThreads
-    // (row = flat / chunks per row, chunk = flat % chunks per row).
-    const int ld_chunk = (int)threadIdx.x % TL::kChunks;
-    u32x4_t pre_k[kCpt], pre_v[kCpt];
-    auto ld_ok = [&](int j) __attribute__((always_inline)) {
-        return TL::kTotalChunks % kThreads == 0 || (int)threadIdx.x + j * kThreads < TL::kTotalChunks;
+    // ---- tile loads: this wave's pieces, piece index w + j * kWaves (K
+    // pieces first, then V).
+    auto piece_ok = [&](int j) __attribute__((always_inline)) {
+        return (2 * kPieces) % kWaves == 0 || wave + j * kWaves < 2 * kPieces;
     };
-    auto ld_row = [&](int j) __attribute__((always_inline)) {
-        return ((int)threadIdx.x + j * kThreads) / TL::kChunks;
+    auto piece_is_v = [&](int j) __attribute__((always_inline)) { return (wave + j * kWaves) >= kPieces; };
+    auto piece_sub = [&](int j) __attribute__((always_inline)) { return (wave + j * kWaves) % kPieces; };
+    auto piece_half = [&](int j) __attribute__((always_inline)) {
+        return piece_is_v(j) ? (piece_sub(j) * kRowsPerPiece) >> 4 : piece_sub(j) / (TL::kChunks / 4);
     };
-    auto load_tile = [&](int t0) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < kCpt; ++j) {
-            if (!ld_ok(j)) continue;
-            const int row = ld_row(j);                                // 0 .. kLdsTokens-1
-            const int tb = t0 + (row & ~15);                          // the row's 16-token half
-            const int rows = min(16, max(0, ctx - tb));
-            const int phys = rows > 0 ? table[tb >> bs_log2] : 0;
-            const int64_t slot0 = ((int64_t)phys << bs_log2) + (tb & bs_mask);
-            const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(kbase + slot0 * rb32), 0, rows * (int)rb32, kRsrcFlags);
-            const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(vbase + slot0 * rb32), 0, rows * (int)rb32, kRsrcFlags);
-            const int off = (int)((uint32_t)(row & 15) * rb32 + (uint32_t)(ld_chunk * 16));
-            pre_k[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
-            pre_v[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
+    // During iteration i, K pieces load tile i + 2 and V pieces tile i.
+    auto piece_lead = [&](int j) __attribute__((always_inline)) { return piece_is_v(j) ? 0 : 2; };
+    // Block-table window: lane l holds entry wbase + l, the next 64 entries
+    // are loaded when the window slides (64 blocks ahead of their use), and a
+    // tile's blocks are read from a lane (v_readlane), not from memory: a
+    // load between a tile's K/V loads and their use would wait for them too.
+    const int nblk = ((min(ctx, n_tiles * kTileTokens) - 1) >> bs_log2) + 1;   // entries read
+    auto load_window = [&](int base) __attribute__((always_inline)) {
+        const int e = base + lane;
+        return e < nblk ? table[e] : 0;
+    };
+    int wbase = 0;
+    int win = load_window(0), win_next = load_window(64);
+    auto phys_of = [&](int tile, int j) __attribute__((always_inline)) {
+        const int tb = tile * kTileTokens + 16 * piece_half(j);
+        if (tb >= ctx) return 0;
+        const int o = (tb >> bs_log2) - wbase;            // 0 <= o < 128 (see the slide below)
+        int b;
+        if (o < 64) b = __builtin_amdgcn_readlane(win, o);
+        else b = __builtin_amdgcn_readlane(win_next, o - 64);
+        return b;
+    };
+    auto issue = [&](int tile, int j, int phys) __attribute__((always_inline)) {
+        const int sub = piece_sub(j);
+        const int tb = tile * kTileTokens + 16 * piece_half(j);
+        const int rows = min(16, max(0, ctx - tb));      // the buffer range: nothing past the context
+        const int64_t slot0 = ((int64_t)phys << bs_log2) + (tb & bs_mask);
+        const uint64_t addr = (uint64_t)(uintptr_t)((piece_is_v(j) ? vbase : kbase) + slot0 * rb32);
+        // wave-uniform by construction; stated, so the resource is built in
+        // scalar registers without a per-lane loop
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+        const int range = __builtin_amdgcn_readfirstlane(rows * (int)rb32);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(uintptr_t)(((uint64_t)hi << 32) | lo), 0, range, kRsrcFlags);
+        // the lane's 16 B: K piece = 4 chunks x 16 tokens of one half (chunk
+        // 4 (sub % (chunks/4)) + lane / 16, token lane % 16); V piece = whole
+        // tokens (token lane / chunks, stored chunk position lane % chunks,
+        // which holds dims chunk (lane % chunks) ^ f(token))
+        int r16, chunk;
+        if (piece_is_v(j)) {
+            const int row = sub * kRowsPerPiece + lane / TL::kChunks;
+            r16 = row & 15;
+            chunk = (lane % TL::kChunks) ^ TL::v_swz(row);
+        } else {
+            r16 = lane & 15;
+            chunk = 4 * (sub % (TL::kChunks / 4)) + (lane >> 4);
         }
+        const int voff = (int)((uint32_t)r16 * rb32 + (uint32_t)(chunk * 16));
+        char *dst = (piece_is_v(j) ? lds_v[tile & 1] : lds_k[tile & 1]) + sub * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst, 16, voff, 0, 0, 0);
     };
-    auto store_tile = [&](int buf) __attribute__((always_inline)) {
+
+    // ---- S^T = K Q^T of one tile from LDS: lane l gets column (row) l%16 of
+    // block cb and tokens 16 bb + 4 (l/16) + i.  The k-step loop is outermost,
+    // so the 2 kNc accumulation chains interleave.
+    typedef f32x4_t Scores[2][kNc];
+    auto scores = [&](const char *kl, Scores &S) __attribute__((always_inline)) {
+        bf16x8_t kop[2][kSteps];
 #pragma unroll
-        for (int j = 0; j < kCpt; ++j) {
-            if (!ld_ok(j)) continue;
-            const int row = ld_row(j);
-            const int o = TL::offset(row, ld_chunk);
-            *(u32x4_t *)(&lds_kv[buf][0][o]) = pre_k[j];
-            *(u32x4_t *)(&lds_kv[buf][1][o]) = pre_v[j];
-        }
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int st = 0; st < kSteps; ++st)
+                kop[bb][st] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(kl + TL::k_offset(16 * bb + l16, 4 * st + hgrp)));
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st)
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int cb = 0; cb < kNc; ++cb)
+                    S[bb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        kop[bb][st], qop[cb][st], st == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : S[bb][cb], 0, 0, 0);
     };
 
     f32x4_t acc[kDpl][kNc];
@@ -255,127 +314,207 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         l_run[cb] = 0.f;
     }
 
-    load_tile(0);
-    store_tile(0);
-    for (int tile = 0; tile < n_tiles; ++tile) {
-        const int buf = tile & 1;
-        if (tile + 1 < n_tiles) load_tile((tile + 1) * kLdsTokens);   // in flight during the compute
-        __syncthreads();      // tile `tile` is in LDS; every wave is done with the other buffer
-#pragma unroll 1
-        for (int sub = 0; sub < kLdsTokens / kTileTokens; ++sub) {
-          const int step = tile * (kLdsTokens / kTileTokens) + sub;
-          const int t0 = step * kTileTokens;
-          if (wave_live && step < my_steps) {
-            const char *kl = lds_kv[buf][0] + sub * kTileTokens * TL::kRowBytes;
-            const char *vl = lds_kv[buf][1] + sub * kTileTokens * TL::kRowBytes;
-            // ---- S^T = K Q^T from LDS, masked online softmax, weights as B operand
-            bf16x8_t pop[kNc], pop_lo[kNc];
-            float alpha[kNc];
-            f32x4_t sacc[2][kNc];
+    // ---- online softmax of tile t's scores S into the weights (bf16 high
+    // part and remainder, both rounded to nearest even: hi + lo is the fp32
+    // weight to 2^-17), masked on the tiles that cross a row's position.  The
+    // running max moves only when a row's tile max exceeds it by more than 8
+    // (log2 units): weights stay <= 2^8 and the accumulators are rarely
+    // rescaled.  Returns whether any row of the wave moved; alpha[cb] is then
+    // log2 of that row's rescale factor (0 where it did not move).
+    typedef bf16x8_t Weights[kNc];
+    auto softmax = [&](const int t, const Scores &S, Weights &Phi, Weights &Plo, float (&alpha)[kNc],
+                       auto masked) __attribute__((always_inline)) {
+        constexpr bool kMasked = decltype(masked)::value;
+        const int t0 = t * kTileTokens;
+        bool grow = false;
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                bf16x8_t kop[kSteps];
-#pragma unroll
-                for (int st = 0; st < kSteps; ++st)
-                    kop[st] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(kl + TL::offset(16 * bb + l16, 4 * st + hgrp)));
-#pragma unroll
-                for (int cb = 0; cb < kNc; ++cb) {
-                    sacc[bb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int st = 0; st < kSteps; ++st)
-                        sacc[bb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st], qop[cb][st], sacc[bb][cb], 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int cb = 0; cb < kNc; ++cb) {
-                float sc[8];
-                float mx = -INFINITY;
-                if (t0 + kTileTokens - 1 <= pmin) {   // every token of the tile is visible
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        sc[e] = sacc[e >> 2][cb][e & 3] * p.scale_log2;
-                        mx = fmaxf(mx, sc[e]);
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int t = t0 + 16 * (e >> 2) + 4 * hgrp + (e & 3);
-                        sc[e] = t <= pos[cb] ? sacc[e >> 2][cb][e & 3] * p.scale_log2 : -INFINITY;
-                        mx = fmaxf(mx, sc[e]);
-                    }
-                }
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float m_new = fmaxf(m_run[cb], mx);   // finite: token 0 <= every position
-                alpha[cb] = __builtin_amdgcn_exp2f(m_run[cb] - m_new);
-                float pr[8], psum = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pr[e] = __builtin_amdgcn_exp2f(sc[e] - m_new);
-                    psum += pr[e];
-                }
-                l_run[cb] = l_run[cb] * alpha[cb] + psum;
-                m_run[cb] = m_new;
-                // the weights as a bf16 high part plus a bf16 remainder, both
-                // rounded to nearest even: hi + lo is the fp32 weight to 2^-17
-                u32x4_t pw, pl;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const f32x2_t w2 = f32x2_t{pr[2 * e], pr[2 * e + 1]};
-                    const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, bf16x2_t));
-                    const f32x2_t r2 = w2 - f32x2_t{__uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
-                    pw[e] = hi;
-                    pl[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2_t));
-                }
-                pop[cb] = __builtin_bit_cast(bf16x8_t, pw);
-                pop_lo[cb] = __builtin_bit_cast(bf16x8_t, pl);
-            }
-            bool moved = false;
-#pragma unroll
-            for (int cb = 0; cb < kNc; ++cb) moved = moved || alpha[cb] != 1.f;
-            if (__ballot(moved)) {
-#pragma unroll
-                for (int j = 0; j < kDpl; ++j)
-#pragma unroll
-                    for (int cb = 0; cb < kNc; ++cb) acc[j][cb] *= alpha[cb];
-            }
-            // ---- O^T += V^T P^T: the lane's dims of its 8 tokens (row order
-            // e -> 16 (e/4) + 4 hgrp + e%4), output block j from element j.
-            uint32_t vw[8][kDpl / 2];
+        for (int cb = 0; cb < kNc; ++cb) {
+            bool vis[8];
+            float mx = -INFINITY;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int row = 16 * (e >> 2) + 4 * hgrp + (e & 3);
-                if constexpr (D == 128) {
-                    const u32x4_t c = *(const u32x4_t *)(vl + TL::offset(row, l16));
-                    vw[e][0] = c.x; vw[e][1] = c.y; vw[e][2] = c.z; vw[e][3] = c.w;
-                } else {
-                    const u32x2_t c = *(const u32x2_t *)(vl + TL::offset(row, l16 >> 1) + 8 * (l16 & 1));
-                    vw[e][0] = c.x; vw[e][1] = c.y;
-                }
+                vis[e] = !kMasked || t0 + 16 * (e >> 2) + 4 * hgrp + (e & 3) <= pos[cb];
+                mx = fmaxf(mx, vis[e] ? S[e >> 2][cb][e & 3] : -INFINITY);
             }
+            mx = group_max(mx);
+            const float mt = mx * c;                         // -inf: nothing visible
+            const bool up = mt > m_run[cb] + 8.f;
+            const float m_new = up ? mt : m_run[cb];
+            alpha[cb] = m_run[cb] - m_new;
+            grow = grow || up;
+            float pr[8], psum = 0.f;
 #pragma unroll
-            for (int j = 0; j < kDpl; ++j) {
-                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-                u32x4_t a;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    a[e] = __builtin_amdgcn_perm(vw[2 * e + 1][j >> 1], vw[2 * e][j >> 1], sel);
-                const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, a);
-#pragma unroll
-                for (int cb = 0; cb < kNc; ++cb) {
-                    acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[cb], acc[j][cb], 0, 0, 0);
-                    acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo[cb], acc[j][cb], 0, 0, 0);
-                }
+            for (int e = 0; e < 8; ++e) {
+                const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 2][cb][e & 3], c, -m_new));
+                pr[e] = vis[e] ? w : 0.f;
+                psum += pr[e];
             }
-          }
+            l_run[cb] = (up ? l_run[cb] * __builtin_amdgcn_exp2f(alpha[cb]) : l_run[cb]) + psum;
+            m_run[cb] = m_new;
+            u32x4_t pw, pl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f32x2_t w2 = f32x2_t{pr[2 * e], pr[2 * e + 1]};
+                const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, bf16x2_t));
+                const f32x2_t r2 = w2 - f32x2_t{__uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+                pw[e] = hi;
+                pl[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2_t));
+            }
+            Phi[cb] = __builtin_bit_cast(bf16x8_t, pw);
+            Plo[cb] = __builtin_bit_cast(bf16x8_t, pl);
         }
-        // The next tile goes to the other buffer, which every wave finished
-        // reading before the barrier above.
-        if (tile + 1 < n_tiles) store_tile(buf ^ 1);
+        return __ballot(grow) != 0;
+    };
+    auto rescale = [&](const float (&alpha)[kNc]) __attribute__((always_inline)) {
+        float f[kNc];
+#pragma unroll
+        for (int cb = 0; cb < kNc; ++cb) f[cb] = __builtin_amdgcn_exp2f(alpha[cb]);
+#pragma unroll
+        for (int j = 0; j < kDpl; ++j)
+#pragma unroll
+            for (int cb = 0; cb < kNc; ++cb) acc[j][cb] *= f[cb];
+    };
+
+    // ---- O^T += V^T P^T for one tile.  The A operand of output block j
+    // (dims 16 j .. +15) is read transposed from the token-major V tile: in a
+    // lane group, lane i names 4 dims (16 j + 4 (i % 4) ..) of token
+    // 4 (group) + i / 4 (and 16 tokens further for the second read), and
+    // gets dim 16 j + i of the group's 4 tokens -- its k-elements in the
+    // weights' token order.
+    const int tr_tok = 4 * hgrp + (l16 >> 2);
+    const int tr_lane = tr_tok * TL::kRowBytes + 8 * (l16 & 1);   // + chunk position
+    auto weighted_values = [&](const char *vl, const Weights &Phi, const Weights &Plo) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kDpl; ++j) {
+            const int chunk = 2 * j + ((l16 >> 1) & 1);
+            const char *a0 = vl + tr_lane + ((chunk ^ TL::v_swz(tr_tok)) * 16);
+            const i16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t *)(a0));
+            const i16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t *)(a0 + 16 * TL::kRowBytes));
+            const bf16x8_t vop = __builtin_bit_cast(
+                bf16x8_t, u32x4_t{__builtin_bit_cast(u32x2_t, x0).x, __builtin_bit_cast(u32x2_t, x0).y,
+                                  __builtin_bit_cast(u32x2_t, x1).x, __builtin_bit_cast(u32x2_t, x1).y});
+#pragma unroll
+            for (int cb = 0; cb < kNc; ++cb)
+                acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, Phi[cb], acc[j][cb], 0, 0, 0);
+#pragma unroll
+            for (int cb = 0; cb < kNc; ++cb)
+                acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, Plo[cb], acc[j][cb], 0, 0, 0);
+        }
+    };
+
+    // ---- prologue: K of tiles 0 and 1 in LDS, then the scores of tile 0.
+#pragma unroll
+    for (int j = 0; j < kPiecesPerWave; ++j) {
+        if (!piece_ok(j) || piece_is_v(j)) continue;
+        issue(0, j, phys_of(0, j));
+        if (n_tiles > 1) issue(1, j, phys_of(1, j));
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    Scores S;                  // scores of the tile whose softmax is next
+    Weights Phi, Plo;          // weights of the tile whose weighted sum is next
+    if (wave_live) scores(lds_k[0], S);
+    __syncthreads();           // K(0) read by every wave before iteration 0 loads K(2) over it
+
+    // ---- iteration i (K(i+1) and V(i-1) in LDS; K(i+2) and V(i) loading):
+    //   softmax(i)  -- vector unit, on the scores from the last iteration
+    //   PV(i-1), scores(i+1)  -- matrix cores, issued among the softmax's
+    //   instructions by the scheduler (independent registers)
+    //   then the rescale of the accumulators if a row's max moved.
+    // The first and last tiles of a wave take a general path with the
+    // missing parts switched off.
+    // One iteration's compute: from (Sc, Ph, Pl) -- the scores of tile i and
+    // the weights of tile i-1 -- to (Sn, Pn_hi, Pn_lo).  `full`: every part
+    // present (a middle tile), one straight-line block in which the compiler
+    // interleaves the three independent streams.
+    bool pend_grow = false;    // a softmax moved a running max: rescale before the next weighted sum
+    float pend_alpha[kNc];
+    auto step = [&](const int i, const Scores &Sc, const Weights &Ph, const Weights &Pl, Scores &Sn,
+                    Weights &Pn_hi, Weights &Pn_lo, auto masked, auto full) __attribute__((always_inline)) {
+        constexpr bool kFull = decltype(full)::value;
+        const bool do_sm = kFull || i < my_steps;
+        const bool do_pv = kFull || (i >= 1 && i - 1 < my_steps);
+        const bool do_qk = kFull || i + 1 < my_steps;
+        // the rescale the last softmax asked for: after the weighted sum of
+        // tile i-2 (last iteration), before that of tile i-1
+        if (pend_grow) rescale(pend_alpha);
+        pend_grow = false;
+        if (do_sm) pend_grow = softmax(i, Sc, Pn_hi, Pn_lo, pend_alpha, masked);
+        if (do_pv) weighted_values(lds_v[(i - 1) & 1], Ph, Pl);
+        if (do_qk) scores(lds_k[(i + 1) & 1], Sn);
+    };
+    auto loads = [&](const int i) __attribute__((always_inline)) {
+        // The oldest block iteration i loads is V(i)'s first; once it leaves
+        // the window, slide (the newest, K(i+2)'s last, is at most
+        // 80 / block_size blocks further, so a slide never skips a window).
+        if (((i * kTileTokens) >> bs_log2) >= wbase + 64) {
+            wbase += 64;
+            win = win_next;
+            win_next = load_window(wbase + 64);
+        }
+#pragma unroll
+        for (int j = 0; j < kPiecesPerWave; ++j) {
+            if (!piece_ok(j)) continue;
+            const int tile = i + piece_lead(j);
+            if (tile < n_tiles) issue(tile, j, phys_of(tile, j));
+        }
+    };
+    auto tile_done = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);       // this wave's pieces are in LDS
+        __syncthreads();
+    };
+    // Three loops with one barrier per iteration each, n_tiles in all: the
+    // wave's first tile, its middle tiles (every part present, no mask: one
+    // straight-line body), and the rest (diagonal tiles, the last weighted
+    // sum, then loads only).
+    const int first_masked = pmin >= kTileTokens - 1 ? (pmin - (kTileTokens - 1)) / kTileTokens + 1 : 0;
+    const int full_end = wave_live ? max(1, min(first_masked, my_steps - 1)) : 1;
+    Scores S2;
+    Weights Phi2, Plo2;
+    loads(0);
+    if (wave_live) step(0, S, Phi, Plo, S2, Phi2, Plo2, std::true_type{}, std::false_type{});
+    tile_done();
+    // The state alternates between the two register sets, so the middle
+    // tiles run in pairs without copies; after the pairs it is in (S2, P2).
+    int i = 1;
+    for (; i + 1 < full_end; i += 2) {
+        loads(i);
+        step(i, S2, Phi2, Plo2, S, Phi, Plo, std::false_type{}, std::true_type{});
+        tile_done();
+        loads(i + 1);
+        step(i + 1, S, Phi, Plo, S2, Phi2, Plo2, std::false_type{}, std::true_type{});
+        tile_done();
+    }
+    // the general iterations (an odd middle tile, the diagonal tiles, the
+    // last weighted sum, then loads only), each followed by a copy back into
+    // (S2, P2)
+    for (; i < n_tiles; ++i) {
+        loads(i);
+        if (wave_live && i <= my_steps) {
+            Scores Sn;
+            Weights Pn_hi, Pn_lo;
+            step(i, S2, Phi2, Plo2, Sn, Pn_hi, Pn_lo, std::true_type{}, std::false_type{});
+#pragma unroll
+            for (int cb = 0; cb < kNc; ++cb) {
+                Phi2[cb] = Pn_hi[cb];
+                Plo2[cb] = Pn_lo[cb];
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) S2[bb][cb] = Sn[bb][cb];
+            }
+        }
+        tile_done();
+    }
+    // the last tile's weighted sum (V(n_tiles-1) landed in the last iteration)
+    if (wave_live && my_steps == n_tiles) {
+        if (pend_grow) rescale(pend_alpha);
+        weighted_values(lds_v[(n_tiles - 1) & 1], Phi2, Plo2);
     }
 
     if (!wave_live) return;
-    // ---- the four lane groups hold partial sums over different tokens
+    // ---- the four lane groups hold partial sums over different tokens;
+    // lane l has dims 16 j + 4 (l/16) + e of row l%16 of each column block
 #pragma unroll
     for (int cb = 0; cb < kNc; ++cb) {
         float l = l_run[cb];
@@ -386,13 +525,9 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         const int i = r / G;
         const int hh = r - i * G;
         const float inv = 1.f / l;
-        float *dst = p.out + ((int64_t)(q0 + i) * Hq + g * G + hh) * D + 4 * kDpl * hgrp;
+        float *dst = p.out + ((int64_t)(q0 + i) * Hq + g * G + hh) * D + 4 * hgrp;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int j = 0; j < kDpl; j += 4)
-                *(f32x4_t *)(dst + e * kDpl + j) = f32x4_t{acc[j][cb][e] * inv, acc[j + 1][cb][e] * inv,
-                                                           acc[j + 2][cb][e] * inv, acc[j + 3][cb][e] * inv};
+        for (int j = 0; j < kDpl; ++j) *(f32x4_t *)(dst + 16 * j) = acc[j][cb] * inv;
     }
 }
 
@@ -438,7 +573,8 @@ extern "C" int paged_attn_prefill(const void *q, const void *k_cache, const void
     p.context_lens = context_lens;
     p.q_offsets = q_offsets;
     p.out = out;
-    p.scale_log2 = scale * kLog2e;
+    p.scale_log2 = fabsf(scale) * kLog2e;
+    p.q_sign = scale < 0.f ? 0x80008000u : 0u;
     p.num_q_heads = sh->num_q_heads;
     p.num_kv_heads = sh->num_kv_heads;
     p.group = group;

@@ -34,17 +34,19 @@ def make(ctx, nq, Hq, Hkv, D, bs, seed):
     return v, q, q_off
 
 
-def run(v, q, q_off, max_q=None):
+def run(v, q, q_off, max_q=None, scale=None):
     out = B.prefill(q, v["k_cache"], v["v_cache"], v["block_tables"], v["context_lens"],
-                    q_off.to(DEV), v["scale"], max_q or int((q_off[1:] - q_off[:-1]).max()))
+                    q_off.to(DEV), v["scale"] if scale is None else scale,
+                    max_q or int((q_off[1:] - q_off[:-1]).max()))
     torch.cuda.synchronize()
     return out
 
 
-def ref(v, q, q_off):
+def ref(v, q, q_off, scale=None):
     return oracle.paged_prefill_bf16(I.bf16_bits(q), I.bf16_bits(v["k_cache"]),
                                      I.bf16_bits(v["v_cache"]), v["block_tables"].cpu().numpy(),
-                                     v["context_lens"].cpu().numpy(), q_off.numpy(), v["scale"])
+                                     v["context_lens"].cpu().numpy(), q_off.numpy(),
+                                     v["scale"] if scale is None else scale)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -78,6 +80,36 @@ def test_prefill_mixed_chunk_and_decodes_and_empty():
     nq = [512, 1, 1, 0, 1]
     v, q, q_off = make(ctx, nq, 32, 8, 128, 16, seed=511)
     assert_parity(run(v, q, q_off), ref(v, q, q_off), "mixed")
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.6])
+def test_prefill_any_scale(scale):
+    # A negative scale flips every score (the kernel negates q and uses
+    # |scale|); scale 0 gives every visible token the same weight; 0.6 makes
+    # the weights peaked.
+    note(f"prefill scale={scale}")
+    ctx = (40, 700, 129)
+    v, q, q_off = make(ctx, [40, 300, 65], 16, 4, 128, 16, seed=514)
+    assert_parity(run(v, q, q_off, scale=scale), ref(v, q, q_off, scale=scale), f"scale {scale}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_growing_keys_move_the_running_max(D):
+    # Keys whose magnitude grows block after block along each context: the
+    # scores of later tiles exceed the running max by many powers of two, so
+    # the accumulators are rescaled again and again (and the first tiles'
+    # weights underflow to 0), in both causal and unmasked tiles.
+    note(f"prefill growing keys D={D}")
+    bs = 16
+    ctx = (1000, 333, 64)
+    v, q, q_off = make(ctx, [200, 333, 64], 8, 2, D, bs, seed=515 + D)
+    k = v["k_cache"].float()
+    bt = v["block_tables"].cpu()
+    for s_, c in enumerate(ctx):
+        for j in range((c + bs - 1) // bs):
+            k[int(bt[s_, j])] *= 0.5 + 0.75 * j
+    v["k_cache"].copy_(k.to(torch.bfloat16))
+    assert_parity(run(v, q, q_off), ref(v, q, q_off), "growing keys")
 
 
 def test_prefill_poisoned_padding_bit_identical():
