@@ -51,6 +51,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 #ifndef PF_WAVES_PER_EU
 #define PF_WAVES_PER_EU 2
@@ -67,7 +68,14 @@ constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
 constexpr int kTileTokens = 32;            // tokens per staged tile and step (two 16-token halves)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRsrcFlags = 0x00020000;     // word 3 of a raw buffer resource on CDNA3/CDNA4
-constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0) alone (gfx9 field layout)
+constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0) alone (gfx9 field layout; + n: vmcnt(n))
+#ifndef PF_RING
+#define PF_RING 2
+#endif
+// K/V tiles in flight: K(i+kRing) and V(i+kRing-2) are loaded during
+// iteration i, which reads K(i+1) and V(i-1); ring slot = tile % kRing.
+constexpr int kRing = PF_RING;
+static_assert(kRing == 2 || kRing == 3, "ring depth");
 
 struct PrefillParams {
     const uint16_t *q;
@@ -133,8 +141,8 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     constexpr int kPiecesPerWave = (2 * kPieces + kWaves - 1) / kWaves;
     static_assert(TL::kBytes % 1024 == 0 && 16 % kRowsPerPiece == 0 && TL::kChunks % 4 == 0,
                   "pieces within one half");
-    __shared__ __attribute__((aligned(1024))) char lds_k[2][TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) char lds_v[2][TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_k[kRing][TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_v[kRing][TL::kBytes];
     __shared__ int lds_pmax[kWaves];
 
 #if PF_XCD_MAP
@@ -228,8 +236,9 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     auto piece_half = [&](int j) __attribute__((always_inline)) {
         return piece_is_v(j) ? (piece_sub(j) * kRowsPerPiece) >> 4 : piece_sub(j) / (TL::kChunks / 4);
     };
-    // During iteration i, K pieces load tile i + 2 and V pieces tile i.
-    auto piece_lead = [&](int j) __attribute__((always_inline)) { return piece_is_v(j) ? 0 : 2; };
+    // During iteration i, K pieces load tile i + kRing and V pieces tile
+    // i + kRing - 2.
+    auto piece_lead = [&](int j) __attribute__((always_inline)) { return piece_is_v(j) ? kRing - 2 : kRing; };
     // Block-table window: lane l holds entry wbase + l, the next 64 entries
     // are loaded when the window slides (64 blocks ahead of their use), and a
     // tile's blocks are read from a lane (v_readlane), not from memory: a
@@ -261,8 +270,8 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
         const int range = __builtin_amdgcn_readfirstlane(rows * (int)rb32);
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(uintptr_t)(((uint64_t)hi << 32) | lo), 0, range, kRsrcFlags);
+        // raw buffer resource: base, stride 0, num_records = range
+        const i32x4_t rs = {(int32_t)lo, (int32_t)(hi & 0xffffu), range, kRsrcFlags};
         // the lane's 16 B: K piece = 4 chunks x 16 tokens of one half (chunk
         // 4 (sub % (chunks/4)) + lane / 16, token lane % 16); V piece = whole
         // tokens (token lane / chunks, stored chunk position lane % chunks,
@@ -277,8 +286,18 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
             chunk = 4 * (sub % (TL::kChunks / 4)) + (lane >> 4);
         }
         const int voff = (int)((uint32_t)r16 * rb32 + (uint32_t)(chunk * 16));
-        char *dst = (piece_is_v(j) ? lds_v[tile & 1] : lds_k[tile & 1]) + sub * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst, 16, voff, 0, 0, 0);
+        char *dst = (piece_is_v(j) ? lds_v[tile % kRing] : lds_k[tile % kRing]) + sub * 1024;
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)dst);
+        // Direct-to-LDS load (lane l's 16 B land at dst + 16 l).  Written as
+        // asm so the compiler does not order LDS reads of the other ring
+        // slots after it (it cannot tell the slots apart and would wait for
+        // the load): the explicit waits and barriers order the slots.  The
+        // nops cover the SGPR / M0 writes read by the load.
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(m0), "v"(voff), "s"(rs)
+                     : "memory");
     };
 
     // ---- S^T = K Q^T of one tile from LDS: lane l gets column (row) l%16 of
@@ -326,31 +345,42 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                        auto masked) __attribute__((always_inline)) {
         constexpr bool kMasked = decltype(masked)::value;
         const int t0 = t * kTileTokens;
-        bool grow = false;
+        bool vis[kNc][8];
+        float mx[kNc];
+        bool exceed = false;
 #pragma unroll
         for (int cb = 0; cb < kNc; ++cb) {
-            bool vis[8];
-            float mx = -INFINITY;
+            mx[cb] = -INFINITY;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                vis[e] = !kMasked || t0 + 16 * (e >> 2) + 4 * hgrp + (e & 3) <= pos[cb];
-                mx = fmaxf(mx, vis[e] ? S[e >> 2][cb][e & 3] : -INFINITY);
+                vis[cb][e] = !kMasked || t0 + 16 * (e >> 2) + 4 * hgrp + (e & 3) <= pos[cb];
+                mx[cb] = fmaxf(mx[cb], vis[cb][e] ? S[e >> 2][cb][e & 3] : -INFINITY);
             }
-            mx = group_max(mx);
-            const float mt = mx * c;                         // -inf: nothing visible
-            const bool up = mt > m_run[cb] + 8.f;
-            const float m_new = up ? mt : m_run[cb];
-            alpha[cb] = m_run[cb] - m_new;
-            grow = grow || up;
+            exceed = exceed || mx[cb] * c > m_run[cb] + 8.f;
+        }
+        // Only when one of the lane's scores passes its row's running max by
+        // more than 8 are the row maxima (over the four lane groups) needed.
+        const bool grow = __ballot(exceed) != 0;
+        if (grow) {
+#pragma unroll
+            for (int cb = 0; cb < kNc; ++cb) {
+                const float mt = group_max(mx[cb]) * c;       // -inf: nothing visible
+                const float m_new = mt > m_run[cb] + 8.f ? mt : m_run[cb];
+                alpha[cb] = m_run[cb] - m_new;                 // log2 of the rescale; 0 if unmoved
+                l_run[cb] *= __builtin_amdgcn_exp2f(alpha[cb]);
+                m_run[cb] = m_new;
+            }
+        }
+#pragma unroll
+        for (int cb = 0; cb < kNc; ++cb) {
             float pr[8], psum = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 2][cb][e & 3], c, -m_new));
-                pr[e] = vis[e] ? w : 0.f;
+                const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 2][cb][e & 3], c, -m_run[cb]));
+                pr[e] = vis[cb][e] ? w : 0.f;
                 psum += pr[e];
             }
-            l_run[cb] = (up ? l_run[cb] * __builtin_amdgcn_exp2f(alpha[cb]) : l_run[cb]) + psum;
-            m_run[cb] = m_new;
+            l_run[cb] += psum;
             u32x4_t pw, pl;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -363,7 +393,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
             Phi[cb] = __builtin_bit_cast(bf16x8_t, pw);
             Plo[cb] = __builtin_bit_cast(bf16x8_t, pl);
         }
-        return __ballot(grow) != 0;
+        return grow;
     };
     auto rescale = [&](const float (&alpha)[kNc]) __attribute__((always_inline)) {
         float f[kNc];
@@ -404,7 +434,9 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         }
     };
 
-    // ---- prologue: K of tiles 0 and 1 in LDS, then the scores of tile 0.
+    // ---- prologue: K of tiles 0 and 1 in LDS, then the scores of tile 0;
+    // the tiles iteration 0 does not load (K(2) and V(0) for a 3-deep ring)
+    // are issued meanwhile.
 #pragma unroll
     for (int j = 0; j < kPiecesPerWave; ++j) {
         if (!piece_ok(j) || piece_is_v(j)) continue;
@@ -413,10 +445,18 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+    if constexpr (kRing == 3) {
+#pragma unroll
+        for (int j = 0; j < kPiecesPerWave; ++j) {
+            if (!piece_ok(j)) continue;
+            if (piece_is_v(j)) issue(0, j, phys_of(0, j));
+            else if (n_tiles > 2) issue(2, j, phys_of(2, j));
+        }
+    }
     Scores S;                  // scores of the tile whose softmax is next
     Weights Phi, Plo;          // weights of the tile whose weighted sum is next
     if (wave_live) scores(lds_k[0], S);
-    __syncthreads();           // K(0) read by every wave before iteration 0 loads K(2) over it
+    __syncthreads();           // K(0) read by every wave before iteration 0 loads over it
 
     // ---- iteration i (K(i+1) and V(i-1) in LDS; K(i+2) and V(i) loading):
     //   softmax(i)  -- vector unit, on the scores from the last iteration
@@ -442,27 +482,44 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         if (pend_grow) rescale(pend_alpha);
         pend_grow = false;
         if (do_sm) pend_grow = softmax(i, Sc, Pn_hi, Pn_lo, pend_alpha, masked);
-        if (do_pv) weighted_values(lds_v[(i - 1) & 1], Ph, Pl);
-        if (do_qk) scores(lds_k[(i + 1) & 1], Sn);
+        if (do_pv) weighted_values(lds_v[(i - 1) % kRing], Ph, Pl);
+        if (do_qk) scores(lds_k[(i + 1) % kRing], Sn);
     };
+    // Returns how many loads the wave issued (wave-uniform), or -1 when the
+    // table window slid: that iteration ends with vmcnt(0), so the window's
+    // load is known complete before any lookup reads it.
     auto loads = [&](const int i) __attribute__((always_inline)) {
-        // The oldest block iteration i loads is V(i)'s first; once it leaves
-        // the window, slide (the newest, K(i+2)'s last, is at most
-        // 80 / block_size blocks further, so a slide never skips a window).
-        if (((i * kTileTokens) >> bs_log2) >= wbase + 64) {
+        // The oldest block iteration i loads is V(i+kRing-2)'s first; once
+        // it leaves the window, slide (the newest, K(i+kRing)'s last, is at
+        // most 80 / block_size blocks further, so a slide never skips a
+        // window).
+        bool slid = false;
+        if ((((i + kRing - 2) * kTileTokens) >> bs_log2) >= wbase + 64) {
             wbase += 64;
             win = win_next;
             win_next = load_window(wbase + 64);
+            slid = true;
         }
+        int n = 0;
 #pragma unroll
         for (int j = 0; j < kPiecesPerWave; ++j) {
             if (!piece_ok(j)) continue;
             const int tile = i + piece_lead(j);
-            if (tile < n_tiles) issue(tile, j, phys_of(tile, j));
+            if (tile < n_tiles) {
+                issue(tile, j, phys_of(tile, j));
+                ++n;
+            }
         }
+        return slid ? -1 : n;
     };
-    auto tile_done = [&]() __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);       // this wave's pieces are in LDS
+    // End of an iteration: the loads of earlier iterations have landed
+    // (those of this one, n, may still fly: their tiles are read two
+    // iterations on), then the barrier.  Loads return in order.
+    auto tile_done = [&](const int n) __attribute__((always_inline)) {
+        static_assert(kPiecesPerWave <= 2, "vmcnt cases");
+        if (kRing == 2 || n <= 0) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        else if (n == 1) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 + 1);
+        else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 + 2);
         __syncthreads();
     };
     // Three loops with one barrier per iteration each, n_tiles in all: the
@@ -473,25 +530,25 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int full_end = wave_live ? max(1, min(first_masked, my_steps - 1)) : 1;
     Scores S2;
     Weights Phi2, Plo2;
-    loads(0);
+    int nl = loads(0);
     if (wave_live) step(0, S, Phi, Plo, S2, Phi2, Plo2, std::true_type{}, std::false_type{});
-    tile_done();
+    tile_done(nl);
     // The state alternates between the two register sets, so the middle
     // tiles run in pairs without copies; after the pairs it is in (S2, P2).
     int i = 1;
     for (; i + 1 < full_end; i += 2) {
-        loads(i);
+        nl = loads(i);
         step(i, S2, Phi2, Plo2, S, Phi, Plo, std::false_type{}, std::true_type{});
-        tile_done();
-        loads(i + 1);
+        tile_done(nl);
+        nl = loads(i + 1);
         step(i + 1, S, Phi, Plo, S2, Phi2, Plo2, std::false_type{}, std::true_type{});
-        tile_done();
+        tile_done(nl);
     }
     // the general iterations (an odd middle tile, the diagonal tiles, the
     // last weighted sum, then loads only), each followed by a copy back into
     // (S2, P2)
     for (; i < n_tiles; ++i) {
-        loads(i);
+        nl = loads(i);
         if (wave_live && i <= my_steps) {
             Scores Sn;
             Weights Pn_hi, Pn_lo;
@@ -504,12 +561,12 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                 for (int bb = 0; bb < 2; ++bb) S2[bb][cb] = Sn[bb][cb];
             }
         }
-        tile_done();
+        tile_done(nl);
     }
     // the last tile's weighted sum (V(n_tiles-1) landed in the last iteration)
     if (wave_live && my_steps == n_tiles) {
         if (pend_grow) rescale(pend_alpha);
-        weighted_values(lds_v[(n_tiles - 1) & 1], Phi2, Plo2);
+        weighted_values(lds_v[(n_tiles - 1) % kRing], Phi2, Plo2);
     }
 
     if (!wave_live) return;
