@@ -112,6 +112,17 @@ def test_prefill_growing_keys_move_the_running_max(D):
     assert_parity(run(v, q, q_off), ref(v, q, q_off), "growing keys")
 
 
+@pytest.mark.parametrize("bs", [16, 4096])
+def test_prefill_long_context_many_table_windows(bs):
+    # A 30000-token context at block size 16 is 1875 blocks: the kernel's
+    # 64-entry block-table window slides about 30 times (and the last chunk
+    # tile crosses a slide); block size 4096 puts a whole tile in one block.
+    note(f"prefill long context bs={bs}")
+    ctx = (30000, 1500, 7)
+    v, q, q_off = make(ctx, [96, 1, 7], 8, 2, 128, bs, seed=516)
+    assert_parity(run(v, q, q_off), ref(v, q, q_off), f"long context bs {bs}")
+
+
 def test_prefill_poisoned_padding_bit_identical():
     note("prefill poison")
     for bs in (16, 256):
