@@ -95,6 +95,12 @@ class OracleLib:
         lib.oracle_paged_prefill_bf16.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
                                                   i64, ctypes.c_float, P]
         lib.oracle_paged_prefill_bf16.restype = i32
+        lib.oracle_paged_prefill_int8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                                  i32, i64, ctypes.c_float, P]
+        lib.oracle_paged_prefill_int8.restype = i32
+        lib.oracle_paged_prefill_fp8.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                                 i64, ctypes.c_float, P]
+        lib.oracle_paged_prefill_fp8.restype = i32
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i32
         lib.oracle_set_num_threads.argtypes = [i32]
@@ -411,6 +417,63 @@ def paged_prefill_bf16(q_bits, k_bits, v_bits, block_tables, context_lens, q_off
     rc = L.oracle_paged_prefill_bf16(_ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(bt), _ptr(cl),
                                      _ptr(qo), S, Hq, Hkv, D, BS, MB, NB, ctypes.c_float(scale),
                                      _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return out
+
+
+def _prefill_checked(q_bits, k, v, block_tables, context_lens, q_offsets):
+    as_i32 = lambda a: np.asarray(a, dtype=np.int32) if isinstance(a, (list, tuple)) else a
+    bt = _c(block_tables, np.int32)
+    cl = _c(as_i32(context_lens), np.int32)
+    qo = _c(as_i32(q_offsets), np.int32)
+    Nq, Hq, D = q_bits.shape
+    NB, BS, Hkv, D2 = k.shape
+    S, MB = bt.shape
+    if D2 != D or v.shape != k.shape or cl.shape != (S,) or qo.shape != (S + 1,) or \
+            int(qo[-1]) != Nq:
+        raise ValueError("shapes disagree")
+    return bt, cl, qo, (Nq, Hq, D, NB, BS, Hkv, S, MB)
+
+
+def paged_prefill_int8(q_bits, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens,
+                       q_offsets, scale, lib: "OracleLib | None" = None) -> np.ndarray:
+    """The chunked prefill of paged_prefill_bf16 over an int8 cache: element =
+    code * scale of its (slot, kv head); scales fp32 [NB, BS, Hkv]."""
+    q_bits = _c(q_bits, np.uint16)
+    k_codes = _c(k_codes, np.int8)
+    v_codes = _c(v_codes, np.int8)
+    ks = _c(k_scales, np.float32)
+    vs = _c(v_scales, np.float32)
+    bt, cl, qo, (Nq, Hq, D, NB, BS, Hkv, S, MB) = _prefill_checked(q_bits, k_codes, v_codes,
+                                                                   block_tables, context_lens,
+                                                                   q_offsets)
+    if ks.shape != (NB, BS, Hkv) or vs.shape != (NB, BS, Hkv):
+        raise ValueError("scales must be [NB, BS, Hkv]")
+    out = np.zeros((Nq, Hq, D), dtype=np.float64)
+    L = lib.lib if lib is not None else _load()
+    rc = L.oracle_paged_prefill_int8(_ptr(q_bits), _ptr(k_codes), _ptr(v_codes), _ptr(ks), _ptr(vs),
+                                     _ptr(bt), _ptr(cl), _ptr(qo), S, Hq, Hkv, D, BS, MB, NB,
+                                     ctypes.c_float(scale), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return out
+
+
+def paged_prefill_fp8(q_bits, k_codes, v_codes, block_tables, context_lens, q_offsets, scale,
+                      lib: "OracleLib | None" = None) -> np.ndarray:
+    """The chunked prefill of paged_prefill_bf16 over an FP8 E4M3 cache (uint8 codes)."""
+    q_bits = _c(q_bits, np.uint16)
+    k_codes = _c(k_codes, np.uint8)
+    v_codes = _c(v_codes, np.uint8)
+    bt, cl, qo, (Nq, Hq, D, NB, BS, Hkv, S, MB) = _prefill_checked(q_bits, k_codes, v_codes,
+                                                                   block_tables, context_lens,
+                                                                   q_offsets)
+    out = np.zeros((Nq, Hq, D), dtype=np.float64)
+    L = lib.lib if lib is not None else _load()
+    rc = L.oracle_paged_prefill_fp8(_ptr(q_bits), _ptr(k_codes), _ptr(v_codes), _ptr(bt), _ptr(cl),
+                                    _ptr(qo), S, Hq, Hkv, D, BS, MB, NB, ctypes.c_float(scale),
+                                    _ptr(out))
     if rc != 0:
         raise ValueError(f"oracle rejected the inputs (code {rc})")
     return out

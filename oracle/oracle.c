@@ -623,13 +623,13 @@ static void attend_prefix(const double *qd, const kv_src *src, const int32_t *ta
     for (int i = 0; i < D; ++i) o[i] /= denom;
 }
 
-int oracle_paged_prefill_bf16(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
-                              const int32_t *block_tables, const int32_t *context_lens,
-                              const int32_t *q_offsets, int S, int Hq, int Hkv, int D, int BS,
-                              int MB, int64_t NB, float scale, double *out)
+static int prefill_common(const uint16_t *q, const kv_src *src, const int32_t *block_tables,
+                          const int32_t *context_lens, const int32_t *q_offsets, int S, int Hq,
+                          int Hkv, int D, int BS, int MB, int64_t NB, float scale, double *out)
 {
-    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !q_offsets || !out)
+    if (!q || !src->k || !src->v || !block_tables || !context_lens || !q_offsets || !out)
         return ORC_ERR_ARG;
+    if (src->kind == KV_INT8 && (!src->k_scales || !src->v_scales)) return ORC_ERR_ARG;
     if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || MB < 0 || NB < 0 || Hq % Hkv)
         return ORC_ERR_ARG;
     if (q_offsets[0] != 0) return ORC_ERR_ARG;
@@ -643,7 +643,6 @@ int oracle_paged_prefill_bf16(const uint16_t *q, const uint16_t *k_cache, const 
             if (b < 0 || (int64_t)b >= NB) return ORC_ERR_TABLE;
         }
     }
-    kv_src src = {KV_BF16, k_cache, v_cache, NULL, NULL};
     const int G = Hq / Hkv;
     const int64_t rows = (int64_t)q_offsets[S] * Hq;
     int err = ORC_OK;
@@ -666,10 +665,44 @@ int oracle_paged_prefill_bf16(const uint16_t *q, const uint16_t *k_cache, const 
             continue;
         }
         for (int x = 0; x < D; ++x) qd[x] = bf16_bits_to_double(q[row * D + x]);
-        attend_prefix(qd, &src, block_tables + (int64_t)s * MB, p + 1, h / G, Hkv, D, BS,
+        attend_prefix(qd, src, block_tables + (int64_t)s * MB, p + 1, h / G, Hkv, D, BS,
                       (double)scale, scores, out + row * D);
         free(scores);
         free(qd);
     }
     return err;
+}
+
+int oracle_paged_prefill_bf16(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                              const int32_t *block_tables, const int32_t *context_lens,
+                              const int32_t *q_offsets, int S, int Hq, int Hkv, int D, int BS,
+                              int MB, int64_t NB, float scale, double *out)
+{
+    kv_src src = {KV_BF16, k_cache, v_cache, NULL, NULL};
+    return prefill_common(q, &src, block_tables, context_lens, q_offsets, S, Hq, Hkv, D, BS, MB,
+                          NB, scale, out);
+}
+
+/* The same chunked prefill over an int8 cache (element = code * its (slot, kv
+ * head) scale, ybb.press page section 6.1) or an FP8 E4M3 cache (element = the
+ * code's value). */
+int oracle_paged_prefill_int8(const uint16_t *q, const int8_t *k_cache, const int8_t *v_cache,
+                              const float *k_scales, const float *v_scales,
+                              const int32_t *block_tables, const int32_t *context_lens,
+                              const int32_t *q_offsets, int S, int Hq, int Hkv, int D, int BS,
+                              int MB, int64_t NB, float scale, double *out)
+{
+    kv_src src = {KV_INT8, k_cache, v_cache, k_scales, v_scales};
+    return prefill_common(q, &src, block_tables, context_lens, q_offsets, S, Hq, Hkv, D, BS, MB,
+                          NB, scale, out);
+}
+
+int oracle_paged_prefill_fp8(const uint16_t *q, const uint8_t *k_cache, const uint8_t *v_cache,
+                             const int32_t *block_tables, const int32_t *context_lens,
+                             const int32_t *q_offsets, int S, int Hq, int Hkv, int D, int BS,
+                             int MB, int64_t NB, float scale, double *out)
+{
+    kv_src src = {KV_FP8, k_cache, v_cache, NULL, NULL};
+    return prefill_common(q, &src, block_tables, context_lens, q_offsets, S, Hq, Hkv, D, BS, MB,
+                          NB, scale, out);
 }

@@ -81,6 +81,10 @@ MUTANTS = {
                                 "block_tables + (int64_t)s * MB, p, h / G,"),
     "prefill_head_mod": ("block_tables + (int64_t)s * MB, p + 1, h / G,",
                          "block_tables + (int64_t)s * MB, p + 1, h % Hkv,"),
+    "prefill_int8_scales_swapped": ("kv_src src = {KV_INT8, k_cache, v_cache, k_scales, v_scales};\n    return prefill_common",
+                                    "kv_src src = {KV_INT8, k_cache, v_cache, v_scales, k_scales};\n    return prefill_common"),
+    "prefill_fp8_caches_swapped": ("kv_src src = {KV_FP8, k_cache, v_cache, NULL, NULL};\n    return prefill_common",
+                                   "kv_src src = {KV_FP8, v_cache, k_cache, NULL, NULL};\n    return prefill_common"),
     "prefill_k_as_v": ("const double e = exp(scores[t] - m);\n        denom += e;\n        for (int i = 0; i < D; ++i) o[i] += e * kv_elem(src, 1,",
                        "const double e = exp(scores[t] - m);\n        denom += e;\n        for (int i = 0; i < D; ++i) o[i] += e * kv_elem(src, 0,"),
 }
@@ -118,6 +122,10 @@ PIN_FUNCS = [
     "test_prefill_whole_prompt_matches_causal_sdpa",
     "test_prefill_chunk_after_a_cached_prefix_matches_masked_sdpa",
     "test_prefill_is_causal",
+    "test_prefill_int8_single_query_is_the_decode",
+    "test_prefill_fp8_single_query_is_the_decode",
+    "test_prefill_int8_chunk_matches_masked_sdpa_on_dequantized_cache",
+    "test_prefill_fp8_chunk_matches_masked_sdpa_on_decoded_cache",
 ]
 
 RUNNER = r"""

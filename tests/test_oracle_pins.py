@@ -568,8 +568,8 @@ def test_decode_after_eviction_equals_attention_without_the_block():
 # n_q context tokens are queries attending causally over the paged cache.
 
 
-def _prefill_case(ctx, nq, Hq=8, Hkv=2, D=64, bs=16, seed=61):
-    _, v = C.make_case(len(ctx), Hq, Hkv, D, bs, ctx=ctx, seed=seed)
+def _prefill_case(ctx, nq, Hq=8, Hkv=2, D=64, bs=16, seed=61, kv_dtype="bf16"):
+    _, v = C.make_case(len(ctx), Hq, Hkv, D, bs, ctx=ctx, seed=seed, kv_dtype=kv_dtype)
     q_off = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
     gen = torch.Generator().manual_seed(seed + 1)
     q = torch.randn(int(q_off[-1]), Hq, D, generator=gen).to(torch.bfloat16)
@@ -580,6 +580,19 @@ def _prefill_oracle(v, q, q_off):
     return oracle.paged_prefill_bf16(I.bf16_bits(q), I.bf16_bits(v["k_cache"]),
                                      I.bf16_bits(v["v_cache"]), v["block_tables"].numpy(),
                                      v["context_lens"].numpy(), q_off, v["scale"])
+
+
+def _prefill_oracle_any(v, q, q_off):
+    """The oracle's prefill for the cache kind of the views (bf16, int8, fp8)."""
+    qb, bt, cl = I.bf16_bits(q), v["block_tables"].numpy(), v["context_lens"].numpy()
+    if "k_scales" in v:
+        return oracle.paged_prefill_int8(qb, v["k_cache"].numpy(), v["v_cache"].numpy(),
+                                         v["k_scales"].numpy(), v["v_scales"].numpy(), bt, cl,
+                                         q_off, v["scale"])
+    if v["k_cache"].dtype == torch.float8_e4m3fn:
+        return oracle.paged_prefill_fp8(qb, C.fp8_codes(v["k_cache"]), C.fp8_codes(v["v_cache"]),
+                                        bt, cl, q_off, v["scale"])
+    return _prefill_oracle(v, q, q_off)
 
 
 def _sdpa_masked(v, q, q_off, bs):
@@ -641,3 +654,39 @@ def test_prefill_is_causal():
     v["v_cache"][b, 49 % 16] = -2.0
     got = _prefill_oracle(v, q, q_off)
     assert np.array_equal(got[:19], base[:19]) and not np.array_equal(got[19], base[19])
+
+
+# The same prefill over the quantized caches: element = code * scale (int8,
+# ybb.press page section 6.1) or the E4M3 code's value (fp8).  Pinned to the
+# decode oracle of the same kind and to torch SDPA over caches dequantized by
+# numpy (int8) and by torch's float8_e4m3fn (fp8).
+
+
+def _prefill_quantized_single_query_is_the_decode(kind):
+    ctx = (1, 17, 100, 250)
+    v, q, q_off = _prefill_case(ctx, [1, 1, 1, 1], seed=66, kv_dtype=kind)
+    assert np.array_equal(_prefill_oracle_any(v, q, q_off), C.oracle_out(dict(v, q=q)))
+
+
+def _prefill_quantized_chunk_matches_masked_sdpa(kind):
+    ctx = (600, 100, 35, 512)
+    nq = [88, 100, 1, 512]
+    v, q, q_off = _prefill_case(ctx, nq, Hq=16, Hkv=2, seed=67, kv_dtype=kind)
+    assert np.allclose(_prefill_oracle_any(v, q, q_off), _sdpa_masked(v, q, q_off, 16),
+                       rtol=0, atol=1e-12)
+
+
+def test_prefill_int8_single_query_is_the_decode():
+    _prefill_quantized_single_query_is_the_decode("int8")
+
+
+def test_prefill_fp8_single_query_is_the_decode():
+    _prefill_quantized_single_query_is_the_decode("fp8")
+
+
+def test_prefill_int8_chunk_matches_masked_sdpa_on_dequantized_cache():
+    _prefill_quantized_chunk_matches_masked_sdpa("int8")
+
+
+def test_prefill_fp8_chunk_matches_masked_sdpa_on_decoded_cache():
+    _prefill_quantized_chunk_matches_masked_sdpa("fp8")
