@@ -467,8 +467,7 @@ def bench_prefill(args) -> int:
     print(f"[bench] inputs for {pw.name} ready", file=sys.stderr, flush=True)
 
     def step():
-        B.prefill(v["q"], v["k_cache"], v["v_cache"], v["block_tables"], v["context_lens"],
-                  v["q_offsets"], v["scale"], v["max_q_len"], out=out, stream=stream)
+        B.prefill_views(v, v["q"], v["q_offsets"], v["max_q_len"], out=out, stream=stream)
 
     flush_buf = None if args.no_flush else torch.ones((2 << 30) // 4, dtype=torch.float32,
                                                        device=dev)
@@ -488,7 +487,7 @@ def bench_prefill(args) -> int:
     print(f"[bench] {args.steps} timed steps done", file=sys.stderr, flush=True)
     flops = A.prefill_flops(pw.ctx, pw.n_q, pw.num_q_heads, pw.head_dim)
     nbytes = A.prefill_bytes(pw.ctx, pw.n_q, pw.num_q_heads, pw.num_kv_heads, pw.head_dim,
-                             pw.block_size)
+                             pw.block_size, pw.kv_dtype)
     t_s = ms_mean / 1e3
     tflops = flops / t_s / 1e12
     copy_for_counters(args, dev, stream)
@@ -506,7 +505,8 @@ def bench_prefill(args) -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) q/K/V, shuffled block pool)",
-        "config": {"workload": pw.name, "context_lens": list(pw.ctx), "query_tokens": list(pw.n_q),
+        "config": {"workload": pw.name, "kv_dtype": pw.kv_dtype, "context_lens": list(pw.ctx),
+                   "query_tokens": list(pw.n_q),
                    "num_q_heads": pw.num_q_heads, "num_kv_heads": pw.num_kv_heads,
                    "head_dim": pw.head_dim, "block_size": pw.block_size,
                    "cache_evict_between_steps": "2 GiB read" if flush_buf is not None else None},
@@ -536,6 +536,7 @@ def cpu_baseline_prefill(pw, v, out, flops_total):
     runs up to about 3 s, scaled to the whole call by flop count; and its
     largest difference from the GPU output on that chunk."""
     import numpy as np
+    import torch
 
     import oracle
     from paged_kv_cache_393_amd import accounting as A
@@ -545,13 +546,23 @@ def cpu_baseline_prefill(pw, v, out, flops_total):
         oracle.build()
     sub = I.select_sequences(v, [0], pw.block_size)
     nq = pw.n_q[0]
-    q0 = v["q"][:nq].cpu()
-    args = (I.bf16_bits(q0), I.bf16_bits(sub["k_cache"]), I.bf16_bits(sub["v_cache"]),
-            sub["block_tables"].numpy(), sub["context_lens"].numpy(), [0, nq], sub["scale"])
+    q0 = I.bf16_bits(v["q"][:nq].cpu())
+    tail = (sub["block_tables"].numpy(), sub["context_lens"].numpy(), [0, nq], sub["scale"])
+    if pw.kv_dtype == "int8":
+        fn = oracle.paged_prefill_int8
+        args = (q0, sub["k_cache"].numpy(), sub["v_cache"].numpy(), sub["k_scales"].numpy(),
+                sub["v_scales"].numpy()) + tail
+    elif pw.kv_dtype == "fp8":
+        fn = oracle.paged_prefill_fp8
+        codes = lambda t: t.contiguous().view(torch.uint8).numpy()
+        args = (q0, codes(sub["k_cache"]), codes(sub["v_cache"])) + tail
+    else:
+        fn = oracle.paged_prefill_bf16
+        args = (q0, I.bf16_bits(sub["k_cache"]), I.bf16_bits(sub["v_cache"])) + tail
     times, ref = [], None
     while sum(times) < 3.0 and len(times) < 25:
         t = time.perf_counter()
-        ref = oracle.paged_prefill_bf16(*args)
+        ref = fn(*args)
         times.append(time.perf_counter() - t)
     t_med = statistics.median(times)
     f0 = A.prefill_flops(pw.ctx[:1], pw.n_q[:1], pw.num_q_heads, pw.head_dim)

@@ -64,6 +64,30 @@ int paged_attn_prefill(const void *q, const void *k_cache, const void *v_cache,
                        const int32_t *q_offsets, float scale, float *out,
                        const pa_prefill_shape *shape, void *stream);
 
+/*
+ * The same chunked prefill over an int8 cache (ybb.press page, section 6.1:
+ * element = code * scale): k_cache / v_cache int8 codes [num_blocks,
+ * block_size, Hkv, head_dim] (8-byte aligned), k_scales / v_scales fp32
+ * [num_blocks, block_size, Hkv] (4-byte aligned), as written by
+ * paged_kv_write_int8.  The codes enter the matrix products exactly (bf16);
+ * the K scales multiply the scores, the V scales the weights.
+ */
+int paged_attn_prefill_int8(const void *q, const int8_t *k_cache, const int8_t *v_cache,
+                            const float *k_scales, const float *v_scales,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            const int32_t *q_offsets, float scale, float *out,
+                            const pa_prefill_shape *shape, void *stream);
+
+/*
+ * The same chunked prefill over an FP8 E4M3 cache (uint8 codes, OCP E4M3 as
+ * torch's float8_e4m3fn, 8-byte aligned), as written by paged_kv_write_fp8.
+ * Every code's value is exact in bf16.
+ */
+int paged_attn_prefill_fp8(const void *q, const uint8_t *k_cache, const uint8_t *v_cache,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           const int32_t *q_offsets, float scale, float *out,
+                           const pa_prefill_shape *shape, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -91,12 +91,14 @@ def prefill_flops(context_lens: Iterable[int], n_q: Iterable[int], num_q_heads: 
 
 
 def prefill_bytes(context_lens: Iterable[int], n_q: Iterable[int], num_q_heads: int,
-                  num_kv_heads: int, head_dim: int, block_size: int) -> int:
+                  num_kv_heads: int, head_dim: int, block_size: int, kv_dtype: str = "bf16") -> int:
     """Bytes one chunked-prefill call must move at least once: each context's
-    K and V, the queries (bf16) and outputs (fp32), the table entries."""
+    K and V (2, or 1 byte a code, + two fp32 scales a token and kv head for
+    int8), the queries (bf16) and outputs (fp32), the table entries."""
     ctx = [int(c) for c in context_lens]
     nq = [int(n) for n in n_q]
-    kv = sum(ctx) * 2 * num_kv_heads * head_dim * 2
+    elem = 2 if kv_dtype == "bf16" else 1
+    kv = sum(ctx) * 2 * num_kv_heads * (head_dim * elem + (4 if kv_dtype == "int8" else 0))
     qo = sum(nq) * num_q_heads * head_dim * (2 + 4)
     tables = sum((c + block_size - 1) // block_size for c in ctx) * 4
     return kv + qo + tables + 8 * len(ctx) + 4

@@ -103,6 +103,12 @@ def load() -> ctypes.CDLL:
     lib.paged_attn_prefill.argtypes = [P, P, P, P, P, P, ctypes.c_float, P,
                                        ctypes.POINTER(PaPrefillShape), P]
     lib.paged_attn_prefill.restype = ctypes.c_int
+    lib.paged_attn_prefill_int8.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, P,
+                                            ctypes.POINTER(PaPrefillShape), P]
+    lib.paged_attn_prefill_int8.restype = ctypes.c_int
+    lib.paged_attn_prefill_fp8.argtypes = [P, P, P, P, P, P, ctypes.c_float, P,
+                                           ctypes.POINTER(PaPrefillShape), P]
+    lib.paged_attn_prefill_fp8.restype = ctypes.c_int
     lib.paged_attn_strerror.argtypes = [ctypes.c_int]
     lib.paged_attn_strerror.restype = ctypes.c_char_p
     lib.paged_attn_abi_version.argtypes = []
@@ -425,32 +431,83 @@ def evict_lowest_block(scores, block_tables, context_lens, evict_mask, evicted=N
     return evicted
 
 
-def prefill(q, k_cache, v_cache, block_tables, context_lens, q_offsets, scale: float,
-            max_q_len: int, out=None, stream=None) -> torch.Tensor:
-    """out fp32 [q_offsets[-1], Hq, D] = paged_attn_prefill(...): every sequence's
-    last (q_offsets[s+1] - q_offsets[s]) context tokens attend causally over
-    the paged bf16 cache.  max_q_len bounds the query tokens of any sequence."""
+def _prefill_shape(q, k_cache, v_cache, block_tables, context_lens, q_offsets, max_q_len,
+                   cache_dtypes, scales=()):
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                     ("block_tables", block_tables), ("context_lens", context_lens),
-                    ("q_offsets", q_offsets)):
+                    ("q_offsets", q_offsets)) + tuple(scales):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
-    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
-        raise TypeError("q and the cache must be bf16")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q must be bf16")
+    if k_cache.dtype not in cache_dtypes or v_cache.dtype not in cache_dtypes:
+        raise TypeError(f"the cache must be one of {cache_dtypes}")
     if k_cache.shape != v_cache.shape or q.shape[2] != k_cache.shape[3]:
         raise ValueError("q / cache shapes disagree")
     for name, t in (("block_tables", block_tables), ("context_lens", context_lens),
                     ("q_offsets", q_offsets)):
         if t.dtype != torch.int32:
             raise TypeError(f"{name} must be int32")
+    for name, t in scales:
+        if t.dtype != torch.float32 or tuple(t.shape) != tuple(k_cache.shape[:3]):
+            raise ValueError(f"{name} must be fp32 [NB, bs, Hkv]")
     S, MB = block_tables.shape
     if tuple(q_offsets.shape) != (S + 1,) or tuple(context_lens.shape) != (S,):
         raise ValueError("q_offsets must be [S + 1] and context_lens [S]")
     NB, bs, Hkv, D = k_cache.shape
-    sh = PaPrefillShape(S, q.shape[1], Hkv, D, bs, MB, NB, int(max_q_len))
+    return PaPrefillShape(S, q.shape[1], Hkv, D, bs, MB, NB, int(max_q_len))
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, q_offsets, scale: float,
+            max_q_len: int, out=None, stream=None) -> torch.Tensor:
+    """out fp32 [q_offsets[-1], Hq, D] = paged_attn_prefill(...): every sequence's
+    last (q_offsets[s+1] - q_offsets[s]) context tokens attend causally over
+    the paged bf16 cache.  max_q_len bounds the query tokens of any sequence."""
+    sh = _prefill_shape(q, k_cache, v_cache, block_tables, context_lens, q_offsets, max_q_len,
+                        (torch.bfloat16,))
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     _check(load().paged_attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                      _ptr(context_lens), _ptr(q_offsets), ctypes.c_float(scale),
                                      _ptr(out), ctypes.byref(sh), _stream_handle(stream)))
     return out
+
+
+def prefill_int8(q, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens, q_offsets,
+                 scale: float, max_q_len: int, out=None, stream=None) -> torch.Tensor:
+    """paged_attn_prefill_int8: prefill over an int8 cache with fp32 scales [NB, bs, Hkv]."""
+    sh = _prefill_shape(q, k_cache, v_cache, block_tables, context_lens, q_offsets, max_q_len,
+                        (torch.int8,), (("k_scales", k_scales), ("v_scales", v_scales)))
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _check(load().paged_attn_prefill_int8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
+                                          _ptr(v_scales), _ptr(block_tables), _ptr(context_lens),
+                                          _ptr(q_offsets), ctypes.c_float(scale), _ptr(out),
+                                          ctypes.byref(sh), _stream_handle(stream)))
+    return out
+
+
+def prefill_fp8(q, k_cache, v_cache, block_tables, context_lens, q_offsets, scale: float,
+                max_q_len: int, out=None, stream=None) -> torch.Tensor:
+    """paged_attn_prefill_fp8: prefill over an FP8 E4M3 cache (float8_e4m3fn or uint8 codes)."""
+    sh = _prefill_shape(q, k_cache, v_cache, block_tables, context_lens, q_offsets, max_q_len,
+                        FP8_DTYPES)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _check(load().paged_attn_prefill_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                         _ptr(context_lens), _ptr(q_offsets), ctypes.c_float(scale),
+                                         _ptr(out), ctypes.byref(sh), _stream_handle(stream)))
+    return out
+
+
+def prefill_views(views, q, q_offsets, max_q_len: int, out=None, stream=None, scale=None):
+    """Prefill of query tokens q [q_offsets[-1], Hq, D] over the per-layer
+    views of the input generator, whatever the cache kind."""
+    sc = views["scale"] if scale is None else scale
+    args = (views["block_tables"], views["context_lens"], q_offsets, sc, max_q_len)
+    if views["k_cache"].dtype in FP8_DTYPES:
+        return prefill_fp8(q, views["k_cache"], views["v_cache"], *args, out=out, stream=stream)
+    if "k_scales" in views:
+        return prefill_int8(q, views["k_cache"], views["v_cache"], views["k_scales"],
+                            views["v_scales"], *args, out=out, stream=stream)
+    return prefill(q, views["k_cache"], views["v_cache"], *args, out=out, stream=stream)

@@ -69,18 +69,20 @@ constexpr int kTileTokens = 32;            // tokens per staged tile and step (t
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRsrcFlags = 0x00020000;     // word 3 of a raw buffer resource on CDNA3/CDNA4
 constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0) alone (gfx9 field layout; + n: vmcnt(n))
-#ifndef PF_RING
-#define PF_RING 2
-#endif
-// K/V tiles in flight: K(i+kRing) and V(i+kRing-2) are loaded during
-// iteration i, which reads K(i+1) and V(i-1); ring slot = tile % kRing.
-constexpr int kRing = PF_RING;
-static_assert(kRing == 2 || kRing == 3, "ring depth");
+// Double-buffered K and V tiles: K(i+2) and V(i) are loaded during
+// iteration i, which reads K(i+1) and V(i-1); ring slot = tile % 2.
+constexpr int kRing = 2;
+
+// Element kinds of the cache read: bf16, int8 codes with an fp32 scale per
+// (slot, kv head), FP8 E4M3 codes.
+enum KvKind : int { kBf16 = 0, kInt8 = 1, kFp8 = 2 };
 
 struct PrefillParams {
     const uint16_t *q;
-    const uint16_t *k;
-    const uint16_t *v;
+    const void *k;
+    const void *v;
+    const float *k_scales;   // int8: [NB, bs, Hkv]
+    const float *v_scales;
     const int32_t *block_tables;
     const int32_t *context_lens;
     const int32_t *q_offsets;
@@ -128,7 +130,37 @@ __device__ __forceinline__ float group_max(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int D>
+// Bits of the bf16 pair (x, y), x in the low half, from two floats whose low
+// 16 bits are zero.
+__device__ __forceinline__ uint32_t pack_hi16(float x, float y) {
+    return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
+}
+// Signed byte b of w as float (exact).
+__device__ __forceinline__ float i8_at(uint32_t w, int b) { return (float)(int)(int8_t)((w >> (8 * b)) & 0xffu); }
+
+// Eight codes (8 bytes) of an int8 or FP8 E4M3 cache -> eight bf16 (16 B),
+// exactly: an int8 code has at most 8 significant bits, and every E4M3 value
+// (subnormals and NaN included) is a bf16 value (conversion scale 1).
+template <int KV>
+__device__ __forceinline__ u32x4_t codes_to_bf16x8(const u32x2_t w) {
+    u32x4_t r;
+    if constexpr (KV == kFp8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            r[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.0f, false));
+            r[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.0f, true));
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            r[2 * h] = pack_hi16(i8_at(w[h], 0), i8_at(w[h], 1));
+            r[2 * h + 1] = pack_hi16(i8_at(w[h], 2), i8_at(w[h], 3));
+        }
+    }
+    return r;
+}
+
+template <int D, int KV>
 __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(const PrefillParams p) {
     constexpr int kSteps = D / 32;    // QK k-steps of 32 dims
     constexpr int kDpl = D / 16;      // PV output blocks of 16 dims
@@ -144,6 +176,9 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     __shared__ __attribute__((aligned(1024))) char lds_k[kRing][TL::kBytes];
     __shared__ __attribute__((aligned(1024))) char lds_v[kRing][TL::kBytes];
     __shared__ int lds_pmax[kWaves];
+    // int8: the tiles' K and V scales (one per token of the kv head)
+    __shared__ __attribute__((aligned(16))) float lds_sc[KV == kInt8 ? 2 : 1][kRing][kTileTokens];
+    constexpr int kVsc = KV == kInt8 ? 1 : 0;
 
 #if PF_XCD_MAP
     // Workgroup L runs on XCD L % 8 (round-robin dispatch).  (sequence, kv
@@ -176,9 +211,10 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int ctx = p.context_lens[s];
     const int Hq = p.num_q_heads;
     const int Hkv = p.num_kv_heads;
-    const uint32_t rb32 = (uint32_t)(Hkv * D * 2);     // bytes of one token slot (all kv heads)
-    const char *kbase = (const char *)p.k + (int64_t)g * D * 2;
-    const char *vbase = (const char *)p.v + (int64_t)g * D * 2;
+    constexpr int kElem = KV == kBf16 ? 2 : 1;             // bytes per cache element
+    const uint32_t rb32 = (uint32_t)(Hkv * D * kElem);     // bytes of one token slot (all kv heads)
+    const char *kbase = (const char *)p.k + (int64_t)g * D * kElem;
+    const char *vbase = (const char *)p.v + (int64_t)g * D * kElem;
     const int32_t *table = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
     const int bs_log2 = p.log2_block_size;
     const int bs_mask = (1 << bs_log2) - 1;
@@ -236,9 +272,8 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     auto piece_half = [&](int j) __attribute__((always_inline)) {
         return piece_is_v(j) ? (piece_sub(j) * kRowsPerPiece) >> 4 : piece_sub(j) / (TL::kChunks / 4);
     };
-    // During iteration i, K pieces load tile i + kRing and V pieces tile
-    // i + kRing - 2.
-    auto piece_lead = [&](int j) __attribute__((always_inline)) { return piece_is_v(j) ? kRing - 2 : kRing; };
+    // During iteration i, K pieces load tile i + 2 and V pieces tile i.
+    auto piece_lead = [&](int j) __attribute__((always_inline)) { return piece_is_v(j) ? 0 : 2; };
     // Block-table window: lane l holds entry wbase + l, the next 64 entries
     // are loaded when the window slides (64 blocks ahead of their use), and a
     // tile's blocks are read from a lane (v_readlane), not from memory: a
@@ -250,14 +285,17 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     };
     int wbase = 0;
     int win = load_window(0), win_next = load_window(64);
-    auto phys_of = [&](int tile, int j) __attribute__((always_inline)) {
-        const int tb = tile * kTileTokens + 16 * piece_half(j);
+    // physical block of token tb (0 past the context end)
+    auto phys_at = [&](int tb) __attribute__((always_inline)) {
         if (tb >= ctx) return 0;
         const int o = (tb >> bs_log2) - wbase;            // 0 <= o < 128 (see the slide below)
         int b;
         if (o < 64) b = __builtin_amdgcn_readlane(win, o);
         else b = __builtin_amdgcn_readlane(win_next, o - 64);
         return b;
+    };
+    auto phys_of = [&](int tile, int j) __attribute__((always_inline)) {
+        return phys_at(tile * kTileTokens + 16 * piece_half(j));
     };
     auto issue = [&](int tile, int j, int phys) __attribute__((always_inline)) {
         const int sub = piece_sub(j);
@@ -300,11 +338,85 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                      : "memory");
     };
 
+    // ---- int8 / FP8 tiles come through registers: each thread loads 8 codes
+    // (8 B) of one token of a K or V tile, load number tid + jj * threads
+    // (K loads first; a wave's 64 loads are whole tokens of one 16-token
+    // half), one iteration ahead, and at the end of the next iteration
+    // writes them as bf16 into the same LDS layouts (int8 scales go to
+    // lds_sc), so the loads have a whole iteration to land.
+    constexpr int kQLoads = D / 64;                      // per thread per iteration (K + V)
+    constexpr int kCodeChunks = D / 8;                   // 8-code chunks per token
+    u32x2_t st_codes[kQLoads];
+    float st_scale[kQLoads];
+    // keys and values read: the workgroup's tiles, within the context
+    const int kv_end = min(ctx, n_tiles * kTileTokens);
+    // K or V: wave-uniform (4 D loads per tile and kind, a multiple of 64)
+    auto qload_is_v = [&](int jj) __attribute__((always_inline)) {
+        return (wave * 64 + jj * kThreads) >= 4 * D;
+    };
+    // V: a wave's 64 loads are 64 / kCodeChunks whole tokens (one LDS row
+    // each); K: 16 tokens of one half by 4 chunks, so each 16 lanes store
+    // one 256 B run of the chunk-major layout (whole tokens there would put
+    // a token's chunks, 256 B apart, in the same banks).
+    constexpr int kChunkGroups = kCodeChunks / 4;        // K: 4-chunk groups per half
+    auto qload_wpart = [&](int jj) __attribute__((always_inline)) {   // wave-uniform
+        return ((wave * 64 + jj * kThreads) % (4 * D)) / 64;
+    };
+    auto qload_token = [&](int jj) __attribute__((always_inline)) {
+        if (qload_is_v(jj)) return (((int)threadIdx.x + jj * kThreads) % (4 * D)) / kCodeChunks;
+        return 16 * (qload_wpart(jj) / kChunkGroups) + (lane & 15);
+    };
+    auto qload_chunk = [&](int jj) __attribute__((always_inline)) {
+        if (qload_is_v(jj)) return (((int)threadIdx.x + jj * kThreads) % (4 * D)) % kCodeChunks;
+        return 4 * (qload_wpart(jj) % kChunkGroups) + (lane >> 4);
+    };
+    // the 16-token half of load jj, wave-uniform
+    auto qload_half = [&](int jj) __attribute__((always_inline)) {
+        if (qload_is_v(jj)) return (qload_wpart(jj) * 64 / kCodeChunks) >> 4;
+        return qload_wpart(jj) / kChunkGroups;
+    };
+    auto make_rsrc = [&](const void *base, int range) __attribute__((always_inline)) {
+        const uint64_t addr = (uint64_t)(uintptr_t)base;
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)(((uint64_t)hi << 32) | lo), 0,
+                                                 __builtin_amdgcn_readfirstlane(range), kRsrcFlags);
+    };
+    auto qissue = [&](int tile, int jj, int phys) __attribute__((always_inline)) {
+        const bool is_v = qload_is_v(jj);
+        const int tb = tile * kTileTokens + 16 * qload_half(jj);
+        const int rows = min(16, max(0, kv_end - tb));   // none past the tiles or the context is read
+        const int64_t slot0 = ((int64_t)phys << bs_log2) + (tb & bs_mask);
+        const int r16 = qload_token(jj) & 15;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc((is_v ? vbase : kbase) + slot0 * rb32, rows * (int)rb32);
+        st_codes[jj] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+            rs, (int)((uint32_t)r16 * rb32 + (uint32_t)(qload_chunk(jj) * 8)), 0, 0));
+        if constexpr (KV == kInt8) {
+            // every lane of the token loads its scale (one dword line per wave)
+            const float *sb = (is_v ? p.v_scales : p.k_scales) + slot0 * Hkv + g;
+            const __amdgpu_buffer_rsrc_t ss = make_rsrc(sb, rows * Hkv * 4);
+            st_scale[jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ss, r16 * Hkv * 4, 0, 0));
+        }
+    };
+    // tile `tile` of load jj; past the tiles the codes read as 0
+    auto qissue_tile = [&](int tile, int jj) __attribute__((always_inline)) {
+        qissue(tile, jj, phys_at(tile * kTileTokens + 16 * qload_half(jj)));
+    };
+    auto qstore = [&](int jj, int slot) __attribute__((always_inline)) {
+        const int tok = qload_token(jj), ch = qload_chunk(jj);
+        const u32x4_t b = codes_to_bf16x8<KV>(st_codes[jj]);
+        if (qload_is_v(jj)) *(u32x4_t *)(lds_v[slot] + TL::v_offset(tok, ch)) = b;
+        else *(u32x4_t *)(lds_k[slot] + TL::k_offset(tok, ch)) = b;
+        if constexpr (KV == kInt8)
+            if (ch == 0) lds_sc[qload_is_v(jj) ? 1 : 0][slot][tok] = st_scale[jj];
+    };
+
     // ---- S^T = K Q^T of one tile from LDS: lane l gets column (row) l%16 of
     // block cb and tokens 16 bb + 4 (l/16) + i.  The k-step loop is outermost,
-    // so the 2 kNc accumulation chains interleave.
+    // so the 2 kNc accumulation chains interleave.  int8: times the tokens' K
+    // scales (the K tile holds the codes).
     typedef f32x4_t Scores[2][kNc];
-    auto scores = [&](const char *kl, Scores &S) __attribute__((always_inline)) {
+    auto scores = [&](const char *kl, const float *ksc, Scores &S) __attribute__((always_inline)) {
         bf16x8_t kop[2][kSteps];
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
@@ -319,6 +431,14 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                 for (int cb = 0; cb < kNc; ++cb)
                     S[bb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         kop[bb][st], qop[cb][st], st == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : S[bb][cb], 0, 0, 0);
+        if constexpr (KV == kInt8) {
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const f32x4_t ks = *(const f32x4_t *)(ksc + 16 * bb + 4 * hgrp);
+#pragma unroll
+                for (int cb = 0; cb < kNc; ++cb) S[bb][cb] *= ks;
+            }
+        }
     };
 
     f32x4_t acc[kDpl][kNc];
@@ -341,6 +461,21 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // rescaled.  Returns whether any row of the wave moved; alpha[cb] is then
     // log2 of that row's rescale factor (0 where it did not move).
     typedef bf16x8_t Weights[kNc];
+    // the 8 weights as a bf16 high part plus a bf16 remainder, both rounded
+    // to nearest even: hi + lo is the fp32 weight to 2^-17
+    auto split_weights = [&](const float (&pr)[8], bf16x8_t &hi8, bf16x8_t &lo8) __attribute__((always_inline)) {
+        u32x4_t pw, pl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const f32x2_t w2 = f32x2_t{pr[2 * e], pr[2 * e + 1]};
+            const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, bf16x2_t));
+            const f32x2_t r2 = w2 - f32x2_t{__uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+            pw[e] = hi;
+            pl[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2_t));
+        }
+        hi8 = __builtin_bit_cast(bf16x8_t, pw);
+        lo8 = __builtin_bit_cast(bf16x8_t, pl);
+    };
     auto softmax = [&](const int t, const Scores &S, Weights &Phi, Weights &Plo, float (&alpha)[kNc],
                        auto masked) __attribute__((always_inline)) {
         constexpr bool kMasked = decltype(masked)::value;
@@ -381,17 +516,13 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                 psum += pr[e];
             }
             l_run[cb] += psum;
-            u32x4_t pw, pl;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const f32x2_t w2 = f32x2_t{pr[2 * e], pr[2 * e + 1]};
-                const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(w2, bf16x2_t));
-                const f32x2_t r2 = w2 - f32x2_t{__uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
-                pw[e] = hi;
-                pl[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2_t));
+            if constexpr (KV == kInt8) {
+                // fp32 weights, split once the V scales are in LDS (next step)
+                Phi[cb] = __builtin_bit_cast(bf16x8_t, f32x4_t{pr[0], pr[1], pr[2], pr[3]});
+                Plo[cb] = __builtin_bit_cast(bf16x8_t, f32x4_t{pr[4], pr[5], pr[6], pr[7]});
+            } else {
+                split_weights(pr, Phi[cb], Plo[cb]);
             }
-            Phi[cb] = __builtin_bit_cast(bf16x8_t, pw);
-            Plo[cb] = __builtin_bit_cast(bf16x8_t, pl);
         }
         return grow;
     };
@@ -413,7 +544,27 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // weights' token order.
     const int tr_tok = 4 * hgrp + (l16 >> 2);
     const int tr_lane = tr_tok * TL::kRowBytes + 8 * (l16 & 1);   // + chunk position
-    auto weighted_values = [&](const char *vl, const Weights &Phi, const Weights &Plo) __attribute__((always_inline)) {
+    auto weighted_values = [&](const char *vl, const float *vsc, const Weights &Pin_hi, const Weights &Pin_lo)
+                               __attribute__((always_inline)) {
+        Weights Phi, Plo;
+        if constexpr (KV == kInt8) {
+            // the weights times their tokens' V scales (token order e -> 16 (e/4) + 4 (l/16) + e%4)
+            const f32x4_t vs0 = *(const f32x4_t *)(vsc + 4 * hgrp);
+            const f32x4_t vs1 = *(const f32x4_t *)(vsc + 16 + 4 * hgrp);
+#pragma unroll
+            for (int cb = 0; cb < kNc; ++cb) {
+                const f32x4_t w0 = __builtin_bit_cast(f32x4_t, Pin_hi[cb]) * vs0;
+                const f32x4_t w1 = __builtin_bit_cast(f32x4_t, Pin_lo[cb]) * vs1;
+                const float pr[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+                split_weights(pr, Phi[cb], Plo[cb]);
+            }
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < kNc; ++cb) {
+                Phi[cb] = Pin_hi[cb];
+                Plo[cb] = Pin_lo[cb];
+            }
+        }
 #pragma unroll
         for (int j = 0; j < kDpl; ++j) {
             const int chunk = 2 * j + ((l16 >> 1) & 1);
@@ -434,28 +585,32 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         }
     };
 
-    // ---- prologue: K of tiles 0 and 1 in LDS, then the scores of tile 0;
-    // the tiles iteration 0 does not load (K(2) and V(0) for a 3-deep ring)
-    // are issued meanwhile.
-#pragma unroll
-    for (int j = 0; j < kPiecesPerWave; ++j) {
-        if (!piece_ok(j) || piece_is_v(j)) continue;
-        issue(0, j, phys_of(0, j));
-        if (n_tiles > 1) issue(1, j, phys_of(1, j));
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if constexpr (kRing == 3) {
+    // ---- prologue: K of tiles 0 and 1 in LDS, then the scores of tile 0.
+    if constexpr (KV == kBf16) {
 #pragma unroll
         for (int j = 0; j < kPiecesPerWave; ++j) {
-            if (!piece_ok(j)) continue;
-            if (piece_is_v(j)) issue(0, j, phys_of(0, j));
-            else if (n_tiles > 2) issue(2, j, phys_of(2, j));
+            if (!piece_ok(j) || piece_is_v(j)) continue;
+            issue(0, j, phys_of(0, j));
+            if (n_tiles > 1) issue(1, j, phys_of(1, j));
         }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    } else {
+        for (int t = 0; t < min(2, n_tiles); ++t) {
+#pragma unroll
+            for (int jj = 0; jj < kQLoads; ++jj) {
+                if (qload_is_v(jj)) continue;
+                qissue_tile(t, jj);
+                qstore(jj, t % kRing);
+            }
+        }
+        // in flight into iteration 0: K(2) and V(0)
+#pragma unroll
+        for (int jj = 0; jj < kQLoads; ++jj) qissue_tile(qload_is_v(jj) ? 0 : 2, jj);
     }
+    __syncthreads();
     Scores S;                  // scores of the tile whose softmax is next
     Weights Phi, Plo;          // weights of the tile whose weighted sum is next
-    if (wave_live) scores(lds_k[0], S);
+    if (wave_live) scores(lds_k[0], lds_sc[0][0], S);
     __syncthreads();           // K(0) read by every wave before iteration 0 loads over it
 
     // ---- iteration i (K(i+1) and V(i-1) in LDS; K(i+2) and V(i) loading):
@@ -482,44 +637,44 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         if (pend_grow) rescale(pend_alpha);
         pend_grow = false;
         if (do_sm) pend_grow = softmax(i, Sc, Pn_hi, Pn_lo, pend_alpha, masked);
-        if (do_pv) weighted_values(lds_v[(i - 1) % kRing], Ph, Pl);
-        if (do_qk) scores(lds_k[(i + 1) % kRing], Sn);
+        if (do_pv) weighted_values(lds_v[(i - 1) % kRing], lds_sc[kVsc][(i - 1) % kRing], Ph, Pl);
+        if (do_qk) scores(lds_k[(i + 1) % kRing], lds_sc[0][(i + 1) % kRing], Sn);
     };
-    // Returns how many loads the wave issued (wave-uniform), or -1 when the
-    // table window slid: that iteration ends with vmcnt(0), so the window's
-    // load is known complete before any lookup reads it.
     auto loads = [&](const int i) __attribute__((always_inline)) {
-        // The oldest block iteration i loads is V(i+kRing-2)'s first; once
-        // it leaves the window, slide (the newest, K(i+kRing)'s last, is at
-        // most 80 / block_size blocks further, so a slide never skips a
-        // window).
-        bool slid = false;
-        if ((((i + kRing - 2) * kTileTokens) >> bs_log2) >= wbase + 64) {
+        // The oldest block iteration i loads is V(i)'s first (int8 / FP8:
+        // V(i+1)'s, one iteration ahead); once it leaves the window, slide
+        // (the newest, K(i+2)'s last (K(i+3)'s), is at most 80 (96) tokens
+        // further, under 64 blocks, so a slide never skips a window).
+        if ((((i + (KV == kBf16 ? 0 : 1)) * kTileTokens) >> bs_log2) >= wbase + 64) {
             wbase += 64;
             win = win_next;
             win_next = load_window(wbase + 64);
-            slid = true;
         }
-        int n = 0;
+        if constexpr (KV == kBf16) {
 #pragma unroll
-        for (int j = 0; j < kPiecesPerWave; ++j) {
-            if (!piece_ok(j)) continue;
-            const int tile = i + piece_lead(j);
-            if (tile < n_tiles) {
-                issue(tile, j, phys_of(tile, j));
-                ++n;
+            for (int j = 0; j < kPiecesPerWave; ++j) {
+                if (!piece_ok(j)) continue;
+                const int tile = i + piece_lead(j);
+                if (tile < n_tiles) issue(tile, j, phys_of(tile, j));
             }
         }
-        return slid ? -1 : n;
+        return i;
     };
-    // End of an iteration: the loads of earlier iterations have landed
-    // (those of this one, n, may still fly: their tiles are read two
-    // iterations on), then the barrier.  Loads return in order.
-    auto tile_done = [&](const int n) __attribute__((always_inline)) {
-        static_assert(kPiecesPerWave <= 2, "vmcnt cases");
-        if (kRing == 2 || n <= 0) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        else if (n == 1) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 + 1);
-        else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 + 2);
+    // End of iteration i: this wave's loads have landed (int8 / FP8: K(i+2)
+    // and V(i), loaded during the last iteration, written to LDS as bf16 --
+    // into the slots no wave reads this iteration -- and K(i+3), V(i+1)
+    // issued into the same registers), then the barrier.
+    auto tile_done = [&](const int i, auto more) __attribute__((always_inline)) {
+        if constexpr (KV == kBf16) {
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < kQLoads; ++jj) qstore(jj, i % kRing);
+            if (decltype(more)::value || i + 1 < n_tiles) {
+#pragma unroll
+                for (int jj = 0; jj < kQLoads; ++jj) qissue_tile(i + (qload_is_v(jj) ? 1 : 3), jj);
+            }
+        }
         __syncthreads();
     };
     // Three loops with one barrier per iteration each, n_tiles in all: the
@@ -532,17 +687,17 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     Weights Phi2, Plo2;
     int nl = loads(0);
     if (wave_live) step(0, S, Phi, Plo, S2, Phi2, Plo2, std::true_type{}, std::false_type{});
-    tile_done(nl);
+    tile_done(nl, std::false_type{});
     // The state alternates between the two register sets, so the middle
     // tiles run in pairs without copies; after the pairs it is in (S2, P2).
     int i = 1;
     for (; i + 1 < full_end; i += 2) {
         nl = loads(i);
         step(i, S2, Phi2, Plo2, S, Phi, Plo, std::false_type{}, std::true_type{});
-        tile_done(nl);
+        tile_done(nl, std::true_type{});       // i + 2 < full_end < n_tiles
         nl = loads(i + 1);
         step(i + 1, S, Phi, Plo, S2, Phi2, Plo2, std::false_type{}, std::true_type{});
-        tile_done(nl);
+        tile_done(nl, std::true_type{});
     }
     // the general iterations (an odd middle tile, the diagonal tiles, the
     // last weighted sum, then loads only), each followed by a copy back into
@@ -561,12 +716,12 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                 for (int bb = 0; bb < 2; ++bb) S2[bb][cb] = Sn[bb][cb];
             }
         }
-        tile_done(nl);
+        tile_done(nl, std::false_type{});
     }
     // the last tile's weighted sum (V(n_tiles-1) landed in the last iteration)
     if (wave_live && my_steps == n_tiles) {
         if (pend_grow) rescale(pend_alpha);
-        weighted_values(lds_v[(n_tiles - 1) % kRing], Phi2, Plo2);
+        weighted_values(lds_v[(n_tiles - 1) % kRing], lds_sc[kVsc][(n_tiles - 1) % kRing], Phi2, Plo2);
     }
 
     if (!wave_live) return;
@@ -596,12 +751,10 @@ int ilog2(int x) {
 }
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
-}  // namespace
-
-extern "C" int paged_attn_prefill(const void *q, const void *k_cache, const void *v_cache,
-                                  const int32_t *block_tables, const int32_t *context_lens,
-                                  const int32_t *q_offsets, float scale, float *out,
-                                  const pa_prefill_shape *sh, void *stream) {
+int prefill_common(int kind, const void *q, const void *k_cache, const void *v_cache,
+                   const float *k_scales, const float *v_scales, const int32_t *block_tables,
+                   const int32_t *context_lens, const int32_t *q_offsets, float scale, float *out,
+                   const pa_prefill_shape *sh, void *stream) {
     if (!sh) return PA_ERR_NULL;
     if (sh->num_seqs < 0 || sh->num_q_heads < 1 || sh->num_kv_heads < 1 ||
         sh->max_blocks_per_seq < 1 || sh->num_blocks < 1 || sh->max_q_len < 1)
@@ -620,12 +773,18 @@ extern "C" int paged_attn_prefill(const void *q, const void *k_cache, const void
     if (sh->num_seqs == 0) return PA_OK;
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !q_offsets || !out)
         return PA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    if (kind == kInt8 && (!k_scales || !v_scales)) return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out)) return PA_ERR_ALIGNMENT;
+    if (kind == kBf16 ? (!aligned16(k_cache) || !aligned16(v_cache))
+                      : (((uintptr_t)k_cache | (uintptr_t)v_cache) & 7u) != 0)
         return PA_ERR_ALIGNMENT;
+    if (kind == kInt8 && (((uintptr_t)k_scales | (uintptr_t)v_scales) & 3u) != 0) return PA_ERR_ALIGNMENT;
     PrefillParams p;
     p.q = (const uint16_t *)q;
-    p.k = (const uint16_t *)k_cache;
-    p.v = (const uint16_t *)v_cache;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.k_scales = k_scales;
+    p.v_scales = v_scales;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
     p.q_offsets = q_offsets;
@@ -649,7 +808,41 @@ extern "C" int paged_attn_prefill(const void *q, const void *k_cache, const void
 #endif
     const dim3 block(kThreads);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (sh->head_dim == 128) hipLaunchKernelGGL(pa_prefill_kernel<128>, grid, block, 0, st, p);
-    else hipLaunchKernelGGL(pa_prefill_kernel<64>, grid, block, 0, st, p);
+    if (sh->head_dim == 128) {
+        if (kind == kInt8) hipLaunchKernelGGL((pa_prefill_kernel<128, kInt8>), grid, block, 0, st, p);
+        else if (kind == kFp8) hipLaunchKernelGGL((pa_prefill_kernel<128, kFp8>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((pa_prefill_kernel<128, kBf16>), grid, block, 0, st, p);
+    } else {
+        if (kind == kInt8) hipLaunchKernelGGL((pa_prefill_kernel<64, kInt8>), grid, block, 0, st, p);
+        else if (kind == kFp8) hipLaunchKernelGGL((pa_prefill_kernel<64, kFp8>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((pa_prefill_kernel<64, kBf16>), grid, block, 0, st, p);
+    }
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int paged_attn_prefill(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  const int32_t *q_offsets, float scale, float *out,
+                                  const pa_prefill_shape *sh, void *stream) {
+    return prefill_common(kBf16, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,
+                          q_offsets, scale, out, sh, stream);
+}
+
+extern "C" int paged_attn_prefill_int8(const void *q, const int8_t *k_cache, const int8_t *v_cache,
+                                       const float *k_scales, const float *v_scales,
+                                       const int32_t *block_tables, const int32_t *context_lens,
+                                       const int32_t *q_offsets, float scale, float *out,
+                                       const pa_prefill_shape *sh, void *stream) {
+    return prefill_common(kInt8, q, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens,
+                          q_offsets, scale, out, sh, stream);
+}
+
+extern "C" int paged_attn_prefill_fp8(const void *q, const uint8_t *k_cache, const uint8_t *v_cache,
+                                      const int32_t *block_tables, const int32_t *context_lens,
+                                      const int32_t *q_offsets, float scale, float *out,
+                                      const pa_prefill_shape *sh, void *stream) {
+    return prefill_common(kFp8, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,
+                          q_offsets, scale, out, sh, stream);
 }

@@ -313,6 +313,7 @@ class PrefillWorkload:
     head_dim: int
     block_size: int
     seed: int
+    kv_dtype: str = "bf16"
 
 
 PREFILL_WORKLOADS = {
@@ -321,6 +322,13 @@ PREFILL_WORKLOADS = {
     # attends over 512 (k + 1) tokens.
     "prefill_llama3_8b": PrefillWorkload("prefill_llama3_8b", tuple(512 * (k + 1) for k in range(8)),
                                          (512,) * 8, 32, 8, 128, 16, seed=10),
+    # The same batch over int8 (per-token scales) and FP8 E4M3 caches.
+    "prefill_int8_llama3_8b": PrefillWorkload("prefill_int8_llama3_8b",
+                                              tuple(512 * (k + 1) for k in range(8)), (512,) * 8,
+                                              32, 8, 128, 16, seed=11, kv_dtype="int8"),
+    "prefill_fp8_llama3_8b": PrefillWorkload("prefill_fp8_llama3_8b",
+                                             tuple(512 * (k + 1) for k in range(8)), (512,) * 8,
+                                             32, 8, 128, 16, seed=12, kv_dtype="fp8"),
 }
 
 
@@ -329,7 +337,7 @@ def make_prefill_inputs(pw: PrefillWorkload, device="cpu") -> dict:
     the chunk queries q bf16 [sum n_q, Hq, d] (fp32 N(0,1) rounded) and
     q_offsets int32 [S + 1]."""
     wl = Workload(pw.name, len(pw.ctx), pw.num_q_heads, pw.num_kv_heads, pw.head_dim,
-                  pw.block_size, seed=pw.seed, ctx_fixed=pw.ctx)
+                  pw.block_size, seed=pw.seed, ctx_fixed=pw.ctx, kv_dtype=pw.kv_dtype)
     inp = make_inputs(wl, device)
     views = layer_views(inp, 0)
     nq = torch.tensor((0,) + tuple(pw.n_q), dtype=torch.int64)

@@ -126,3 +126,22 @@ def sdpa_reference(views, bs) -> np.ndarray:
             scale=float(np.float32(views["scale"])), enable_gqa=True)
         out[s] = o[0, :, 0, :].numpy()
     return out
+
+
+def prefill_oracle(views, q, q_offsets, scale=None):
+    """fp64 oracle chunked prefill for the cache kind of the views (any device)."""
+    qb = I.bf16_bits(q)
+    bt = views["block_tables"].cpu().numpy()
+    cl = views["context_lens"].cpu().numpy()
+    qo = np.asarray(q_offsets.cpu().numpy() if isinstance(q_offsets, torch.Tensor) else q_offsets,
+                    dtype=np.int32)
+    sc = views["scale"] if scale is None else scale
+    if "k_scales" in views:
+        return oracle.paged_prefill_int8(qb, views["k_cache"].cpu().numpy(), views["v_cache"].cpu().numpy(),
+                                         views["k_scales"].cpu().numpy(), views["v_scales"].cpu().numpy(),
+                                         bt, cl, qo, sc)
+    if views["k_cache"].dtype == torch.float8_e4m3fn:
+        return oracle.paged_prefill_fp8(qb, fp8_codes(views["k_cache"]), fp8_codes(views["v_cache"]),
+                                        bt, cl, qo, sc)
+    return oracle.paged_prefill_bf16(qb, I.bf16_bits(views["k_cache"]), I.bf16_bits(views["v_cache"]),
+                                     bt, cl, qo, sc)

@@ -10,7 +10,8 @@ DECLARED = {"paged_attn_plan", "paged_attn_workspace_bytes", "paged_attn_decode"
             "paged_attn_decode_int8", "paged_attn_strerror", "paged_attn_abi_version",
             "paged_kv_write", "paged_kv_write_int8", "paged_attn_decode_fp8", "paged_kv_write_fp8",
             "paged_kv_token_scores", "paged_kv_token_scores_int8", "paged_kv_token_scores_fp8",
-            "paged_kv_evict_lowest_block", "paged_attn_prefill"}
+            "paged_kv_evict_lowest_block", "paged_attn_prefill", "paged_attn_prefill_int8",
+            "paged_attn_prefill_fp8"}
 
 
 def lib():
@@ -313,3 +314,26 @@ def test_prefill_null_alignment_and_empty():
     for name in ("q", "k", "v", "out"):
         assert pcall(pshape(), **{name: ctypes.c_void_p(0x100008)}) == B.PA_ERR_ALIGNMENT, name
     assert pcall(pshape(num_seqs=0), q=None, k=None) == B.PA_OK
+
+
+def pcall_q(kind, sh, q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, cl=FAKE, qo=FAKE, out=FAKE):
+    if kind == "int8":
+        return lib().paged_attn_prefill_int8(q, k, v, ks, vs, bt, cl, qo, ctypes.c_float(0.1), out,
+                                             ctypes.byref(sh), None)
+    return lib().paged_attn_prefill_fp8(q, k, v, bt, cl, qo, ctypes.c_float(0.1), out,
+                                        ctypes.byref(sh), None)
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+def test_quantized_prefill_host_checks(kind):
+    assert pcall_q(kind, pshape(head_dim=96)) == B.PA_ERR_UNSUPPORTED
+    assert pcall_q(kind, pshape(num_q_heads=6, num_kv_heads=4)) == B.PA_ERR_SHAPE
+    names = ("q", "k", "v", "bt", "cl", "qo", "out") + (("ks", "vs") if kind == "int8" else ())
+    for name in names:
+        assert pcall_q(kind, pshape(), **{name: ctypes.c_void_p(0)}) == B.PA_ERR_NULL, name
+    # the codes need 8-byte alignment only; q and out 16 bytes; int8 scales 4 bytes
+    assert pcall_q(kind, pshape(), k=ctypes.c_void_p(0x100004)) == B.PA_ERR_ALIGNMENT
+    assert pcall_q(kind, pshape(), q=ctypes.c_void_p(0x100008)) == B.PA_ERR_ALIGNMENT
+    if kind == "int8":
+        assert pcall_q(kind, pshape(), vs=ctypes.c_void_p(0x100002)) == B.PA_ERR_ALIGNMENT
+    assert pcall_q(kind, pshape(num_seqs=0), q=None, k=None) == B.PA_OK

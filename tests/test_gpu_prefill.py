@@ -160,3 +160,87 @@ def test_full_size_prefill_workload_sampled(seqs):
                                       I.bf16_bits(sub["v_cache"]), sub["block_tables"].numpy(),
                                       sub["context_lens"].numpy(), [0, q_s.shape[0]], sub["scale"])
         assert_parity(out[rows], r, f"prefill seq {s}")
+
+
+
+# ---- int8 (per-token scales) and FP8 E4M3 caches: the same bar against the
+# oracle over the codes' exact values.
+
+def make_kind(ctx, nq, Hq, Hkv, D, bs, seed, kind):
+    NB = sum((c + bs - 1) // bs for c in ctx) + 3
+    _, v = C.make_case(len(ctx), Hq, Hkv, D, bs, ctx=ctx, NB=NB, seed=seed, device=DEV,
+                       kv_dtype=kind)
+    q_off = torch.tensor(np.concatenate([[0], np.cumsum(nq)]), dtype=torch.int32)
+    gen = torch.Generator(device=DEV).manual_seed(seed + 1)
+    q = torch.randn(int(q_off[-1]), Hq, D, generator=gen, device=DEV).to(torch.bfloat16)
+    return v, q, q_off
+
+
+def run_kind(v, q, q_off, max_q=None):
+    out = B.prefill_views(v, q, q_off.to(DEV), max_q or int((q_off[1:] - q_off[:-1]).max()))
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (12, 2), (32, 8)])
+@pytest.mark.parametrize("bs", [16, 256])
+def test_quantized_prefill_chunk_shapes(kind, D, Hq, Hkv, bs):
+    note(f"prefill {kind} D={D} Hq={Hq} Hkv={Hkv} bs={bs}")
+    ctx = (1, 17, 100, 300, 513, 64)
+    nq = [1, 17, 33, 128, 200, 1]
+    v, q, q_off = make_kind(ctx, nq, Hq, Hkv, D, bs, 520 + D + Hq + bs, kind)
+    assert_parity(run_kind(v, q, q_off), C.prefill_oracle(v, q, q_off), f"prefill {kind}")
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+def test_quantized_prefill_single_queries_match_decode(kind):
+    note(f"prefill {kind} n_q=1 vs decode")
+    ctx = (1, 17, 100, 250, 4000)
+    v, q, q_off = make_kind(ctx, [1] * 5, 32, 8, 128, 16, 521, kind)
+    got = run_kind(v, q, q_off)
+    r = C.prefill_oracle(v, q, q_off)
+    assert_parity(got, r, f"prefill {kind} as decode")
+    dec = B.decode_views(dict(v, q=q))
+    torch.cuda.synchronize()
+    assert_parity(dec, r, f"decode {kind}")
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+def test_quantized_prefill_long_context_and_loose_max_q_len(kind):
+    note(f"prefill {kind} long context")
+    ctx = (30000, 1500, 7)
+    v, q, q_off = make_kind(ctx, [96, 1, 7], 8, 2, 128, 16, 522, kind)
+    a = run_kind(v, q, q_off)
+    assert_parity(a, C.prefill_oracle(v, q, q_off), f"long context {kind}")
+    a = a.clone()
+    assert torch.equal(run_kind(v, q, q_off, max_q=4096).view(torch.int32), a.view(torch.int32))
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+def test_quantized_prefill_poisoned_padding_bit_identical(kind):
+    note(f"prefill {kind} poison")
+    for bs in (16, 256):
+        ctx = (17, 300, 513)
+        v, q, q_off = make_kind(ctx, [17, 40, 100], 8, 2, 128, bs, 523, kind)
+        clean = run_kind(v, q, q_off).clone()
+        C.poison(v, bs, table_pad=-1)
+        assert torch.equal(run_kind(v, q, q_off).view(torch.int32), clean.view(torch.int32)), bs
+
+
+@pytest.mark.parametrize("wl,seqs", [("prefill_int8_llama3_8b", (0, 7)), ("prefill_fp8_llama3_8b", (0, 7))])
+def test_full_size_quantized_prefill_workload_sampled(wl, seqs):
+    # The bench's workloads at full size, same launch as the bench; the oracle
+    # checks the whole chunk of the sampled sequences.
+    note(f"full-size {wl} {seqs}")
+    pw = I.PREFILL_WORKLOADS[wl]
+    inp = I.make_prefill_inputs(pw, DEV)
+    out = B.prefill_views(inp, inp["q"], inp["q_offsets"], inp["max_q_len"])
+    torch.cuda.synchronize()
+    qo = inp["q_offsets"].cpu()
+    for s in seqs:
+        sub = I.select_sequences(inp, [s], pw.block_size)
+        rows = slice(int(qo[s]), int(qo[s + 1]))
+        r = C.prefill_oracle(sub, inp["q"][rows].cpu(), [0, int(qo[s + 1] - qo[s])])
+        assert_parity(out[rows], r, f"{wl} seq {s}")
