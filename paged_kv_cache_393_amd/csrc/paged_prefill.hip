@@ -9,7 +9,7 @@
 // Unlike decode, this is a dense contraction: a 512-token chunk of a
 // Llama-3-8B layer does 4 d Hq flops per (query, context token) pair, far
 // above the HBM ridge, so the work is laid out for the matrix cores
-// (v_mfma_f32_16x16x32_bf16: A 16x32, B 32x16, lane l holding row / column l%16
+// (v_mfma_f32_16x16x32_bf16 / _f16: A 16x32, B 32x16, lane l holding row / column l%16
 // and k-elements 8*(l/16) .. +7; C lane l holding column l%16, rows 4*(l/16)+i).
 //
 // A "row" is a (query token, query head of the kv head's group) pair.  One
@@ -28,7 +28,11 @@
 //     through LDS transpose reads.  The weights enter as a bf16 high part
 //     plus a bf16 remainder (two products), exact to 2^-17 relative: a single
 //     bf16 rounding (2^-9) of the weights alone exceeds a 2e-3 absolute bar
-//     on short contexts.
+//     on short contexts.  FP8 caches instead stage V as fp16 (every E4M3
+//     value is one) and take the weights as fp16 (one product, 2^-11
+//     relative rounding), times 2^7 -- the row sums alike -- so that small
+//     weights stay out of fp16's subnormal range.  (A bf16 V does not fit
+//     fp16 in general, and int8 V scales can push the weights past it.)
 // Software pipeline: on this chip a wave co-issues vector instructions with
 // its own in-flight matrix instructions (not with another wave's), so one
 // iteration runs the softmax of tile i between the MFMAs of the scores of
@@ -51,6 +55,8 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 #ifndef PF_WAVES_PER_EU
@@ -160,6 +166,18 @@ __device__ __forceinline__ u32x4_t codes_to_bf16x8(const u32x2_t w) {
     return r;
 }
 
+// Eight FP8 E4M3 codes -> eight fp16 values, exactly (every E4M3 value,
+// subnormals and NaN included, is an fp16 value; conversion scale 1).
+__device__ __forceinline__ u32x4_t fp8x8_to_f16x8(const u32x2_t w) {
+    u32x4_t r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        r[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[h], 1.0f, false));
+        r[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[h], 1.0f, true));
+    }
+    return r;
+}
+
 template <int D, int KV>
 __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(const PrefillParams p) {
     constexpr int kSteps = D / 32;    // QK k-steps of 32 dims
@@ -173,8 +191,11 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     constexpr int kPiecesPerWave = (2 * kPieces + kWaves - 1) / kWaves;
     static_assert(TL::kBytes % 1024 == 0 && 16 % kRowsPerPiece == 0 && TL::kChunks % 4 == 0,
                   "pieces within one half");
+    // FP8: the weighted sum on fp16 (V tile as fp16), the weights times 2^kPBias
+    constexpr bool kF16 = KV == kFp8;
+    constexpr float kPBias = kF16 ? 7.f : 0.f;
     __shared__ __attribute__((aligned(1024))) char lds_k[kRing][TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) char lds_v[kRing][TL::kBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_v[kRing][TL::kBytes];   // bf16 or fp16 V
     __shared__ int lds_pmax[kWaves];
     // int8: the tiles' K and V scales (one per token of the kv head)
     __shared__ __attribute__((aligned(16))) float lds_sc[KV == kInt8 ? 2 : 1][kRing][kTileTokens];
@@ -340,10 +361,10 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
 
     // ---- int8 / FP8 tiles come through registers: each thread loads 8 codes
     // (8 B) of one token of a K or V tile, load number tid + jj * threads
-    // (K loads first; a wave's 64 loads are whole tokens of one 16-token
-    // half), one iteration ahead, and at the end of the next iteration
-    // writes them as bf16 into the same LDS layouts (int8 scales go to
-    // lds_sc), so the loads have a whole iteration to land.
+    // (K loads first), one iteration ahead, and at the end of the next
+    // iteration writes them into the same LDS layouts, as bf16 (FP8 V: as
+    // fp16; int8 scales go to lds_sc), so the loads have a whole iteration to
+    // land.
     constexpr int kQLoads = D / 64;                      // per thread per iteration (K + V)
     constexpr int kCodeChunks = D / 8;                   // 8-code chunks per token
     u32x2_t st_codes[kQLoads];
@@ -404,9 +425,11 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     };
     auto qstore = [&](int jj, int slot) __attribute__((always_inline)) {
         const int tok = qload_token(jj), ch = qload_chunk(jj);
-        const u32x4_t b = codes_to_bf16x8<KV>(st_codes[jj]);
-        if (qload_is_v(jj)) *(u32x4_t *)(lds_v[slot] + TL::v_offset(tok, ch)) = b;
-        else *(u32x4_t *)(lds_k[slot] + TL::k_offset(tok, ch)) = b;
+        if (qload_is_v(jj))
+            *(u32x4_t *)(lds_v[slot] + TL::v_offset(tok, ch)) =
+                kF16 ? fp8x8_to_f16x8(st_codes[jj]) : codes_to_bf16x8<KV>(st_codes[jj]);
+        else
+            *(u32x4_t *)(lds_k[slot] + TL::k_offset(tok, ch)) = codes_to_bf16x8<KV>(st_codes[jj]);
         if constexpr (KV == kInt8)
             if (ch == 0) lds_sc[qload_is_v(jj) ? 1 : 0][slot][tok] = st_scale[jj];
     };
@@ -455,10 +478,11 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
 
     // ---- online softmax of tile t's scores S into the weights (bf16 high
     // part and remainder, both rounded to nearest even: hi + lo is the fp32
-    // weight to 2^-17), masked on the tiles that cross a row's position.  The
-    // running max moves only when a row's tile max exceeds it by more than 8
-    // (log2 units): weights stay <= 2^8 and the accumulators are rarely
-    // rescaled.  Returns whether any row of the wave moved; alpha[cb] is then
+    // weight to 2^-17; FP8: fp16 times 2^kPBias; int8: fp32, split with the V
+    // scales in the weighted sum), masked on the tiles that cross a row's
+    // position.  The running max moves only when a row's tile max exceeds it
+    // by more than 8 (log2 units): weights stay <= 2^(8 + kPBias) <= 2^15 and
+    // the accumulators are rarely rescaled.  Returns whether any row of the wave moved; alpha[cb] is then
     // log2 of that row's rescale factor (0 where it did not move).
     typedef bf16x8_t Weights[kNc];
     // the 8 weights as a bf16 high part plus a bf16 remainder, both rounded
@@ -509,17 +533,36 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
 #pragma unroll
         for (int cb = 0; cb < kNc; ++cb) {
             float pr[8], psum = 0.f;
+            const float nm = kPBias - m_run[cb];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 2][cb][e & 3], c, -m_run[cb]));
+                const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 2][cb][e & 3], c, nm));
                 pr[e] = vis[cb][e] ? w : 0.f;
-                psum += pr[e];
+                if constexpr (!kF16) psum += pr[e];
+            }
+            if constexpr (kF16) {
+                // the row sum adds the weights as rounded to fp16, the values
+                // the weighted sum multiplies: their rounding then cancels in
+                // the quotient where one weight dominates
+                // (each pair in its own f16x2 variable: a bit_cast of a vector
+                // element feeding fdot2 was compiled as element 0 every time)
+                f16x2_t hv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hv[e] = __builtin_convertvector(f32x2_t{pr[2 * e], pr[2 * e + 1]}, f16x2_t);
+                    psum = __builtin_amdgcn_fdot2(hv[e], f16x2_t{1.0f16, 1.0f16}, psum, false);
+                }
+                Phi[cb] = __builtin_bit_cast(bf16x8_t, u32x4_t{__builtin_bit_cast(uint32_t, hv[0]), __builtin_bit_cast(uint32_t, hv[1]),
+                                                             __builtin_bit_cast(uint32_t, hv[2]), __builtin_bit_cast(uint32_t, hv[3])});
+                Plo[cb] = bf16x8_t{};
             }
             l_run[cb] += psum;
             if constexpr (KV == kInt8) {
                 // fp32 weights, split once the V scales are in LDS (next step)
                 Phi[cb] = __builtin_bit_cast(bf16x8_t, f32x4_t{pr[0], pr[1], pr[2], pr[3]});
                 Plo[cb] = __builtin_bit_cast(bf16x8_t, f32x4_t{pr[4], pr[5], pr[6], pr[7]});
+            } else if constexpr (kF16) {
+                // weights packed above
             } else {
                 split_weights(pr, Phi[cb], Plo[cb]);
             }
@@ -576,12 +619,19 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
             const bf16x8_t vop = __builtin_bit_cast(
                 bf16x8_t, u32x4_t{__builtin_bit_cast(u32x2_t, x0).x, __builtin_bit_cast(u32x2_t, x0).y,
                                   __builtin_bit_cast(u32x2_t, x1).x, __builtin_bit_cast(u32x2_t, x1).y});
+            if constexpr (kF16) {
 #pragma unroll
-            for (int cb = 0; cb < kNc; ++cb)
-                acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, Phi[cb], acc[j][cb], 0, 0, 0);
+                for (int cb = 0; cb < kNc; ++cb)
+                    acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(f16x8_t, vop), __builtin_bit_cast(f16x8_t, Phi[cb]), acc[j][cb], 0, 0, 0);
+            } else {
 #pragma unroll
-            for (int cb = 0; cb < kNc; ++cb)
-                acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, Plo[cb], acc[j][cb], 0, 0, 0);
+                for (int cb = 0; cb < kNc; ++cb)
+                    acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, Phi[cb], acc[j][cb], 0, 0, 0);
+#pragma unroll
+                for (int cb = 0; cb < kNc; ++cb)
+                    acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, Plo[cb], acc[j][cb], 0, 0, 0);
+            }
         }
     };
 

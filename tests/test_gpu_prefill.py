@@ -244,3 +244,61 @@ def test_full_size_quantized_prefill_workload_sampled(wl, seqs):
         rows = slice(int(qo[s]), int(qo[s + 1]))
         r = C.prefill_oracle(sub, inp["q"][rows].cpu(), [0, int(qo[s + 1] - qo[s])])
         assert_parity(out[rows], r, f"{wl} seq {s}")
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("qmul", [4.0, 64.0])
+def test_prefill_large_scores_every_cache_kind(kind, qmul):
+    # Scores of tens to hundreds (log2 units): rows close to one-hot, where
+    # the rounding of the dominant weight would show, and most weights far
+    # below the running max.
+    note(f"prefill {kind} q x {qmul}")
+    ctx = (40, 300, 1100)
+    v, q, q_off = make_kind(ctx, [40, 77, 300], 8, 2, 128, 16, 530, kind)
+    q = (q.float() * qmul).to(torch.bfloat16)
+    assert_parity(run_kind(v, q, q_off), C.prefill_oracle(v, q, q_off), f"{kind} q x {qmul}")
+
+
+def _nan_at(v, kind, s, t, g, bs):
+    """Make V of token t of sequence s, kv head g, non-finite (NaN)."""
+    bt = v["block_tables"].cpu()
+    b, r = int(bt[s, t // bs]), t % bs
+    if kind == "int8":
+        v["v_scales"][b, r, g] = float("nan")
+    elif kind == "fp8":
+        v["v_cache"].view(torch.uint8)[b, r, g, 5] = 0x7F
+    else:
+        v["v_cache"][b, r, g, 5] = float("nan")
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8", "fp8"])
+def test_prefill_nonfinite_value_inside_the_context(kind):
+    # A NaN in V of token t (kv head 1; int8: its scale, so the whole row):
+    # every query that sees t has NaN exactly where the definition puts it
+    # (the oracle's NaN elements) and the oracle's values elsewhere; queries
+    # more than one 32-token tile before t's tile, and the other group, are
+    # untouched.  (The 32 rows of a wave -- up to 32 query tokens -- multiply
+    # every tile the wave takes, so queries that share a wave with one that
+    # reaches t's tile may get a zero weight times NaN: not checked.)
+    note(f"prefill {kind} NaN inside the context")
+    ctx, nq = (700,), [400]
+    Hq, Hkv, D, bs = 8, 2, 128, 16
+    v, q, q_off = make_kind(ctx, nq, Hq, Hkv, D, bs, 531, kind)
+    t, g = 555, 1
+    _nan_at(v, kind, 0, t, g, bs)
+    got = run_kind(v, q, q_off).double().cpu().numpy()
+    ref = C.prefill_oracle(v, q, q_off)
+    pos = ctx[0] - nq[0] + np.arange(nq[0])
+    G = Hq // Hkv
+    sees = pos >= t
+    nan_ref = np.isnan(ref)
+    assert nan_ref[sees][:, g * G:(g + 1) * G].any() and not nan_ref[~sees].any()
+    assert np.array_equal(np.isnan(got[sees]), nan_ref[sees])
+    fin = ~nan_ref & sees[:, None, None]
+    assert np.abs(got[fin] - ref[fin]).max() <= 2e-3
+    before = pos < (t // 32 - 1) * 32
+    assert before.sum() > 100
+    assert_parity(torch.from_numpy(got[before]), ref[before], f"{kind} before the NaN tile")
+    other = slice(0, g * G)
+    assert_parity(torch.from_numpy(np.ascontiguousarray(got[:, other])), np.ascontiguousarray(ref[:, other]),
+                  f"{kind} other group")
