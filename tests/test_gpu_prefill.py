@@ -302,3 +302,30 @@ def test_prefill_nonfinite_value_inside_the_context(kind):
     other = slice(0, g * G)
     assert_parity(torch.from_numpy(np.ascontiguousarray(got[:, other])), np.ascontiguousarray(ref[:, other]),
                   f"{kind} other group")
+
+
+def test_prefill_bf16_values_past_fp16_range():
+    # bf16 V beyond fp16's range (the FP8 path's fp16 tiles would not hold
+    # it): the bf16 path keeps such values exact to the bar (compared in units
+    # of the scale where the outputs are that big).
+    note("prefill bf16 V x 2^16")
+    ctx, nq = (300, 700, 90), [50, 300, 90]
+    v, q, q_off = make_kind(ctx, nq, 8, 2, 128, 16, 532, "bf16")
+    clean = C.prefill_oracle(v, q, q_off)
+    # (a) the whole cache times 2^16 (exact in bf16): the outputs are 2^16
+    # times the unscaled oracle's
+    v_big = dict(v, v_cache=v["v_cache"] * 65536.0)
+    got = run_kind(v_big, q, q_off)
+    assert_parity(got / 65536.0, clean, "V x 2^16")
+    # (b) tokens 100..139 of sequence 1, kv head 0, times 2^16: tiles mixing
+    # large and ordinary values; rows whose outputs are large compared in
+    # units of 2^16
+    bt = v["block_tables"].cpu()
+    for t in range(100, 140):
+        b = int(bt[1, t // 16])
+        v["v_cache"][b, t % 16, 0] *= 65536.0
+    got = run_kind(v, q, q_off).double().cpu().numpy()
+    ref = C.prefill_oracle(v, q, q_off)
+    unit = np.where(np.abs(ref).max(axis=-1, keepdims=True) > 64.0, 65536.0, 1.0)
+    assert (unit > 1).any() and (unit == 1).any()
+    assert_parity(torch.from_numpy(got / unit), ref / unit, "V partly x 2^16")
