@@ -329,3 +329,26 @@ def test_prefill_bf16_values_past_fp16_range():
     unit = np.where(np.abs(ref).max(axis=-1, keepdims=True) > 64.0, 65536.0, 1.0)
     assert (unit > 1).any() and (unit == 1).any()
     assert_parity(torch.from_numpy(got / unit), ref / unit, "V partly x 2^16")
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+@pytest.mark.parametrize("bs", [16, 256])
+def test_quantized_prefill_mixed_chunk_decodes_empty(kind, bs):
+    # A 512-token chunk after a 1500-token prefix, decodes, a sequence with
+    # no query tokens, and an empty context with none, in one call.
+    note(f"prefill {kind} mixed batch bs={bs}")
+    ctx = (2012, 37, 900, 5, 0, 128)
+    nq = [512, 1, 1, 0, 0, 1]
+    v, q, q_off = make_kind(ctx, nq, 32, 8, 128, bs, 533 + bs, kind)
+    assert_parity(run_kind(v, q, q_off), C.prefill_oracle(v, q, q_off), f"{kind} mixed")
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+def test_quantized_prefill_any_scale(kind):
+    note(f"prefill {kind} scales")
+    ctx = (40, 300, 700)
+    v, q, q_off = make_kind(ctx, [40, 77, 200], 8, 2, 128, 16, 534, kind)
+    for scale in (-0.09, 0.0, 0.6):
+        out = B.prefill_views(v, q, q_off.to(DEV), 200, scale=scale)
+        torch.cuda.synchronize()
+        assert_parity(out, C.prefill_oracle(v, q, q_off, scale=scale), f"{kind} scale {scale}")
