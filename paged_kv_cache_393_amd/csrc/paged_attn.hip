@@ -702,13 +702,14 @@ struct MergeParams {
 // Merge the partial records of one (sequence, query head) row whose sequence
 // was split over several items: M = max_p m_p, w_p = 2^(m_p - M),
 // out = sum_p w_p acc_p / sum_p w_p l_p.  Wave w takes pieces w, w + 4, ...
-// in index order and merges them online (running max, rescaled sums), four
-// pieces' loads in flight at a time; the four wave results are then combined
-// in wave order, so the result does not depend on timing.
-template <int D>
+// in index order and merges them online (running max, rescaled sums),
+// kUnroll pieces' loads in flight at a time (16 where a sequence can have
+// hundreds of pieces, 4 otherwise -- more only adds latency to short
+// merges; the order, hence the result, is the same); the four wave results
+// are then combined in wave order, so the result does not depend on timing.
+template <int D, int kUnroll>
 __global__ __launch_bounds__(kThreads) void pa_merge_kernel(const MergeParams p) {
     constexpr int kPer = D / 64;   // dims per lane
-    constexpr int kUnroll = 4;     // pieces loaded together
     __shared__ float lds_m[kWaves], lds_l[kWaves];
     __shared__ __attribute__((aligned(16))) float lds_acc[kWaves][D];
     const int row = blockIdx.x;    // s * Hq + h
@@ -938,17 +939,21 @@ int decode_common(int kind, const void *q, const void *k, const void *v, const f
     mp.max_pieces = pl.max_pieces;
     const dim3 grid(wgs, pl.groups), block(kThreads);
     const dim3 mgrid((unsigned)((int64_t)sh->num_seqs * sh->num_q_heads));
+    // fixed items that can give a sequence 64 or more pieces: more loads in flight
+    const bool long_merge = pl.item_tiles > 0 && ((int64_t)pl.max_ctx + kTile - 1) / kTile >= 64LL * pl.item_tiles;
     hipStream_t st = (hipStream_t)stream;
     if (sh->head_dim == 128) {
         if (kind == kInt8) hipLaunchKernelGGL((pa_decode_kernel<128, kInt8>), grid, block, 0, st, prm);
         else if (kind == kFp8) hipLaunchKernelGGL((pa_decode_kernel<128, kFp8>), grid, block, 0, st, prm);
         else hipLaunchKernelGGL((pa_decode_kernel<128, kBf16>), grid, block, 0, st, prm);
-        hipLaunchKernelGGL((pa_merge_kernel<128>), mgrid, block, 0, st, mp);
+        if (long_merge) hipLaunchKernelGGL((pa_merge_kernel<128, 16>), mgrid, block, 0, st, mp);
+        else hipLaunchKernelGGL((pa_merge_kernel<128, 4>), mgrid, block, 0, st, mp);
     } else {
         if (kind == kInt8) hipLaunchKernelGGL((pa_decode_kernel<64, kInt8>), grid, block, 0, st, prm);
         else if (kind == kFp8) hipLaunchKernelGGL((pa_decode_kernel<64, kFp8>), grid, block, 0, st, prm);
         else hipLaunchKernelGGL((pa_decode_kernel<64, kBf16>), grid, block, 0, st, prm);
-        hipLaunchKernelGGL((pa_merge_kernel<64>), mgrid, block, 0, st, mp);
+        if (long_merge) hipLaunchKernelGGL((pa_merge_kernel<64, 16>), mgrid, block, 0, st, mp);
+        else hipLaunchKernelGGL((pa_merge_kernel<64, 4>), mgrid, block, 0, st, mp);
     }
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
