@@ -31,6 +31,15 @@ constexpr int kThreads = 256;
 enum ScoreKind : int { kScoreBf16 = 0, kScoreInt8 = 1, kScoreFp8 = 2 };
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Cache rows are read once per call: non-temporal loads (nt), so the
+// streamed lines are not kept in the caches.
+template <typename T>
+__device__ __forceinline__ T stream_load(const char *p) {
+    return __builtin_nontemporal_load((const T *)p);
+}
 
 struct ScoreParams {
     const void *k;
@@ -111,18 +120,18 @@ __global__ __launch_bounds__(kThreads) void token_scores_kernel(ScoreParams p) {
         float kk = 0.f, vv = 0.f;
         for (int c = li; c < p.chunks; c += L) {
             if constexpr (KIND == kScoreBf16) {
-                const uint4 kw = *(const uint4 *)(krow + c * 16);
-                const uint4 vw = *(const uint4 *)(vrow + c * 16);
+                const u32x4_t kw = stream_load<u32x4_t>(krow + c * 16);
+                const u32x4_t vw = stream_load<u32x4_t>(vrow + c * 16);
                 kk = sumsq_bf16x2(kw.w, sumsq_bf16x2(kw.z, sumsq_bf16x2(kw.y, sumsq_bf16x2(kw.x, kk))));
                 vv = sumsq_bf16x2(vw.w, sumsq_bf16x2(vw.z, sumsq_bf16x2(vw.y, sumsq_bf16x2(vw.x, vv))));
             } else if constexpr (KIND == kScoreFp8) {
-                const uint2 kw = *(const uint2 *)(krow + c * 8);
-                const uint2 vw = *(const uint2 *)(vrow + c * 8);
+                const u32x2_t kw = stream_load<u32x2_t>(krow + c * 8);
+                const u32x2_t vw = stream_load<u32x2_t>(vrow + c * 8);
                 kk = sumsq_fp8x4(kw.y, sumsq_fp8x4(kw.x, kk));
                 vv = sumsq_fp8x4(vw.y, sumsq_fp8x4(vw.x, vv));
             } else {
-                const uint2 kw = *(const uint2 *)(krow + c * 8);
-                const uint2 vw = *(const uint2 *)(vrow + c * 8);
+                const u32x2_t kw = stream_load<u32x2_t>(krow + c * 8);
+                const u32x2_t vw = stream_load<u32x2_t>(vrow + c * 8);
                 // sum of the 8 codes' squares: exact (at most 8 * 128^2)
                 const int ksq = __builtin_amdgcn_sdot4((int)kw.y, (int)kw.y,
                                                        __builtin_amdgcn_sdot4((int)kw.x, (int)kw.x, 0, false), false);

@@ -2,8 +2,8 @@
 //
 // Two plain kernels with a known number of HBM bytes, used to put the decode
 // kernel's bandwidth in context:
-//   * pa_probe_read: streams a buffer once with 16-byte loads (the practical
-//     read ceiling of the device for a perfectly coalesced stream);
+//   * pa_probe_read: streams a buffer once with 16-byte loads, each
+//     workgroup a contiguous share (the practical read ceiling of the device);
 //   * pa_probe_copy: copies a buffer (reads N and writes N bytes), the
 //     reference against which hardware fetch/write byte counters are scaled.
 // Neither is part of the decode path.
@@ -19,20 +19,30 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
-// Grid-stride read with two independent 16-B loads in flight per iteration;
-// the XOR of everything read is stored only if it equals an unlikely value,
-// which keeps the loads alive without writing.
+// Each workgroup streams one contiguous share of the buffer, four
+// non-temporal 16-B loads in flight per thread.  Measured on MI355X, this
+// reads 577 MB at 6.7 TB/s and 2 GiB at 6.8 TB/s, where a grid-stride loop
+// over the whole buffer reached 5.7 and 5.9.  The XOR of everything read is
+// stored only if it equals an unlikely value, which keeps the loads alive
+// without writing.
+constexpr int kReadUnroll = 4;
+constexpr int kReadWgPerCu = 16;
+
 __global__ __launch_bounds__(kThreads) void probe_read_kernel(const u32x4_t *__restrict__ p, int64_t n16,
                                                               uint32_t *__restrict__ sink) {
     uint32_t acc = 0;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (; i + stride < n16; i += 2 * stride) {
-        const u32x4_t a = __builtin_nontemporal_load(p + i);
-        const u32x4_t b = __builtin_nontemporal_load(p + i + stride);
-        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = (int64_t)blockIdx.x * per;
+    const int64_t hi = lo + per < n16 ? lo + per : n16;
+    int64_t i = lo + threadIdx.x;
+    for (; i + (kReadUnroll - 1) * kThreads < hi; i += kReadUnroll * kThreads) {
+        u32x4_t a[kReadUnroll];
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u) a[u] = __builtin_nontemporal_load(p + i + u * kThreads);
+#pragma unroll
+        for (int u = 0; u < kReadUnroll; ++u) acc ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
     }
-    for (; i < n16; i += stride) {
+    for (; i < hi; i += kThreads) {
         const u32x4_t a = p[i];
         acc ^= a.x ^ a.y ^ a.z ^ a.w;
     }
@@ -45,12 +55,12 @@ __global__ __launch_bounds__(kThreads) void probe_copy_kernel(const u32x4_t *__r
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
-int grid_for(int64_t n16) {
+int grid_for(int64_t n16, int wg_per_cu) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return 0;
-    int64_t g = (int64_t)cus * 8;   // 8 workgroups per compute unit
+    int64_t g = (int64_t)cus * wg_per_cu;
     const int64_t need = (n16 + kThreads - 1) / kThreads;
     return (int)(g < need ? g : (need > 0 ? need : 1));
 }
@@ -64,7 +74,7 @@ extern "C" {
 int pa_probe_read(const void *buf, int64_t bytes, void *sink, void *stream) {
     if (!buf || !sink) return PA_PROBE_ERR_ARG;
     if (bytes <= 0 || bytes % 16 != 0 || !aligned16(buf)) return PA_PROBE_ERR_ARG;
-    const int grid = grid_for(bytes / 16);
+    const int grid = grid_for(bytes / 16, kReadWgPerCu);
     if (grid <= 0) return PA_PROBE_ERR_LAUNCH;
     hipLaunchKernelGGL(probe_read_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
                        (const u32x4_t *)buf, bytes / 16, (uint32_t *)sink);
@@ -74,7 +84,7 @@ int pa_probe_read(const void *buf, int64_t bytes, void *sink, void *stream) {
 int pa_probe_copy(const void *src, void *dst, int64_t bytes, void *stream) {
     if (!src || !dst) return PA_PROBE_ERR_ARG;
     if (bytes <= 0 || bytes % 16 != 0 || !aligned16(src) || !aligned16(dst)) return PA_PROBE_ERR_ARG;
-    const int grid = grid_for(bytes / 16);
+    const int grid = grid_for(bytes / 16, 8);
     if (grid <= 0) return PA_PROBE_ERR_LAUNCH;
     hipLaunchKernelGGL(probe_copy_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
                        (const u32x4_t *)src, (u32x4_t *)dst, bytes / 16);
