@@ -92,6 +92,9 @@ class OracleLib:
             fn.restype = i32
         lib.oracle_evict_lowest_block.argtypes = [P, P, P, P, P, i32, i32, i32, i64]
         lib.oracle_evict_lowest_block.restype = i32
+        lib.oracle_compress_prefill.argtypes = [P, P, i64, P, P, i32, P, P, P, i32, i32, i32, i64,
+                                                i32]
+        lib.oracle_compress_prefill.restype = i32
         lib.oracle_paged_prefill_bf16.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
                                                   i64, ctypes.c_float, P]
         lib.oracle_paged_prefill_bf16.restype = i32
@@ -393,6 +396,39 @@ def evict_lowest_block(scores, block_tables, context_lens, evict_mask,
     if rc != 0:
         raise ValueError(f"oracle rejected the inputs (code {rc})")
     return bt, cl, ev
+
+
+def compress_prefill(views, scores, budget: int, lib: "OracleLib | None" = None):
+    """Prefill-phase PagedEviction on copies: for every sequence whose context
+    exceeds `budget`, keep the `budget` most important tokens (NaN first, then
+    higher importance, then earlier position), in order, at logical positions
+    0 .. budget-1.  views: per-layer views (bf16, int8 or fp8 cache); scores:
+    float32 per-slot importances [NB, BS].  Returns a dict of host arrays:
+    k_cache / v_cache (the cache's raw bytes, [NB, BS, Hkv, D * elem] uint8),
+    k_scales / v_scales (int8 only), scores, context_lens."""
+    import torch
+
+    kc, vc = views["k_cache"].detach().cpu().contiguous(), views["v_cache"].detach().cpu().contiguous()
+    NB, BS, Hkv, D = kc.shape
+    kb = np.array(kc.view(torch.uint8).numpy(), copy=True).reshape(NB, BS, Hkv, -1)
+    vb = np.array(vc.view(torch.uint8).numpy(), copy=True).reshape(NB, BS, Hkv, -1)
+    row_bytes = Hkv * kb.shape[-1]
+    sc = np.array(_c(scores, np.float32), copy=True)
+    bt = _c(views["block_tables"].cpu().numpy(), np.int32)
+    cl = np.array(_c(views["context_lens"].cpu().numpy(), np.int32), copy=True)
+    S, MB = bt.shape
+    out = {"k_cache": kb, "v_cache": vb, "scores": sc, "context_lens": cl}
+    ksp = vsp = None
+    if "k_scales" in views:
+        out["k_scales"] = np.array(_c(views["k_scales"].cpu().numpy(), np.float32), copy=True)
+        out["v_scales"] = np.array(_c(views["v_scales"].cpu().numpy(), np.float32), copy=True)
+        ksp, vsp = _ptr(out["k_scales"]), _ptr(out["v_scales"])
+    L = lib.lib if lib is not None else _load()
+    rc = L.oracle_compress_prefill(_ptr(kb), _ptr(vb), row_bytes, ksp, vsp, Hkv, _ptr(sc),
+                                   _ptr(bt), _ptr(cl), S, MB, BS, NB, int(budget))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the inputs (code {rc})")
+    return out
 
 
 def paged_prefill_bf16(q_bits, k_bits, v_bits, block_tables, context_lens, q_offsets, scale,

@@ -706,3 +706,120 @@ int oracle_paged_prefill_fp8(const uint16_t *q, const uint8_t *k_cache, const ui
     return prefill_common(q, &src, block_tables, context_lens, q_offsets, S, Hq, Hkv, D, BS, MB,
                           NB, scale, out);
 }
+
+/*
+ * PagedEviction, prefill phase (blog.hotdry.top page, section "PagedEviction
+ * 块级驱逐机制": in the prefill phase each token's importance is computed and
+ * the low-scoring tokens are evicted down to the budget; compression there is
+ * per token, not per block).
+ *
+ * Reading taken: for each sequence with n = context_lens[s] > budget, the
+ * tokens are ranked by importance, highest first (a NaN importance ranks
+ * above every number, as the decode-phase rule never evicts a NaN block; equal
+ * importances, -0 and +0 included, rank by position, earlier first); the
+ * first `budget` of that ranking are kept, in their original order, and moved
+ * to logical positions 0 .. budget-1 of the same sequence.  A kept token takes
+ * its whole cache row with it: its K and V rows (all kv heads; any element
+ * type, moved as bytes), its int8 scales when present, and its importance.
+ * context_lens[s] becomes budget.  Slots at logical positions >= budget, and
+ * every other sequence, are left as they were; the block table is not
+ * changed (entries from ceil(budget / BS) on no longer belong to the context).
+ *
+ * Plain form: the ranking is a full sort of (importance, position) pairs,
+ * and the kept rows are copied out to a buffer before any is written back.
+ * Checked caller contract: valid and pairwise distinct block ids for every
+ * logical block of every compressed sequence.
+ */
+typedef struct {
+    float score;
+    int32_t pos;
+} ranked_token;
+
+static int rank_cmp(const void *pa, const void *pb)
+{
+    const ranked_token *a = (const ranked_token *)pa, *b = (const ranked_token *)pb;
+    const int an = isnan(a->score), bn = isnan(b->score);
+    if (an != bn) return an ? -1 : 1;                 /* NaN first */
+    if (!an && a->score != b->score) return a->score > b->score ? -1 : 1;   /* higher first */
+    return (a->pos > b->pos) - (a->pos < b->pos);     /* then earlier first */
+}
+
+static int int_cmp(const void *pa, const void *pb)
+{
+    const int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+int oracle_compress_prefill(uint8_t *k_cache, uint8_t *v_cache, int64_t row_bytes, float *k_scales,
+                            float *v_scales, int Hkv, float *scores, const int32_t *block_tables,
+                            int32_t *context_lens, int S, int MB, int BS, int64_t NB, int budget)
+{
+    if (!k_cache || !v_cache || !scores || !block_tables || !context_lens) return ORC_ERR_ARG;
+    if (S < 0 || MB <= 0 || BS <= 0 || NB < 0 || row_bytes <= 0 || budget < 0) return ORC_ERR_ARG;
+    if ((k_scales == NULL) != (v_scales == NULL) || (k_scales && Hkv <= 0)) return ORC_ERR_ARG;
+    unsigned char *used = (unsigned char *)calloc((size_t)(NB > 0 ? NB : 1), 1);
+    if (!used) return ORC_ERR_NOMEM;
+    int rc = ORC_OK;
+    for (int s = 0; s < S && rc == ORC_OK; ++s) {
+        const int n = context_lens[s];
+        if (n < 0 || (int64_t)n > (int64_t)MB * BS) rc = ORC_ERR_TABLE;
+        else if (n > budget)
+            for (int j = 0; j < (n + BS - 1) / BS; ++j) {
+                const int32_t b = block_tables[(int64_t)s * MB + j];
+                if (b < 0 || (int64_t)b >= NB || used[b]) { rc = ORC_ERR_TABLE; break; }
+                used[b] = 1;
+            }
+    }
+    free(used);
+    if (rc != ORC_OK) return rc;
+    const int ns = k_scales ? Hkv : 0;
+    for (int s = 0; s < S; ++s) {
+        const int n = context_lens[s];
+        if (n <= budget) continue;
+        const int32_t *row = block_tables + (int64_t)s * MB;
+        ranked_token *rk = (ranked_token *)malloc((size_t)n * sizeof *rk);
+        int32_t *keep = (int32_t *)malloc((size_t)(budget > 0 ? budget : 1) * sizeof *keep);
+        uint8_t *kb = (uint8_t *)malloc((size_t)(budget > 0 ? budget : 1) * (size_t)row_bytes);
+        uint8_t *vb = (uint8_t *)malloc((size_t)(budget > 0 ? budget : 1) * (size_t)row_bytes);
+        float *fb = (float *)malloc((size_t)(budget > 0 ? budget : 1) * (size_t)(2 * ns + 1) * sizeof(float));
+        if (!rk || !keep || !kb || !vb || !fb) {
+            free(rk); free(keep); free(kb); free(vb); free(fb);
+            return ORC_ERR_NOMEM;
+        }
+        for (int t = 0; t < n; ++t) {
+            const int64_t slot = (int64_t)row[t / BS] * BS + t % BS;
+            rk[t].score = scores[slot];
+            rk[t].pos = t;
+        }
+        qsort(rk, (size_t)n, sizeof *rk, rank_cmp);
+        for (int j = 0; j < budget; ++j) keep[j] = rk[j].pos;
+        qsort(keep, (size_t)budget, sizeof *keep, int_cmp);
+        /* copy the kept rows out, then write them to positions 0 .. budget-1 */
+        for (int j = 0; j < budget; ++j) {
+            const int t = keep[j];
+            const int64_t slot = (int64_t)row[t / BS] * BS + t % BS;
+            memcpy(kb + (size_t)j * row_bytes, k_cache + slot * row_bytes, (size_t)row_bytes);
+            memcpy(vb + (size_t)j * row_bytes, v_cache + slot * row_bytes, (size_t)row_bytes);
+            float *f = fb + (size_t)j * (2 * ns + 1);
+            for (int g = 0; g < ns; ++g) {
+                f[g] = k_scales[slot * Hkv + g];
+                f[ns + g] = v_scales[slot * Hkv + g];
+            }
+            f[2 * ns] = scores[slot];
+        }
+        for (int j = 0; j < budget; ++j) {
+            const int64_t slot = (int64_t)row[j / BS] * BS + j % BS;
+            memcpy(k_cache + slot * row_bytes, kb + (size_t)j * row_bytes, (size_t)row_bytes);
+            memcpy(v_cache + slot * row_bytes, vb + (size_t)j * row_bytes, (size_t)row_bytes);
+            const float *f = fb + (size_t)j * (2 * ns + 1);
+            for (int g = 0; g < ns; ++g) {
+                k_scales[slot * Hkv + g] = f[g];
+                v_scales[slot * Hkv + g] = f[ns + g];
+            }
+            scores[slot] = f[2 * ns];
+        }
+        context_lens[s] = budget;
+        free(rk); free(keep); free(kb); free(vb); free(fb);
+    }
+    return ORC_OK;
+}

@@ -87,6 +87,18 @@ MUTANTS = {
                                    "kv_src src = {KV_FP8, v_cache, k_cache, NULL, NULL};\n    return prefill_common"),
     "prefill_k_as_v": ("const double e = exp(scores[t] - m);\n        denom += e;\n        for (int i = 0; i < D; ++i) o[i] += e * kv_elem(src, 1,",
                        "const double e = exp(scores[t] - m);\n        denom += e;\n        for (int i = 0; i < D; ++i) o[i] += e * kv_elem(src, 0,"),
+    "compress_keeps_lowest": ("if (!an && a->score != b->score) return a->score > b->score ? -1 : 1;",
+                              "if (!an && a->score != b->score) return a->score > b->score ? 1 : -1;"),
+    "compress_ties_keep_later": ("return (a->pos > b->pos) - (a->pos < b->pos);     /* then earlier first */",
+                                 "return (a->pos < b->pos) - (a->pos > b->pos);"),
+    "compress_nan_ranks_last": ("if (an != bn) return an ? -1 : 1;", "if (an != bn) return an ? 1 : -1;"),
+    "compress_kept_in_rank_order": ("qsort(keep, (size_t)budget, sizeof *keep, int_cmp);", ""),
+    "compress_scores_stay": ("            scores[slot] = f[2 * ns];\n", ""),
+    "compress_v_from_k": ("memcpy(vb + (size_t)j * row_bytes, v_cache + slot", "memcpy(vb + (size_t)j * row_bytes, k_cache + slot"),
+    "compress_context_kept": ("        context_lens[s] = budget;\n", ""),
+    "compress_k_scales_stay": ("                k_scales[slot * Hkv + g] = f[g];\n", ""),
+    "compress_one_kept_short": ("for (int j = 0; j < budget; ++j) keep[j] = rk[j].pos;",
+                                "for (int j = 0; j < budget; ++j) keep[j] = rk[j > 0 ? j - 1 : 0].pos;"),
 }
 
 PIN_FUNCS = [
@@ -126,6 +138,13 @@ PIN_FUNCS = [
     "test_prefill_fp8_single_query_is_the_decode",
     "test_prefill_int8_chunk_matches_masked_sdpa_on_dequantized_cache",
     "test_prefill_fp8_chunk_matches_masked_sdpa_on_decoded_cache",
+    "test_compress_keeps_the_newest_tokens_when_importance_rises",
+    "test_compress_keeps_the_prefix_when_importance_falls",
+    "test_compress_ties_keep_earlier_tokens_and_nan_ranks_first",
+    "test_compress_matches_brute_force_on_tiny_sequences",
+    "test_compress_moves_int8_scales_with_their_rows",
+    "test_decode_after_compression_equals_attention_over_the_kept_tokens",
+    "test_compress_rejects_shared_blocks",
 ]
 
 RUNNER = r"""

@@ -690,3 +690,170 @@ def test_prefill_int8_chunk_matches_masked_sdpa_on_dequantized_cache():
 
 def test_prefill_fp8_chunk_matches_masked_sdpa_on_decoded_cache():
     _prefill_quantized_chunk_matches_masked_sdpa("fp8")
+
+
+# --- PagedEviction, prefill phase: token-level compression to a budget ---
+
+def _raw(t):
+    """uint8 bytes [NB, BS, Hkv, row bytes per head] of a cache tensor."""
+    t = t.detach().cpu().contiguous()
+    return t.view(torch.uint8).numpy().reshape(t.shape[0], t.shape[1], t.shape[2], -1)
+
+
+def _logical_rows(cache_bytes, table_row, positions, bs):
+    return np.stack([cache_bytes[table_row[p // bs], p % bs] for p in positions])
+
+
+def _slot_scores(views, bs, per_seq):
+    """fp32 per-slot scores [NB, BS] whose logical order in sequence s is per_seq[s]."""
+    NB = views["k_cache"].shape[0]
+    sc = np.full((NB, bs), -7.0, dtype=np.float32)
+    bt = views["block_tables"].numpy()
+    for s, vals in enumerate(per_seq):
+        for t, x in enumerate(vals):
+            sc[bt[s, t // bs], t % bs] = x
+    return sc
+
+
+def _check_compressed(v, res, bs, kept_by_seq, ctx, budget):
+    """The compressed cache holds, at logical positions 0..len(kept)-1 of each
+    sequence, the original rows (K, V, scales, scores) of the kept positions;
+    every other byte of the pool is unchanged."""
+    kb0, vb0 = _raw(v["k_cache"]), _raw(v["v_cache"])
+    bt = v["block_tables"].numpy()
+    expect_k, expect_v = kb0.copy(), vb0.copy()
+    for s, kept in enumerate(kept_by_seq):
+        if ctx[s] <= budget or not kept:
+            continue
+        rows_k = _logical_rows(kb0, bt[s], kept, bs)
+        rows_v = _logical_rows(vb0, bt[s], kept, bs)
+        for j in range(len(kept)):
+            expect_k[bt[s, j // bs], j % bs] = rows_k[j]
+            expect_v[bt[s, j // bs], j % bs] = rows_v[j]
+    assert np.array_equal(res["k_cache"], expect_k)
+    assert np.array_equal(res["v_cache"], expect_v)
+    assert np.array_equal(res["context_lens"], [min(n, budget) for n in ctx])
+
+
+def test_compress_keeps_the_newest_tokens_when_importance_rises():
+    bs, budget = 16, 40
+    ctx = (100, 40, 7, 73)
+    _, v = C.make_case(4, 8, 2, 64, bs, ctx=ctx, seed=71)
+    sc = _slot_scores(v, bs, [np.arange(n, dtype=np.float32) * 0.5 for n in ctx])
+    res = oracle.compress_prefill(v, sc, budget)
+    kept = [list(range(n - budget, n)) if n > budget else list(range(n)) for n in ctx]
+    _check_compressed(v, res, bs, kept, ctx, budget)
+    bt = v["block_tables"].numpy()
+    for s, n in enumerate(ctx):
+        if n > budget:
+            got = [res["scores"][bt[s, j // bs], j % bs] for j in range(budget)]
+            assert np.array_equal(got, np.arange(n - budget, n, dtype=np.float32) * 0.5)
+
+
+def test_compress_keeps_the_prefix_when_importance_falls():
+    bs, budget = 16, 33
+    ctx = (80, 33, 50)
+    _, v = C.make_case(3, 8, 2, 64, bs, ctx=ctx, seed=72)
+    sc = _slot_scores(v, bs, [-np.arange(n, dtype=np.float32) for n in ctx])
+    res = oracle.compress_prefill(v, sc, budget)
+    assert np.array_equal(res["k_cache"], _raw(v["k_cache"]))
+    assert np.array_equal(res["v_cache"], _raw(v["v_cache"]))
+    assert np.array_equal(res["scores"], sc)
+    assert np.array_equal(res["context_lens"], [33, 33, 33])
+
+
+def test_compress_ties_keep_earlier_tokens_and_nan_ranks_first():
+    bs, budget = 16, 20
+    n = 64
+    _, v = C.make_case(1, 8, 2, 64, bs, ctx=(n,), seed=73)
+    vals = np.where(np.arange(n) % 2 == 0, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    vals[50] = np.nan
+    vals[60] = 1.0
+    res = oracle.compress_prefill(v, _slot_scores(v, bs, [vals]), budget)
+    kept = sorted([50, 60] + list(range(budget - 2)))   # NaN, the one larger value, then earliest zeros
+    _check_compressed(v, res, bs, [kept], (n,), budget)
+
+
+def test_compress_matches_brute_force_on_tiny_sequences():
+    # Among all budget-subsets, exactly one has no evicted token ranking
+    # above a kept one (NaN above numbers, larger above smaller, equal values
+    # by position); the oracle must keep that one.
+    import itertools
+
+    bs = 16
+    rng = np.random.default_rng(74)
+    palette = np.array([0.0, 1.0, 2.0, np.inf, np.nan], dtype=np.float32)
+    for trial in range(40):
+        n = int(rng.integers(1, 9))
+        budget = int(rng.integers(0, n + 2))
+        vals = palette[rng.integers(0, len(palette), n)]
+        _, v = C.make_case(1, 4, 1, 64, bs, ctx=(n,), seed=200 + trial)
+
+        def above(a, b):   # token a ranks above token b
+            xa, xb = vals[a], vals[b]
+            if np.isnan(xa) != np.isnan(xb):
+                return bool(np.isnan(xa))
+            if np.isnan(xa) or xa == xb:
+                return a < b
+            return bool(xa > xb)
+
+        if budget >= n:
+            want = list(range(n))
+        else:
+            ok = [c for c in itertools.combinations(range(n), budget)
+                  if all(above(a, b) for a in c for b in set(range(n)) - set(c))]
+            assert len(ok) == 1
+            want = list(ok[0])
+        res = oracle.compress_prefill(v, _slot_scores(v, bs, [vals]), budget)
+        _check_compressed(v, res, bs, [want], (n,), budget)
+
+
+def test_compress_moves_int8_scales_with_their_rows():
+    bs, budget = 16, 24
+    ctx = (60, 30)
+    _, v = C.make_case(2, 8, 2, 64, bs, ctx=ctx, seed=75, kv_dtype="int8")
+    sc = _slot_scores(v, bs, [np.arange(n, dtype=np.float32) for n in ctx])
+    res = oracle.compress_prefill(v, sc, budget)
+    bt = v["block_tables"].numpy()
+    ks0, vs0 = v["k_scales"].numpy(), v["v_scales"].numpy()
+    for s, n in enumerate(ctx):
+        for j in range(budget):
+            t = n - budget + j
+            dst, src = (bt[s, j // bs], j % bs), (bt[s, t // bs], t % bs)
+            assert np.array_equal(res["k_scales"][dst], ks0[src])
+            assert np.array_equal(res["v_scales"][dst], vs0[src])
+    kept = [list(range(n - budget, n)) for n in ctx]
+    _check_compressed(v, res, bs, kept, ctx, budget)
+
+
+def test_decode_after_compression_equals_attention_over_the_kept_tokens():
+    bs, budget = 16, 37
+    ctx = (90, 37, 64)
+    _, v = C.make_case(3, 8, 2, 64, bs, ctx=ctx, seed=76)
+    rng = np.random.default_rng(76)
+    per_seq = [rng.permutation(n).astype(np.float32) for n in ctx]   # distinct importances
+    res = oracle.compress_prefill(v, _slot_scores(v, bs, per_seq), budget)
+    kc = torch.from_numpy(res["k_cache"].reshape(-1)).view(torch.bfloat16).reshape(v["k_cache"].shape)
+    vc = torch.from_numpy(res["v_cache"].reshape(-1)).view(torch.bfloat16).reshape(v["v_cache"].shape)
+    w = dict(v, k_cache=kc, v_cache=vc, context_lens=torch.from_numpy(res["context_lens"]))
+    out = C.oracle_out(w)
+    q = v["q"].to(torch.float64)
+    for s, n in enumerate(ctx):
+        keep = np.sort(np.argsort(-per_seq[s])[:budget]) if n > budget else np.arange(n)
+        K, V = C.gathered(v, bs, s)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[s][None, :, None, :], torch.from_numpy(K[:, keep])[None],
+            torch.from_numpy(V[:, keep])[None], scale=float(np.float32(v["scale"])),
+            enable_gqa=True)[0, :, 0, :].numpy()
+        assert np.allclose(out[s], ref, rtol=0, atol=1e-12), s
+
+
+def test_compress_rejects_shared_blocks():
+    bs = 16
+    _, v = C.make_case(2, 4, 1, 64, bs, ctx=(40, 40), seed=77)
+    bt = v["block_tables"].clone()
+    bt[1, 0] = bt[0, 1]
+    w = dict(v, block_tables=bt)
+    sc = np.zeros((v["k_cache"].shape[0], bs), np.float32)
+    with pytest.raises(ValueError):
+        oracle.compress_prefill(w, sc, 10)
