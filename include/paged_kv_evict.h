@@ -1,7 +1,8 @@
 /*
  * paged_kv_evict.h -- C-ABI of the PagedEviction part of the MI355X (gfx950)
- * paged KV cache library: token importance over the paged cache, and the
- * decode-phase eviction of whole blocks.
+ * paged KV cache library: token importance over the paged cache, the
+ * decode-phase eviction of whole blocks, and the prefill-phase compression
+ * of each sequence to a token budget.
  *
  * The method (page "KV缓存内存布局优化：分页策略、量化压缩与动态驱逐的工程实践",
  * blog.hotdry.top, section "PagedEviction 块级驱逐机制"): a token's importance
@@ -97,6 +98,48 @@ int paged_kv_token_scores_fp8(const uint8_t *k_cache, const uint8_t *v_cache,
 int paged_kv_evict_lowest_block(const float *scores, int32_t *block_tables,
                                 int32_t *context_lens, const int32_t *evict_mask,
                                 int32_t *evicted, const pa_score_shape *shape, void *stream);
+
+/*
+ * Prefill-phase token compression (same page and section: in the prefill
+ * phase the tokens of low importance are evicted until the cache holds the
+ * budget).  For each sequence s with n = context_lens[s] > budget:
+ *   - tokens are ranked by their importance scores[slot] (as written by
+ *     paged_kv_token_scores*): highest first, a NaN above every number, equal
+ *     values (-0 and +0 included) by position, earlier first;
+ *   - the first `budget` tokens of that ranking are kept, in their original
+ *     order, and move to logical positions 0 .. budget-1 of the same
+ *     sequence: each takes its K and V rows (all kv heads), its int8 scales
+ *     and its importance with it;
+ *   - context_lens[s] becomes budget.
+ * Sequences with n <= budget, slots at positions >= budget and the block
+ * tables are left unchanged; table entries from ceil(budget / block_size) on
+ * no longer belong to the context, and the caller may reuse their blocks.
+ * k_cache, v_cache (and the scales, and scores) are updated in place, and
+ * must be 16-byte aligned.
+ *
+ * Workspace: paged_kv_compress_workspace_bytes(shape, budget) bytes of device
+ * memory (kept positions and context lengths), 16-byte aligned, contents
+ * irrelevant; no two calls may use it at once.  Two kernel launches.
+ * Caller contract (not checked): valid and pairwise distinct block ids for
+ * every logical block of every sequence with n > budget.
+ */
+size_t paged_kv_compress_workspace_bytes(const pa_score_shape *shape, int32_t budget);
+
+int paged_kv_compress_prefill(void *k_cache, void *v_cache, float *scores,
+                              const int32_t *block_tables, int32_t *context_lens, int32_t budget,
+                              const pa_score_shape *shape, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+int paged_kv_compress_prefill_int8(int8_t *k_cache, int8_t *v_cache, float *k_scales,
+                                   float *v_scales, float *scores, const int32_t *block_tables,
+                                   int32_t *context_lens, int32_t budget,
+                                   const pa_score_shape *shape, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+int paged_kv_compress_prefill_fp8(uint8_t *k_cache, uint8_t *v_cache, float *scores,
+                                  const int32_t *block_tables, int32_t *context_lens,
+                                  int32_t budget, const pa_score_shape *shape, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

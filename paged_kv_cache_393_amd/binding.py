@@ -100,6 +100,15 @@ def load() -> ctypes.CDLL:
     lib.paged_kv_token_scores_fp8.restype = ctypes.c_int
     lib.paged_kv_evict_lowest_block.argtypes = [P, P, P, P, P, CP, P]
     lib.paged_kv_evict_lowest_block.restype = ctypes.c_int
+    lib.paged_kv_compress_workspace_bytes.argtypes = [CP, ctypes.c_int32]
+    lib.paged_kv_compress_workspace_bytes.restype = ctypes.c_size_t
+    lib.paged_kv_compress_prefill.argtypes = [P, P, P, P, P, ctypes.c_int32, CP, P, ctypes.c_size_t, P]
+    lib.paged_kv_compress_prefill.restype = ctypes.c_int
+    lib.paged_kv_compress_prefill_int8.argtypes = [P, P, P, P, P, P, P, ctypes.c_int32, CP, P,
+                                                   ctypes.c_size_t, P]
+    lib.paged_kv_compress_prefill_int8.restype = ctypes.c_int
+    lib.paged_kv_compress_prefill_fp8.argtypes = [P, P, P, P, P, ctypes.c_int32, CP, P, ctypes.c_size_t, P]
+    lib.paged_kv_compress_prefill_fp8.restype = ctypes.c_int
     lib.paged_attn_prefill.argtypes = [P, P, P, P, P, P, ctypes.c_float, P,
                                        ctypes.POINTER(PaPrefillShape), P]
     lib.paged_attn_prefill.restype = ctypes.c_int
@@ -429,6 +438,51 @@ def evict_lowest_block(scores, block_tables, context_lens, evict_mask, evicted=N
                                               _ptr(evict_mask), _ptr(evicted), ctypes.byref(sh),
                                               _stream_handle(stream)))
     return evicted
+
+
+def compress_workspace_bytes(k_cache, block_tables, budget: int) -> int:
+    return int(load().paged_kv_compress_workspace_bytes(ctypes.byref(score_shape(k_cache, block_tables)),
+                                                        int(budget)))
+
+
+def compress_prefill(views: dict, scores, budget: int, workspace=None, stream=None) -> None:
+    """paged_kv_compress_prefill*: every sequence longer than `budget` keeps
+    its `budget` most important tokens (scores fp32 [num_blocks, block_size]),
+    in order, at positions 0 .. budget-1; the cache, its int8 scales, the
+    scores and context_lens are updated in place."""
+    kc, vc = views["k_cache"], views["v_cache"]
+    bt, cl = views["block_tables"], views["context_lens"]
+    for name, t in (("k_cache", kc), ("v_cache", vc), ("block_tables", bt), ("context_lens", cl),
+                    ("scores", scores)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if bt.dtype != torch.int32 or cl.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    NB, bs = kc.shape[0], kc.shape[1]
+    if scores.dtype != torch.float32 or tuple(scores.shape) != (NB, bs):
+        raise ValueError("scores must be fp32 [num_blocks, block_size]")
+    if tuple(cl.shape) != (bt.shape[0],):
+        raise ValueError("context_lens must be [num_seqs]")
+    sh = score_shape(kc, bt)
+    L = load()
+    need = int(L.paged_kv_compress_workspace_bytes(ctypes.byref(sh), int(budget)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=kc.device)
+    st = _stream_handle(stream)
+    ws, wsb = _ptr(workspace), workspace.numel() * workspace.element_size()
+    if kc.dtype in FP8_DTYPES:
+        rc = L.paged_kv_compress_prefill_fp8(_ptr(kc), _ptr(vc), _ptr(scores), _ptr(bt), _ptr(cl),
+                                             int(budget), ctypes.byref(sh), ws, wsb, st)
+    elif "k_scales" in views:
+        rc = L.paged_kv_compress_prefill_int8(_ptr(kc), _ptr(vc), _ptr(views["k_scales"]),
+                                              _ptr(views["v_scales"]), _ptr(scores), _ptr(bt),
+                                              _ptr(cl), int(budget), ctypes.byref(sh), ws, wsb, st)
+    else:
+        if kc.dtype != torch.bfloat16:
+            raise TypeError("cache must be bf16, int8 (with scales) or fp8")
+        rc = L.paged_kv_compress_prefill(_ptr(kc), _ptr(vc), _ptr(scores), _ptr(bt), _ptr(cl),
+                                         int(budget), ctypes.byref(sh), ws, wsb, st)
+    _check(rc)
 
 
 def _prefill_shape(q, k_cache, v_cache, block_tables, context_lens, q_offsets, max_q_len,

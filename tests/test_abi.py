@@ -11,7 +11,9 @@ DECLARED = {"paged_attn_plan", "paged_attn_workspace_bytes", "paged_attn_decode"
             "paged_kv_write", "paged_kv_write_int8", "paged_attn_decode_fp8", "paged_kv_write_fp8",
             "paged_kv_token_scores", "paged_kv_token_scores_int8", "paged_kv_token_scores_fp8",
             "paged_kv_evict_lowest_block", "paged_attn_prefill", "paged_attn_prefill_int8",
-            "paged_attn_prefill_fp8"}
+            "paged_attn_prefill_fp8", "paged_kv_compress_workspace_bytes",
+            "paged_kv_compress_prefill", "paged_kv_compress_prefill_int8",
+            "paged_kv_compress_prefill_fp8"}
 
 
 def lib():
@@ -279,6 +281,49 @@ def test_score_and_evict_null_alignment_and_empty():
         assert L.paged_kv_evict_lowest_block(*args, ctypes.byref(sshape()), None) == B.PA_ERR_NULL
     assert L.paged_kv_evict_lowest_block(None, None, None, None, None,
                                          ctypes.byref(sshape(num_seqs=0)), None) == B.PA_OK
+
+
+# ---- prefill-phase compression (include/paged_kv_evict.h) ----
+
+def ccall(sh, budget=8, k=FAKE, v=FAKE, sc=FAKE, bt=FAKE, cl=FAKE, ws=FAKE, wsb=1 << 20):
+    return lib().paged_kv_compress_prefill(k, v, sc, bt, cl, budget, ctypes.byref(sh), ws, wsb, None)
+
+
+def test_compress_workspace_size():
+    L = lib()
+    assert L.paged_kv_compress_workspace_bytes(ctypes.byref(sshape(num_seqs=3)), 100) == 1280 + 256
+    assert L.paged_kv_compress_workspace_bytes(ctypes.byref(sshape(num_seqs=3)), 0) == 256
+    assert L.paged_kv_compress_workspace_bytes(ctypes.byref(sshape()), -1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_seqs=-1), B.PA_ERR_SHAPE),
+    (dict(num_kv_heads=0), B.PA_ERR_SHAPE),
+    (dict(block_size=0), B.PA_ERR_SHAPE),
+    (dict(max_blocks_per_seq=0), B.PA_ERR_SHAPE),
+    (dict(num_blocks=0), B.PA_ERR_SHAPE),
+    (dict(head_dim=96), B.PA_ERR_UNSUPPORTED),
+    (dict(block_size=8192), B.PA_ERR_UNSUPPORTED),
+    (dict(num_seqs=70000), B.PA_ERR_UNSUPPORTED),
+])
+def test_compress_shape_errors(kw, code):
+    assert ccall(sshape(**kw)) == code
+
+
+def test_compress_host_checks():
+    L = lib()
+    assert ccall(sshape(), budget=-1) == B.PA_ERR_SHAPE
+    for name in ("k", "v", "sc", "bt", "cl"):
+        assert ccall(sshape(), **{name: ctypes.c_void_p(0)}) == B.PA_ERR_NULL, name
+    assert ccall(sshape(), ws=None) == B.PA_ERR_WORKSPACE
+    assert ccall(sshape(), wsb=16) == B.PA_ERR_WORKSPACE
+    assert ccall(sshape(), k=ctypes.c_void_p(0x100008)) == B.PA_ERR_ALIGNMENT
+    assert ccall(sshape(), ws=ctypes.c_void_p(0x100004)) == B.PA_ERR_ALIGNMENT
+    assert ccall(sshape(num_seqs=0), k=None, v=None, sc=None, bt=None, cl=None, ws=None) == B.PA_OK
+    assert L.paged_kv_compress_prefill_int8(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 8,
+                                            ctypes.byref(sshape()), FAKE, 1 << 20, None) == B.PA_ERR_NULL
+    assert L.paged_kv_compress_prefill_fp8(FAKE, ctypes.c_void_p(0x100004), FAKE, FAKE, FAKE, 8,
+                                           ctypes.byref(sshape()), FAKE, 1 << 20, None) == B.PA_ERR_ALIGNMENT
 
 
 # ---- chunked prefill (include/paged_prefill.h) ----
