@@ -29,7 +29,9 @@ line for it; with --workload scores_<decode workload> (e.g. scores_llama3_8b)
 it times PagedEviction's token scoring over that workload's whole cache; with
 --workload prefill_llama3_8b it times chunked-prefill attention (the eight
 512-token chunks of a 4096-token prompt in one call) against the bf16
-matrix-core peak.
+matrix-core peak; with --workload compress_<decode workload> it times
+PagedEviction's prefill-phase compression of that workload's cache to a
+1024-token budget per sequence.
 """
 from __future__ import annotations
 
@@ -140,6 +142,8 @@ def main() -> int:
         return bench_write(args)
     if args.workload.startswith("scores_"):
         return bench_scores(args)
+    if args.workload.startswith("compress_"):
+        return bench_compress(args)
     if args.workload in I.PREFILL_WORKLOADS:
         return bench_prefill(args)
     wl = I.WORKLOADS[args.workload]
@@ -444,6 +448,160 @@ def bench_scores(args) -> int:
     }
     print(json.dumps(record), flush=True)
     return 0
+
+
+COMPRESS_BUDGET = 1024   # tokens kept per sequence (the PagedEviction section's cache budget)
+
+
+def bench_compress(args) -> int:
+    """PagedEviction's prefill phase on its own: one paged_kv_compress_prefill
+    call per step, compressing every sequence of a decode workload's cache
+    (importances from paged_kv_token_scores) to COMPRESS_BUDGET tokens.  The
+    call works in place, so the cache, importances and lengths are restored
+    from a pristine copy before each step, outside the timed region."""
+    import torch
+
+    from paged_kv_cache_393_amd import accounting as A
+    from paged_kv_cache_393_amd import binding as B
+    from paged_kv_cache_393_amd import inputs as I
+
+    wl = I.WORKLOADS[args.workload[len("compress_"):]]
+    if wl.num_layers != 1:
+        raise SystemExit("compression bench takes a single-layer workload")
+    budget = COMPRESS_BUDGET
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = I.make_inputs(wl, dev)
+    v = I.layer_views(inp, 0)
+    scores = B.token_scores(v)
+    names = ["k_cache", "v_cache", "context_lens"] + (["k_scales", "v_scales"] if "k_scales" in v else [])
+    pristine = {n: v[n].clone() for n in names}
+    pristine_scores = scores.clone()
+    ws = torch.empty(max(16, B.compress_workspace_bytes(v["k_cache"], v["block_tables"], budget)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    print(f"[bench] inputs for compression of {wl.name} ready", file=sys.stderr, flush=True)
+
+    def step():
+        B.compress_prefill(v, scores, budget, workspace=ws, stream=stream)
+
+    flush_buf = None if args.no_flush else torch.ones((2 << 30) // 4, dtype=torch.float32,
+                                                       device=dev)
+
+    def restore_and_evict():
+        for n in names:
+            v[n].copy_(pristine[n])
+        scores.copy_(pristine_scores)
+        if flush_buf is not None:
+            flush_buf.amax()
+
+    for _ in range(args.warmup):
+        restore_and_evict()
+        step()
+    torch.cuda.synchronize()
+    ms = event_ms(stream, step, args.steps, before=restore_and_evict)
+    ms_sorted = sorted(ms)
+    ms_mean = statistics.fmean(ms)
+    pct = lambda q: ms_sorted[min(len(ms_sorted) - 1, int(q * len(ms_sorted)))]
+    print(f"[bench] {args.steps} timed steps done", file=sys.stderr, flush=True)
+
+    ctx = pristine["context_lens"].cpu().tolist()
+    sc_host = pristine_scores.cpu().numpy()
+    bt_host = v["block_tables"].cpu().numpy()
+    bs = wl.block_size
+    logical = []
+    for s_, n in enumerate(ctx):
+        t = list(range(n))
+        logical.append(sc_host[bt_host[s_][[x // bs for x in t]], [x % bs for x in t]])
+    moved = A.compress_moved_tokens(logical, budget)
+    nbytes = A.compress_bytes(ctx, budget, moved, wl.num_kv_heads, wl.head_dim, bs, wl.kv_dtype)
+    t_s = ms_mean / 1e3
+    gbps = nbytes / t_s / 1e9
+    copy_for_counters(args, dev, stream)
+    name = "compress_" + wl.name
+    over = [c for c in ctx if c > budget]
+    record = {
+        "metric": "PagedEviction prefill-phase compression context tokens/s and achieved HBM GB/s "
+                  "(% of peak), Llama-3-8B shape",
+        "value": sum(over) / t_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_mean,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype,
+        "data": "synthetic (seeded N(0,1) K/V, shuffled block pool; importances ||V||/||K|| of it)",
+        "config": {"workload": name, "num_seqs": wl.num_seqs, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "block_size": bs, "budget": budget,
+                   "context_tokens": sum(ctx), "compressed_seqs": len(over),
+                   "compressed_context_tokens": sum(over), "moved_tokens": moved,
+                   "kv_dtype": wl.kv_dtype,
+                   "cache_evict_between_steps": "2 GiB read" if flush_buf is not None else None},
+        "pct_of_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
+        "ms_p10": pct(0.10), "ms_median": pct(0.50), "ms_p90": pct(0.90),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_kv_compress_prefill call: compress_select_kernel + compress_move_kernel",
+            "achieved": gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS,
+            "traffic": measured_traffic(name, "compress"),
+            "algorithmic_bytes_per_call": nbytes,
+            "calls_per_step": 1,
+            "ms_per_call": ms_mean,
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_compress(
+            {n: pristine[n] for n in names} | {"block_tables": v["block_tables"]}, pristine_scores,
+            budget, v, scores, sum(over)),
+    }
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+def cpu_baseline_compress(pristine, pristine_scores, budget, gpu_views, gpu_scores, tokens,
+                          budget_s=12.0):
+    """The oracle's compression of the whole workload (one thread), median of
+    repeated runs on the host copy, scaled to compressed context tokens/s; and
+    whether the GPU's last result is bit-identical to it."""
+    import numpy as np
+
+    import oracle
+
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+    host = {n: t.cpu() for n, t in pristine.items()}
+    sc = pristine_scores.cpu().numpy()
+    times, ref = [], None
+    while sum(times) < budget_s and len(times) < 5:
+        t = time.perf_counter()
+        ref = oracle.compress_prefill(host, sc, budget)
+        times.append(time.perf_counter() - t)
+    t_med = statistics.median(times)
+    raw = lambda x: x.detach().cpu().contiguous().view(torch_uint8()).numpy().reshape(ref["k_cache"].shape)
+    same = (np.array_equal(raw(gpu_views["k_cache"]), ref["k_cache"]) and
+            np.array_equal(raw(gpu_views["v_cache"]), ref["v_cache"]) and
+            np.array_equal(gpu_views["context_lens"].cpu().numpy(), ref["context_lens"]) and
+            np.array_equal(gpu_scores.cpu().numpy().view(np.uint32), ref["scores"].view(np.uint32)))
+    return {
+        "value": tokens / t_med,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"the whole workload ({tokens} context tokens of compressed sequences), one "
+                  f"thread, median of {len(times)} runs of {t_med:.2f}s",
+        "parity_bit_identical_vs_gpu": bool(same),
+    }
+
+
+def torch_uint8():
+    import torch
+
+    return torch.uint8
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak, published

@@ -102,3 +102,41 @@ def prefill_bytes(context_lens: Iterable[int], n_q: Iterable[int], num_q_heads: 
     qo = sum(nq) * num_q_heads * head_dim * (2 + 4)
     tables = sum((c + block_size - 1) // block_size for c in ctx) * 4
     return kv + qo + tables + 8 * len(ctx) + 4
+
+
+def compress_moved_tokens(logical_scores, budget: int) -> int:
+    """Kept tokens that change position in a prefill-phase compression (the
+    rows the move kernel reads and writes), from each sequence's importances
+    in logical order: the budget highest-ranked tokens (NaN first, then
+    larger, then earlier) in position order, minus those already in place."""
+    import numpy as np
+
+    moved = 0
+    for vals in logical_scores:
+        vals = np.asarray(vals, dtype=np.float32)
+        n = len(vals)
+        if n <= budget:
+            continue
+        nan = np.isnan(vals)
+        key = np.where(nan, 0.0, vals).astype(np.float64)
+        order = np.lexsort((np.arange(n), -key, ~nan))
+        kept = np.sort(order[:budget])
+        moved += int(np.count_nonzero(kept != np.arange(budget)))
+    return moved
+
+
+def compress_bytes(context_lens: Iterable[int], budget: int, moved: int, num_kv_heads: int,
+                   head_dim: int, block_size: int, kv_dtype: str = "bf16") -> int:
+    """Algorithmic bytes of one prefill-phase compression call: the context
+    lengths (read, and written where a sequence is compressed); for each
+    compressed sequence its valid table entries and its importances (read
+    once); each moved token's K and V rows, int8 scales and importance (read
+    and written).  The kept-position list in the workspace is not counted."""
+    ctx = [int(c) for c in context_lens]
+    over = [c for c in ctx if c > budget]
+    elem = 2 if kv_dtype == "bf16" else 1
+    row = 2 * num_kv_heads * head_dim * elem + 4
+    if kv_dtype == "int8":
+        row += 2 * num_kv_heads * 4
+    tables = sum((c + block_size - 1) // block_size for c in over) * 4
+    return 4 * len(ctx) + 4 * len(over) + tables + 4 * sum(over) + 2 * moved * row
