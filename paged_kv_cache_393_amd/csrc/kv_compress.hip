@@ -14,13 +14,16 @@
 //   * select: one workgroup per sequence.  Each importance maps to a 32-bit
 //     key whose unsigned order is the ranking (without the position); a
 //     4-pass MSB-first radix select over 8-bit digits finds the key T of the
-//     budget-th token and how many tokens of key T are kept; a last pass in
+//     budget-th token and how many tokens of key T are kept (LDS histogram;
+//     on the first digit, which a sequence's keys mostly share, the lanes of
+//     a wave with equal digits add to its bin once); a last pass in
 //     position order marks the kept tokens (key > T, or key == T among the
 //     first ones) and writes their positions, compacted, to the workspace.
 //     Keys sit in LDS when the context fits, else they are recomputed from
 //     the table and the scores on each pass.
-//   * move: one workgroup per (kv head, sequence) moves that head's part of
-//     each kept row (K, V, int8 scales; the importance with head 0).  Kept
+//   * move: one workgroup per (kv head, sequence) -- or per slice of a head's
+//     row -- moves that part of each kept row (K, V, int8 scales; the
+//     importance with head 0).  Kept
 //     token j comes from position t_j >= j, so a row is only ever overwritten
 //     by a token at a lower position: destinations are taken in chunks, all
 //     reads of a chunk complete (vmcnt(0), barrier) before its writes, and a
@@ -41,7 +44,15 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kLdsKeys = 12288;      // contexts up to this many tokens keep their keys in LDS
 constexpr int kMoveThreads = 256;
-constexpr int kMoveRounds = 8;       // 16-B pieces in flight per thread and chunk
+#ifndef KC_ROUNDS
+#define KC_ROUNDS 8
+#endif
+#ifndef KC_SLICE
+#define KC_SLICE 256
+#endif
+constexpr int kMoveRounds = KC_ROUNDS;   // 16-B pieces in flight per thread and chunk
+constexpr int kSliceBytes = KC_SLICE;    // bytes of a head row one workgroup moves (whole lines)
+constexpr int kMoveWindow = 1024;        // kept tokens whose slots are resolved at once
 
 struct CompressParams {
     void *k;
@@ -55,6 +66,7 @@ struct CompressParams {
     int32_t *ctx;           // workspace: [S] context length at the call
     int hkv;
     int head_bytes;         // bytes of one kv head's row: head_dim * element size
+    int slices;             // workgroups per head row: head_bytes / slice bytes
     int block_size;
     int max_blocks_per_seq;
     int max_ctx;
@@ -91,7 +103,26 @@ __global__ __launch_bounds__(kSelThreads) void compress_select_kernel(CompressPa
         return rank_key(p.scores[slot_of(row, t, bs)]);
     };
     if (in_lds) {
-        for (int t = tid; t < n; t += kSelThreads) lds_key[t] = key_from_memory(t);
+        // four tokens per thread at a time: their table and score loads in flight together
+        for (int c0 = 0; c0 < n; c0 += 4 * kSelThreads) {
+            int64_t slot[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = c0 + u * kSelThreads + tid;
+                slot[u] = t < n ? slot_of(row, t, bs) : 0;
+            }
+            float x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = c0 + u * kSelThreads + tid;
+                x[u] = t < n ? p.scores[slot[u]] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = c0 + u * kSelThreads + tid;
+                if (t < n) lds_key[t] = rank_key(x[u]);
+            }
+        }
     }
     auto key_at = [&](int t) __attribute__((always_inline)) {
         return in_lds ? lds_key[t] : key_from_memory(t);
@@ -103,9 +134,25 @@ __global__ __launch_bounds__(kSelThreads) void compress_select_kernel(CompressPa
     for (int shift = 24; shift >= 0; shift -= 8) {
         if (tid < 256) hist[tid] = 0;
         __syncthreads();
-        for (int t = tid; t < n; t += kSelThreads) {
-            const uint32_t k = key_at(t);
-            if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        if (shift == 24) {
+            // first digit: the keys of a sequence mostly share it, so lanes of
+            // a wave with the same digit add to its bin once
+            for (int c0 = 0; c0 < n; c0 += kSelThreads) {
+                const int t = c0 + tid;
+                const uint32_t d = t < n ? key_at(t) >> 24 : 0u;
+                uint64_t todo = __ballot(t < n);
+                while (todo) {
+                    const uint32_t dl = __shfl(d, __builtin_ctzll(todo));
+                    const uint64_t same = __ballot(t < n && d == dl);
+                    if (lane == __builtin_ctzll(todo)) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
+                    todo &= ~same;
+                }
+            }
+        } else {
+            for (int t = tid; t < n; t += kSelThreads) {
+                const uint32_t k = key_at(t);
+                if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+            }
         }
         __syncthreads();
         if (wave == 0) {
@@ -114,11 +161,12 @@ __global__ __launch_bounds__(kSelThreads) void compress_select_kernel(CompressPa
             for (int b = 0; b < 4; ++b) c[b] = hist[4 * lane + b];
             const uint32_t mine = c[0] + c[1] + c[2] + c[3];
             // keys in the bins of higher lanes (every lane takes part in each shuffle)
-            uint32_t above = 0;
-            for (int l = 0; l < 64; ++l) {
-                const uint32_t o = __shfl(mine, l);
-                if (l > lane) above += o;
+            uint32_t incl = mine;   // inclusive suffix sum over lanes lane .. 63
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t o = __shfl_down(incl, off);
+                if (lane + off < 64) incl += o;
             }
+            uint32_t above = incl - mine;
             for (int b = 3; b >= 0; --b) {
                 if (above < (uint32_t)need && (uint32_t)need <= above + c[b]) {
                     lds_pick[0] = 4 * lane + b;
@@ -170,51 +218,75 @@ __global__ __launch_bounds__(kSelThreads) void compress_select_kernel(CompressPa
     }
 }
 
-// Moves the kept rows' part of kv head blockIdx.x of sequence blockIdx.y.
+// Moves slice blockIdx.x % slices of kv head blockIdx.x / slices of the kept
+// rows of sequence blockIdx.y.  The source and destination slots of a window
+// of kept tokens are resolved once into LDS (their keep-list and table loads
+// in flight together), so a chunk waits only for its own K/V loads.
 template <bool kScales>
 __global__ __launch_bounds__(kMoveThreads) void compress_move_kernel(CompressParams p) {
-    const int g = blockIdx.x;
+    __shared__ int64_t lds_src[kMoveWindow];   // source slot of kept token w0 + i, or -1 (in place)
+    __shared__ int64_t lds_dst[kMoveWindow];
+    const int g = blockIdx.x / p.slices;
+    const int slice = blockIdx.x - g * p.slices;
     const int s = blockIdx.y;
     const int tid = threadIdx.x;
     const int n = p.ctx[s];
     const int budget = p.budget;
     if (n <= budget) return;
-    if (budget > 0) {
-        const int bs = p.block_size;
-        const int32_t *row = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
-        const int32_t *keep = p.keep + (int64_t)s * budget;
-        const int pieces = p.head_bytes / 16;          // 16-B pieces of this head's row
-        const int tok_per_round = kMoveThreads / pieces;
-        const int piece = tid % pieces;
-        const int64_t row_bytes = (int64_t)p.hkv * p.head_bytes;
-        const int64_t col = (int64_t)g * p.head_bytes + piece * 16;
-        char *kbase = (char *)p.k + col;
-        char *vbase = (char *)p.v + col;
-        const bool lead = piece == 0;                   // moves the per-token floats
-        for (int c0 = 0; c0 < budget; c0 += kMoveRounds * tok_per_round) {
+    const int bs = p.block_size;
+    const int32_t *row = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
+    const int32_t *keep = p.keep + (int64_t)s * budget;
+    const int pieces = p.head_bytes / p.slices / 16;   // 16-B pieces of this slice
+    const int tok_per_round = kMoveThreads / pieces;
+    const int piece = tid % pieces;
+    const int64_t row_bytes = (int64_t)p.hkv * p.head_bytes;
+    const int64_t col = (int64_t)g * p.head_bytes + (int64_t)slice * pieces * 16 + piece * 16;
+    char *kbase = (char *)p.k + col;
+    char *vbase = (char *)p.v + col;
+    const bool lead = slice == 0 && piece == 0;     // moves the per-token floats
+    for (int w0 = 0; w0 < budget; w0 += kMoveWindow) {
+        const int wn = min(kMoveWindow, budget - w0);
+        __syncthreads();   // the previous window's slots have been read
+        constexpr int kPer = kMoveWindow / kMoveThreads;
+        int tk[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int i = u * kMoveThreads + tid;
+            tk[u] = i < wn ? keep[w0 + i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int i = u * kMoveThreads + tid;
+            const int j = w0 + i;
+            const bool mv = i < wn && tk[u] > j && tk[u] < n;   // kept token tk moves down to j
+            if (i < wn) {
+                lds_src[i] = mv ? slot_of(row, tk[u], bs) : -1;
+                lds_dst[i] = mv ? slot_of(row, j, bs) : -1;
+            }
+        }
+        __syncthreads();
+        for (int c0 = 0; c0 < wn; c0 += kMoveRounds * tok_per_round) {
             u32x4_t kr[kMoveRounds], vr[kMoveRounds];
             float ks[kMoveRounds], vs[kMoveRounds], sc[kMoveRounds];
-            int dst_j[kMoveRounds];
-            int64_t src_slot[kMoveRounds];
+            int64_t src[kMoveRounds], dst[kMoveRounds];
 #pragma unroll
             for (int r = 0; r < kMoveRounds; ++r) {
-                const int j = c0 + r * tok_per_round + tid / pieces;
-                const int t = j < budget ? keep[j] : j;
-                dst_j[r] = (j < budget && t != j && t > j && t < n) ? j : -1;
-                src_slot[r] = dst_j[r] >= 0 ? slot_of(row, t, bs) : 0;
+                const int i = c0 + r * tok_per_round + tid / pieces;
+                src[r] = i < wn ? lds_src[i] : -1;
+                dst[r] = i < wn ? lds_dst[i] : -1;
             }
 #pragma unroll
             for (int r = 0; r < kMoveRounds; ++r) {
-                if (dst_j[r] < 0) continue;
-                const int64_t off = src_slot[r] * row_bytes;
+                if (src[r] < 0) continue;
+                const int64_t off = src[r] * row_bytes;
                 kr[r] = __builtin_nontemporal_load((const u32x4_t *)(kbase + off));
                 vr[r] = __builtin_nontemporal_load((const u32x4_t *)(vbase + off));
                 if (lead) {
                     if constexpr (kScales) {
-                        ks[r] = p.k_scales[src_slot[r] * p.hkv + g];
-                        vs[r] = p.v_scales[src_slot[r] * p.hkv + g];
+                        ks[r] = p.k_scales[src[r] * p.hkv + g];
+                        vs[r] = p.v_scales[src[r] * p.hkv + g];
                     }
-                    if (g == 0) sc[r] = p.scores[src_slot[r]];
+                    if (g == 0) sc[r] = p.scores[src[r]];
                 }
             }
             // Every read of this chunk has returned before any thread writes.
@@ -222,22 +294,21 @@ __global__ __launch_bounds__(kMoveThreads) void compress_move_kernel(CompressPar
             __syncthreads();
 #pragma unroll
             for (int r = 0; r < kMoveRounds; ++r) {
-                if (dst_j[r] < 0) continue;
-                const int64_t dslot = slot_of(row, dst_j[r], bs);
-                const int64_t off = dslot * row_bytes;
+                if (src[r] < 0) continue;
+                const int64_t off = dst[r] * row_bytes;
                 *(u32x4_t *)(kbase + off) = kr[r];
                 *(u32x4_t *)(vbase + off) = vr[r];
                 if (lead) {
                     if constexpr (kScales) {
-                        p.k_scales[dslot * p.hkv + g] = ks[r];
-                        p.v_scales[dslot * p.hkv + g] = vs[r];
+                        p.k_scales[dst[r] * p.hkv + g] = ks[r];
+                        p.v_scales[dst[r] * p.hkv + g] = vs[r];
                     }
-                    if (g == 0) p.scores[dslot] = sc[r];
+                    if (g == 0) p.scores[dst[r]] = sc[r];
                 }
             }
         }
     }
-    if (g == 0 && tid == 0) p.context_lens[s] = budget;
+    if (blockIdx.x == 0 && tid == 0) p.context_lens[s] = budget;
 }
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
@@ -252,7 +323,7 @@ int compress_common(bool int8, int elem, void *k, void *v, float *ks, float *vs,
         sh->max_blocks_per_seq < 1 || sh->num_blocks < 1 || budget < 0)
         return PA_ERR_SHAPE;
     if (sh->head_dim != 64 && sh->head_dim != 128) return PA_ERR_UNSUPPORTED;
-    if (sh->block_size > 4096 || sh->num_seqs > 65535 || sh->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+    if (sh->block_size > 4096 || sh->num_seqs > 65535 || sh->num_kv_heads > 32767) return PA_ERR_UNSUPPORTED;
     const int64_t max_ctx = (int64_t)sh->max_blocks_per_seq * sh->block_size;
     if (max_ctx >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
     if (sh->num_seqs == 0) return PA_OK;
@@ -274,13 +345,14 @@ int compress_common(bool int8, int elem, void *k, void *v, float *ks, float *vs,
     p.ctx = (int32_t *)((char *)ws + keep_bytes(sh->num_seqs, budget));
     p.hkv = sh->num_kv_heads;
     p.head_bytes = sh->head_dim * elem;
+    p.slices = p.head_bytes > kSliceBytes ? p.head_bytes / kSliceBytes : 1;
     p.block_size = sh->block_size;
     p.max_blocks_per_seq = sh->max_blocks_per_seq;
     p.max_ctx = (int)max_ctx;
     p.budget = budget;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(compress_select_kernel, dim3((unsigned)sh->num_seqs), dim3(kSelThreads), 0, st, p);
-    const dim3 mgrid((unsigned)sh->num_kv_heads, (unsigned)sh->num_seqs);
+    const dim3 mgrid((unsigned)(sh->num_kv_heads * p.slices), (unsigned)sh->num_seqs);
     if (int8) hipLaunchKernelGGL(compress_move_kernel<true>, mgrid, dim3(kMoveThreads), 0, st, p);
     else hipLaunchKernelGGL(compress_move_kernel<false>, mgrid, dim3(kMoveThreads), 0, st, p);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
