@@ -569,6 +569,7 @@ def cpu_baseline_compress(pristine, pristine_scores, budget, gpu_views, gpu_scor
     repeated runs on the host copy, scaled to compressed context tokens/s; and
     whether the GPU's last result is bit-identical to it."""
     import numpy as np
+    import torch
 
     import oracle
 
@@ -582,7 +583,7 @@ def cpu_baseline_compress(pristine, pristine_scores, budget, gpu_views, gpu_scor
         ref = oracle.compress_prefill(host, sc, budget)
         times.append(time.perf_counter() - t)
     t_med = statistics.median(times)
-    raw = lambda x: x.detach().cpu().contiguous().view(torch_uint8()).numpy().reshape(ref["k_cache"].shape)
+    raw = lambda x: x.detach().cpu().contiguous().view(torch.uint8).numpy().reshape(ref["k_cache"].shape)
     same = (np.array_equal(raw(gpu_views["k_cache"]), ref["k_cache"]) and
             np.array_equal(raw(gpu_views["v_cache"]), ref["v_cache"]) and
             np.array_equal(gpu_views["context_lens"].cpu().numpy(), ref["context_lens"]) and
@@ -596,12 +597,6 @@ def cpu_baseline_compress(pristine, pristine_scores, budget, gpu_views, gpu_scor
                   f"thread, median of {len(times)} runs of {t_med:.2f}s",
         "parity_bit_identical_vs_gpu": bool(same),
     }
-
-
-def torch_uint8():
-    import torch
-
-    return torch.uint8
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak, published

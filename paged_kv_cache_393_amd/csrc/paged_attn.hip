@@ -92,12 +92,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 enum KvKind : int { kBf16 = 0, kInt8 = 1, kFp8 = 2 };
 // Word 3 of a raw (unformatted, stride 0) buffer resource on CDNA3/CDNA4.
 constexpr int kRsrcFlags = 0x00020000;
-// Cache-policy operand of the K/V buffer loads: the non-temporal bit (nt).
-// Every K/V byte is read once per call, so the streamed lines are not kept in
-// the caches; with it the Llama-3-8B batch step went from 112 to 102 us, the
-// 70B-shaped layers from 1344 to 1210 us.  The int8 scale loads keep the
-// default policy: a scale line holds the scales of all kv heads of 4 slots
-// and is read by both workgroups of a slot (219 vs 215 us with nt).
+// Cache-policy operand of the V buffer loads: the non-temporal bit (nt).
+// Every V byte is read once per call, and a V load instruction reads whole
+// 256-B runs, so the streamed lines are not kept in the caches; with it the
+// Llama-3-8B batch step went from 112 to 102 us, the 70B-shaped layers from
+// 1344 to 1210 us.  K loads keep the default policy: a K load instruction
+// reads 64 B (32 B for 1-byte caches) of each of 16 token rows and the rest of
+// each 128-B line comes with the next instructions, which then hit in the
+// cache (int8 215 -> 202 us, fp8 198 -> 193 us against nt on K too).  The
+// int8 scale loads keep it as well: a scale line holds the scales of all kv
+// heads of 4 slots and is read by both workgroups of a slot.
 constexpr int kStreamPolicy = 2;
 
 struct Params {
@@ -423,7 +427,7 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
 #pragma unroll
             for (int m = 0; m < L::kKLoads; ++m)
                 r.k[m] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                             kr, k_off + m * 4 * L::kKElemsPerLoad * L::kElem, 0, kStreamPolicy));
+                             kr, k_off + m * 4 * L::kKElemsPerLoad * L::kElem, 0, 0));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if constexpr (L::kVBytes == 16)
