@@ -136,6 +136,22 @@ int paged_attn_decode_fp8(const void *q, const uint8_t *k_cache, const uint8_t *
                           float *out, const pa_shape *shape, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/*
+ * Device-side check of the caller contract that the decode (and the prefill,
+ * scoring and compression) entry points do not check, since it needs a device
+ * read: for every sequence s, 0 <= context_lens[s] <= max_blocks_per_seq *
+ * block_size, and block_tables[s][j] lies in [0, num_blocks) for every
+ * j < ceil(context_lens[s] / block_size).  It reads only block_tables and
+ * context_lens (device memory), never a cache, so it is safe on arguments
+ * that break the contract.  It writes, in device memory, result[0] = the
+ * number of sequences that break it and result[1] = the lowest such s, or -1.
+ * One kernel launch of one workgroup on `stream`; no workspace.  Meant for
+ * debugging a caller: it does not change what the other entry points do.
+ */
+int paged_attn_check_tables(const int32_t *block_tables, const int32_t *context_lens,
+                            int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
+                            int32_t num_blocks, int32_t *result, void *stream);
+
 /* Static description of an error code; never NULL. */
 const char *paged_attn_strerror(int code);
 

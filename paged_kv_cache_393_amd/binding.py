@@ -100,6 +100,9 @@ def load() -> ctypes.CDLL:
     lib.paged_kv_token_scores_fp8.restype = ctypes.c_int
     lib.paged_kv_evict_lowest_block.argtypes = [P, P, P, P, P, CP, P]
     lib.paged_kv_evict_lowest_block.restype = ctypes.c_int
+    lib.paged_attn_check_tables.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, P, P]
+    lib.paged_attn_check_tables.restype = ctypes.c_int
     lib.paged_kv_compress_workspace_bytes.argtypes = [CP, ctypes.c_int32]
     lib.paged_kv_compress_workspace_bytes.restype = ctypes.c_size_t
     lib.paged_kv_compress_prefill.argtypes = [P, P, P, P, P, ctypes.c_int32, CP, P, ctypes.c_size_t, P]
@@ -438,6 +441,23 @@ def evict_lowest_block(scores, block_tables, context_lens, evict_mask, evicted=N
                                               _ptr(evict_mask), _ptr(evicted), ctypes.byref(sh),
                                               _stream_handle(stream)))
     return evicted
+
+
+def check_tables(block_tables, context_lens, num_blocks: int, block_size: int, stream=None):
+    """paged_attn_check_tables: (number of sequences breaking the caller
+    contract, lowest such sequence or -1), checked on the device."""
+    for name, t in (("block_tables", block_tables), ("context_lens", context_lens)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.int32:
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    S, MB = block_tables.shape
+    if tuple(context_lens.shape) != (S,):
+        raise ValueError("context_lens must be [num_seqs]")
+    res = torch.empty(2, dtype=torch.int32, device=block_tables.device)
+    _check(load().paged_attn_check_tables(_ptr(block_tables), _ptr(context_lens), S, MB,
+                                          int(block_size), int(num_blocks), _ptr(res),
+                                          _stream_handle(stream)))
+    r = res.cpu().tolist()   # synchronises with the stream
+    return r[0], r[1]
 
 
 def compress_workspace_bytes(k_cache, block_tables, budget: int) -> int:

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(_HERE)
 LIBS = [
     ([os.path.join(_HERE, "csrc", "paged_attn.hip"), os.path.join(_HERE, "csrc", "kv_write.hip"),
       os.path.join(_HERE, "csrc", "kv_evict.hip"), os.path.join(_HERE, "csrc", "paged_prefill.hip"),
-      os.path.join(_HERE, "csrc", "kv_compress.hip")],
+      os.path.join(_HERE, "csrc", "kv_compress.hip"), os.path.join(_HERE, "csrc", "check_tables.hip")],
      os.path.join(_HERE, "libpagedattn.so")),
     ([os.path.join(_HERE, "csrc", "pa_probe.hip")], os.path.join(_HERE, "libpaprobe.so")),
 ]

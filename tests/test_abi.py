@@ -13,7 +13,7 @@ DECLARED = {"paged_attn_plan", "paged_attn_workspace_bytes", "paged_attn_decode"
             "paged_kv_evict_lowest_block", "paged_attn_prefill", "paged_attn_prefill_int8",
             "paged_attn_prefill_fp8", "paged_kv_compress_workspace_bytes",
             "paged_kv_compress_prefill", "paged_kv_compress_prefill_int8",
-            "paged_kv_compress_prefill_fp8"}
+            "paged_kv_compress_prefill_fp8", "paged_attn_check_tables"}
 
 
 def lib():
@@ -281,6 +281,17 @@ def test_score_and_evict_null_alignment_and_empty():
         assert L.paged_kv_evict_lowest_block(*args, ctypes.byref(sshape()), None) == B.PA_ERR_NULL
     assert L.paged_kv_evict_lowest_block(None, None, None, None, None,
                                          ctypes.byref(sshape(num_seqs=0)), None) == B.PA_OK
+
+
+def test_check_tables_host_errors():
+    L = lib()
+    assert L.paged_attn_check_tables(FAKE, FAKE, -1, 4, 16, 8, FAKE, None) == B.PA_ERR_SHAPE
+    assert L.paged_attn_check_tables(FAKE, FAKE, 2, 0, 16, 8, FAKE, None) == B.PA_ERR_SHAPE
+    assert L.paged_attn_check_tables(FAKE, FAKE, 2, 4, 0, 8, FAKE, None) == B.PA_ERR_SHAPE
+    assert L.paged_attn_check_tables(FAKE, FAKE, 2, 4, 16, 0, FAKE, None) == B.PA_ERR_SHAPE
+    assert L.paged_attn_check_tables(FAKE, FAKE, 2, 4, 16, 8, None, None) == B.PA_ERR_NULL
+    assert L.paged_attn_check_tables(None, FAKE, 2, 4, 16, 8, FAKE, None) == B.PA_ERR_NULL
+    assert L.paged_attn_check_tables(FAKE, None, 2, 4, 16, 8, FAKE, None) == B.PA_ERR_NULL
 
 
 # ---- prefill-phase compression (include/paged_kv_evict.h) ----
