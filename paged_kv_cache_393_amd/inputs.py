@@ -94,6 +94,9 @@ WORKLOADS = {
                                ctx_range=(1024, 8192), kv_dtype="int8"),
     "fp8_llama3_8b": Workload("fp8_llama3_8b", 128, 32, 8, 128, 16, seed=9,
                               ctx_range=(1024, 8192), kv_dtype="fp8"),
+    # One tensor-parallel rank's share of the llama3_8b batch at TP = 8: one kv
+    # head and its 4 query heads per rank, the same sequences and lengths.
+    "llama3_8b_tp8": Workload("llama3_8b_tp8", 64, 4, 1, 128, 16, seed=2, ctx_range=(512, 4096)),
 }
 
 

@@ -260,7 +260,7 @@ def test_fp8_nan_code_reaches_only_its_output_elements():
 # checks a seeded sample of sequences (all of their heads, all of their tokens).
 FULL = [("tiny", None, 0), ("llama3_8b", (0, 17, 63), 0), ("long_context", (2,), 0),
         ("nano_vllm_70b", (5, 30), 0), ("int8_llama3_8b", (0, 64, 127), 0),
-        ("fp8_llama3_8b", (0, 64, 127), 0)]
+        ("fp8_llama3_8b", (0, 64, 127), 0), ("llama3_8b_tp8", (0, 17, 63), 0)]
 
 
 @pytest.mark.parametrize("name,sample,layer", FULL)
