@@ -118,7 +118,9 @@ int paged_kv_evict_lowest_block(const float *scores, int32_t *block_tables,
  * must be 16-byte aligned.
  *
  * Workspace: paged_kv_compress_workspace_bytes(shape, budget) bytes of device
- * memory (kept positions and context lengths), 16-byte aligned, contents
+ * memory (kept positions int32 [num_seqs, budget], then context lengths int32
+ * [num_seqs], each part rounded up to 256 bytes; 0 for a NULL shape, a
+ * negative num_seqs or a negative budget), 16-byte aligned, contents
  * irrelevant; no two calls may use it at once.  Two kernel launches.
  * Caller contract (not checked): valid and pairwise distinct block ids for
  * every logical block of every sequence with n > budget.
