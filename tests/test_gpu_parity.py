@@ -84,6 +84,18 @@ def test_group_sizes_not_powers_of_two_and_large(Hq, Hkv):
     assert_parity(run(v, 256), ref, "split 256")
 
 
+def test_batches_beyond_the_lds_prefix():
+    # More than 2048 sequences: each workgroup finds its item's first sequence
+    # by a running scan over the context lengths instead of the LDS prefix.
+    rng = np.random.default_rng(60)
+    ctx = tuple(int(x) for x in rng.integers(0, 60, 3000))
+    note(f"3000 sequences, ctx 0..59")
+    _, v = C.make_case(len(ctx), 8, 2, 64, 16, ctx=ctx, seed=60, device=DEV)
+    ref = C.oracle_out(v)
+    for st in (0, 16, 64):
+        assert_parity(run(v, st), ref, f"split={st}")
+
+
 def test_context_one_is_exactly_v():
     note("ctx=1 exact")
     _, v = C.make_case(3, 8, 2, 128, 16, ctx=(1, 1, 1), NB=9, seed=31, device=DEV)
