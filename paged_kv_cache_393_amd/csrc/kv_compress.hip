@@ -19,8 +19,8 @@
 //     a wave with equal digits add to its bin once); a last pass in
 //     position order marks the kept tokens (key > T, or key == T among the
 //     first ones) and writes their positions, compacted, to the workspace.
-//     Keys sit in LDS when the context fits, else they are recomputed from
-//     the table and the scores on each pass.
+//     Keys sit in LDS when the context fits, else in the workspace, written
+//     once and read back by every pass.
 //   * move: one workgroup per (kv head, sequence) -- or per slice of a head's
 //     row -- moves that part of each kept row (K, V, int8 scales; the
 //     importance with head 0).  Kept
@@ -64,6 +64,7 @@ struct CompressParams {
     int32_t *context_lens;
     int32_t *keep;          // workspace: [S, budget] kept positions
     int32_t *ctx;           // workspace: [S] context length at the call
+    uint32_t *keys;         // workspace: [S, max_ctx] ranking keys of contexts too long for LDS
     int hkv;
     int head_bytes;         // bytes of one kv head's row: head_dim * element size
     int slices;             // workgroups per head row: head_bytes / slice bytes
@@ -99,10 +100,9 @@ __global__ __launch_bounds__(kSelThreads) void compress_select_kernel(CompressPa
     const int bs = p.block_size;
     const int32_t *row = p.block_tables + (int64_t)s * p.max_blocks_per_seq;
     const bool in_lds = n <= kLdsKeys;
-    auto key_from_memory = [&](int t) __attribute__((always_inline)) {
-        return rank_key(p.scores[slot_of(row, t, bs)]);
-    };
-    if (in_lds) {
+    // Keys of a context too long for LDS go to this sequence's workspace row.
+    uint32_t *gkeys = p.keys + (int64_t)s * p.max_ctx;
+    {
         // four tokens per thread at a time: their table and score loads in flight together
         for (int c0 = 0; c0 < n; c0 += 4 * kSelThreads) {
             int64_t slot[4];
@@ -120,12 +120,17 @@ __global__ __launch_bounds__(kSelThreads) void compress_select_kernel(CompressPa
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int t = c0 + u * kSelThreads + tid;
-                if (t < n) lds_key[t] = rank_key(x[u]);
+                if (t < n) {
+                    if (in_lds) lds_key[t] = rank_key(x[u]);
+                    else gkeys[t] = rank_key(x[u]);
+                }
             }
         }
+        // the workgroup's global key stores are complete and visible to all its waves
+        if (!in_lds) __threadfence_block();
     }
     auto key_at = [&](int t) __attribute__((always_inline)) {
-        return in_lds ? lds_key[t] : key_from_memory(t);
+        return in_lds ? lds_key[t] : gkeys[t];
     };
 
     // Radix select of the budget-th largest key, 8 bits a pass from the top.
@@ -149,9 +154,18 @@ __global__ __launch_bounds__(kSelThreads) void compress_select_kernel(CompressPa
                 }
             }
         } else {
-            for (int t = tid; t < n; t += kSelThreads) {
-                const uint32_t k = key_at(t);
-                if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+            for (int c0 = 0; c0 < n; c0 += 4 * kSelThreads) {
+                uint32_t k[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int t = c0 + u * kSelThreads + tid;
+                    k[u] = t < n ? key_at(t) : 0u;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int t = c0 + u * kSelThreads + tid;
+                    if (t < n && (k[u] & mask) == prefix) atomicAdd(&hist[(k[u] >> shift) & 255u], 1u);
+                }
             }
         }
         __syncthreads();
@@ -188,9 +202,11 @@ __global__ __launch_bounds__(kSelThreads) void compress_select_kernel(CompressPa
     int eq_before = 0, kept_before = 0;
     int32_t *keep = p.keep + (int64_t)s * budget;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t k_next = tid < n ? key_at(tid) : 0u;
     for (int c0 = 0; c0 < n; c0 += kSelThreads) {
         const int t = c0 + tid;
-        const uint32_t k = t < n ? key_at(t) : 0u;
+        const uint32_t k = k_next;   // this chunk's key; the next one's load is in flight meanwhile
+        k_next = t + kSelThreads < n ? key_at(t + kSelThreads) : 0u;
         const bool eq = t < n && k == T;
         const uint64_t eq_bal = __ballot(eq);
         if (lane == 0) lds_wave[0][wave] = __popcll(eq_bal);
@@ -314,6 +330,11 @@ __global__ __launch_bounds__(kMoveThreads) void compress_move_kernel(CompressPar
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 size_t keep_bytes(int64_t S, int64_t budget) { return (size_t)(((S * budget * 4) + 255) & ~(int64_t)255); }
+size_t ctx_bytes(int64_t S) { return (size_t)(((S * 4) + 255) & ~(int64_t)255); }
+// Key rows are needed only for contexts longer than the LDS holds.
+size_t key_bytes(int64_t S, int64_t max_ctx) {
+    return max_ctx > kLdsKeys ? (size_t)(((S * max_ctx * 4) + 255) & ~(int64_t)255) : 0;
+}
 
 int compress_common(bool int8, int elem, void *k, void *v, float *ks, float *vs, float *scores,
                     const int32_t *bt, int32_t *cl, int32_t budget, const pa_score_shape *sh,
@@ -343,6 +364,7 @@ int compress_common(bool int8, int elem, void *k, void *v, float *ks, float *vs,
     p.context_lens = cl;
     p.keep = (int32_t *)ws;
     p.ctx = (int32_t *)((char *)ws + keep_bytes(sh->num_seqs, budget));
+    p.keys = (uint32_t *)((char *)ws + keep_bytes(sh->num_seqs, budget) + ctx_bytes(sh->num_seqs));
     p.hkv = sh->num_kv_heads;
     p.head_bytes = sh->head_dim * elem;
     p.slices = p.head_bytes > kSliceBytes ? p.head_bytes / kSliceBytes : 1;
@@ -364,7 +386,8 @@ extern "C" {
 
 size_t paged_kv_compress_workspace_bytes(const pa_score_shape *shape, int32_t budget) {
     if (!shape || shape->num_seqs < 0 || budget < 0) return 0;
-    return keep_bytes(shape->num_seqs, budget) + (size_t)((((int64_t)shape->num_seqs * 4) + 255) & ~(int64_t)255);
+    return keep_bytes(shape->num_seqs, budget) + ctx_bytes(shape->num_seqs) +
+           key_bytes(shape->num_seqs, (int64_t)shape->max_blocks_per_seq * shape->block_size);
 }
 
 int paged_kv_compress_prefill(void *k_cache, void *v_cache, float *scores,

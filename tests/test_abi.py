@@ -305,6 +305,9 @@ def test_compress_workspace_size():
     assert L.paged_kv_compress_workspace_bytes(ctypes.byref(sshape(num_seqs=3)), 100) == 1280 + 256
     assert L.paged_kv_compress_workspace_bytes(ctypes.byref(sshape(num_seqs=3)), 0) == 256
     assert L.paged_kv_compress_workspace_bytes(ctypes.byref(sshape()), -1) == 0
+    # contexts longer than the LDS key buffer (12288) add a key row per sequence
+    long = sshape(num_seqs=2, max_blocks_per_seq=1000, block_size=16)
+    assert L.paged_kv_compress_workspace_bytes(ctypes.byref(long), 100) == 1024 + 256 + 2 * 16000 * 4
 
 
 @pytest.mark.parametrize("kw,code", [
