@@ -85,3 +85,39 @@ def test_select_sequences_relabels_blocks():
     assert sub["block_tables"][0, :16].tolist() == list(range(16))
     b_old = int(v["block_tables"][1, 1])
     assert torch.equal(sub["k_cache"][17].view(torch.int16), v["k_cache"][b_old].view(torch.int16))
+
+
+def test_compress_moved_tokens_closed_forms_and_oracle():
+    import numpy as np
+
+    import oracle
+    from tests import _cases as C
+
+    rise = np.arange(50, dtype=np.float32)
+    assert A.compress_moved_tokens([rise], 20) == 20          # newest kept: every row moves
+    assert A.compress_moved_tokens([-rise], 20) == 0          # prefix kept: nothing moves
+    assert A.compress_moved_tokens([rise[:10]], 20) == 0      # under the budget: untouched
+    tail_nan = -rise.copy()
+    tail_nan[45] = np.nan                                      # NaN kept first: one row moves
+    assert A.compress_moved_tokens([tail_nan], 20) == 1
+    # against the rows the oracle actually moves, on a random case
+    bs, budget, ctx = 16, 37, (90, 37, 64, 5)
+    _, v = C.make_case(4, 4, 1, 64, bs, ctx=ctx, seed=81)
+    rng = np.random.default_rng(81)
+    per_seq = [np.round(rng.standard_normal(n), 1).astype(np.float32) for n in ctx]
+    NB = v["k_cache"].shape[0]
+    sc = np.zeros((NB, bs), np.float32)
+    bt = v["block_tables"].numpy()
+    for s, vals in enumerate(per_seq):
+        for t, x in enumerate(vals):
+            sc[bt[s, t // bs], t % bs] = x
+    res = oracle.compress_prefill(v, sc, budget)
+    kb0 = v["k_cache"].contiguous().view(torch.uint8).numpy().reshape(NB, bs, -1)
+    moved = 0
+    for s, n in enumerate(ctx):
+        if n <= budget:
+            continue
+        for j in range(budget):
+            blk, r = bt[s, j // bs], j % bs
+            moved += int(not np.array_equal(res["k_cache"][blk, r].reshape(-1), kb0[blk, r]))
+    assert A.compress_moved_tokens(per_seq, budget) == moved
