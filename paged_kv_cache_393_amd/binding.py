@@ -7,6 +7,7 @@ missing or a call fails, this module raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
@@ -170,6 +171,14 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _on(stream):
+    """Context for the tensors a wrapper allocates for a call on `stream`:
+    made under it, they belong to that stream, so the caching allocator does
+    not hand their memory to other work before the call's kernels are done,
+    and a fill that initialises one runs on that stream, before the call."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _stream_handle(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -214,10 +223,11 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out=No
     """out fp32 [S, Hq, D] = paged_attn_decode(...) on the current (or given) stream."""
     _validate(q, k_cache, v_cache, block_tables, context_lens, torch.bfloat16)
     shape = shape_of(q, k_cache, block_tables, split_tokens)
-    if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = alloc_workspace(shape, q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = alloc_workspace(shape, q.device)
     ws_n = workspace.numel() if workspace is not None else 0
     rc = load().paged_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                   _ptr(context_lens), ctypes.c_float(scale), _ptr(out),
@@ -238,10 +248,11 @@ def decode_int8(q, k_cache, v_cache, k_scales, v_scales, block_tables, context_l
         if tuple(t.shape) != tuple(k_cache.shape[:3]):
             raise ValueError(f"{name} must be [num_blocks, block_size, num_kv_heads]")
     shape = shape_of(q, k_cache, block_tables, split_tokens)
-    if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = alloc_workspace(shape, q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = alloc_workspace(shape, q.device)
     ws_n = workspace.numel() if workspace is not None else 0
     rc = load().paged_attn_decode_int8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
                                        _ptr(v_scales), _ptr(block_tables), _ptr(context_lens),
@@ -263,10 +274,11 @@ def decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale: float, ou
         raise TypeError("fp8 cache must be float8_e4m3fn (or uint8 codes)")
     _validate(q, k_cache, v_cache, block_tables, context_lens, k_cache.dtype)
     shape = shape_of(q, k_cache, block_tables, split_tokens)
-    if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = alloc_workspace(shape, q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = alloc_workspace(shape, q.device)
     rc = load().paged_attn_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                       _ptr(context_lens), ctypes.c_float(scale), _ptr(out),
                                       ctypes.byref(shape), _ptr(workspace),
@@ -396,7 +408,8 @@ def token_scores(views: dict, scores=None, token_begin=None, stream=None) -> tor
         raise TypeError("block_tables and context_lens must be int32")
     NB, bs = kc.shape[0], kc.shape[1]
     if scores is None:
-        scores = torch.full((NB, bs), float("nan"), dtype=torch.float32, device=kc.device)
+        with _on(stream):
+            scores = torch.full((NB, bs), float("nan"), dtype=torch.float32, device=kc.device)
     if scores.dtype != torch.float32 or tuple(scores.shape) != (NB, bs) or not scores.is_contiguous():
         raise ValueError("scores must be contiguous fp32 [num_blocks, block_size]")
     if token_begin is not None and (token_begin.dtype != torch.int32 or not token_begin.is_cuda):
@@ -435,7 +448,8 @@ def evict_lowest_block(scores, block_tables, context_lens, evict_mask, evicted=N
     if tuple(context_lens.shape) != (S,) or tuple(evict_mask.shape) != (S,):
         raise ValueError("context_lens and evict_mask must be [S]")
     if evicted is None:
-        evicted = torch.empty(S, dtype=torch.int32, device=scores.device)
+        with _on(stream):
+            evicted = torch.empty(S, dtype=torch.int32, device=scores.device)
     sh = PaScoreShape(S, 1, 64, bs, MB, NB)     # heads / head_dim are not used here
     _check(load().paged_kv_evict_lowest_block(_ptr(scores), _ptr(block_tables), _ptr(context_lens),
                                               _ptr(evict_mask), _ptr(evicted), ctypes.byref(sh),
@@ -452,11 +466,12 @@ def check_tables(block_tables, context_lens, num_blocks: int, block_size: int, s
     S, MB = block_tables.shape
     if tuple(context_lens.shape) != (S,):
         raise ValueError("context_lens must be [num_seqs]")
-    res = torch.empty(2, dtype=torch.int32, device=block_tables.device)
-    _check(load().paged_attn_check_tables(_ptr(block_tables), _ptr(context_lens), S, MB,
-                                          int(block_size), int(num_blocks), _ptr(res),
-                                          _stream_handle(stream)))
-    r = res.cpu().tolist()   # synchronises with the stream
+    with _on(stream):
+        res = torch.empty(2, dtype=torch.int32, device=block_tables.device)
+        _check(load().paged_attn_check_tables(_ptr(block_tables), _ptr(context_lens), S, MB,
+                                              int(block_size), int(num_blocks), _ptr(res),
+                                              _stream_handle(stream)))
+        r = res.cpu().tolist()   # copied on the call's stream, after the check
     return r[0], r[1]
 
 
@@ -487,7 +502,8 @@ def compress_prefill(views: dict, scores, budget: int, workspace=None, stream=No
     L = load()
     need = int(L.paged_kv_compress_workspace_bytes(ctypes.byref(sh), int(budget)))
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=kc.device)
+        with _on(stream):
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=kc.device)
     st = _stream_handle(stream)
     ws, wsb = _ptr(workspace), workspace.numel() * workspace.element_size()
     if kc.dtype in FP8_DTYPES:
@@ -540,7 +556,8 @@ def prefill(q, k_cache, v_cache, block_tables, context_lens, q_offsets, scale: f
     sh = _prefill_shape(q, k_cache, v_cache, block_tables, context_lens, q_offsets, max_q_len,
                         (torch.bfloat16,))
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        with _on(stream):
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     _check(load().paged_attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                      _ptr(context_lens), _ptr(q_offsets), ctypes.c_float(scale),
                                      _ptr(out), ctypes.byref(sh), _stream_handle(stream)))
@@ -553,7 +570,8 @@ def prefill_int8(q, k_cache, v_cache, k_scales, v_scales, block_tables, context_
     sh = _prefill_shape(q, k_cache, v_cache, block_tables, context_lens, q_offsets, max_q_len,
                         (torch.int8,), (("k_scales", k_scales), ("v_scales", v_scales)))
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        with _on(stream):
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     _check(load().paged_attn_prefill_int8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
                                           _ptr(v_scales), _ptr(block_tables), _ptr(context_lens),
                                           _ptr(q_offsets), ctypes.c_float(scale), _ptr(out),
@@ -567,7 +585,8 @@ def prefill_fp8(q, k_cache, v_cache, block_tables, context_lens, q_offsets, scal
     sh = _prefill_shape(q, k_cache, v_cache, block_tables, context_lens, q_offsets, max_q_len,
                         FP8_DTYPES)
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        with _on(stream):
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     _check(load().paged_attn_prefill_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                          _ptr(context_lens), _ptr(q_offsets), ctypes.c_float(scale),
                                          _ptr(out), ctypes.byref(sh), _stream_handle(stream)))

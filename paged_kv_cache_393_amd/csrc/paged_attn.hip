@@ -57,6 +57,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "paged_attn.h"
@@ -853,14 +854,17 @@ hipError_t blocks_per_cu(int *n) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, pa_decode_kernel<D, KV>, kThreads, 0);
 }
 
+// The cache entries are atomics: host threads making their first call at
+// the same time may both query and store, but they store the same value.
 int device_capacity(int head_dim, int kind) {
     constexpr int kMaxDev = 64;
-    static int cache[kMaxDev][6];
+    static std::atomic<int> cache[kMaxDev][6];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
     const int slot = (head_dim == 128 ? 3 : 0) + kind;
-    int &c = cache[dev][slot];
-    if (c > 0) return c;
+    std::atomic<int> &c = cache[dev][slot];
+    const int known = c.load(std::memory_order_relaxed);
+    if (known > 0) return known;
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return 0;
@@ -875,8 +879,9 @@ int device_capacity(int head_dim, int kind) {
         default: e = blocks_per_cu<128, kFp8>(&per_cu); break;
     }
     if (e != hipSuccess || per_cu <= 0) per_cu = 1;
-    c = cus * per_cu;
-    return c;
+    const int total = cus * per_cu;
+    c.store(total, std::memory_order_relaxed);
+    return total;
 }
 
 struct WsLayout {

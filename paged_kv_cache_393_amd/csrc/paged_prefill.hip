@@ -351,11 +351,12 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         // Direct-to-LDS load (lane l's 16 B land at dst + 16 l).  Written as
         // asm so the compiler does not order LDS reads of the other ring
         // slots after it (it cannot tell the slots apart and would wait for
-        // the load): the explicit waits and barriers order the slots.  The
-        // nops cover the SGPR / M0 writes read by the load.
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+        // the load): the explicit waits and barriers order the slots.  M0 is
+        // an input operand, so the compiler writes it and knows what it holds;
+        // the nops cover the SGPR / M0 writes read by the load.
+        asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                      :
-                     : "s"(m0), "v"(voff), "s"(rs)
+                     : "{m0}"(m0), "v"(voff), "s"(rs)
                      : "memory");
     };
 

@@ -141,26 +141,17 @@ def test_prefill_max_q_len_larger_than_needed_is_harmless():
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
-@pytest.mark.parametrize("seqs", [(0,), (7,)])
-def test_full_size_prefill_workload_sampled(seqs):
+def test_full_size_prefill_workload_every_chunk():
     # The bench's workload at full size, same launch as the bench; the oracle
-    # checks the whole chunk of the sampled sequences (all queries, all heads).
-    note(f"full-size prefill {seqs}")
+    # checks every query of all eight chunks, every head.
+    note("full-size prefill, all chunks")
     pw = I.PREFILL_WORKLOADS["prefill_llama3_8b"]
     inp = I.make_prefill_inputs(pw, DEV)
     out = B.prefill(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
                     inp["context_lens"], inp["q_offsets"], inp["scale"], inp["max_q_len"])
     torch.cuda.synchronize()
-    qo = inp["q_offsets"].cpu()
-    for s in seqs:
-        sub = I.select_sequences(inp, [s], pw.block_size)
-        rows = slice(int(qo[s]), int(qo[s + 1]))
-        q_s = inp["q"][rows].cpu()
-        r = oracle.paged_prefill_bf16(I.bf16_bits(q_s), I.bf16_bits(sub["k_cache"]),
-                                      I.bf16_bits(sub["v_cache"]), sub["block_tables"].numpy(),
-                                      sub["context_lens"].numpy(), [0, q_s.shape[0]], sub["scale"])
-        assert_parity(out[rows], r, f"prefill seq {s}")
-
+    r = C.prefill_oracle(inp, inp["q"], inp["q_offsets"])
+    assert_parity(out, r, "prefill_llama3_8b")
 
 
 # ---- int8 (per-token scales) and FP8 E4M3 caches: the same bar against the
@@ -229,21 +220,17 @@ def test_quantized_prefill_poisoned_padding_bit_identical(kind):
         assert torch.equal(run_kind(v, q, q_off).view(torch.int32), clean.view(torch.int32)), bs
 
 
-@pytest.mark.parametrize("wl,seqs", [("prefill_int8_llama3_8b", (0, 7)), ("prefill_fp8_llama3_8b", (0, 7))])
-def test_full_size_quantized_prefill_workload_sampled(wl, seqs):
+@pytest.mark.parametrize("wl", ["prefill_int8_llama3_8b", "prefill_fp8_llama3_8b"])
+def test_full_size_quantized_prefill_workload_every_chunk(wl):
     # The bench's workloads at full size, same launch as the bench; the oracle
-    # checks the whole chunk of the sampled sequences.
-    note(f"full-size {wl} {seqs}")
+    # checks every query of all eight chunks.
+    note(f"full-size {wl}, all chunks")
     pw = I.PREFILL_WORKLOADS[wl]
     inp = I.make_prefill_inputs(pw, DEV)
     out = B.prefill_views(inp, inp["q"], inp["q_offsets"], inp["max_q_len"])
     torch.cuda.synchronize()
-    qo = inp["q_offsets"].cpu()
-    for s in seqs:
-        sub = I.select_sequences(inp, [s], pw.block_size)
-        rows = slice(int(qo[s]), int(qo[s + 1]))
-        r = C.prefill_oracle(sub, inp["q"][rows].cpu(), [0, int(qo[s + 1] - qo[s])])
-        assert_parity(out[rows], r, f"{wl} seq {s}")
+    r = C.prefill_oracle(inp, inp["q"], inp["q_offsets"])
+    assert_parity(out, r, wl)
 
 
 @pytest.mark.parametrize("kind", ["bf16", "int8", "fp8"])
