@@ -28,7 +28,8 @@
  *   * slice; the library needs nothing else for that layout.
  *
  * Ownership and state: the library allocates nothing and keeps no per-call
- * state.  Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ * state (paged_attn_decode_noalloc works in a static device array of the
+ * library instead of a caller workspace; see there).  Every call is asynchronous on `stream` (a hipStream_t; NULL = the
  * null stream) and stream-ordered with the caller's other work.
  *
  * Errors: every entry point returns PA_OK (0) or a negative PA_ERR_* code.
@@ -56,6 +57,7 @@ extern "C" {
 #define PA_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than paged_attn_workspace_bytes */
 #define PA_ERR_LAUNCH (-5)      /* the HIP runtime reported a launch error */
 #define PA_ERR_ALIGNMENT (-6)   /* q, k_cache, v_cache, out or workspace not 16-byte aligned */
+#define PA_ERR_SCRATCH (-7)     /* more scratch needed than paged_attn_decode_noalloc holds */
 
 typedef struct pa_shape {
     int32_t num_seqs;           /* S  >= 0 (0 is a no-op) */
@@ -135,6 +137,28 @@ int paged_attn_decode_fp8(const void *q, const uint8_t *k_cache, const uint8_t *
                           const int32_t *block_tables, const int32_t *context_lens, float scale,
                           float *out, const pa_shape *shape, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/*
+ * Allocation-free bf16 decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, kernels and results (bit for bit) as
+ * paged_attn_decode, with the partial results and item ranges in a static
+ * device array of the library (32 MiB, held by each device the library runs
+ * on until the process ends) instead of a caller workspace.  The caller still
+ * passes the inputs and `out`; the call allocates nothing.
+ * Scratch needed: ceil256(ceil(units/4) * (S + items) * 4 * min(G, 16) *
+ * (head_dim + 2) * 4) + ceil256(8 * S) bytes, where items is the number of
+ * workgroups of the decode grid (at most 512 on MI355X) with split_tokens == 0,
+ * else the number of split_tokens items the table rows can hold.  A shape
+ * needing more than 32 MiB is rejected with PA_ERR_SCRATCH before anything
+ * is launched.  Nothing in the array needs clearing: a call writes every
+ * entry it reads.  Every call on one device shares that device's array, so
+ * calls that overlap on one device (other streams, other host threads) race:
+ * the caller serialises them.
+ */
+int paged_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *block_tables, const int32_t *context_lens,
+                              float scale, float *out, const pa_shape *shape, void *stream);
 
 /*
  * Device-side check of the caller contract that the decode (and the prefill,

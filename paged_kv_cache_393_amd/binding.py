@@ -29,6 +29,7 @@ PA_ERR_UNSUPPORTED = -3
 PA_ERR_WORKSPACE = -4
 PA_ERR_LAUNCH = -5
 PA_ERR_ALIGNMENT = -6
+PA_ERR_SCRATCH = -7
 
 
 class PaShape(ctypes.Structure):
@@ -79,6 +80,8 @@ def load() -> ctypes.CDLL:
     lib.paged_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.paged_attn_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, SP, P, ctypes.c_size_t, P]
     lib.paged_attn_decode.restype = ctypes.c_int
+    lib.paged_attn_decode_noalloc.argtypes = [P, P, P, P, P, ctypes.c_float, P, SP, P]
+    lib.paged_attn_decode_noalloc.restype = ctypes.c_int
     lib.paged_attn_decode_int8.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, SP, P,
                                            ctypes.c_size_t, P]
     lib.paged_attn_decode_int8.restype = ctypes.c_int
@@ -234,6 +237,23 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out=No
                                   ctypes.byref(shape), _ptr(workspace), ctypes.c_size_t(ws_n),
                                   _stream_handle(stream))
     _check(rc)
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
+                   split_tokens: int = 0, stream=None) -> torch.Tensor:
+    """paged_attn_decode_noalloc: the bf16 decode with its partial results in
+    the library's static device scratch; `out` fp32 [S, Hq, D] is the caller's
+    and nothing is allocated."""
+    _validate(q, k_cache, v_cache, block_tables, context_lens, torch.bfloat16)
+    if out is None or out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape) or \
+            not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous fp32 device tensor shaped like q")
+    shape = shape_of(q, k_cache, block_tables, split_tokens)
+    _check(load().paged_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(block_tables), _ptr(context_lens),
+                                            ctypes.c_float(scale), _ptr(out), ctypes.byref(shape),
+                                            _stream_handle(stream)))
     return out
 
 

@@ -58,6 +58,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "paged_attn.h"
@@ -900,26 +901,37 @@ WsLayout workspace_layout(const pa_shape *sh, const Plan &pl) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-int decode_common(int kind, const void *q, const void *k, const void *v, const float *ks,
-                  const float *vs, const int32_t *bt, const int32_t *cl, float scale, float *out,
-                  const pa_shape *sh, void *ws, size_t ws_bytes, void *stream) {
-    const bool int8 = kind == kInt8;
-    Plan pl;
-    int rc = make_plan(sh, &pl);
+// Argument checks shared by every decode entry point, then the grid: returns
+// PA_OK with *pl and *wgs (workgroups per unit group) filled, or an error.
+int decode_prepare(int kind, const void *q, const void *k, const void *v, const float *ks,
+                   const float *vs, const int32_t *bt, const int32_t *cl, const float *out,
+                   const pa_shape *sh, Plan *pl) {
+    int rc = make_plan(sh, pl);
     if (rc != PA_OK) return rc;
     if (sh->num_seqs == 0) return PA_OK;
     if (!q || !k || !v || !bt || !cl || !out) return PA_ERR_NULL;
-    if (int8 && (!ks || !vs)) return PA_ERR_NULL;
+    if (kind == kInt8 && (!ks || !vs)) return PA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PA_ERR_ALIGNMENT;
-    const WsLayout wl = workspace_layout(sh, pl);
-    if (!ws || ws_bytes < wl.total) return PA_ERR_WORKSPACE;
-    if (!aligned16(ws)) return PA_ERR_ALIGNMENT;
+    return PA_OK;
+}
+
+// Workgroups per unit group of the decode grid on the current device, or 0.
+int decode_grid(int kind, const pa_shape *sh, const Plan &pl) {
     const int cap = device_capacity(sh->head_dim, kind);
-    if (cap <= 0) return PA_ERR_LAUNCH;
+    if (cap <= 0) return 0;
     int wgs = cap / pl.groups;
     if (wgs < 1) wgs = 1;
     if (wgs > kMaxItems) wgs = kMaxItems;
+    return wgs;
+}
 
+// The decode and merge launches, with the partial records at `part` (room
+// for `max_pieces` records per (unit group, wave)) and the item range of each
+// sequence at `seg`.
+int decode_launch(int kind, const void *q, const void *k, const void *v, const float *ks,
+                  const float *vs, const int32_t *bt, const int32_t *cl, float scale, float *out,
+                  const pa_shape *sh, const Plan &pl, int wgs, int max_pieces, float *part,
+                  int32_t *seg, void *stream) {
     Params prm;
     prm.q = (const uint16_t *)q;
     prm.k = k;
@@ -929,8 +941,8 @@ int decode_common(int kind, const void *q, const void *k, const void *v, const f
     prm.block_tables = bt;
     prm.context_lens = cl;
     prm.out = out;
-    prm.part = (float *)ws;
-    prm.seg_items = (int32_t *)((char *)ws + wl.seg_offset);
+    prm.part = part;
+    prm.seg_items = seg;
     prm.scale_log2 = scale * kLog2e;
     prm.num_seqs = sh->num_seqs;
     prm.num_q_heads = sh->num_q_heads;
@@ -943,7 +955,7 @@ int decode_common(int kind, const void *q, const void *k, const void *v, const f
     prm.max_ctx = pl.max_ctx;
     prm.log2_block_size = pl.log2_bs;
     prm.item_tiles = pl.item_tiles;
-    prm.max_pieces = pl.max_pieces;
+    prm.max_pieces = max_pieces;
     MergeParams mp;
     mp.part = prm.part;
     mp.seg_items = prm.seg_items;
@@ -952,7 +964,7 @@ int decode_common(int kind, const void *q, const void *k, const void *v, const f
     mp.group = prm.group;
     mp.n_chunks = pl.n_chunks;
     mp.rec_heads = pl.rec_heads;
-    mp.max_pieces = pl.max_pieces;
+    mp.max_pieces = max_pieces;
     const dim3 grid(wgs, pl.groups), block(kThreads);
     const dim3 mgrid((unsigned)((int64_t)sh->num_seqs * sh->num_q_heads));
     // fixed items that can give a sequence 64 or more pieces: more loads in flight
@@ -972,6 +984,63 @@ int decode_common(int kind, const void *q, const void *k, const void *v, const f
         else hipLaunchKernelGGL((pa_merge_kernel<64, 4>), mgrid, block, 0, st, mp);
     }
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int decode_common(int kind, const void *q, const void *k, const void *v, const float *ks,
+                  const float *vs, const int32_t *bt, const int32_t *cl, float scale, float *out,
+                  const pa_shape *sh, void *ws, size_t ws_bytes, void *stream) {
+    Plan pl;
+    int rc = decode_prepare(kind, q, k, v, ks, vs, bt, cl, out, sh, &pl);
+    if (rc != PA_OK || sh->num_seqs == 0) return rc;
+    const WsLayout wl = workspace_layout(sh, pl);
+    if (!ws || ws_bytes < wl.total) return PA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return PA_ERR_ALIGNMENT;
+    const int wgs = decode_grid(kind, sh, pl);
+    if (wgs <= 0) return PA_ERR_LAUNCH;
+    return decode_launch(kind, q, k, v, ks, vs, bt, cl, scale, out, sh, pl, wgs, pl.max_pieces,
+                         (float *)ws, (int32_t *)((char *)ws + wl.seg_offset), stream);
+}
+
+// Scratch of the allocation-free decode (paged_attn_decode_noalloc): its
+// partial records and item ranges, at most kScratchBytes.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+
+}  // namespace
+
+// The array behind kScratchBytes.  Each device the library runs on holds its
+// own copy until the process ends.  In host code this name stands for a
+// host-side shadow, not a device address: kernels only ever get the address
+// hipGetSymbolAddress reports for the current device (scratch_address).
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current and kept; nullptr if the lookup fails.
+void *scratch_address() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<void *> addr[kMaxDev];
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
+// Bytes of scratch a call needs: partial records for the pieces it can make
+// (sequences + items; with the balanced split the items are at most the
+// workgroups of the grid) and the item ranges, each rounded up to 256 bytes.
+size_t noalloc_bytes(const pa_shape *sh, const Plan &pl, int items_upper, int *max_pieces) {
+    *max_pieces = sh->num_seqs + items_upper;
+    const size_t rec_floats = (size_t)pl.rec_heads * (sh->head_dim + 2);
+    const size_t part = (size_t)pl.groups * (size_t)*max_pieces * kWaves * rec_floats * sizeof(float);
+    return ((part + 255) & ~(size_t)255) + (((size_t)sh->num_seqs * 2 * sizeof(int32_t) + 255) & ~(size_t)255);
 }
 
 }  // namespace
@@ -1018,6 +1087,30 @@ int paged_attn_decode_int8(const void *q, const int8_t *k_cache, const int8_t *v
                          context_lens, scale, out, shape, workspace, workspace_bytes, stream);
 }
 
+int paged_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *block_tables, const int32_t *context_lens,
+                              float scale, float *out, const pa_shape *shape, void *stream) {
+    Plan pl;
+    int rc = decode_prepare(kBf16, q, k_cache, v_cache, nullptr, nullptr, block_tables,
+                            context_lens, out, shape, &pl);
+    if (rc != PA_OK || shape->num_seqs == 0) return rc;
+    int max_pieces = 0;
+    // Fixed items: their number is known from the shape alone.
+    const int fixed_items = pl.item_tiles ? pl.max_pieces - shape->num_seqs : 0;
+    if (fixed_items && noalloc_bytes(shape, pl, fixed_items, &max_pieces) > kScratchBytes)
+        return PA_ERR_SCRATCH;
+    const int wgs = decode_grid(kBf16, shape, pl);
+    if (wgs <= 0) return PA_ERR_LAUNCH;
+    const size_t need = noalloc_bytes(shape, pl, fixed_items ? fixed_items : wgs, &max_pieces);
+    if (need > kScratchBytes) return PA_ERR_SCRATCH;
+    char *base = (char *)scratch_address();
+    if (!base) return PA_ERR_LAUNCH;
+    const size_t seg_offset = need - (((size_t)shape->num_seqs * 2 * sizeof(int32_t) + 255) & ~(size_t)255);
+    return decode_launch(kBf16, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,
+                         scale, out, shape, pl, wgs, max_pieces, (float *)base,
+                         (int32_t *)(base + seg_offset), stream);
+}
+
 const char *paged_attn_strerror(int code) {
     switch (code) {
         case PA_OK: return "ok";
@@ -1027,6 +1120,8 @@ const char *paged_attn_strerror(int code) {
         case PA_ERR_WORKSPACE: return "workspace missing or too small";
         case PA_ERR_LAUNCH: return "kernel launch failed or no usable device";
         case PA_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+        case PA_ERR_SCRATCH:
+            return "problem needs more than the 32 MiB static scratch of paged_attn_decode_noalloc";
         default: return "unknown error";
     }
 }

@@ -13,7 +13,8 @@ DECLARED = {"paged_attn_plan", "paged_attn_workspace_bytes", "paged_attn_decode"
             "paged_kv_evict_lowest_block", "paged_attn_prefill", "paged_attn_prefill_int8",
             "paged_attn_prefill_fp8", "paged_kv_compress_workspace_bytes",
             "paged_kv_compress_prefill", "paged_kv_compress_prefill_int8",
-            "paged_kv_compress_prefill_fp8", "paged_attn_check_tables"}
+            "paged_kv_compress_prefill_fp8", "paged_attn_check_tables",
+            "paged_attn_decode_noalloc"}
 
 
 def lib():
@@ -57,7 +58,7 @@ def test_probe_rejects_bad_arguments_on_the_host():
 
 def test_abi_version_and_strerror():
     assert lib().paged_attn_abi_version() == 1
-    for code in (0, -1, -2, -3, -4, -5, -6, -99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         assert isinstance(B.strerror(code), str) and B.strerror(code)
 
 
@@ -396,3 +397,25 @@ def test_quantized_prefill_host_checks(kind):
     if kind == "int8":
         assert pcall_q(kind, pshape(), vs=ctypes.c_void_p(0x100002)) == B.PA_ERR_ALIGNMENT
     assert pcall_q(kind, pshape(num_seqs=0), q=None, k=None) == B.PA_OK
+
+
+def call_noalloc(sh, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, out=FAKE):
+    return lib().paged_attn_decode_noalloc(q, k, v, bt, cl, ctypes.c_float(0.125), out,
+                                           ctypes.byref(sh), None)
+
+
+def test_noalloc_decode_host_checks():
+    # Shape, NULL and alignment errors as for paged_attn_decode; zero sequences
+    # is a no-op; a shape whose fixed items need more than the 32 MiB static
+    # scratch is rejected before any device call.
+    assert call_noalloc(shape(num_q_heads=6, num_kv_heads=4)) == B.PA_ERR_SHAPE
+    assert call_noalloc(shape(head_dim=96)) == B.PA_ERR_UNSUPPORTED
+    for name in ("q", "k", "v", "bt", "cl", "out"):
+        assert call_noalloc(shape(), **{name: ctypes.c_void_p(0)}) == B.PA_ERR_NULL, name
+    assert call_noalloc(shape(), q=ctypes.c_void_p(0x100008)) == B.PA_ERR_ALIGNMENT
+    assert call_noalloc(shape(num_seqs=0)) == B.PA_OK
+    # 4096 sequences of up to 1024 tokens in 16-token items: 262144 items of
+    # 4 records of 2 heads x 66 floats, far beyond 32 MiB.
+    big = shape(num_seqs=4096, max_blocks_per_seq=64, split_tokens=16)
+    assert call_noalloc(big) == B.PA_ERR_SCRATCH
+    assert "32 MiB" in B.strerror(B.PA_ERR_SCRATCH)
