@@ -545,7 +545,7 @@ def bench_compress(args) -> int:
         "ms_p10": pct(0.10), "ms_median": pct(0.50), "ms_p90": pct(0.90),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_kv_compress_prefill call: compress_select_kernel + compress_move_kernel",
+            "kernel": "paged_kv_compress_prefill call: select kernel(s) + compress_move_kernel",
             "achieved": gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -118,10 +118,17 @@ int paged_kv_evict_lowest_block(const float *scores, int32_t *block_tables,
  * must be 16-byte aligned.
  *
  * Workspace: paged_kv_compress_workspace_bytes(shape, budget) bytes of device
- * memory (kept positions int32 [num_seqs, budget], then context lengths int32
- * [num_seqs], each part rounded up to 256 bytes; 0 for a NULL shape, a
- * negative num_seqs or a negative budget), 16-byte aligned, contents
- * irrelevant; no two calls may use it at once.  Two kernel launches.
+ * memory: kept positions int32 [num_seqs, budget], then context lengths int32
+ * [num_seqs]; when max_blocks_per_seq * block_size exceeds 12288 tokens (the
+ * selection is then split over 4096-token chunks, nch = ceil(max_ctx / 4096)
+ * of them) also ranking keys uint32 [num_seqs, max_ctx rounded up to a
+ * multiple of 4], per-chunk histograms uint32 [num_seqs, nch, 256], per-sequence histograms uint32 [num_seqs, 2,
+ * 256], states int32 [3, num_seqs, 2] and per-chunk counts uint32 [num_seqs,
+ * nch, 257]; each part rounded up to 256 bytes (0 for a NULL shape, a
+ * negative num_seqs or a negative budget).  16-byte aligned, contents
+ * irrelevant; no two calls may use it at once.  Two kernel launches, or seven
+ * for the split selection (whose move is also split: first the kept tokens
+ * whose source lies below the budget, in order, then all others at once).
  * Caller contract (not checked): valid and pairwise distinct block ids for
  * every logical block of every sequence with n > budget.
  */

@@ -32,14 +32,18 @@ PREFILL_SOURCE = os.path.join(_HERE, "csrc", "paged_prefill.hip")
 COMPRESS_SOURCE = os.path.join(_HERE, "csrc", "kv_compress.hip")
 KERNELS = ("pa_decode_kernel", "pa_merge_kernel", "kv_write_kernel", "token_scores_kernel",
            "evict_lowest_block_kernel", "pa_prefill_kernel", "probe_copy_kernel",
-           "probe_read_kernel", "compress_select_kernel", "compress_move_kernel")
+           "probe_read_kernel", "compress_select_kernel", "compress_move_kernel",
+           "compress_split_keys_kernel", "compress_split_pass_kernel", "compress_split_write_kernel",
+           "compress_move_far_kernel")
 # The kernels of each timed operation and the source file they are built from.
 OPERATIONS = {
     "decode": (("pa_decode_kernel", "pa_merge_kernel"), KERNEL_SOURCE),
     "write": (("kv_write_kernel",), WRITE_SOURCE),
     "scores": (("token_scores_kernel",), EVICT_SOURCE),
     "prefill": (("pa_prefill_kernel",), PREFILL_SOURCE),
-    "compress": (("compress_select_kernel", "compress_move_kernel"), COMPRESS_SOURCE),
+    "compress": (("compress_select_kernel", "compress_split_keys_kernel", "compress_split_pass_kernel",
+                  "compress_split_write_kernel", "compress_move_kernel", "compress_move_far_kernel"),
+                 COMPRESS_SOURCE),
 }
 
 

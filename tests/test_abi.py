@@ -306,9 +306,14 @@ def test_compress_workspace_size():
     assert L.paged_kv_compress_workspace_bytes(ctypes.byref(sshape(num_seqs=3)), 100) == 1280 + 256
     assert L.paged_kv_compress_workspace_bytes(ctypes.byref(sshape(num_seqs=3)), 0) == 256
     assert L.paged_kv_compress_workspace_bytes(ctypes.byref(sshape()), -1) == 0
-    # contexts longer than the LDS key buffer (12288) add a key row per sequence
+    # contexts longer than the LDS key buffer (12288) split the selection into
+    # 4096-token chunks (4 here): a key row per sequence, first-digit histograms
+    # per chunk, two digit histograms per sequence, three states per sequence
+    # and last-digit counts per chunk, each part rounded up to 256 bytes
     long = sshape(num_seqs=2, max_blocks_per_seq=1000, block_size=16)
-    assert L.paged_kv_compress_workspace_bytes(ctypes.byref(long), 100) == 1024 + 256 + 2 * 16000 * 4
+    r = lambda b: (b + 255) // 256 * 256
+    split = r(2 * 16000 * 4) + r(2 * 4 * 256 * 4) + r(2 * 512 * 4) + r(3 * 2 * 2 * 4) + r(2 * 4 * 257 * 4)
+    assert L.paged_kv_compress_workspace_bytes(ctypes.byref(long), 100) == 1024 + 256 + split
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -108,6 +108,33 @@ def test_compress_long_context_keys_outside_lds():
     check(v, tie_heavy_scores(v, seed=413, levels=32.0), budget=5000)
 
 
+@pytest.mark.parametrize("budget", [1, 4095, 4096, 4097, 12289, 20000])
+def test_compress_split_select_ties_across_chunks(budget):
+    # Contexts longer than 12288 tokens select over 4096-token chunks: few
+    # score levels make the tied key span many chunks, and the budgets put the
+    # cut inside, at and around chunk boundaries.
+    ctx = (30000, 12289, 16385, 5, 8192)
+    note(f"compress split select budget={budget} ctx={ctx}")
+    _, v = C.make_case(len(ctx), 2, 1, 64, 16, ctx=ctx, seed=415 + budget, device=DEV)
+    check(v, tie_heavy_scores(v, seed=budget, nan_fraction=0.01, levels=2.0), budget)
+
+
+@pytest.mark.parametrize("kv", ["int8", "fp8"])
+def test_compress_split_select_quantized_caches(kv):
+    ctx = (20000, 13001, 4000)
+    note(f"compress split select kv={kv} ctx={ctx}")
+    _, v = C.make_case(len(ctx), 4, 2, 128, 16, ctx=ctx, seed=416, kv_dtype=kv, device=DEV)
+    check(v, tie_heavy_scores(v, seed=416, levels=16.0), budget=4097)
+
+
+def test_compress_long_context_full_size():
+    # The bench's long-context workload: four 131072-token sequences to 1024.
+    wl = I.WORKLOADS["long_context"]
+    note(f"compress full size {wl.name} budget 1024")
+    v = I.layer_views(I.make_inputs(wl, DEV), 0)
+    check(v, B.token_scores(v), budget=1024)
+
+
 def test_compress_twice_then_decode_matches_oracle_decode():
     ctx = (900, 333, 2000)
     note(f"compress twice then decode ctx={ctx}")
