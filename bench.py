@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--no-probe", action="store_true", help="skip the read-probe ceiling")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--split-decodes", action="store_true",
+                    help="prefill workloads: send the one-token queries of the batch to "
+                         "paged_attn_decode and only the chunks to paged_attn_prefill (two calls)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, copy this many bytes 3x with the probe copy kernel "
                          "(reference for hardware byte counters)")
@@ -622,6 +625,16 @@ def bench_prefill(args) -> int:
     def step():
         B.prefill_views(v, v["q"], v["q_offsets"], v["max_q_len"], out=out, stream=stream)
 
+    split = None
+    if args.split_decodes:
+        split = split_decode_batch(pw, v, out, dev)
+
+        def step():
+            B.prefill_views(split["chunks"], split["chunks"]["q"], split["chunks"]["q_offsets"],
+                            split["chunks"]["max_q_len"], out=split["chunk_out"], stream=stream)
+            B.decode_views(split["decodes"], out=split["decode_out"], workspace=split["ws"],
+                           stream=stream)
+
     flush_buf = None if args.no_flush else torch.ones((2 << 30) // 4, dtype=torch.float32,
                                                        device=dev)
 
@@ -643,6 +656,17 @@ def bench_prefill(args) -> int:
                              pw.block_size, pw.kv_dtype)
     t_s = ms_mean / 1e3
     tflops = flops / t_s / 1e12
+    gbps = nbytes / t_s / 1e9
+    # The bound is whichever resource the batch would saturate first: a batch
+    # of long chunks is matrix-core work, one chunk among many decodes mostly
+    # streams the decodes' K/V.
+    hbm_bound = nbytes / (HBM_PEAK_GBPS * 1e9) > flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    split_check = None
+    if split is not None:
+        # the same queries through one paged_attn_prefill call, for comparison
+        whole = B.prefill_views(v, v["q"], v["q_offsets"], v["max_q_len"])
+        torch.cuda.synchronize()
+        split_check = split_max_diff(split, whole)
     copy_for_counters(args, dev, stream)
     record = {
         "metric": "chunked-prefill attention query tokens/s and achieved bf16 matrix-core "
@@ -664,15 +688,20 @@ def bench_prefill(args) -> int:
                    "head_dim": pw.head_dim, "block_size": pw.block_size,
                    "cache_evict_between_steps": "2 GiB read" if flush_buf is not None else None},
         "ms_p10": pct(0.10), "ms_median": pct(0.50), "ms_p90": pct(0.90),
-        "hbm_gbps": nbytes / t_s / 1e9,
+        "hbm_gbps": gbps,
+        "tflops": tflops,
+        "calls": ("paged_attn_prefill (chunks) + paged_attn_decode (one-token queries)"
+                  if split is not None else "paged_attn_prefill"),
+        "split_vs_single_call_max_abs_diff": split_check,
         "roofline": {
-            "bound": "mfma",
-            "kernel": "pa_prefill_kernel",
-            "achieved": tflops,
-            "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
-            "traffic": measured_traffic(pw.name, "prefill"),
+            "bound": "hbm" if hbm_bound else "mfma",
+            "kernel": ("pa_prefill_kernel + pa_decode_kernel + pa_merge_kernel" if split is not None
+                       else "pa_prefill_kernel"),
+            "achieved": gbps if hbm_bound else tflops,
+            "peak": HBM_PEAK_GBPS if hbm_bound else MFMA_BF16_PEAK_TFLOPS,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": gbps / HBM_PEAK_GBPS if hbm_bound else tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": None if split is not None else measured_traffic(pw.name, "prefill"),
             "algorithmic_flops_per_call": flops,
             "algorithmic_bytes_per_call": nbytes,
             "calls_per_step": 1,
@@ -682,6 +711,51 @@ def bench_prefill(args) -> int:
     }
     print(json.dumps(record), flush=True)
     return 0
+
+
+def split_decode_batch(pw, v, out, dev):
+    """The batch of a prefill workload as two calls' inputs: its multi-token
+    chunks (a paged_attn_prefill batch) and its one-token queries (a
+    paged_attn_decode batch), views of the same cache, with their outputs and
+    the decode workspace."""
+    import torch
+
+    from paged_kv_cache_393_amd import binding as B
+
+    qo = v["q_offsets"].cpu().tolist()
+    chunk_ids = [s for s, n in enumerate(pw.n_q) if n > 1]
+    dec_ids = [s for s, n in enumerate(pw.n_q) if n == 1]
+    if not chunk_ids or not dec_ids:
+        raise SystemExit("--split-decodes needs a batch with both chunks and one-token queries")
+    base = {n: v[n] for n in ("k_cache", "v_cache", "scale") if n in v}
+    for n in ("k_scales", "v_scales"):
+        if n in v:
+            base[n] = v[n]
+    ci = torch.tensor(chunk_ids, device=dev)
+    di = torch.tensor(dec_ids, device=dev)
+    rows_c = torch.cat([torch.arange(qo[s], qo[s + 1]) for s in chunk_ids]).to(dev)
+    rows_d = torch.tensor([qo[s] for s in dec_ids], device=dev)
+    nq_c = torch.tensor([0] + [pw.n_q[s] for s in chunk_ids], dtype=torch.int64)
+    chunks = dict(base, q=v["q"].index_select(0, rows_c).contiguous(),
+                  q_offsets=torch.cumsum(nq_c, 0).to(torch.int32).to(dev),
+                  max_q_len=max(pw.n_q[s] for s in chunk_ids),
+                  block_tables=v["block_tables"].index_select(0, ci).contiguous(),
+                  context_lens=v["context_lens"].index_select(0, ci).contiguous())
+    decodes = dict(base, q=v["q"].index_select(0, rows_d).contiguous(),
+                   block_tables=v["block_tables"].index_select(0, di).contiguous(),
+                   context_lens=v["context_lens"].index_select(0, di).contiguous())
+    shape = B.shape_of(decodes["q"], decodes["k_cache"], decodes["block_tables"], 0)
+    return {"chunks": chunks, "decodes": decodes, "rows_c": rows_c, "rows_d": rows_d,
+            "chunk_out": torch.empty(chunks["q"].shape, dtype=torch.float32, device=dev),
+            "decode_out": torch.empty(decodes["q"].shape, dtype=torch.float32, device=dev),
+            "ws": B.alloc_workspace(shape, dev)}
+
+
+def split_max_diff(split, whole) -> float:
+    """Largest |difference| between the two-call outputs and one paged_attn_prefill call's."""
+    a = (split["chunk_out"] - whole.index_select(0, split["rows_c"])).abs().max()
+    b = (split["decode_out"] - whole.index_select(0, split["rows_d"])).abs().max()
+    return float(max(a, b))
 
 
 def cpu_baseline_prefill(pw, v, out, flops_total):

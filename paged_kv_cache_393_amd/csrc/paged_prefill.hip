@@ -178,6 +178,77 @@ __device__ __forceinline__ u32x4_t fp8x8_to_f16x8(const u32x2_t w) {
     return r;
 }
 
+// Dispatch order of the sequences, heaviest first.  A sequence's work is
+// about its query rows times its visible context; sequences go by work
+// bucket (0 for no rows, else 1 + floor(log2(rows * context)), at most 63),
+// heavier buckets first, and within a bucket by index, later first.  Every
+// workgroup computes the same order from the lengths; returns the sequence of
+// rank r.  Batches of more than kRankSeqs sequences keep the index order
+// (later first).  Workgroup-uniform; contains barriers.
+constexpr int kRankSeqs = 2048;
+constexpr int kRankBuckets = 64;
+__device__ __forceinline__ int work_bucket(const PrefillParams &p, int s) {
+    const int64_t rows = (int64_t)(p.q_offsets[s + 1] - p.q_offsets[s]) * p.group;
+    const int64_t w = rows * (int64_t)max(p.context_lens[s], 0);
+    if (rows <= 0 || w <= 0) return 0;
+    return min(kRankBuckets - 1, 64 - __builtin_clzll((unsigned long long)w));
+}
+
+__device__ __forceinline__ int sequence_of_rank(const PrefillParams &p, int r, uint8_t *lds_b,
+                                                int *lds_cnt, int *lds_sel) {
+    const int S = p.num_seqs;
+    if (S > kRankSeqs) return S - 1 - r;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid < kRankBuckets) lds_cnt[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < S; i += kThreads) {
+        const int b = work_bucket(p, i);
+        lds_b[i] = (uint8_t)b;
+        atomicAdd(&lds_cnt[b], 1);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // lane l holds bucket 63 - l: sequences of heavier buckets come first
+        const int cnt = lds_cnt[kRankBuckets - 1 - lane];
+        int incl = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+        }
+        if (incl - cnt <= r && r < incl) {
+            lds_sel[0] = kRankBuckets - 1 - lane;   // the bucket of rank r
+            lds_sel[1] = r - (incl - cnt);          // its place there, by index from the top
+        }
+    }
+    __syncthreads();
+    const int B = lds_sel[0];
+    int k = lds_sel[1];
+    __syncthreads();   // lds_cnt is reused below
+    // the k-th sequence of bucket B, scanning indices downward kThreads at a time
+    for (int top = S - 1; top >= 0; top -= kThreads) {
+        const int i = top - tid;
+        const bool in = i >= 0 && lds_b[i] == B;
+        const uint64_t bal = __ballot(in);
+        if (lane == 0) lds_cnt[wave] = __popcll(bal);
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int c = lds_cnt[w];
+            if (w < wave) before += c;
+            total += c;
+        }
+        const int mine = before + __popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+        if (in && mine == k) lds_sel[0] = i;
+        __syncthreads();
+        if (k < total) return lds_sel[0];   // uniform: every thread has the same k and total
+        k -= total;
+        __syncthreads();   // lds_cnt and lds_sel are rewritten by the next pass
+    }
+    return S - 1 - r;   // not reached: rank r < S lies in some bucket
+}
+
 template <int D, int KV>
 __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(const PrefillParams p) {
     constexpr int kSteps = D / 32;    // QK k-steps of 32 dims
@@ -197,6 +268,9 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     __shared__ __attribute__((aligned(1024))) char lds_k[kRing][TL::kBytes];
     __shared__ __attribute__((aligned(1024))) char lds_v[kRing][TL::kBytes];   // bf16 or fp16 V
     __shared__ int lds_pmax[kWaves];
+    __shared__ uint8_t lds_rank_b[kRankSeqs];
+    __shared__ int lds_rank_cnt[kWaves > kRankBuckets ? kWaves : kRankBuckets];
+    __shared__ int lds_rank_sel[2];
     // int8: the tiles' K and V scales (one per token of the kv head)
     __shared__ __attribute__((aligned(16))) float lds_sc[KV == kInt8 ? 2 : 1][kRing][kTileTokens];
     constexpr int kVsc = KV == kInt8 ? 1 : 0;
@@ -210,7 +284,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int y = (int)(blockIdx.x / 8);
     const int P = (y / p.tiles_x) * 8 + xcd;
     if (P >= p.num_kv_heads * p.num_seqs) return;    // uniform: the whole workgroup
-    const int s = p.num_seqs - 1 - P / p.num_kv_heads;
+    const int s = sequence_of_rank(p, P / p.num_kv_heads, lds_rank_b, lds_rank_cnt, lds_rank_sel);
     const int g = P % p.num_kv_heads;
     const int bx = p.tiles_x - 1 - y % p.tiles_x;
 #else

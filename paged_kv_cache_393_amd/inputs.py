@@ -335,6 +335,21 @@ PREFILL_WORKLOADS = {
 }
 
 
+def _sarathi_contexts(num_seqs: int, lo: int, hi: int, seed: int) -> tuple:
+    g = torch.Generator().manual_seed(seed)
+    return tuple(int(c) for c in torch.randint(lo, hi + 1, (num_seqs,), generator=g).tolist())
+
+
+# A chunked-prefill serving batch: one prefill chunk plus every running
+# decode (t6page "KV cache" page, chunked-prefill section; ybb.press page,
+# section 7.3): sequence 0's last 512 context tokens are the chunk, the other
+# 63 sequences decode one token each; Llama-3-8B layer shape, contexts
+# uniform in [512, 4096] as in the decode batch.
+PREFILL_WORKLOADS["sarathi_llama3_8b"] = PrefillWorkload(
+    "sarathi_llama3_8b", _sarathi_contexts(64, 512, 4096, seed=13), (512,) + (1,) * 63,
+    32, 8, 128, 16, seed=13)
+
+
 def make_prefill_inputs(pw: PrefillWorkload, device="cpu") -> dict:
     """Cache, tables and lengths as make_inputs (seeded, shuffled pool), plus
     the chunk queries q bf16 [sum n_q, Hq, d] (fp32 N(0,1) rounded) and

@@ -154,6 +154,30 @@ def test_full_size_prefill_workload_every_chunk():
     assert_parity(out, r, "prefill_llama3_8b")
 
 
+def test_full_size_serving_batch_one_call_and_split():
+    # One 512-token chunk and 63 decodes over the Llama-3-8B decode shapes, as
+    # the bench times it: in one paged_attn_prefill call, and as the chunk
+    # through paged_attn_prefill plus the decodes through paged_attn_decode;
+    # every output row against the oracle.
+    import bench
+
+    note("full-size serving batch (1 chunk + 63 decodes)")
+    pw = I.PREFILL_WORKLOADS["sarathi_llama3_8b"]
+    inp = I.make_prefill_inputs(pw, DEV)
+    out = B.prefill(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                    inp["context_lens"], inp["q_offsets"], inp["scale"], inp["max_q_len"])
+    torch.cuda.synchronize()
+    r = C.prefill_oracle(inp, inp["q"], inp["q_offsets"])
+    assert_parity(out, r, "serving batch, one call")
+    sp = bench.split_decode_batch(pw, inp, None, DEV)
+    B.prefill_views(sp["chunks"], sp["chunks"]["q"], sp["chunks"]["q_offsets"],
+                    sp["chunks"]["max_q_len"], out=sp["chunk_out"])
+    B.decode_views(sp["decodes"], out=sp["decode_out"], workspace=sp["ws"])
+    torch.cuda.synchronize()
+    assert_parity(sp["chunk_out"], r[sp["rows_c"].cpu().numpy()], "serving batch, chunk call")
+    assert_parity(sp["decode_out"], r[sp["rows_d"].cpu().numpy()], "serving batch, decode call")
+
+
 # ---- int8 (per-token scales) and FP8 E4M3 caches: the same bar against the
 # oracle over the codes' exact values.
 
