@@ -378,11 +378,22 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
                     ((t_end - 1) >> bs_log2) + 1);
     };
 
+    // Tile buffers of the register pipeline, kept across the pieces of an
+    // item: a piece whose tile count is a multiple of the depth loads the next
+    // piece's first tile into buf[0] in its last step, in place of a re-load
+    // past its end, and `pre_ok` tells the next piece that it is there.
+    constexpr int kStages = PA_STAGES;
+    static_assert(kStages >= 2 && kStages <= 6, "pipeline depth");
+    TileRegs<D, KV> buf[kStages];
+    bool pre_ok = false;
+
     // One piece: tiles [ta, tb) of sequence s for this wave's unit, with its
     // operands in `mt`.  Items `first` .. `last` are those that hold the
-    // sequence; `item` holds this piece.
-    auto process = [&](int s, int ctx, int ta, int tb, int first, int last, int item, Meta &mt)
-        __attribute__((always_inline)) {
+    // sequence; `item` holds this piece.  The item's next piece (if
+    // next_rows > 0) is sequence s + 1 from token 0, with operands `mnx`;
+    // next_rows is the number of valid rows of its first tile.
+    auto process = [&](int s, int ctx, int ta, int tb, int first, int last, int item, Meta &mt,
+                       Meta &mnx, int next_rows) __attribute__((always_inline)) {
         const int64_t row0 = (int64_t)s * Hq + h_base;   // output row of head column 0
         if (ctx == 0) {   // empty context: the output row is zero (always one whole piece)
             if (live) {
@@ -390,6 +401,7 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
 #pragma unroll
                 for (int e = 0; e < 4 * kDpl; e += 4) *(f32x4_t *)(dst + e) = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
+            pre_ok = false;
             return;
         }
         const int t_begin = ta * kTile;
@@ -418,9 +430,7 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
         // A tile never crosses a block (block_size is a multiple of 16); rows
         // at or past the context end fall outside the range and read as 0
         // without touching memory.
-        auto load_tile = [&](TileRegs<D, KV> &r, int tile) __attribute__((always_inline)) {
-            const int64_t slot0 = tile_slot(tile);
-            const int rows = min(kTile, t_end - (t_begin + tile * kTile));
+        auto load_rows = [&](TileRegs<D, KV> &r, int64_t slot0, int rows) __attribute__((always_inline)) {
             const int range = rows * (int)rb32;
             const __amdgpu_buffer_rsrc_t kr =
                 __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + slot0 * row_bytes), 0, range, kRsrcFlags);
@@ -448,6 +458,28 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
                 r.ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksr, s_off, 0, 0));
                 r.vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsr, s_off, 0, 0));
             }
+        };
+        auto load_tile = [&](TileRegs<D, KV> &r, int tile) __attribute__((always_inline)) {
+            load_rows(r, tile_slot(tile), min(kTile, t_end - (t_begin + tile * kTile)));
+        };
+        // Tile k of the pipeline: this piece's tile k; past the end, the next
+        // piece's first tile if there is one (its first block is lane 0 of
+        // its window), else this piece's last tile again (a cache hit).  The
+        // branches are uniform and every path issues the same loads into r.
+        auto load_ext = [&](TileRegs<D, KV> &r, int k) __attribute__((always_inline)) {
+            int64_t slot0;
+            int rows;
+            if (k < n_tiles) {
+                slot0 = tile_slot(k);
+                rows = min(kTile, t_end - (t_begin + k * kTile));
+            } else if (next_rows > 0) {
+                slot0 = (int64_t)__builtin_amdgcn_readlane(mnx.w0, 0) << bs_log2;
+                rows = next_rows;
+            } else {
+                slot0 = tile_slot(n_tiles - 1);
+                rows = min(kTile, t_end - (t_begin + (n_tiles - 1) * kTile));
+            }
+            load_rows(r, slot0, rows);
         };
 
         // Online-softmax state of head l16 (the same in the four lane groups)
@@ -556,15 +588,14 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
         // tiles (one back edge, no early exit), so the set of pending loads at
         // its head is the same on entry and on every iteration; the last
         // 0..kStages-1 tiles, already in flight, are processed after it.
-        // Prefetches past the end re-load the last tile (a cache hit), which
-        // keeps every load unconditional.
-        constexpr int kStages = PA_STAGES;
-        static_assert(kStages >= 2 && kStages <= 6, "pipeline depth");
+        // Prefetches past the end load the next piece's first tile, or
+        // re-load the last tile (a cache hit), which keeps every load
+        // unconditional.
         {
-            TileRegs<D, KV> buf[kStages];
             auto tile_of = [&](int k) __attribute__((always_inline)) { return min(k, n_tiles - 1); };
             static_for<0, kStages - 1>([&](auto I) __attribute__((always_inline)) {
-                load_tile(buf[decltype(I)::value], tile_of(decltype(I)::value));
+                // tile 0 may already be in buf[0], loaded by the previous piece
+                if (decltype(I)::value != 0 || !pre_ok) load_tile(buf[decltype(I)::value], tile_of(decltype(I)::value));
                 __builtin_amdgcn_sched_barrier(0);
             });
             const int rounds = n_tiles / kStages;
@@ -574,7 +605,7 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
                 static_for<0, kStages>([&](auto I) __attribute__((always_inline)) {
                     constexpr int i = decltype(I)::value;
                     const int k = rd * kStages + i;
-                    load_tile(buf[(i + kStages - 1) % kStages], tile_of(k + kStages - 1));
+                    load_ext(buf[(i + kStages - 1) % kStages], k + kStages - 1);
                     __builtin_amdgcn_sched_barrier(0);
                     compute_tile(buf[i], k);
                 });
@@ -584,6 +615,8 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
                 constexpr int i = decltype(I)::value;
                 if (rem > i) compute_tile(buf[i], rounds * kStages + i);
             });
+            // tile n_tiles went to buf[n_tiles % kStages] exactly when rem == 0
+            pre_ok = next_rows > 0 && rem == 0;
         }
 
         // The four lane groups hold partial sums over different token rows.
@@ -680,6 +713,7 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
         // before the current one streams, so a piece starts without waiting
         // for its query and block ids.
         Meta mc, mn;
+        pre_ok = false;
         int ctx = seq_ctx(s);
         if (ctx > 0) load_meta(mc, s, (lo - seg) * kTile, min(ctx, (hi - seg) * kTile));
         for (int x = lo; x < hi; ++s) {
@@ -691,8 +725,10 @@ __global__ __launch_bounds__(kThreads, PA_WAVES_PER_EU) void pa_decode_kernel(co
                 p.seg_items[2 * s + 1] = last;
             }
             const int ctx_next = end < hi ? seq_ctx(s + 1) : 0;
-            if (ctx_next > 0) load_meta(mn, s + 1, 0, min(ctx_next, (hi - end) * kTile));
-            process(s, ctx, x - seg, end - seg, first, last, item, mc);
+            const int next_end = min(ctx_next, (hi - end) * kTile);   // tokens of the next piece
+            if (ctx_next > 0) load_meta(mn, s + 1, 0, next_end);
+            process(s, ctx, x - seg, end - seg, first, last, item, mc, mn,
+                    ctx_next > 0 ? min(kTile, next_end) : 0);
             if (ctx_next > 0) mc = mn;   // (an empty next sequence needs none)
             ctx = ctx_next;
             x = end;
