@@ -60,15 +60,15 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 #ifndef PF_WAVES_PER_EU
-#define PF_WAVES_PER_EU 2
+#define PF_WAVES_PER_EU 4
 #endif
 #ifndef PF_XCD_MAP
 #define PF_XCD_MAP 1
 #endif
 
-constexpr int kWaves = 8;                  // waves per workgroup (rows share each staged tile)
+constexpr int kWaves = 16;                 // waves per workgroup (rows share each staged tile)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kNc = 2;                     // MFMA column blocks (16 rows each) per wave
+constexpr int kNc = 1;                     // MFMA column blocks (16 rows each) per wave
 constexpr int kRowsPerWave = 16 * kNc;
 constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
 constexpr int kTileTokens = 32;            // tokens per staged tile and step (two 16-token halves)
@@ -440,13 +440,19 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // iteration writes them into the same LDS layouts, as bf16 (FP8 V: as
     // fp16; int8 scales go to lds_sc), so the loads have a whole iteration to
     // land.
-    constexpr int kQLoads = D / 64;                      // per thread per iteration (K + V)
+    // 8-B code loads per thread per iteration (K + V): 8 D per tile over the
+    // workgroup; with more threads than loads (D = 64) the later waves load
+    // nothing (qload_ok, wave-uniform).
+    constexpr int kQLoads = 8 * D / kThreads > 0 ? 8 * D / kThreads : 1;
     constexpr int kCodeChunks = D / 8;                   // 8-code chunks per token
     u32x2_t st_codes[kQLoads];
     float st_scale[kQLoads];
     // keys and values read: the workgroup's tiles, within the context
     const int kv_end = min(ctx, n_tiles * kTileTokens);
     // K or V: wave-uniform (4 D loads per tile and kind, a multiple of 64)
+    auto qload_ok = [&](int jj) __attribute__((always_inline)) {
+        return wave * 64 + jj * kThreads < 8 * D;
+    };
     auto qload_is_v = [&](int jj) __attribute__((always_inline)) {
         return (wave * 64 + jj * kThreads) >= 4 * D;
     };
@@ -723,14 +729,15 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         for (int t = 0; t < min(2, n_tiles); ++t) {
 #pragma unroll
             for (int jj = 0; jj < kQLoads; ++jj) {
-                if (qload_is_v(jj)) continue;
+                if (!qload_ok(jj) || qload_is_v(jj)) continue;
                 qissue_tile(t, jj);
                 qstore(jj, t % kRing);
             }
         }
         // in flight into iteration 0: K(2) and V(0)
 #pragma unroll
-        for (int jj = 0; jj < kQLoads; ++jj) qissue_tile(qload_is_v(jj) ? 0 : 2, jj);
+        for (int jj = 0; jj < kQLoads; ++jj)
+            if (qload_ok(jj)) qissue_tile(qload_is_v(jj) ? 0 : 2, jj);
     }
     __syncthreads();
     Scores S;                  // scores of the tile whose softmax is next
@@ -794,10 +801,12 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         } else {
 #pragma unroll
-            for (int jj = 0; jj < kQLoads; ++jj) qstore(jj, i % kRing);
+            for (int jj = 0; jj < kQLoads; ++jj)
+                if (qload_ok(jj)) qstore(jj, i % kRing);
             if (decltype(more)::value || i + 1 < n_tiles) {
 #pragma unroll
-                for (int jj = 0; jj < kQLoads; ++jj) qissue_tile(i + (qload_is_v(jj) ? 1 : 3), jj);
+                for (int jj = 0; jj < kQLoads; ++jj)
+                    if (qload_ok(jj)) qissue_tile(i + (qload_is_v(jj) ? 1 : 3), jj);
             }
         }
         __syncthreads();
