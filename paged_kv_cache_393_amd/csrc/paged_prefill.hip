@@ -13,30 +13,36 @@
 // and k-elements 8*(l/16) .. +7; C lane l holding column l%16, rows 4*(l/16)+i).
 //
 // A "row" is a (query token, query head of the kv head's group) pair.  One
-// workgroup takes 256 rows of one (sequence, kv head); each of its 8 waves
-// owns 32 rows as two MFMA column blocks.  The workgroup streams the context
-// in 32-token tiles through the block table with direct-to-LDS buffer loads
-// (whose range is each 16-token half's valid rows, so nothing past the
-// context end is touched), double-buffered, one barrier per tile:
+// workgroup takes 256 rows of one (sequence, kv head); each of its 16 waves
+// owns 16 rows (one MFMA column block).  The workgroup streams the context in
+// 32-token tiles through the block table:
 //   * S^T = K Q^T: K tokens are the A operand, 16 B per lane from LDS; the
-//     wave's query rows are the B operand, held in registers throughout.
+//     wave's query rows are the B operand, held in registers throughout.  K
+//     tiles arrive by direct-to-LDS buffer loads whose range is each
+//     16-token half's valid rows, so nothing past the context end is read.
 //   * causal mask and online softmax in the accumulator registers: lane l
 //     holds column (row) l%16 and tokens 16 h + 4*(l/16) + i of half h.
 //   * O^T += V^T P^T: the 8 weights a lane holds ARE its B-operand k-elements,
-//     under the token order e -> 16*(e/4) + 4*(l/16) + e%4; the A operand
-//     (16 dims x those 8 tokens) comes straight from the token-major V tile
-//     through LDS transpose reads.  The weights enter as a bf16 high part
-//     plus a bf16 remainder (two products), exact to 2^-17 relative: a single
-//     bf16 rounding (2^-9) of the weights alone exceeds a 2e-3 absolute bar
-//     on short contexts.  FP8 caches instead stage V as fp16 (every E4M3
-//     value is one) and take the weights as fp16 (one product, 2^-11
-//     relative rounding), times 2^7 -- the row sums alike -- so that small
-//     weights stay out of fp16's subnormal range.  (A bf16 V does not fit
-//     fp16 in general, and int8 V scales can push the weights past it.)
-// Software pipeline: on this chip a wave co-issues vector instructions with
-// its own in-flight matrix instructions (not with another wave's), so one
-// iteration runs the softmax of tile i between the MFMAs of the scores of
-// tile i+1 and the weighted sum of tile i-1.
+//     under the token order e -> 16*(e/4) + 4*(l/16) + e%4.
+// bf16 caches: V passes through the registers of 8 waves into a dim-major
+// (transposed) LDS tile as fp16 -- exact for every bf16 value below 2^16 in
+// magnitude -- so the A operand is one 16-B LDS read per lane, and the
+// weights enter as fp16 times 2^7 (2^-11 relative rounding; the row sums add
+// the same rounded weights, and the 2^7 keeps small weights out of fp16's
+// subnormals): one product per 16 dims.  A workgroup that meets a larger V
+// value runs again with the tile as bf16 and the fp16 weights split exactly
+// into a bf16 high part and remainder.  The tiles run in segments of four,
+// one barrier each, through a ring of 8.
+// FP8 caches stage K and V through registers, V as fp16 (every E4M3 value is
+// one), and take the weights as fp16 likewise; int8 caches stage bf16 codes
+// (exact) and take the weights times the V scales as a bf16 pair (high part +
+// remainder, exact to 2^-17: int8 V scales can push the weights past fp16).
+// Both read V token-major through LDS transpose reads, one barrier per tile.
+// Scheduling: on this chip a matrix instruction holds its SIMD's vector issue
+// for most of its 16 cycles (transcendentals excepted), so the vector work a
+// step needs -- softmax, staging -- is as costly as its products; one step
+// issues the softmax of tile i among the MFMAs of the weighted sum of tile
+// i-1 and the scores of tile i+1.
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -62,22 +68,37 @@ typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 #ifndef PF_WAVES_PER_EU
 #define PF_WAVES_PER_EU 4
 #endif
+#ifndef PF_BF16_GROUP
+#define PF_BF16_GROUP 4
+#endif
 #ifndef PF_XCD_MAP
 #define PF_XCD_MAP 1
 #endif
 
-constexpr int kWaves = 16;                 // waves per workgroup (rows share each staged tile)
+#ifndef PF_WAVES
+#define PF_WAVES 16
+#endif
+#ifndef PF_NC
+#define PF_NC 1
+#endif
+constexpr int kWaves = PF_WAVES;           // waves per workgroup (rows share each staged tile)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kNc = 1;                     // MFMA column blocks (16 rows each) per wave
+constexpr int kNc = PF_NC;                 // MFMA column blocks (16 rows each) per wave
 constexpr int kRowsPerWave = 16 * kNc;
 constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
 constexpr int kTileTokens = 32;            // tokens per staged tile and step (two 16-token halves)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRsrcFlags = 0x00020000;     // word 3 of a raw buffer resource on CDNA3/CDNA4
 constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0) alone (gfx9 field layout; + n: vmcnt(n))
-// Double-buffered K and V tiles: K(i+2) and V(i) are loaded during
-// iteration i, which reads K(i+1) and V(i-1); ring slot = tile % 2.
-constexpr int kRing = 2;
+// Iterations run in segments of kGroup (one barrier at the end of each);
+// iteration i reads K(i+1) and V(i-1) and loads K(i+kGroup+1) and
+// V(i+kGroup-1), the tiles of the next segment, into a ring of 2 kGroup
+// slots (slot = tile % ring): the slot a load overwrites was last read in
+// the previous segment.  bf16 tiles go straight to LDS and take segments of
+// two iterations (half the barriers); int8 / FP8 tiles come through
+// registers, one tile's worth, and take segments of one.
+template <int KV>
+constexpr int kGroupOf = KV == 0 ? PF_BF16_GROUP : 1;
 
 // Element kinds of the cache read: bf16, int8 codes with an fp32 scale per
 // (slot, kv head), FP8 E4M3 codes.
@@ -114,8 +135,20 @@ struct PrefillParams {
 //   V: token-major, chunk c of token r at r * chunks + (c ^ f(r)), f(r) even
 //      -- a transpose read takes 8 B (4 dims) of 16 tokens; f spreads the
 //      16 tokens' 32-B dim ranges over distinct banks, 8 tokens a pass.
+//   V^T (bf16 caches): dim-major, one 80-B row per dim holding the tile's 32
+//      tokens as 2-B values in the weights' k-order (16-B chunk h: tokens
+//      4h .. 4h+3 then 16+4h .. 16+4h+3) plus 16 B of padding.  A weighted
+//      sum reads 16 B (one chunk of one dim) a lane: the 16 lanes of a pass
+//      read rows i = 0..15, at i * 80 mod 256 -- 16 distinct 16-B bank
+//      groups.  It is written 8 B (4 tokens of one dim) a lane, 32 lanes a
+//      pass spanning 4 consecutive dim quads, whose rows 4q+k sit 64 B apart
+//      mod 256 -- four disjoint 64-B bank ranges.
 template <int D>
 struct TileLds {
+    static constexpr int kVtPitch = 80;
+    static constexpr int kVtBytes = D * kVtPitch;
+    // bytes of tokens 4g .. 4g+3 in a V^T row
+    __device__ static int vt_group(int g) { return 16 * (g & 3) + 8 * (g >> 2); }
     static constexpr int kChunks = D / 8;
     static constexpr int kRowBytes = D * 2;
     static constexpr int kBytes = kTileTokens * kRowBytes;            // one tensor
@@ -254,19 +287,29 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     constexpr int kSteps = D / 32;    // QK k-steps of 32 dims
     constexpr int kDpl = D / 16;      // PV output blocks of 16 dims
     using TL = TileLds<D>;
-    // A tile of one tensor is loaded as 1-KB pieces, one direct-to-LDS load
-    // of 16 B per lane each, within one 16-token half: the piece's
-    // block-table entry, and its buffer resource, are wave-uniform.
+    // bf16: a K tile is loaded as 1-KB pieces, one direct-to-LDS load of 16
+    // B per lane each, within one 16-token half (the piece's block-table
+    // entry, and its buffer resource, are wave-uniform), by waves 0 ..
+    // kPieces-1; the V tile comes through the registers of the next kVWaves
+    // waves, 16 dims each, transposed (V^T).
     constexpr int kPieces = TL::kBytes / 1024;
-    constexpr int kRowsPerPiece = 64 / TL::kChunks;      // V pieces: whole tokens
-    constexpr int kPiecesPerWave = (2 * kPieces + kWaves - 1) / kWaves;
-    static_assert(TL::kBytes % 1024 == 0 && 16 % kRowsPerPiece == 0 && TL::kChunks % 4 == 0,
-                  "pieces within one half");
-    // FP8: the weighted sum on fp16 (V tile as fp16), the weights times 2^kPBias
-    constexpr bool kF16 = KV == kFp8;
+    constexpr int kPiecesPerWave = (kPieces + kWaves - 1) / kWaves;
+    static_assert(TL::kBytes % 1024 == 0 && TL::kChunks % 4 == 0, "pieces within one half");
+    constexpr int kVWaves = D / 16;                      // V^T staging waves: one per 16-dim block
+    constexpr int kVWave0 = kPieces + kVWaves <= kWaves ? kPieces : 0;
+    static_assert(kVWave0 + kVWaves <= kWaves && kVWaves <= 8, "staging waves");
+    // bf16 and FP8: the weighted sum on fp16 (V as fp16: exact for every
+    // E4M3 value, and for every bf16 value of magnitude below 2^16), the
+    // weights times 2^kPBias
+    constexpr bool kF16 = KV == kFp8 || KV == kBf16;
     constexpr float kPBias = kF16 ? 7.f : 0.f;
+    constexpr int kGroup = kGroupOf<KV>;
+    constexpr int kRing = 2 * kGroup;
+    constexpr bool kVt = KV == kBf16;     // V staged transposed (V^T), as fp16
     __shared__ __attribute__((aligned(1024))) char lds_k[kRing][TL::kBytes];
-    __shared__ __attribute__((aligned(1024))) char lds_v[kRing][TL::kBytes];   // bf16 or fp16 V
+    __shared__ __attribute__((aligned(1024))) char lds_v[kRing][kVt ? TL::kVtBytes : TL::kBytes];   // fp16 V^T, or bf16 / fp16 V
+    // V^T: set when a staging wave met a value beyond fp16 (see vstage_store)
+    __shared__ int lds_wide;
     __shared__ int lds_pmax[kWaves];
     __shared__ uint8_t lds_rank_b[kRankSeqs];
     __shared__ int lds_rank_cnt[kWaves > kRankBuckets ? kWaves : kRankBuckets];
@@ -350,6 +393,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     pmax = __builtin_amdgcn_readfirstlane(pmax);      // wave-uniform after the reduction
     pmin = __builtin_amdgcn_readfirstlane(pmin);
     if (lane == 0) lds_pmax[wave] = wave_live ? pmax : -1;
+    if (threadIdx.x == 0) lds_wide = 0;
     __syncthreads();
     int wg_pmax = lds_pmax[0];
 #pragma unroll
@@ -357,18 +401,13 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int n_tiles = wg_pmax / kTileTokens + 1;     // the workgroup's tiles (uniform)
     const int my_steps = pmax / kTileTokens + 1;       // this wave's tiles
 
-    // ---- tile loads: this wave's pieces, piece index w + j * kWaves (K
-    // pieces first, then V).
+    // ---- bf16 K tile loads: this wave's pieces, piece index w + j * kWaves;
+    // during iteration i they load tile i + kGroup + 1.
     auto piece_ok = [&](int j) __attribute__((always_inline)) {
-        return (2 * kPieces) % kWaves == 0 || wave + j * kWaves < 2 * kPieces;
+        return kPieces % kWaves == 0 || wave + j * kWaves < kPieces;
     };
-    auto piece_is_v = [&](int j) __attribute__((always_inline)) { return (wave + j * kWaves) >= kPieces; };
     auto piece_sub = [&](int j) __attribute__((always_inline)) { return (wave + j * kWaves) % kPieces; };
-    auto piece_half = [&](int j) __attribute__((always_inline)) {
-        return piece_is_v(j) ? (piece_sub(j) * kRowsPerPiece) >> 4 : piece_sub(j) / (TL::kChunks / 4);
-    };
-    // During iteration i, K pieces load tile i + 2 and V pieces tile i.
-    auto piece_lead = [&](int j) __attribute__((always_inline)) { return piece_is_v(j) ? 0 : 2; };
+    auto piece_half = [&](int j) __attribute__((always_inline)) { return piece_sub(j) / (TL::kChunks / 4); };
     // Block-table window: lane l holds entry wbase + l, the next 64 entries
     // are loaded when the window slides (64 blocks ahead of their use), and a
     // tile's blocks are read from a lane (v_readlane), not from memory: a
@@ -378,8 +417,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         const int e = base + lane;
         return e < nblk ? table[e] : 0;
     };
-    int wbase = 0;
-    int win = load_window(0), win_next = load_window(64);
+    int wbase = 0, win = 0, win_next = 0;   // set by each pass (run)
     // physical block of token tb (0 past the context end)
     auto phys_at = [&](int tb) __attribute__((always_inline)) {
         if (tb >= ctx) return 0;
@@ -392,12 +430,13 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     auto phys_of = [&](int tile, int j) __attribute__((always_inline)) {
         return phys_at(tile * kTileTokens + 16 * piece_half(j));
     };
-    auto issue = [&](int tile, int j, int phys) __attribute__((always_inline)) {
-        const int sub = piece_sub(j);
-        const int tb = tile * kTileTokens + 16 * piece_half(j);
+    // One direct-to-LDS load of 16 B a lane: the rows of the 16-token half
+    // starting at token tb (physical block phys) of `base` (K or V of the kv
+    // head), at byte voff of the half; lane l's 16 B land at dst + 16 l.
+    auto direct_load = [&](const char *base, int tb, int phys, int voff, char *dst) __attribute__((always_inline)) {
         const int rows = min(16, max(0, ctx - tb));      // the buffer range: nothing past the context
         const int64_t slot0 = ((int64_t)phys << bs_log2) + (tb & bs_mask);
-        const uint64_t addr = (uint64_t)(uintptr_t)((piece_is_v(j) ? vbase : kbase) + slot0 * rb32);
+        const uint64_t addr = (uint64_t)(uintptr_t)(base + slot0 * rb32);
         // wave-uniform by construction; stated, so the resource is built in
         // scalar registers without a per-lane loop
         const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
@@ -405,21 +444,6 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         const int range = __builtin_amdgcn_readfirstlane(rows * (int)rb32);
         // raw buffer resource: base, stride 0, num_records = range
         const i32x4_t rs = {(int32_t)lo, (int32_t)(hi & 0xffffu), range, kRsrcFlags};
-        // the lane's 16 B: K piece = 4 chunks x 16 tokens of one half (chunk
-        // 4 (sub % (chunks/4)) + lane / 16, token lane % 16); V piece = whole
-        // tokens (token lane / chunks, stored chunk position lane % chunks,
-        // which holds dims chunk (lane % chunks) ^ f(token))
-        int r16, chunk;
-        if (piece_is_v(j)) {
-            const int row = sub * kRowsPerPiece + lane / TL::kChunks;
-            r16 = row & 15;
-            chunk = (lane % TL::kChunks) ^ TL::v_swz(row);
-        } else {
-            r16 = lane & 15;
-            chunk = 4 * (sub % (TL::kChunks / 4)) + (lane >> 4);
-        }
-        const int voff = (int)((uint32_t)r16 * rb32 + (uint32_t)(chunk * 16));
-        char *dst = (piece_is_v(j) ? lds_v[tile % kRing] : lds_k[tile % kRing]) + sub * 1024;
         const uint32_t m0 = __builtin_amdgcn_readfirstlane(
             (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)dst);
         // Direct-to-LDS load (lane l's 16 B land at dst + 16 l).  Written as
@@ -432,6 +456,15 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                      :
                      : "{m0}"(m0), "v"(voff), "s"(rs)
                      : "memory");
+    };
+    auto issue = [&](int tile, int j, int phys) __attribute__((always_inline)) {
+        const int sub = piece_sub(j);
+        // the lane's 16 B: 4 chunks x 16 tokens of one half (chunk
+        // 4 (sub % (chunks/4)) + lane / 16, token lane % 16)
+        const int r16 = lane & 15;
+        const int chunk = 4 * (sub % (TL::kChunks / 4)) + (lane >> 4);
+        const int voff = (int)((uint32_t)r16 * rb32 + (uint32_t)(chunk * 16));
+        direct_load(kbase, tile * kTileTokens + 16 * piece_half(j), phys, voff, lds_k[tile % kRing] + sub * 1024);
     };
 
     // ---- int8 / FP8 tiles come through registers: each thread loads 8 codes
@@ -515,6 +548,62 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
             if (ch == 0) lds_sc[qload_is_v(jj) ? 1 : 0][slot][tok] = st_scale[jj];
     };
 
+    // ---- bf16 V^T staging.  Staging wave w takes the 16-token half w % 2 and
+    // dims 32 (w / 2) .. + 31 of a tile; its lane l the tokens 2 p, 2 p + 1
+    // of the half (p = l % 8) and dims 4 q .. 4 q + 3 of those (q = l / 8):
+    // two 8-B loads, issued at the start of an iteration, written at its end
+    // as four 4-B V^T runs (one per dim, its 2 tokens).  The values are
+    // written as fp16; a value beyond fp16 (magnitude >= 2^16, or infinite)
+    // sets lds_wide, and the workgroup then runs again in the safe mode,
+    // which writes them as bf16.  Tokens past the context read as 0 (the
+    // buffer range).
+    const bool v_stager = kVt && wave >= kVWave0 && wave < kVWave0 + kVWaves;   // wave-uniform
+    const int vs_w = v_stager ? wave - kVWave0 : 0;
+    const int vs_half = vs_w & 1;
+    const int vs_p = lane & 7, vs_q = lane >> 3;
+    const int vs_dim = 32 * (vs_w >> 1) + 4 * vs_q;          // the lane's first dim
+    u32x2_t vst[2];
+    auto vstage_issue = [&](int tile) __attribute__((always_inline)) {
+        const int tb = tile * kTileTokens + 16 * vs_half;
+        const int rows = min(16, max(0, ctx - tb));
+        const int64_t slot0 = ((int64_t)phys_at(tb) << bs_log2) + (tb & bs_mask);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(vbase + slot0 * rb32, rows * (int)rb32);
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            vst[e] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                rs, (int)((uint32_t)(2 * vs_p + e) * rb32 + (uint32_t)(2 * vs_dim)), 0, 0));
+    };
+    auto vstage_store = [&](int slot, auto safe) __attribute__((always_inline)) {
+        constexpr bool kSafe = decltype(safe)::value;
+        // (opaque: keeps the conversion below inside the staging waves' branch)
+        __asm__ volatile("" : "+v"(vst[0]), "+v"(vst[1]));
+        // tokens 2 p, 2 p + 1 of half h sit at byte 16 (p / 2) + 8 h + 4 (p % 2) of a row
+        char *row = lds_v[slot] + vs_dim * TL::kVtPitch + 16 * (vs_p >> 1) + 8 * vs_half + 4 * (vs_p & 1);
+        if constexpr (kSafe) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                *(uint32_t *)(row + k * TL::kVtPitch) =
+                    __builtin_amdgcn_perm(vst[1][k >> 1], vst[0][k >> 1], (k & 1) ? 0x07060302u : 0x05040100u);
+            return;
+        }
+        float f[2][4];     // [token e][dim k]
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            f[e][0] = __uint_as_float(vst[e][0] << 16);
+            f[e][1] = __uint_as_float(vst[e][0] & 0xffff0000u);
+            f[e][2] = __uint_as_float(vst[e][1] << 16);
+            f[e][3] = __uint_as_float(vst[e][1] & 0xffff0000u);
+        }
+        // max magnitude (a NaN is skipped: fp16 keeps it)
+        const float mx = fmaxf(fmaxf(fmaxf(fabsf(f[0][0]), fabsf(f[0][1])), fmaxf(fabsf(f[0][2]), fabsf(f[0][3]))),
+                               fmaxf(fmaxf(fabsf(f[1][0]), fabsf(f[1][1])), fmaxf(fabsf(f[1][2]), fabsf(f[1][3]))));
+        if (__ballot(mx >= 65536.f) != 0 && lane == 0) lds_wide = 1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            *(uint32_t *)(row + k * TL::kVtPitch) =
+                __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{f[0][k], f[1][k]}, f16x2_t));
+    };
+
     // ---- S^T = K Q^T of one tile from LDS: lane l gets column (row) l%16 of
     // block cb and tokens 16 bb + 4 (l/16) + i.  The k-step loop is outermost,
     // so the 2 kNc accumulation chains interleave.  int8: times the tokens' K
@@ -545,17 +634,8 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         }
     };
 
-    f32x4_t acc[kDpl][kNc];
-#pragma unroll
-    for (int j = 0; j < kDpl; ++j)
-#pragma unroll
-        for (int cb = 0; cb < kNc; ++cb) acc[j][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[kDpl][kNc];               // set by each pass (run)
     float m_run[kNc], l_run[kNc];
-#pragma unroll
-    for (int cb = 0; cb < kNc; ++cb) {
-        m_run[cb] = -INFINITY;
-        l_run[cb] = 0.f;
-    }
 
     // ---- online softmax of tile t's scores S into the weights (bf16 high
     // part and remainder, both rounded to nearest even: hi + lo is the fp32
@@ -668,6 +748,41 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // weights' token order.
     const int tr_tok = 4 * hgrp + (l16 >> 2);
     const int tr_lane = tr_tok * TL::kRowBytes + 8 * (l16 & 1);   // + chunk position
+    // V^T (bf16 caches): lane (group h, row i) reads 16 B of dim row 16 j + i
+    // -- its 8 tokens in the weights' order -- at a fixed offset per j.
+    const int vt_lane = l16 * TL::kVtPitch + 16 * hgrp;
+    // Safe mode (bf16 V^T): the fp16 weights enter as a bf16 high part plus
+    // remainder, both exact (11 significant bits).
+    auto weighted_values_vt = [&](const char *vl, const Weights &Pin, auto safe) __attribute__((always_inline)) {
+        constexpr bool kSafe = decltype(safe)::value;
+        Weights Bhi, Blo;
+        if constexpr (kSafe) {
+#pragma unroll
+            for (int cb = 0; cb < kNc; ++cb) {
+                const f16x8_t h = __builtin_bit_cast(f16x8_t, Pin[cb]);
+                float pr[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pr[e] = (float)h[e];
+                split_weights(pr, Bhi[cb], Blo[cb]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kDpl; ++j) {
+            const u32x4_t vop = *(const u32x4_t *)(vl + vt_lane + j * 16 * TL::kVtPitch);
+#pragma unroll
+            for (int cb = 0; cb < kNc; ++cb) {
+                if constexpr (kSafe) {
+                    acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vop), Bhi[cb],
+                                                                         acc[j][cb], 0, 0, 0);
+                    acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vop), Blo[cb],
+                                                                         acc[j][cb], 0, 0, 0);
+                } else {
+                    acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(f16x8_t, vop), __builtin_bit_cast(f16x8_t, Pin[cb]), acc[j][cb], 0, 0, 0);
+                }
+            }
+        }
+    };
     auto weighted_values = [&](const char *vl, const float *vsc, const Weights &Pin_hi, const Weights &Pin_lo)
                                __attribute__((always_inline)) {
         Weights Phi, Plo;
@@ -716,13 +831,48 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         }
     };
 
-    // ---- prologue: K of tiles 0 and 1 in LDS, then the scores of tile 0.
+    // The weighted sum of tile t (its V landed at least one barrier ago).
+    auto pv = [&](const int t, const Weights &Ph, const Weights &Pl, auto safe) __attribute__((always_inline)) {
+        if constexpr (kVt)
+            weighted_values_vt(lds_v[t % kRing], Ph, safe);
+        else
+            weighted_values(lds_v[t % kRing], lds_sc[kVsc][t % kRing], Ph, Pl);
+    };
+
+    // ---- one pass over the workgroup's tiles, from a clean state.  `safe`
+    // (bf16 caches only): V^T as bf16, for a workgroup whose fp16 pass met a
+    // value beyond fp16.
+    auto run = [&](auto safe) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kDpl; ++j)
+#pragma unroll
+        for (int cb = 0; cb < kNc; ++cb) acc[j][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < kNc; ++cb) {
+        m_run[cb] = -INFINITY;
+        l_run[cb] = 0.f;
+    }
+    wbase = 0;
+    win = load_window(0);
+    win_next = load_window(64);
+
+    // ---- prologue: the tiles the first segment reads in LDS (K(0) ..
+    // K(kGroup), V(0) .. V(kGroup-2)), then the scores of tile 0.
     if constexpr (KV == kBf16) {
 #pragma unroll
         for (int j = 0; j < kPiecesPerWave; ++j) {
-            if (!piece_ok(j) || piece_is_v(j)) continue;
-            issue(0, j, phys_of(0, j));
-            if (n_tiles > 1) issue(1, j, phys_of(1, j));
+            if (!piece_ok(j)) continue;
+#pragma unroll
+            for (int t = 0; t <= kGroup; ++t)
+                if (t < n_tiles) issue(t, j, phys_of(t, j));
+        }
+#pragma nounroll
+        for (int t = 0; t <= kGroup - 2; ++t) {
+            if (v_stager && t < n_tiles) {
+                vstage_issue(t);
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                vstage_store(t, safe);
+            }
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     } else {
@@ -745,7 +895,8 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     if (wave_live) scores(lds_k[0], lds_sc[0][0], S);
     __syncthreads();           // K(0) read by every wave before iteration 0 loads over it
 
-    // ---- iteration i (K(i+1) and V(i-1) in LDS; K(i+2) and V(i) loading):
+    // ---- iteration i (K(i+1) and V(i-1) in LDS; the tiles of the next
+    // segment loading):
     //   softmax(i)  -- vector unit, on the scores from the last iteration
     //   PV(i-1), scores(i+1)  -- matrix cores, issued among the softmax's
     //   instructions by the scheduler (independent registers)
@@ -769,35 +920,58 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         if (pend_grow) rescale(pend_alpha);
         pend_grow = false;
         if (do_sm) pend_grow = softmax(i, Sc, Pn_hi, Pn_lo, pend_alpha, masked);
-        if (do_pv) weighted_values(lds_v[(i - 1) % kRing], lds_sc[kVsc][(i - 1) % kRing], Ph, Pl);
+        if (do_pv) pv(i - 1, Ph, Pl, safe);
         if (do_qk) scores(lds_k[(i + 1) % kRing], lds_sc[0][(i + 1) % kRing], Sn);
+        // The weights are only read by the next step's weighted sum; left
+        // alone, the compiler sinks their computation into that step, so one
+        // block of a pair holds two softmaxes and the other bare matrix
+        // products.  An empty use here keeps each softmax in its own step,
+        // among the products it can be issued beside.
+        if (kFull && do_sm) {
+#pragma unroll
+            for (int cb = 0; cb < kNc; ++cb) {
+                __asm__ volatile("" ::"v"(__builtin_bit_cast(u32x4_t, Pn_hi[cb])));
+                if constexpr (!kF16) __asm__ volatile("" ::"v"(__builtin_bit_cast(u32x4_t, Pn_lo[cb])));
+            }
+        }
     };
     auto loads = [&](const int i) __attribute__((always_inline)) {
-        // The oldest block iteration i loads is V(i)'s first (int8 / FP8:
-        // V(i+1)'s, one iteration ahead); once it leaves the window, slide
-        // (the newest, K(i+2)'s last (K(i+3)'s), is at most 80 (96) tokens
-        // further, under 64 blocks, so a slide never skips a window).
-        if ((((i + (KV == kBf16 ? 0 : 1)) * kTileTokens) >> bs_log2) >= wbase + 64) {
+        // The oldest block iteration i loads is V(i+kGroup-1)'s first (int8 /
+        // FP8: V(i+1)'s, one iteration ahead); once it leaves the window,
+        // slide (the newest, K(i+kGroup+1)'s last (K(i+3)'s), is at most 96
+        // tokens further, under 64 blocks, so a slide never skips a window).
+        if ((((i + (KV == kBf16 ? kGroup - 1 : 1)) * kTileTokens) >> bs_log2) >= wbase + 64) {
             wbase += 64;
             win = win_next;
             win_next = load_window(wbase + 64);
         }
         if constexpr (KV == kBf16) {
+            if (v_stager && i + kGroup - 1 < n_tiles) vstage_issue(i + kGroup - 1);
 #pragma unroll
             for (int j = 0; j < kPiecesPerWave; ++j) {
                 if (!piece_ok(j)) continue;
-                const int tile = i + piece_lead(j);
+                const int tile = i + kGroup + 1;
                 if (tile < n_tiles) issue(tile, j, phys_of(tile, j));
             }
         }
         return i;
     };
-    // End of iteration i: this wave's loads have landed (int8 / FP8: K(i+2)
-    // and V(i), loaded during the last iteration, written to LDS as bf16 --
-    // into the slots no wave reads this iteration -- and K(i+3), V(i+1)
-    // issued into the same registers), then the barrier.
-    auto tile_done = [&](const int i, auto more) __attribute__((always_inline)) {
+    // End of iteration i.  bf16: V(i+1), loaded by the staging waves during
+    // this iteration, goes into its slot (no wave reads that slot in this
+    // segment: its last reader, the weighted sum of V(i+1-kRing), ran in the
+    // last one); at the end of a segment (`sync`: i is the segment's last
+    // iteration or the workgroup's last) this wave's loads have landed, then
+    // the barrier.  int8 / FP8 (segments of one): K(i+2) and V(i), loaded
+    // during the last iteration, are written to LDS as bf16 -- into the slots
+    // no wave reads this iteration -- and K(i+3), V(i+1) issued into the same
+    // registers, then the barrier.
+    auto tile_done = [&](const int i, auto more, const bool sync) __attribute__((always_inline)) {
         if constexpr (KV == kBf16) {
+            if (v_stager && i + kGroup - 1 < n_tiles) {
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                vstage_store((i + kGroup - 1) % kRing, safe);
+            }
+            if (!sync) return;
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         } else {
 #pragma unroll
@@ -811,33 +985,17 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         }
         __syncthreads();
     };
-    // Three loops with one barrier per iteration each, n_tiles in all: the
-    // wave's first tile, its middle tiles (every part present, no mask: one
+    // Three loops, n_tiles iterations in all: the wave's first tiles (the
+    // first segment), its middle tiles (every part present, no mask: one
     // straight-line body), and the rest (diagonal tiles, the last weighted
     // sum, then loads only).
     const int first_masked = pmin >= kTileTokens - 1 ? (pmin - (kTileTokens - 1)) / kTileTokens + 1 : 0;
     const int full_end = wave_live ? max(1, min(first_masked, my_steps - 1)) : 1;
     Scores S2;
     Weights Phi2, Plo2;
-    int nl = loads(0);
-    if (wave_live) step(0, S, Phi, Plo, S2, Phi2, Plo2, std::true_type{}, std::false_type{});
-    tile_done(nl, std::false_type{});
-    // The state alternates between the two register sets, so the middle
-    // tiles run in pairs without copies; after the pairs it is in (S2, P2).
-    int i = 1;
-    for (; i + 1 < full_end; i += 2) {
-        nl = loads(i);
-        step(i, S2, Phi2, Plo2, S, Phi, Plo, std::false_type{}, std::true_type{});
-        tile_done(nl, std::true_type{});       // i + 2 < full_end < n_tiles
-        nl = loads(i + 1);
-        step(i + 1, S, Phi, Plo, S2, Phi2, Plo2, std::false_type{}, std::true_type{});
-        tile_done(nl, std::true_type{});
-    }
-    // the general iterations (an odd middle tile, the diagonal tiles, the
-    // last weighted sum, then loads only), each followed by a copy back into
-    // (S2, P2)
-    for (; i < n_tiles; ++i) {
-        nl = loads(i);
+    // a general iteration, its state copied back into (S2, P2)
+    auto general = [&](const int i) __attribute__((always_inline)) {
+        const int nl = loads(i);
         if (wave_live && i <= my_steps) {
             Scores Sn;
             Weights Pn_hi, Pn_lo;
@@ -850,12 +1008,43 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                 for (int bb = 0; bb < 2; ++bb) S2[bb][cb] = Sn[bb][cb];
             }
         }
-        tile_done(nl, std::false_type{});
+        tile_done(nl, std::false_type{}, i % kGroup == kGroup - 1 || i == n_tiles - 1);
+    };
+    int nl = loads(0);
+    if (wave_live) step(0, S, Phi, Plo, S2, Phi2, Plo2, std::true_type{}, std::false_type{});
+    tile_done(nl, std::false_type{}, kGroup == 1 || n_tiles == 1);
+    int i = 1;
+#pragma nounroll
+    for (; i < kGroup && i < n_tiles; ++i) general(i);
+    // The state alternates between the two register sets, so the middle
+    // tiles run in pairs without copies (a pair starts a segment); after
+    // the pairs it is in (S2, P2).
+    for (; i + 1 < full_end; i += 2) {
+        nl = loads(i);
+        step(i, S2, Phi2, Plo2, S, Phi, Plo, std::false_type{}, std::true_type{});
+        tile_done(nl, std::true_type{}, i % kGroup == kGroup - 1);       // i + 2 < full_end < n_tiles
+        nl = loads(i + 1);
+        step(i + 1, S, Phi, Plo, S2, Phi2, Plo2, std::false_type{}, std::true_type{});
+        tile_done(nl, std::true_type{}, (i + 1) % kGroup == kGroup - 1);
     }
+    // the general iterations (an odd middle tile, the diagonal tiles, the
+    // last weighted sum, then loads only)
+#pragma nounroll
+    for (; i < n_tiles; ++i) general(i);
     // the last tile's weighted sum (V(n_tiles-1) landed in the last iteration)
     if (wave_live && my_steps == n_tiles) {
         if (pend_grow) rescale(pend_alpha);
-        weighted_values(lds_v[(n_tiles - 1) % kRing], lds_sc[kVsc][(n_tiles - 1) % kRing], Phi2, Plo2);
+        pv(n_tiles - 1, Phi2, Plo2, safe);
+    }
+    };
+
+    run(std::false_type{});
+    if constexpr (kVt) {
+        // every staging write of the pass came before its last barrier
+        if (__builtin_amdgcn_readfirstlane(lds_wide) != 0) {
+            __syncthreads();   // the pass's last LDS reads are done before the rerun loads over them
+            run(std::true_type{});
+        }
     }
 
     if (!wave_live) return;

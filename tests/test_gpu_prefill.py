@@ -1,10 +1,13 @@
 """GPU parity of paged chunked-prefill attention (paged_attn_prefill) through the
 C-ABI against the fp64 oracle, with the decode's bar: max |gpu - oracle| <=
 2e-3 over all elements and, per (query token, head) row, max err / max |oracle|
-<= 1e-2.  The softmax weights enter the second matrix product as a bf16 pair
-(high part + remainder, exact to 2^-17 relative), so the error is fp32
-summation plus bf16-exact inputs, well inside that bar (checked below up to
-4096 tokens).  Bit-exact: padding poison, loose max_q_len.
+<= 1e-2.  bf16 and FP8 caches: V enters the second matrix product as fp16
+(exact for bf16 values below 2^16 and every E4M3 value) and the softmax
+weights as fp16 (2^-11 relative rounding, the row sums adding the same
+rounded weights); a bf16 V beyond fp16 sends the workgroup to a second pass
+with bf16 V and the weights split exactly into a bf16 pair.  int8: the
+weights times the V scales as a bf16 pair (exact to 2^-17).  Checked below
+up to 4096 tokens.  Bit-exact: padding poison, loose max_q_len.
 """
 import numpy as np
 import pytest
@@ -340,6 +343,27 @@ def test_prefill_bf16_values_past_fp16_range():
     unit = np.where(np.abs(ref).max(axis=-1, keepdims=True) > 64.0, 65536.0, 1.0)
     assert (unit > 1).any() and (unit == 1).any()
     assert_parity(torch.from_numpy(got / unit), ref / unit, "V partly x 2^16")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_bf16_values_past_fp16_range_in_some_dims(D):
+    # Large values (x 2^16) in dims 40..47 only, of tokens 200..263 of
+    # sequence 0, kv head 1: in those tiles the 32 dims holding them are
+    # staged as bf16 while the tile's other dims stay fp16, and one weighted
+    # sum mixes both.  Rows whose outputs are large are compared in units of
+    # 2^16.
+    note(f"prefill bf16 V x 2^16 in dims 40..47, D={D}")
+    ctx, nq = (500, 333), [260, 333]
+    v, q, q_off = make_kind(ctx, nq, 8, 2, D, 16, 534 + D, "bf16")
+    bt = v["block_tables"].cpu()
+    for t in range(200, 264):
+        b = int(bt[0, t // 16])
+        v["v_cache"][b, t % 16, 1, 40:48] *= 65536.0
+    got = run_kind(v, q, q_off).double().cpu().numpy()
+    ref = C.prefill_oracle(v, q, q_off)
+    unit = np.where(np.abs(ref).max(axis=-1, keepdims=True) > 64.0, 65536.0, 1.0)
+    assert (unit > 1).any() and (unit == 1).any()
+    assert_parity(torch.from_numpy(got / unit), ref / unit, "V dims 40..47 x 2^16")
 
 
 @pytest.mark.parametrize("kind", ["int8", "fp8"])
