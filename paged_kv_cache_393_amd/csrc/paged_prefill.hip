@@ -68,6 +68,9 @@ typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 #ifndef PF_WAVES_PER_EU
 #define PF_WAVES_PER_EU 4
 #endif
+#ifndef PF_STAGER_PRIO
+#define PF_STAGER_PRIO 3
+#endif
 #ifndef PF_BF16_GROUP
 #define PF_BF16_GROUP 4
 #endif
@@ -558,6 +561,10 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // which writes them as bf16.  Tokens past the context read as 0 (the
     // buffer range).
     const bool v_stager = kVt && wave >= kVWave0 && wave < kVWave0 + kVWaves;   // wave-uniform
+    // The staging waves carry the most work per tile; issued first (wave
+    // priority 3 of 0..3), they reach each barrier no later than the K
+    // waves, which fill the SIMD's remaining issue slots.
+    if (v_stager) __builtin_amdgcn_s_setprio(PF_STAGER_PRIO);
     const int vs_w = v_stager ? wave - kVWave0 : 0;
     const int vs_half = vs_w & 1;
     const int vs_p = lane & 7, vs_q = lane >> 3;
