@@ -138,20 +138,18 @@ struct PrefillParams {
 //   V: token-major, chunk c of token r at r * chunks + (c ^ f(r)), f(r) even
 //      -- a transpose read takes 8 B (4 dims) of 16 tokens; f spreads the
 //      16 tokens' 32-B dim ranges over distinct banks, 8 tokens a pass.
-//   V^T (bf16 caches): dim-major, one 80-B row per dim holding the tile's 32
+//   V^T (bf16 caches): dim-major, one 64-B row per dim holding the tile's 32
 //      tokens as 2-B values in the weights' k-order (16-B chunk h: tokens
-//      4h .. 4h+3 then 16+4h .. 16+4h+3) plus 16 B of padding.  A weighted
-//      sum reads 16 B (one chunk of one dim) a lane: the 16 lanes of a pass
-//      read rows i = 0..15, at i * 80 mod 256 -- 16 distinct 16-B bank
-//      groups.  It is written 8 B (4 tokens of one dim) a lane, 32 lanes a
-//      pass spanning 4 consecutive dim quads, whose rows 4q+k sit 64 B apart
-//      mod 256 -- four disjoint 64-B bank ranges.
+//      4h .. 4h+3 then 16+4h .. 16+4h+3), chunk h of row d at position
+//      h ^ ((d / 2) % 4).  Measured on gfx950 (16 waves a CU, 16-B reads of
+//      16 rows x 4 chunks): this swizzle reads at the contiguous rate, where
+//      unswizzled 64-B or 80-B rows took 1.5x as long.
 template <int D>
 struct TileLds {
-    static constexpr int kVtPitch = 80;
+    static constexpr int kVtPitch = 64;
     static constexpr int kVtBytes = D * kVtPitch;
-    // bytes of tokens 4g .. 4g+3 in a V^T row
-    __device__ static int vt_group(int g) { return 16 * (g & 3) + 8 * (g >> 2); }
+    // byte of 16-B chunk h of V^T row d
+    __device__ static int vt_chunk(int d, int h) { return d * kVtPitch + 16 * (h ^ ((d >> 1) & 3)); }
     static constexpr int kChunks = D / 8;
     static constexpr int kRowBytes = D * 2;
     static constexpr int kBytes = kTileTokens * kRowBytes;            // one tensor
@@ -584,13 +582,18 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         constexpr bool kSafe = decltype(safe)::value;
         // (opaque: keeps the conversion below inside the staging waves' branch)
         __asm__ volatile("" : "+v"(vst[0]), "+v"(vst[1]));
-        // tokens 2 p, 2 p + 1 of half h sit at byte 16 (p / 2) + 8 h + 4 (p % 2) of a row
-        char *row = lds_v[slot] + vs_dim * TL::kVtPitch + 16 * (vs_p >> 1) + 8 * vs_half + 4 * (vs_p & 1);
+        // tokens 2 p, 2 p + 1 of half h sit at byte 8 h + 4 (p % 2) of chunk
+        // p / 2; dims vs_dim + k, k = 0..3, take two chunk swizzles
+        const int in_chunk = 8 * vs_half + 4 * (vs_p & 1);
+        char *row01 = lds_v[slot] + TL::vt_chunk(vs_dim, vs_p >> 1) + in_chunk;
+        char *row23 = lds_v[slot] + TL::vt_chunk(vs_dim + 2, vs_p >> 1) + in_chunk;
+        auto at = [&](int k) __attribute__((always_inline)) {
+            return (uint32_t *)((k < 2 ? row01 : row23) + (k & 1) * TL::kVtPitch);
+        };
         if constexpr (kSafe) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                *(uint32_t *)(row + k * TL::kVtPitch) =
-                    __builtin_amdgcn_perm(vst[1][k >> 1], vst[0][k >> 1], (k & 1) ? 0x07060302u : 0x05040100u);
+                *at(k) = __builtin_amdgcn_perm(vst[1][k >> 1], vst[0][k >> 1], (k & 1) ? 0x07060302u : 0x05040100u);
             return;
         }
         float f[2][4];     // [token e][dim k]
@@ -607,8 +610,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         if (__ballot(mx >= 65536.f) != 0 && lane == 0) lds_wide = 1;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            *(uint32_t *)(row + k * TL::kVtPitch) =
-                __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{f[0][k], f[1][k]}, f16x2_t));
+            *at(k) = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{f[0][k], f[1][k]}, f16x2_t));
     };
 
     // ---- S^T = K Q^T of one tile from LDS: lane l gets column (row) l%16 of
@@ -757,7 +759,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int tr_lane = tr_tok * TL::kRowBytes + 8 * (l16 & 1);   // + chunk position
     // V^T (bf16 caches): lane (group h, row i) reads 16 B of dim row 16 j + i
     // -- its 8 tokens in the weights' order -- at a fixed offset per j.
-    const int vt_lane = l16 * TL::kVtPitch + 16 * hgrp;
+    const int vt_lane = TL::vt_chunk(l16, hgrp);   // row 16 j + i: the same swizzle as row i
     // Safe mode (bf16 V^T): the fp16 weights enter as a bf16 high part plus
     // remainder, both exact (11 significant bits).
     auto weighted_values_vt = [&](const char *vl, const Weights &Pin, auto safe) __attribute__((always_inline)) {
