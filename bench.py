@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--split-decodes", action="store_true",
                     help="prefill workloads: send the one-token queries of the batch to "
                          "paged_attn_decode and only the chunks to paged_attn_prefill (two calls)")
+    ap.add_argument("--key-splits", type=int, default=None,
+                    help="prefill workloads: key pieces per row tile of the prefill call (default: "
+                         "paged_attn_prefill_plan's; 1 = the unsplit call)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, copy this many bytes 3x with the probe copy kernel "
                          "(reference for hardware byte counters)")
@@ -116,8 +119,8 @@ def measured_traffic(workload: str, operation: str = "decode"):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = R.OPERATIONS[operation][1]
-    if rec.get("workload") != workload or rec.get("source_sha256") != R.source_sha256(src):
+    shas = ", ".join(R.source_sha256(src) for src in R.OPERATIONS[operation][1])
+    if rec.get("workload") != workload or rec.get("source_sha256") != shas:
         return None
     return rec.get("bytes_per_call")
 
@@ -622,16 +625,33 @@ def bench_prefill(args) -> int:
     torch.cuda.synchronize()
     print(f"[bench] inputs for {pw.name} ready", file=sys.stderr, flush=True)
 
+    def key_split_of(views):
+        if args.key_splits is not None:
+            return args.key_splits
+        return B.prefill_plan(B.prefill_shape_of(views, views["q"], views["q_offsets"],
+                                                 views["max_q_len"]))
+
+    def pf_workspace(views, ks):
+        sh = B.prefill_shape_of(views, views["q"], views["q_offsets"], views["max_q_len"])
+        return B.alloc_prefill_workspace(sh, ks, dev)
+
+    key_splits = key_split_of(v)
+    pf_ws = pf_workspace(v, key_splits)
+
     def step():
-        B.prefill_views(v, v["q"], v["q_offsets"], v["max_q_len"], out=out, stream=stream)
+        B.prefill_views(v, v["q"], v["q_offsets"], v["max_q_len"], out=out, stream=stream,
+                        key_splits=key_splits, workspace=pf_ws)
 
     split = None
     if args.split_decodes:
         split = split_decode_batch(pw, v, out, dev)
+        key_splits = key_split_of(split["chunks"])
+        pf_ws = pf_workspace(split["chunks"], key_splits)
 
         def step():
             B.prefill_views(split["chunks"], split["chunks"]["q"], split["chunks"]["q_offsets"],
-                            split["chunks"]["max_q_len"], out=split["chunk_out"], stream=stream)
+                            split["chunks"]["max_q_len"], out=split["chunk_out"], stream=stream,
+                            key_splits=key_splits, workspace=pf_ws)
             B.decode_views(split["decodes"], out=split["decode_out"], workspace=split["ws"],
                            stream=stream)
 
@@ -661,6 +681,8 @@ def bench_prefill(args) -> int:
     # of long chunks is matrix-core work, one chunk among many decodes mostly
     # streams the decodes' K/V.
     hbm_bound = nbytes / (HBM_PEAK_GBPS * 1e9) > flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    pf_name = "paged_attn_prefill_split" if key_splits > 1 else "paged_attn_prefill"
+    pf_kernels = "pa_prefill_kernel + pa_prefill_merge_kernel" if key_splits > 1 else "pa_prefill_kernel"
     split_check = None
     if split is not None:
         # the same queries through one paged_attn_prefill call, for comparison
@@ -690,18 +712,20 @@ def bench_prefill(args) -> int:
         "ms_p10": pct(0.10), "ms_median": pct(0.50), "ms_p90": pct(0.90),
         "hbm_gbps": gbps,
         "tflops": tflops,
-        "calls": ("paged_attn_prefill (chunks) + paged_attn_decode (one-token queries)"
-                  if split is not None else "paged_attn_prefill"),
+        "calls": (f"{pf_name} (chunks) + paged_attn_decode (one-token queries)"
+                  if split is not None else pf_name),
+        "key_splits": key_splits,
         "split_vs_single_call_max_abs_diff": split_check,
         "roofline": {
             "bound": "hbm" if hbm_bound else "mfma",
-            "kernel": ("pa_prefill_kernel + pa_decode_kernel + pa_merge_kernel" if split is not None
-                       else "pa_prefill_kernel"),
+            "kernel": (f"{pf_kernels} + pa_decode_kernel + pa_merge_kernel" if split is not None
+                       else pf_kernels),
             "achieved": gbps if hbm_bound else tflops,
             "peak": HBM_PEAK_GBPS if hbm_bound else MFMA_BF16_PEAK_TFLOPS,
             "unit": "GB/s" if hbm_bound else "TFLOP/s",
             "frac": gbps / HBM_PEAK_GBPS if hbm_bound else tflops / MFMA_BF16_PEAK_TFLOPS,
-            "traffic": None if split is not None else measured_traffic(pw.name, "prefill"),
+            "traffic": (None if split is not None or key_splits > 1
+                        else measured_traffic(pw.name, "prefill")),
             "algorithmic_flops_per_call": flops,
             "algorithmic_bytes_per_call": nbytes,
             "calls_per_step": 1,

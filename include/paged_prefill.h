@@ -23,8 +23,8 @@
  *   out           fp32 [q_offsets[S], Hq, head_dim]
  *
  * Ownership and state: the library allocates nothing and keeps no state; one
- * kernel launch, asynchronous on `stream` (a hipStream_t; NULL = the null
- * stream).  Errors: PA_OK or a negative PA_ERR_* code of paged_attn.h,
+ * kernel launch (two for a key-split call, below), asynchronous on `stream` (a
+ * hipStream_t; NULL = the null stream).  Errors: PA_OK or a negative PA_ERR_* code of paged_attn.h,
  * detected on the host before the launch (out untouched then).  Not checked
  * (device data): n_q[s] <= max_q_len, n_q[s] <= context_lens[s] <=
  * max_blocks_per_seq * block_size, valid block ids for every block a context
@@ -55,9 +55,12 @@ typedef struct pa_prefill_shape {
 
 /*
  * Chunked-prefill attention over a bf16 cache.  Matrix cores compute the
- * scores and the weighted values; the softmax weights enter the second product
- * as a bf16 high part plus a bf16 remainder (exact to 2^-17 relative);
- * accumulation is fp32.
+ * scores and the weighted values; accumulation is fp32.  V enters the second
+ * product as fp16 (exact for every bf16 value below 2^16 in magnitude) and the
+ * softmax weights as fp16 (2^-11 relative rounding; the row sums add the same
+ * rounded weights).  A workgroup that meets a V value of magnitude 2^16 or
+ * more (or an infinite one) computes its rows again with V as bf16 and the
+ * weights as a bf16 high part plus remainder, so no V value is rounded.
  */
 int paged_attn_prefill(const void *q, const void *k_cache, const void *v_cache,
                        const int32_t *block_tables, const int32_t *context_lens,
@@ -91,6 +94,67 @@ int paged_attn_prefill_fp8(const void *q, const uint8_t *k_cache, const uint8_t 
                            const int32_t *block_tables, const int32_t *context_lens,
                            const int32_t *q_offsets, float scale, float *out,
                            const pa_prefill_shape *shape, void *stream);
+
+/*
+ * Key-split prefill.  Each (sequence, kv head, tile of 256 query rows) is a
+ * unit whose keys run over tiles of 32 tokens, from token 0 to its last row's
+ * position.  With one workgroup per unit, a batch of few units (one 512-token
+ * chunk of one sequence: 8 kv heads x 8 row tiles = 64 units) leaves most of
+ * the GPU idle.  With key_splits = K > 1, the unit's key tiles are cut into
+ * min(K, tiles) near-equal runs, one workgroup each.  Each run writes its rows'
+ * unnormalised weighted sums, running maximum and row sum (fp32) to
+ * `workspace`, and a second kernel combines the runs of each row: out =
+ * sum_k e^(m_k - M) acc_k / sum_k e^(m_k - M) l_k (M the largest m_k): one
+ * softmax over the row's whole visible context, as the unsplit call and the
+ * decode's merge compute it (ybb.press page, section 2.2), equal to the
+ * unsplit call's result up to fp32 rounding order.  A unit with a single run
+ * writes out directly.
+ *
+ * paged_attn_prefill_plan: a key_splits for `shape` on the current device:
+ * the smallest K for which the units' runs cover the compute units (one
+ * prefill workgroup fills a compute unit), at most max_blocks_per_seq *
+ * block_size / 128 (four or more tiles a run), at most 64; 1 when the units
+ * already cover the GPU.  Units are counted from max_q_len, an upper bound.
+ * Returns PA_OK, PA_ERR_NULL, a shape error as the prefill calls, or
+ * PA_ERR_LAUNCH if the device cannot be queried.
+ *
+ * paged_attn_prefill_workspace_bytes: the workspace a key-split call with
+ * `shape` and key_splits needs: num_seqs * Hkv * ceil(max_q_len * G / 256) *
+ * key_splits * 256 rows of (head_dim + 2) floats; 0 when key_splits == 1 (no
+ * workspace is read) or the shape or key_splits is invalid.
+ *
+ * paged_attn_prefill_split / _int8 / _fp8: the prefill calls above, with the
+ * same arguments and numerics, plus key_splits (1 .. 64; 1 is the unsplit
+ * call and ignores the workspace) and a caller-owned device workspace
+ * (16-byte aligned, at least paged_attn_prefill_workspace_bytes; contents
+ * need no initialisation; calls that may run concurrently must not share
+ * one).  Two kernel launches on `stream` when key_splits > 1.  Errors as the
+ * unsplit calls, plus PA_ERR_SHAPE for key_splits outside 1 .. 64,
+ * PA_ERR_WORKSPACE for a NULL or too small workspace and PA_ERR_ALIGNMENT
+ * for a misaligned one, all before any launch.
+ */
+int paged_attn_prefill_plan(const pa_prefill_shape *shape, int32_t *key_splits);
+
+size_t paged_attn_prefill_workspace_bytes(const pa_prefill_shape *shape, int32_t key_splits);
+
+int paged_attn_prefill_split(const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *block_tables, const int32_t *context_lens,
+                             const int32_t *q_offsets, float scale, float *out,
+                             const pa_prefill_shape *shape, int32_t key_splits, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+int paged_attn_prefill_split_int8(const void *q, const int8_t *k_cache, const int8_t *v_cache,
+                                  const float *k_scales, const float *v_scales,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  const int32_t *q_offsets, float scale, float *out,
+                                  const pa_prefill_shape *shape, int32_t key_splits,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+int paged_attn_prefill_split_fp8(const void *q, const uint8_t *k_cache, const uint8_t *v_cache,
+                                 const int32_t *block_tables, const int32_t *context_lens,
+                                 const int32_t *q_offsets, float scale, float *out,
+                                 const pa_prefill_shape *shape, int32_t key_splits,
+                                 void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -125,6 +125,20 @@ def load() -> ctypes.CDLL:
     lib.paged_attn_prefill_fp8.argtypes = [P, P, P, P, P, P, ctypes.c_float, P,
                                            ctypes.POINTER(PaPrefillShape), P]
     lib.paged_attn_prefill_fp8.restype = ctypes.c_int
+    PS = ctypes.POINTER(PaPrefillShape)
+    lib.paged_attn_prefill_plan.argtypes = [PS, ctypes.POINTER(ctypes.c_int32)]
+    lib.paged_attn_prefill_plan.restype = ctypes.c_int
+    lib.paged_attn_prefill_workspace_bytes.argtypes = [PS, ctypes.c_int32]
+    lib.paged_attn_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.paged_attn_prefill_split.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, PS, ctypes.c_int32,
+                                             P, ctypes.c_size_t, P]
+    lib.paged_attn_prefill_split.restype = ctypes.c_int
+    lib.paged_attn_prefill_split_int8.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, P, PS,
+                                                  ctypes.c_int32, P, ctypes.c_size_t, P]
+    lib.paged_attn_prefill_split_int8.restype = ctypes.c_int
+    lib.paged_attn_prefill_split_fp8.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, PS,
+                                                 ctypes.c_int32, P, ctypes.c_size_t, P]
+    lib.paged_attn_prefill_split_fp8.restype = ctypes.c_int
     lib.paged_attn_strerror.argtypes = [ctypes.c_int]
     lib.paged_attn_strerror.restype = ctypes.c_char_p
     lib.paged_attn_abi_version.argtypes = []
@@ -568,59 +582,108 @@ def _prefill_shape(q, k_cache, v_cache, block_tables, context_lens, q_offsets, m
     return PaPrefillShape(S, q.shape[1], Hkv, D, bs, MB, NB, int(max_q_len))
 
 
+def prefill_plan(shape: PaPrefillShape) -> int:
+    """paged_attn_prefill_plan: a key_splits for `shape` on the current device."""
+    k = ctypes.c_int32()
+    _check(load().paged_attn_prefill_plan(ctypes.byref(shape), ctypes.byref(k)))
+    return k.value
+
+
+def prefill_workspace_bytes(shape: PaPrefillShape, key_splits: int) -> int:
+    return int(load().paged_attn_prefill_workspace_bytes(ctypes.byref(shape), int(key_splits)))
+
+
+def alloc_prefill_workspace(shape: PaPrefillShape, key_splits: int, device) -> Optional[torch.Tensor]:
+    """Workspace of a key-split prefill call (None when key_splits == 1)."""
+    if int(key_splits) == 1:
+        return None
+    n = prefill_workspace_bytes(shape, key_splits)
+    if n <= 0:
+        raise PagedAttnError(PA_ERR_SHAPE, "no prefill workspace size for this shape / key_splits")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _prefill_call(fn_plain, fn_split, lead, sh, key_splits, workspace, q, out, scale, stream):
+    """One prefill call: the plain entry point for key_splits == 1, else the
+    key-split one with `workspace` (allocated on `stream` when None)."""
+    with _on(stream):
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if int(key_splits) != 1 and workspace is None:
+            workspace = alloc_prefill_workspace(sh, key_splits, q.device)
+    tail = (ctypes.c_float(scale), _ptr(out), ctypes.byref(sh))
+    if int(key_splits) == 1:
+        rc = fn_plain(*lead, *tail, _stream_handle(stream))
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        rc = fn_split(*lead, *tail, int(key_splits), _ptr(workspace),
+                      ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                      _stream_handle(stream))
+    _check(rc)
+    return out
+
+
 def prefill(q, k_cache, v_cache, block_tables, context_lens, q_offsets, scale: float,
-            max_q_len: int, out=None, stream=None) -> torch.Tensor:
+            max_q_len: int, out=None, stream=None, key_splits: int = 1,
+            workspace=None) -> torch.Tensor:
     """out fp32 [q_offsets[-1], Hq, D] = paged_attn_prefill(...): every sequence's
     last (q_offsets[s+1] - q_offsets[s]) context tokens attend causally over
-    the paged bf16 cache.  max_q_len bounds the query tokens of any sequence."""
+    the paged bf16 cache.  max_q_len bounds the query tokens of any sequence.
+    key_splits > 1: paged_attn_prefill_split, each row tile's keys over that
+    many workgroups (workspace: alloc_prefill_workspace, or made here)."""
     sh = _prefill_shape(q, k_cache, v_cache, block_tables, context_lens, q_offsets, max_q_len,
                         (torch.bfloat16,))
-    if out is None:
-        with _on(stream):
-            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    _check(load().paged_attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                     _ptr(context_lens), _ptr(q_offsets), ctypes.c_float(scale),
-                                     _ptr(out), ctypes.byref(sh), _stream_handle(stream)))
-    return out
+    L = load()
+    lead = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+            _ptr(q_offsets))
+    return _prefill_call(L.paged_attn_prefill, L.paged_attn_prefill_split, lead, sh, key_splits,
+                         workspace, q, out, scale, stream)
 
 
 def prefill_int8(q, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens, q_offsets,
-                 scale: float, max_q_len: int, out=None, stream=None) -> torch.Tensor:
+                 scale: float, max_q_len: int, out=None, stream=None, key_splits: int = 1,
+                 workspace=None) -> torch.Tensor:
     """paged_attn_prefill_int8: prefill over an int8 cache with fp32 scales [NB, bs, Hkv]."""
     sh = _prefill_shape(q, k_cache, v_cache, block_tables, context_lens, q_offsets, max_q_len,
                         (torch.int8,), (("k_scales", k_scales), ("v_scales", v_scales)))
-    if out is None:
-        with _on(stream):
-            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    _check(load().paged_attn_prefill_int8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales),
-                                          _ptr(v_scales), _ptr(block_tables), _ptr(context_lens),
-                                          _ptr(q_offsets), ctypes.c_float(scale), _ptr(out),
-                                          ctypes.byref(sh), _stream_handle(stream)))
-    return out
+    L = load()
+    lead = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+            _ptr(block_tables), _ptr(context_lens), _ptr(q_offsets))
+    return _prefill_call(L.paged_attn_prefill_int8, L.paged_attn_prefill_split_int8, lead, sh,
+                         key_splits, workspace, q, out, scale, stream)
 
 
 def prefill_fp8(q, k_cache, v_cache, block_tables, context_lens, q_offsets, scale: float,
-                max_q_len: int, out=None, stream=None) -> torch.Tensor:
+                max_q_len: int, out=None, stream=None, key_splits: int = 1,
+                workspace=None) -> torch.Tensor:
     """paged_attn_prefill_fp8: prefill over an FP8 E4M3 cache (float8_e4m3fn or uint8 codes)."""
     sh = _prefill_shape(q, k_cache, v_cache, block_tables, context_lens, q_offsets, max_q_len,
                         FP8_DTYPES)
-    if out is None:
-        with _on(stream):
-            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    _check(load().paged_attn_prefill_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                         _ptr(context_lens), _ptr(q_offsets), ctypes.c_float(scale),
-                                         _ptr(out), ctypes.byref(sh), _stream_handle(stream)))
-    return out
+    L = load()
+    lead = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+            _ptr(q_offsets))
+    return _prefill_call(L.paged_attn_prefill_fp8, L.paged_attn_prefill_split_fp8, lead, sh,
+                         key_splits, workspace, q, out, scale, stream)
 
 
-def prefill_views(views, q, q_offsets, max_q_len: int, out=None, stream=None, scale=None):
+def prefill_shape_of(views, q, q_offsets, max_q_len: int) -> PaPrefillShape:
+    """The pa_prefill_shape of a prefill call over the input generator's views."""
+    return _prefill_shape(q, views["k_cache"], views["v_cache"], views["block_tables"],
+                          views["context_lens"], q_offsets, max_q_len,
+                          (views["k_cache"].dtype,))
+
+
+def prefill_views(views, q, q_offsets, max_q_len: int, out=None, stream=None, scale=None,
+                  key_splits: int = 1, workspace=None):
     """Prefill of query tokens q [q_offsets[-1], Hq, D] over the per-layer
     views of the input generator, whatever the cache kind."""
     sc = views["scale"] if scale is None else scale
     args = (views["block_tables"], views["context_lens"], q_offsets, sc, max_q_len)
+    kw = dict(out=out, stream=stream, key_splits=key_splits, workspace=workspace)
     if views["k_cache"].dtype in FP8_DTYPES:
-        return prefill_fp8(q, views["k_cache"], views["v_cache"], *args, out=out, stream=stream)
+        return prefill_fp8(q, views["k_cache"], views["v_cache"], *args, **kw)
     if "k_scales" in views:
         return prefill_int8(q, views["k_cache"], views["v_cache"], views["k_scales"],
-                            views["v_scales"], *args, out=out, stream=stream)
-    return prefill(q, views["k_cache"], views["v_cache"], *args, out=out, stream=stream)
+                            views["v_scales"], *args, **kw)
+    return prefill(q, views["k_cache"], views["v_cache"], *args, **kw)

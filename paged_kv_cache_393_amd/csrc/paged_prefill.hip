@@ -38,6 +38,16 @@
 // (exact) and take the weights times the V scales as a bf16 pair (high part +
 // remainder, exact to 2^-17: int8 V scales can push the weights past fp16).
 // Both read V token-major through LDS transpose reads, one barrier per tile.
+// Key split (paged_attn_prefill_split*): one chunk of one sequence is only
+// (kv heads x row tiles) workgroups, a quarter of the compute units for a
+// 512-token Llama-3-8B chunk, each walking ~46 tiles.  The split form cuts a
+// row tile's key tiles into near-equal runs over several workgroups; each
+// writes its rows' unnormalised sums with their running max and row sum, and
+// a merge kernel combines the runs with log-sum-exp weights, so each row is
+// still one softmax over its whole visible context (ybb.press page section
+// 2.2) up to fp32 rounding order, as in the decode's merge.  A row can see no key of a
+// run's first tiles (a run starting inside the causal diagonal), so its max
+// starts at -inf there and its rescale factor is taken as 1.
 // Scheduling: on this chip a matrix instruction holds its SIMD's vector issue
 // for most of its 16 cycles (transcendentals excepted), so the vector work a
 // step needs -- softmax, staging -- is as costly as its products; one step
@@ -48,6 +58,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "paged_prefill.h"
@@ -126,6 +137,9 @@ struct PrefillParams {
     int log2_block_size;
     int num_seqs;
     int tiles_x;             // row tiles per (sequence, kv head)
+    int key_splits;          // key pieces per row tile (1: one workgroup takes all the keys)
+    float *part_acc;         // key_splits > 1: unnormalised sums [units][key_splits][256][D]
+    float *part_ml;          //   and (running max, row sum) pairs [units][key_splits][256][2]
 };
 
 // LDS staging of one 32-token tile of one kv head's K or V (D*2 bytes a
@@ -283,7 +297,9 @@ __device__ __forceinline__ int sequence_of_rank(const PrefillParams &p, int r, u
     return S - 1 - r;   // not reached: rank r < S lies in some bucket
 }
 
-template <int D, int KV>
+// kSplit: the key-split form (p.key_splits > 1): a workgroup takes one run of
+// its row tile's key tiles.  The unsplit form compiles with run 0 of 1.
+template <int D, int KV, bool kSplit>
 __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(const PrefillParams p) {
     constexpr int kSteps = D / 32;    // QK k-steps of 32 dims
     constexpr int kDpl = D / 16;      // PV output blocks of 16 dims
@@ -324,16 +340,22 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // head) pair P -- heaviest sequences first -- goes to XCD P % 8, and an
     // XCD runs its pairs in order, all row tiles of a pair together, so the
     // row tiles that read the same K/V share one L2.
+    // With key pieces, a row tile's pieces are consecutive workgroups of its XCD.
     const int xcd = (int)(blockIdx.x % 8);
     const int y = (int)(blockIdx.x / 8);
-    const int P = (y / p.tiles_x) * 8 + xcd;
+    const int splits = kSplit ? p.key_splits : 1;
+    const int per_pair = p.tiles_x * splits;
+    const int P = (y / per_pair) * 8 + xcd;
     if (P >= p.num_kv_heads * p.num_seqs) return;    // uniform: the whole workgroup
     const int s = sequence_of_rank(p, P / p.num_kv_heads, lds_rank_b, lds_rank_cnt, lds_rank_sel);
     const int g = P % p.num_kv_heads;
-    const int bx = p.tiles_x - 1 - y % p.tiles_x;
+    const int bx = p.tiles_x - 1 - (y % per_pair) / splits;
+    const int piece = (y % per_pair) % splits;
 #else
     const int s = gridDim.z - 1 - blockIdx.z;
-    const int bx = gridDim.x - 1 - blockIdx.x;
+    const int splits = kSplit ? p.key_splits : 1;
+    const int bx = p.tiles_x - 1 - (int)blockIdx.x / splits;
+    const int piece = (int)blockIdx.x % splits;
     const int g = blockIdx.y;
 #endif
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -399,8 +421,20 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     int wg_pmax = lds_pmax[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) wg_pmax = max(wg_pmax, lds_pmax[w]);
-    const int n_tiles = wg_pmax / kTileTokens + 1;     // the workgroup's tiles (uniform)
-    const int my_steps = pmax / kTileTokens + 1;       // this wave's tiles
+    // The row tile's tiles 0 .. n_full-1 are cut into `pieces` near-equal
+    // runs; this workgroup takes run `piece`, tiles t_lo .. t_hi-1 (uniform).
+    // Below, tile indices count from t_lo and tok0 is its first token.
+    const int n_full = wg_pmax / kTileTokens + 1;
+    const int pieces = kSplit ? max(1, min(p.key_splits, n_full)) : 1;
+    if (kSplit && piece >= pieces) return;             // uniform: a short context has fewer pieces
+    const int t_lo = kSplit ? piece * n_full / pieces : 0;
+    const int t_hi = kSplit ? (piece + 1) * n_full / pieces : n_full;
+    const int n_tiles = t_hi - t_lo;                   // the workgroup's tiles
+    const int tok0 = t_lo * kTileTokens;
+    // this wave's tiles: those up to its last row's position (none when that
+    // lies before the run)
+    const int my_steps = !kSplit || pieces == 1 ? pmax / kTileTokens + 1
+                                                : min(max(pmax / kTileTokens + 1, t_lo), t_hi) - t_lo;
 
     // ---- bf16 K tile loads: this wave's pieces, piece index w + j * kWaves;
     // during iteration i they load tile i + kGroup + 1.
@@ -413,7 +447,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // are loaded when the window slides (64 blocks ahead of their use), and a
     // tile's blocks are read from a lane (v_readlane), not from memory: a
     // load between a tile's K/V loads and their use would wait for them too.
-    const int nblk = ((min(ctx, n_tiles * kTileTokens) - 1) >> bs_log2) + 1;   // entries read
+    const int nblk = ((min(ctx, tok0 + n_tiles * kTileTokens) - 1) >> bs_log2) + 1;   // entries read
     auto load_window = [&](int base) __attribute__((always_inline)) {
         const int e = base + lane;
         return e < nblk ? table[e] : 0;
@@ -429,7 +463,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         return b;
     };
     auto phys_of = [&](int tile, int j) __attribute__((always_inline)) {
-        return phys_at(tile * kTileTokens + 16 * piece_half(j));
+        return phys_at(tok0 + tile * kTileTokens + 16 * piece_half(j));
     };
     // One direct-to-LDS load of 16 B a lane: the rows of the 16-token half
     // starting at token tb (physical block phys) of `base` (K or V of the kv
@@ -465,7 +499,8 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         const int r16 = lane & 15;
         const int chunk = 4 * (sub % (TL::kChunks / 4)) + (lane >> 4);
         const int voff = (int)((uint32_t)r16 * rb32 + (uint32_t)(chunk * 16));
-        direct_load(kbase, tile * kTileTokens + 16 * piece_half(j), phys, voff, lds_k[tile % kRing] + sub * 1024);
+        direct_load(kbase, tok0 + tile * kTileTokens + 16 * piece_half(j), phys, voff,
+                    lds_k[tile % kRing] + sub * 1024);
     };
 
     // ---- int8 / FP8 tiles come through registers: each thread loads 8 codes
@@ -482,7 +517,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     u32x2_t st_codes[kQLoads];
     float st_scale[kQLoads];
     // keys and values read: the workgroup's tiles, within the context
-    const int kv_end = min(ctx, n_tiles * kTileTokens);
+    const int kv_end = min(ctx, tok0 + n_tiles * kTileTokens);
     // K or V: wave-uniform (4 D loads per tile and kind, a multiple of 64)
     auto qload_ok = [&](int jj) __attribute__((always_inline)) {
         return wave * 64 + jj * kThreads < 8 * D;
@@ -520,7 +555,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     };
     auto qissue = [&](int tile, int jj, int phys) __attribute__((always_inline)) {
         const bool is_v = qload_is_v(jj);
-        const int tb = tile * kTileTokens + 16 * qload_half(jj);
+        const int tb = tok0 + tile * kTileTokens + 16 * qload_half(jj);
         const int rows = min(16, max(0, kv_end - tb));   // none past the tiles or the context is read
         const int64_t slot0 = ((int64_t)phys << bs_log2) + (tb & bs_mask);
         const int r16 = qload_token(jj) & 15;
@@ -536,7 +571,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     };
     // tile `tile` of load jj; past the tiles the codes read as 0
     auto qissue_tile = [&](int tile, int jj) __attribute__((always_inline)) {
-        qissue(tile, jj, phys_at(tile * kTileTokens + 16 * qload_half(jj)));
+        qissue(tile, jj, phys_at(tok0 + tile * kTileTokens + 16 * qload_half(jj)));
     };
     auto qstore = [&](int jj, int slot) __attribute__((always_inline)) {
         const int tok = qload_token(jj), ch = qload_chunk(jj);
@@ -569,7 +604,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int vs_dim = 32 * (vs_w >> 1) + 4 * vs_q;          // the lane's first dim
     u32x2_t vst[2];
     auto vstage_issue = [&](int tile) __attribute__((always_inline)) {
-        const int tb = tile * kTileTokens + 16 * vs_half;
+        const int tb = tok0 + tile * kTileTokens + 16 * vs_half;
         const int rows = min(16, max(0, ctx - tb));
         const int64_t slot0 = ((int64_t)phys_at(tb) << bs_log2) + (tb & bs_mask);
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(vbase + slot0 * rb32, rows * (int)rb32);
@@ -673,7 +708,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     auto softmax = [&](const int t, const Scores &S, Weights &Phi, Weights &Plo, float (&alpha)[kNc],
                        auto masked) __attribute__((always_inline)) {
         constexpr bool kMasked = decltype(masked)::value;
-        const int t0 = t * kTileTokens;
+        const int t0 = tok0 + t * kTileTokens;
         bool vis[kNc][8];
         float mx[kNc];
         bool exceed = false;
@@ -695,7 +730,11 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
             for (int cb = 0; cb < kNc; ++cb) {
                 const float mt = group_max(mx[cb]) * c;       // -inf: nothing visible
                 const float m_new = mt > m_run[cb] + 8.f ? mt : m_run[cb];
-                alpha[cb] = m_run[cb] - m_new;                 // log2 of the rescale; 0 if unmoved
+                // log2 of the rescale; 0 if unmoved -- also for a row that has
+                // seen no key yet (a key run that starts past its position),
+                // whose max stays -inf
+                // (unsplit: every row sees token 0 in its first tile)
+                alpha[cb] = !kSplit ? m_run[cb] - m_new : m_new > m_run[cb] ? m_run[cb] - m_new : 0.f;
                 l_run[cb] *= __builtin_amdgcn_exp2f(alpha[cb]);
                 m_run[cb] = m_new;
             }
@@ -861,9 +900,9 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         m_run[cb] = -INFINITY;
         l_run[cb] = 0.f;
     }
-    wbase = 0;
-    win = load_window(0);
-    win_next = load_window(64);
+    wbase = tok0 >> bs_log2;
+    win = load_window(wbase);
+    win_next = load_window(wbase + 64);
 
     // ---- prologue: the tiles the first segment reads in LDS (K(0) ..
     // K(kGroup), V(0) .. V(kGroup-2)), then the scores of tile 0.
@@ -949,7 +988,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         // FP8: V(i+1)'s, one iteration ahead); once it leaves the window,
         // slide (the newest, K(i+kGroup+1)'s last (K(i+3)'s), is at most 96
         // tokens further, under 64 blocks, so a slide never skips a window).
-        if ((((i + (KV == kBf16 ? kGroup - 1 : 1)) * kTileTokens) >> bs_log2) >= wbase + 64) {
+        if (((tok0 + (i + (KV == kBf16 ? kGroup - 1 : 1)) * kTileTokens) >> bs_log2) >= wbase + 64) {
             wbase += 64;
             win = win_next;
             win_next = load_window(wbase + 64);
@@ -998,7 +1037,8 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // first segment), its middle tiles (every part present, no mask: one
     // straight-line body), and the rest (diagonal tiles, the last weighted
     // sum, then loads only).
-    const int first_masked = pmin >= kTileTokens - 1 ? (pmin - (kTileTokens - 1)) / kTileTokens + 1 : 0;
+    // tiles (counted from t_lo) below every row's position: no mask
+    const int first_masked = (pmin >= kTileTokens - 1 ? (pmin - (kTileTokens - 1)) / kTileTokens + 1 : 0) - t_lo;
     const int full_end = wave_live ? max(1, min(first_masked, my_steps - 1)) : 1;
     Scores S2;
     Weights Phi2, Plo2;
@@ -1058,7 +1098,12 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
 
     if (!wave_live) return;
     // ---- the four lane groups hold partial sums over different tokens;
-    // lane l has dims 16 j + 4 (l/16) + e of row l%16 of each column block
+    // lane l has dims 16 j + 4 (l/16) + e of row l%16 of each column block.
+    // One piece: the normalised rows go to out.  Several: this piece's
+    // unnormalised sums, running max (log2 units, the weights' 2^kPBias
+    // included) and row sum go to its partial rows, for the merge kernel.
+    const int64_t prow0 = !kSplit || pieces == 1 ? 0
+        : ((((int64_t)s * Hkv + g) * p.tiles_x + bx) * p.key_splits + piece) * kRowsPerGroup;
 #pragma unroll
     for (int cb = 0; cb < kNc; ++cb) {
         float l = l_run[cb];
@@ -1066,6 +1111,14 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         l += __shfl_xor(l, 32);
         if (!colv[cb]) continue;
         const int r = row0 + 16 * cb + l16;
+        if (kSplit && pieces > 1) {
+            const int64_t pr = prow0 + (r - bx * kRowsPerGroup);
+            float *dst = p.part_acc + pr * D + 4 * hgrp;
+#pragma unroll
+            for (int j = 0; j < kDpl; ++j) *(f32x4_t *)(dst + 16 * j) = acc[j][cb];
+            if (hgrp == 0) *(f32x2_t *)(p.part_ml + 2 * pr) = f32x2_t{m_run[cb], l};
+            continue;
+        }
         const int i = r / G;
         const int hh = r - i * G;
         const float inv = 1.f / l;
@@ -1073,6 +1126,68 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
 #pragma unroll
         for (int j = 0; j < kDpl; ++j) *(f32x4_t *)(dst + 16 * j) = acc[j][cb] * inv;
     }
+}
+
+// ---- key pieces: the merge.  Block b takes kMergeRows rows of row tile
+// b / kMergeBlocksPerTile (unit order: sequence, kv head, row tile), D/4
+// lanes a row, 4 dims each.  A row tile with one piece was written by the
+// prefill kernel.  Out row = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k,
+// M = max_k m_k, taken piece by piece with a running max (a piece that saw
+// none of the row's keys has m = -inf, l = 0, acc = 0); the loads of four
+// pieces are issued together.
+constexpr int kMergeThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void pa_prefill_merge_kernel(const PrefillParams p) {
+    constexpr int kLanesPerRow = D / 4;
+    constexpr int kMergeRows = kMergeThreads / kLanesPerRow;
+    constexpr int kBlocksPerTile = kRowsPerGroup / kMergeRows;
+    const int64_t unit = (int64_t)blockIdx.x / kBlocksPerTile;
+    const int bx = (int)(unit % p.tiles_x);
+    const int64_t pair = unit / p.tiles_x;
+    const int g = (int)(pair % p.num_kv_heads);
+    const int s = (int)(pair / p.num_kv_heads);
+    const int G = p.group;
+    const int q0 = p.q_offsets[s];
+    const int nq = p.q_offsets[s + 1] - q0;
+    const int R = nq * G;
+    const int rl = (int)(blockIdx.x % kBlocksPerTile) * kMergeRows + (int)threadIdx.x / kLanesPerRow;
+    const int r = bx * kRowsPerGroup + rl;
+    if (r >= R) return;
+    // the prefill kernel's piece count for this row tile: its last row's
+    // position gives its tiles
+    const int last = min(R, (bx + 1) * kRowsPerGroup) - 1;
+    const int n_full = (p.context_lens[s] - nq + last / G) / kTileTokens + 1;
+    const int pieces = max(1, min(p.key_splits, n_full));
+    if (pieces == 1) return;
+    const int d = 4 * ((int)threadIdx.x % kLanesPerRow);
+    const int64_t pr0 = unit * p.key_splits * kRowsPerGroup + rl;   // piece k: + k * 256
+    float M = -INFINITY, L = 0.f;
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < pieces; k0 += 4) {
+        f32x2_t ml[4];
+        f32x4_t a[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t pr = pr0 + (int64_t)min(k0 + u, pieces - 1) * kRowsPerGroup;
+            ml[u] = *(const f32x2_t *)(p.part_ml + 2 * pr);
+            a[u] = *(const f32x4_t *)(p.part_acc + pr * D + d);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (k0 + u >= pieces) break;
+            const float m_new = fmaxf(M, ml[u][0]);
+            if (m_new == -INFINITY) continue;            // nothing seen yet
+            const float f_old = exp2f(M - m_new);         // 0 while M is -inf
+            const float f_k = exp2f(ml[u][0] - m_new);
+            L = L * f_old + ml[u][1] * f_k;
+            o = o * f_old + a[u] * f_k;
+            M = m_new;
+        }
+    }
+    const int i = r / G;
+    const int hh = r - i * G;
+    *(f32x4_t *)(p.out + ((int64_t)(q0 + i) * p.num_q_heads + g * G + hh) * D + d) = o * (1.f / L);
 }
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -1083,10 +1198,11 @@ int ilog2(int x) {
 }
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
-int prefill_common(int kind, const void *q, const void *k_cache, const void *v_cache,
-                   const float *k_scales, const float *v_scales, const int32_t *block_tables,
-                   const int32_t *context_lens, const int32_t *q_offsets, float scale, float *out,
-                   const pa_prefill_shape *sh, void *stream) {
+constexpr int kMaxKeySplits = 64;
+
+// Shape checks shared by every prefill entry point; *tiles receives the row
+// tiles per (sequence, kv head).
+int check_shape(const pa_prefill_shape *sh, int64_t *tiles) {
     if (!sh) return PA_ERR_NULL;
     if (sh->num_seqs < 0 || sh->num_q_heads < 1 || sh->num_kv_heads < 1 ||
         sh->max_blocks_per_seq < 1 || sh->num_blocks < 1 || sh->max_q_len < 1)
@@ -1098,10 +1214,45 @@ int prefill_common(int kind, const void *q, const void *k_cache, const void *v_c
     if ((int64_t)sh->max_blocks_per_seq * sh->block_size >= ((int64_t)1 << 30)) return PA_ERR_UNSUPPORTED;
     const int group = sh->num_q_heads / sh->num_kv_heads;
     const int64_t rows = (int64_t)sh->max_q_len * group;
-    const int64_t tiles = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
-    if (rows >= ((int64_t)1 << 30) || tiles > 0x7fffffff || sh->num_kv_heads > 65535 ||
+    *tiles = (rows + kRowsPerGroup - 1) / kRowsPerGroup;
+    if (rows >= ((int64_t)1 << 30) || *tiles > 0x7fffffff || sh->num_kv_heads > 65535 ||
         sh->num_seqs > 65535)
         return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+// Partial rows of a key-split call: 256 per (sequence, kv head, row tile, piece).
+int64_t partial_rows(const pa_prefill_shape *sh, int64_t tiles, int key_splits) {
+    return (int64_t)sh->num_seqs * sh->num_kv_heads * tiles * key_splits * kRowsPerGroup;
+}
+
+int64_t split_workspace_bytes(const pa_prefill_shape *sh, int64_t tiles, int key_splits) {
+    return key_splits > 1 ? partial_rows(sh, tiles, key_splits) * (sh->head_dim + 2) * 4 : 0;
+}
+
+template <bool kSplit>
+void launch_prefill(int kind, int head_dim, dim3 grid, dim3 block, hipStream_t st, const PrefillParams &p) {
+    if (head_dim == 128) {
+        if (kind == kInt8) hipLaunchKernelGGL((pa_prefill_kernel<128, kInt8, kSplit>), grid, block, 0, st, p);
+        else if (kind == kFp8) hipLaunchKernelGGL((pa_prefill_kernel<128, kFp8, kSplit>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((pa_prefill_kernel<128, kBf16, kSplit>), grid, block, 0, st, p);
+    } else {
+        if (kind == kInt8) hipLaunchKernelGGL((pa_prefill_kernel<64, kInt8, kSplit>), grid, block, 0, st, p);
+        else if (kind == kFp8) hipLaunchKernelGGL((pa_prefill_kernel<64, kFp8, kSplit>), grid, block, 0, st, p);
+        else hipLaunchKernelGGL((pa_prefill_kernel<64, kBf16, kSplit>), grid, block, 0, st, p);
+    }
+}
+
+int prefill_common(int kind, const void *q, const void *k_cache, const void *v_cache,
+                   const float *k_scales, const float *v_scales, const int32_t *block_tables,
+                   const int32_t *context_lens, const int32_t *q_offsets, float scale, float *out,
+                   const pa_prefill_shape *sh, int key_splits, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    int64_t tiles = 0;
+    const int rc = check_shape(sh, &tiles);
+    if (rc != PA_OK) return rc;
+    if (key_splits < 1 || key_splits > kMaxKeySplits) return PA_ERR_SHAPE;
+    const int group = sh->num_q_heads / sh->num_kv_heads;
     if (sh->num_seqs == 0) return PA_OK;
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !q_offsets || !out)
         return PA_ERR_NULL;
@@ -1111,6 +1262,11 @@ int prefill_common(int kind, const void *q, const void *k_cache, const void *v_c
                       : (((uintptr_t)k_cache | (uintptr_t)v_cache) & 7u) != 0)
         return PA_ERR_ALIGNMENT;
     if (kind == kInt8 && (((uintptr_t)k_scales | (uintptr_t)v_scales) & 3u) != 0) return PA_ERR_ALIGNMENT;
+    const int64_t ws_need = split_workspace_bytes(sh, tiles, key_splits);
+    if (key_splits > 1) {
+        if (!workspace || workspace_bytes < (size_t)ws_need) return PA_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PA_ERR_ALIGNMENT;
+    }
     PrefillParams p;
     p.q = (const uint16_t *)q;
     p.k = k_cache;
@@ -1130,26 +1286,33 @@ int prefill_common(int kind, const void *q, const void *k_cache, const void *v_c
     p.log2_block_size = ilog2(sh->block_size);
     p.num_seqs = sh->num_seqs;
     p.tiles_x = (int)tiles;
+    p.key_splits = key_splits;
+    p.part_acc = key_splits > 1 ? (float *)workspace : nullptr;
+    p.part_ml = key_splits > 1 ? (float *)workspace + partial_rows(sh, tiles, key_splits) * sh->head_dim : nullptr;
+    const int64_t units = (int64_t)sh->num_kv_heads * sh->num_seqs * tiles;
+    const int64_t merge_blocks = units * (kRowsPerGroup / (kMergeThreads / (sh->head_dim / 4)));
+    if (merge_blocks >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
 #if PF_XCD_MAP
     const int64_t pairs = (int64_t)sh->num_kv_heads * sh->num_seqs;
-    const int64_t n_wg = 8 * ((pairs + 7) / 8) * tiles;
+    const int64_t n_wg = 8 * ((pairs + 7) / 8) * tiles * key_splits;
     if (n_wg >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)n_wg);
 #else
-    const dim3 grid((unsigned)tiles, (unsigned)sh->num_kv_heads, (unsigned)sh->num_seqs);
+    if (tiles * key_splits > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+    const dim3 grid((unsigned)(tiles * key_splits), (unsigned)sh->num_kv_heads, (unsigned)sh->num_seqs);
 #endif
     const dim3 block(kThreads);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (sh->head_dim == 128) {
-        if (kind == kInt8) hipLaunchKernelGGL((pa_prefill_kernel<128, kInt8>), grid, block, 0, st, p);
-        else if (kind == kFp8) hipLaunchKernelGGL((pa_prefill_kernel<128, kFp8>), grid, block, 0, st, p);
-        else hipLaunchKernelGGL((pa_prefill_kernel<128, kBf16>), grid, block, 0, st, p);
-    } else {
-        if (kind == kInt8) hipLaunchKernelGGL((pa_prefill_kernel<64, kInt8>), grid, block, 0, st, p);
-        else if (kind == kFp8) hipLaunchKernelGGL((pa_prefill_kernel<64, kFp8>), grid, block, 0, st, p);
-        else hipLaunchKernelGGL((pa_prefill_kernel<64, kBf16>), grid, block, 0, st, p);
+    if (key_splits > 1) launch_prefill<true>(kind, sh->head_dim, grid, block, st, p);
+    else launch_prefill<false>(kind, sh->head_dim, grid, block, st, p);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+    if (key_splits > 1) {
+        const dim3 mgrid((unsigned)merge_blocks);
+        if (sh->head_dim == 128) hipLaunchKernelGGL((pa_prefill_merge_kernel<128>), mgrid, dim3(kMergeThreads), 0, st, p);
+        else hipLaunchKernelGGL((pa_prefill_merge_kernel<64>), mgrid, dim3(kMergeThreads), 0, st, p);
+        if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
     }
-    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+    return PA_OK;
 }
 
 }  // namespace
@@ -1159,7 +1322,7 @@ extern "C" int paged_attn_prefill(const void *q, const void *k_cache, const void
                                   const int32_t *q_offsets, float scale, float *out,
                                   const pa_prefill_shape *sh, void *stream) {
     return prefill_common(kBf16, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,
-                          q_offsets, scale, out, sh, stream);
+                          q_offsets, scale, out, sh, 1, nullptr, 0, stream);
 }
 
 extern "C" int paged_attn_prefill_int8(const void *q, const int8_t *k_cache, const int8_t *v_cache,
@@ -1168,7 +1331,7 @@ extern "C" int paged_attn_prefill_int8(const void *q, const int8_t *k_cache, con
                                        const int32_t *q_offsets, float scale, float *out,
                                        const pa_prefill_shape *sh, void *stream) {
     return prefill_common(kInt8, q, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens,
-                          q_offsets, scale, out, sh, stream);
+                          q_offsets, scale, out, sh, 1, nullptr, 0, stream);
 }
 
 extern "C" int paged_attn_prefill_fp8(const void *q, const uint8_t *k_cache, const uint8_t *v_cache,
@@ -1176,5 +1339,60 @@ extern "C" int paged_attn_prefill_fp8(const void *q, const uint8_t *k_cache, con
                                       const int32_t *q_offsets, float scale, float *out,
                                       const pa_prefill_shape *sh, void *stream) {
     return prefill_common(kFp8, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,
-                          q_offsets, scale, out, sh, stream);
+                          q_offsets, scale, out, sh, 1, nullptr, 0, stream);
+}
+
+extern "C" int paged_attn_prefill_plan(const pa_prefill_shape *sh, int32_t *key_splits) {
+    if (!key_splits) return PA_ERR_NULL;
+    int64_t tiles = 0;
+    const int rc = check_shape(sh, &tiles);
+    if (rc != PA_OK) return rc;
+    *key_splits = 1;
+    const int64_t units = (int64_t)sh->num_seqs * sh->num_kv_heads * tiles;
+    if (units == 0) return PA_OK;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return PA_ERR_LAUNCH;
+    // one prefill workgroup fills a compute unit: split the keys until the
+    // units' pieces cover the compute units, keeping 4 or more tiles a piece
+    const int64_t max_tiles = ((int64_t)sh->max_blocks_per_seq * sh->block_size + kTileTokens - 1) / kTileTokens;
+    int64_t k = (cus + units - 1) / units;
+    k = std::min<int64_t>(k, std::max<int64_t>(1, max_tiles / 4));
+    *key_splits = (int32_t)std::max<int64_t>(1, std::min<int64_t>(k, kMaxKeySplits));
+    return PA_OK;
+}
+
+extern "C" size_t paged_attn_prefill_workspace_bytes(const pa_prefill_shape *sh, int32_t key_splits) {
+    int64_t tiles = 0;
+    if (check_shape(sh, &tiles) != PA_OK || key_splits < 1 || key_splits > kMaxKeySplits) return 0;
+    return (size_t)split_workspace_bytes(sh, tiles, key_splits);
+}
+
+extern "C" int paged_attn_prefill_split(const void *q, const void *k_cache, const void *v_cache,
+                                        const int32_t *block_tables, const int32_t *context_lens,
+                                        const int32_t *q_offsets, float scale, float *out,
+                                        const pa_prefill_shape *sh, int32_t key_splits, void *workspace,
+                                        size_t workspace_bytes, void *stream) {
+    return prefill_common(kBf16, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,
+                          q_offsets, scale, out, sh, key_splits, workspace, workspace_bytes, stream);
+}
+
+extern "C" int paged_attn_prefill_split_int8(const void *q, const int8_t *k_cache, const int8_t *v_cache,
+                                             const float *k_scales, const float *v_scales,
+                                             const int32_t *block_tables, const int32_t *context_lens,
+                                             const int32_t *q_offsets, float scale, float *out,
+                                             const pa_prefill_shape *sh, int32_t key_splits,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_common(kInt8, q, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens,
+                          q_offsets, scale, out, sh, key_splits, workspace, workspace_bytes, stream);
+}
+
+extern "C" int paged_attn_prefill_split_fp8(const void *q, const uint8_t *k_cache, const uint8_t *v_cache,
+                                            const int32_t *block_tables, const int32_t *context_lens,
+                                            const int32_t *q_offsets, float scale, float *out,
+                                            const pa_prefill_shape *sh, int32_t key_splits,
+                                            void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_common(kFp8, q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,
+                          q_offsets, scale, out, sh, key_splits, workspace, workspace_bytes, stream);
 }

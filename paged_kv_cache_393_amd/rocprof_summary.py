@@ -30,20 +30,23 @@ WRITE_SOURCE = os.path.join(_HERE, "csrc", "kv_write.hip")
 EVICT_SOURCE = os.path.join(_HERE, "csrc", "kv_evict.hip")
 PREFILL_SOURCE = os.path.join(_HERE, "csrc", "paged_prefill.hip")
 COMPRESS_SOURCE = os.path.join(_HERE, "csrc", "kv_compress.hip")
-KERNELS = ("pa_decode_kernel", "pa_merge_kernel", "kv_write_kernel", "token_scores_kernel",
+KERNELS = ("pa_prefill_merge_kernel", "pa_decode_kernel", "pa_merge_kernel", "kv_write_kernel", "token_scores_kernel",
            "evict_lowest_block_kernel", "pa_prefill_kernel", "probe_copy_kernel",
            "probe_read_kernel", "compress_select_kernel", "compress_move_kernel",
            "compress_split_keys_kernel", "compress_split_pass_kernel", "compress_split_write_kernel",
            "compress_move_far_kernel")
-# The kernels of each timed operation and the source file they are built from.
+# The kernels of each timed operation and the source files they are built from.
 OPERATIONS = {
-    "decode": (("pa_decode_kernel", "pa_merge_kernel"), KERNEL_SOURCE),
-    "write": (("kv_write_kernel",), WRITE_SOURCE),
-    "scores": (("token_scores_kernel",), EVICT_SOURCE),
-    "prefill": (("pa_prefill_kernel",), PREFILL_SOURCE),
+    "decode": (("pa_decode_kernel", "pa_merge_kernel"), (KERNEL_SOURCE,)),
+    "write": (("kv_write_kernel",), (WRITE_SOURCE,)),
+    "scores": (("token_scores_kernel",), (EVICT_SOURCE,)),
+    "prefill": (("pa_prefill_kernel", "pa_prefill_merge_kernel"), (PREFILL_SOURCE,)),
+    # a serving batch: the chunks' prefill call and the decodes' call
+    "serving": (("pa_prefill_kernel", "pa_prefill_merge_kernel", "pa_decode_kernel", "pa_merge_kernel"),
+                (PREFILL_SOURCE, KERNEL_SOURCE)),
     "compress": (("compress_select_kernel", "compress_split_keys_kernel", "compress_split_pass_kernel",
                   "compress_split_write_kernel", "compress_move_kernel", "compress_move_far_kernel"),
-                 COMPRESS_SOURCE),
+                 (COMPRESS_SOURCE,)),
 }
 
 
@@ -94,8 +97,8 @@ def cmd_stats(a) -> int:
     for r in rows:
         lines.append(f"{short_name(r['kernel']):<28} {r['calls']:>6} {r['avg_ns'] / 1e3:>9.2f} "
                      f"{r['min_ns'] / 1e3:>9.2f} {r['max_ns'] / 1e3:>9.2f} {r['pct']:>6.2f}")
-    kernels, src = OPERATIONS[a.operation]
-    lines += ["", f"{os.path.basename(src)} sha256: {source_sha256(src)}"]
+    kernels, srcs = OPERATIONS[a.operation]
+    lines += [""] + [f"{os.path.basename(src)} sha256: {source_sha256(src)}" for src in srcs]
     text = "\n".join(lines) + "\n"
     with open(a.out, "w") as f:
         f.write(text)
@@ -112,7 +115,7 @@ def cmd_traffic(a) -> int:
     sw = a.copy_bytes / (copy_w * 1024.0)
     per_kernel = {}
     total = 0.0
-    kernels, src = OPERATIONS[a.operation]
+    kernels, srcs = OPERATIONS[a.operation]
     for k in kernels:
         fk = fetch.get(k, {}).get("FETCH_SIZE", 0.0)
         wk = write.get(k, {}).get("WRITE_SIZE", 0.0)
@@ -121,8 +124,8 @@ def cmd_traffic(a) -> int:
         total += b
     rec = {
         "workload": a.workload,
-        "source": os.path.basename(src),
-        "source_sha256": source_sha256(src),
+        "source": ", ".join(os.path.basename(src) for src in srcs),
+        "source_sha256": ", ".join(source_sha256(src) for src in srcs),
         "copy_calibration": {"bytes": a.copy_bytes, "fetch_kib": copy_f, "write_kib": copy_w,
                              "fetch_scale": sf, "write_scale": sw},
         "kernels": per_kernel,

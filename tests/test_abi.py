@@ -14,7 +14,9 @@ DECLARED = {"paged_attn_plan", "paged_attn_workspace_bytes", "paged_attn_decode"
             "paged_attn_prefill_fp8", "paged_kv_compress_workspace_bytes",
             "paged_kv_compress_prefill", "paged_kv_compress_prefill_int8",
             "paged_kv_compress_prefill_fp8", "paged_attn_check_tables",
-            "paged_attn_decode_noalloc"}
+            "paged_attn_decode_noalloc", "paged_attn_prefill_plan",
+            "paged_attn_prefill_workspace_bytes", "paged_attn_prefill_split",
+            "paged_attn_prefill_split_int8", "paged_attn_prefill_split_fp8"}
 
 
 def lib():
@@ -402,6 +404,55 @@ def test_quantized_prefill_host_checks(kind):
     if kind == "int8":
         assert pcall_q(kind, pshape(), vs=ctypes.c_void_p(0x100002)) == B.PA_ERR_ALIGNMENT
     assert pcall_q(kind, pshape(num_seqs=0), q=None, k=None) == B.PA_OK
+
+
+def test_prefill_workspace_size():
+    # 2 sequences x 2 kv heads x ceil(64 * 4 / 256) = 1 row tile x K pieces x 256 rows x (D + 2) floats
+    for k in (2, 3, 64):
+        assert lib().paged_attn_prefill_workspace_bytes(ctypes.byref(pshape()), k) == 2 * 2 * 1 * k * 256 * 130 * 4
+    # max_q_len 65 needs a second row tile; head_dim 64
+    assert (lib().paged_attn_prefill_workspace_bytes(ctypes.byref(pshape(max_q_len=65, head_dim=64)), 4)
+            == 2 * 2 * 2 * 4 * 256 * 66 * 4)
+    assert lib().paged_attn_prefill_workspace_bytes(ctypes.byref(pshape()), 1) == 0
+    for k in (0, -1, 65):
+        assert lib().paged_attn_prefill_workspace_bytes(ctypes.byref(pshape()), k) == 0
+    assert lib().paged_attn_prefill_workspace_bytes(ctypes.byref(pshape(head_dim=96)), 2) == 0
+    assert lib().paged_attn_prefill_workspace_bytes(None, 2) == 0
+
+
+def test_prefill_plan_host_checks():
+    k = ctypes.c_int32(-5)
+    assert lib().paged_attn_prefill_plan(ctypes.byref(pshape()), None) == B.PA_ERR_NULL
+    assert lib().paged_attn_prefill_plan(None, ctypes.byref(k)) == B.PA_ERR_NULL
+    assert lib().paged_attn_prefill_plan(ctypes.byref(pshape(head_dim=96)), ctypes.byref(k)) == B.PA_ERR_UNSUPPORTED
+    assert lib().paged_attn_prefill_plan(ctypes.byref(pshape(max_q_len=0)), ctypes.byref(k)) == B.PA_ERR_SHAPE
+    # no sequences: no device query, one piece
+    assert lib().paged_attn_prefill_plan(ctypes.byref(pshape(num_seqs=0)), ctypes.byref(k)) == B.PA_OK
+    assert k.value == 1
+
+
+def pcall_split(kind, sh, key_splits, ws=FAKE, wsb=1 << 30, q=FAKE, k=FAKE, out=FAKE):
+    L = lib()
+    tail = (ctypes.c_float(0.1), out, ctypes.byref(sh), key_splits, ws, wsb, None)
+    if kind == "int8":
+        return L.paged_attn_prefill_split_int8(q, k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, *tail)
+    fn = L.paged_attn_prefill_split_fp8 if kind == "fp8" else L.paged_attn_prefill_split
+    return fn(q, k, FAKE, FAKE, FAKE, FAKE, *tail)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8", "fp8"])
+def test_split_prefill_host_checks(kind):
+    need = lib().paged_attn_prefill_workspace_bytes(ctypes.byref(pshape()), 4)
+    for k in (0, -3, 65):
+        assert pcall_split(kind, pshape(), k) == B.PA_ERR_SHAPE, k
+    assert pcall_split(kind, pshape(), 4, ws=None) == B.PA_ERR_WORKSPACE
+    assert pcall_split(kind, pshape(), 4, wsb=need - 1) == B.PA_ERR_WORKSPACE
+    assert pcall_split(kind, pshape(), 4, ws=ctypes.c_void_p(0x100008), wsb=need) == B.PA_ERR_ALIGNMENT
+    assert pcall_split(kind, pshape(), 4, q=None) == B.PA_ERR_NULL
+    assert pcall_split(kind, pshape(), 4, out=ctypes.c_void_p(0x100008)) == B.PA_ERR_ALIGNMENT
+    assert pcall_split(kind, pshape(head_dim=96), 4) == B.PA_ERR_UNSUPPORTED
+    # the shape is checked before key_splits; no sequences is a no-op either way
+    assert pcall_split(kind, pshape(num_seqs=0), 4, ws=None, q=None, k=None) == B.PA_OK
 
 
 def call_noalloc(sh, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, out=FAKE):
