@@ -325,8 +325,9 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     constexpr bool kVt = KV == kBf16;     // V staged transposed (V^T), as fp16
     __shared__ __attribute__((aligned(1024))) char lds_k[kRing][TL::kBytes];
     __shared__ __attribute__((aligned(1024))) char lds_v[kRing][kVt ? TL::kVtBytes : TL::kBytes];   // fp16 V^T, or bf16 / fp16 V
-    // V^T: set when a staging wave met a value beyond fp16 (see vstage_store)
-    __shared__ int lds_wide;
+    // V^T: set by a staging wave, in its own slot, when it met a value beyond
+    // fp16 (see vstage_store)
+    __shared__ int lds_wide[kWaves];
     __shared__ int lds_pmax[kWaves];
     __shared__ uint8_t lds_rank_b[kRankSeqs];
     __shared__ int lds_rank_cnt[kWaves > kRankBuckets ? kWaves : kRankBuckets];
@@ -415,12 +416,21 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     }
     pmax = __builtin_amdgcn_readfirstlane(pmax);      // wave-uniform after the reduction
     pmin = __builtin_amdgcn_readfirstlane(pmin);
-    if (lane == 0) lds_pmax[wave] = wave_live ? pmax : -1;
-    if (threadIdx.x == 0) lds_wide = 0;
-    __syncthreads();
-    int wg_pmax = lds_pmax[0];
+    // The workgroup's last position.  bf16: its last row's (positions grow
+    // with the row), with no barrier, so the block-table window loads right
+    // after the q loads.  int8 / FP8: the waves' maxima through LDS (the
+    // barrier keeps their prologue within 128 registers).
+    int wg_pmax;
+    if constexpr (kVt) {
+        if (lane == 0) lds_wide[wave] = 0;
+        wg_pmax = ctx - nq + (min(R, (bx + 1) * kRowsPerGroup) - 1) / G;
+    } else {
+        if (lane == 0) lds_pmax[wave] = wave_live ? pmax : -1;
+        __syncthreads();
+        wg_pmax = lds_pmax[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) wg_pmax = max(wg_pmax, lds_pmax[w]);
+        for (int w = 1; w < kWaves; ++w) wg_pmax = max(wg_pmax, lds_pmax[w]);
+    }
     // The row tile's tiles 0 .. n_full-1 are cut into `pieces` near-equal
     // runs; this workgroup takes run `piece`, tiles t_lo .. t_hi-1 (uniform).
     // Below, tile indices count from t_lo and tok0 is its first token.
@@ -642,7 +652,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         // max magnitude (a NaN is skipped: fp16 keeps it)
         const float mx = fmaxf(fmaxf(fmaxf(fabsf(f[0][0]), fabsf(f[0][1])), fmaxf(fabsf(f[0][2]), fabsf(f[0][3]))),
                                fmaxf(fmaxf(fabsf(f[1][0]), fabsf(f[1][1])), fmaxf(fabsf(f[1][2]), fabsf(f[1][3]))));
-        if (__ballot(mx >= 65536.f) != 0 && lane == 0) lds_wide = 1;
+        if (__ballot(mx >= 65536.f) != 0 && lane == 0) lds_wide[wave] = 1;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             *at(k) = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{f[0][k], f[1][k]}, f16x2_t));
@@ -1090,7 +1100,10 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     run(std::false_type{});
     if constexpr (kVt) {
         // every staging write of the pass came before its last barrier
-        if (__builtin_amdgcn_readfirstlane(lds_wide) != 0) {
+        int wide = 0;
+#pragma unroll
+        for (int w = kVWave0; w < kVWave0 + kVWaves; ++w) wide |= lds_wide[w];
+        if (__builtin_amdgcn_readfirstlane(wide) != 0) {
             __syncthreads();   // the pass's last LDS reads are done before the rerun loads over them
             run(std::true_type{});
         }
