@@ -649,9 +649,14 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
             f[e][2] = __uint_as_float(vst[e][1] << 16);
             f[e][3] = __uint_as_float(vst[e][1] & 0xffff0000u);
         }
-        // max magnitude (a NaN is skipped: fp16 keeps it)
-        const float mx = fmaxf(fmaxf(fmaxf(fabsf(f[0][0]), fabsf(f[0][1])), fmaxf(fabsf(f[0][2]), fabsf(f[0][3]))),
-                               fmaxf(fmaxf(fabsf(f[1][0]), fabsf(f[1][1])), fmaxf(fabsf(f[1][2]), fabsf(f[1][3]))));
+        // max magnitude (a NaN is skipped: fp16 keeps it), as three-input
+        // maxima with absolute-value modifiers: written with fmaxf / fabsf the
+        // compiler first quiets each input, 11 instructions instead of 4
+        float m0, m1, m2, mx;
+        asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m0) : "v"(f[0][0]), "v"(f[0][1]), "v"(f[0][2]));
+        asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m1) : "v"(f[0][3]), "v"(f[1][0]), "v"(f[1][1]));
+        asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(m2) : "v"(f[1][2]), "v"(f[1][3]), "v"(m0));
+        asm("v_max_f32 %0, %1, %2" : "=v"(mx) : "v"(m1), "v"(m2));
         if (__ballot(mx >= 65536.f) != 0 && lane == 0) lds_wide[wave] = 1;
 #pragma unroll
         for (int k = 0; k < 4; ++k)

@@ -197,3 +197,26 @@ def test_full_size_serving_chunk_key_split():
     torch.cuda.synchronize()
     r = C.prefill_oracle(ch, ch["q"], ch["q_offsets"].cpu())
     assert_parity(sp["chunk_out"], r, f"serving chunk, key split {k}")
+
+
+def test_split_prefill_on_a_side_stream():
+    # With stream= a non-current stream, the wrapper allocates out and the
+    # workspace for that stream: allocator churn on the current stream while
+    # the side stream runs cannot reuse them.  Every result equals the call
+    # on the current stream bit for bit and passes against the oracle.
+    note("split prefill side stream")
+    ctx = (1513, 300)
+    v, q, q_off = make_kind(ctx, [512, 64], 32, 8, 128, 16, 627, "bf16")
+    main = run_split(v, q, q_off, 4).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        outs.append(B.prefill_views(v, q, q_off.to(DEV), 512, stream=side, key_splits=4))
+        junk = torch.empty(64 << 20, dtype=torch.uint8, device=DEV)
+        junk.fill_(0x7F)
+        del junk
+    side.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int32), main.view(torch.int32))
+    assert_parity(outs[0], C.prefill_oracle(v, q, q_off), "split side stream")
