@@ -227,6 +227,14 @@ def _validate(q, k_cache, v_cache, block_tables, context_lens, kv_dtype):
         raise TypeError("block_tables and context_lens must be int32")
 
 
+def _check_out(out, q):
+    """A caller's `out` must be a contiguous fp32 device tensor shaped like q:
+    the kernels write q's row count times Hq x D floats into it."""
+    if out is not None and (not out.is_cuda or out.dtype != torch.float32 or
+                            tuple(out.shape) != tuple(q.shape) or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous fp32 device tensor shaped like q")
+
+
 def alloc_workspace(shape: PaShape, device) -> torch.Tensor:
     """Scratch workspace for decode calls of `shape` (no initialisation needed)."""
     n = workspace_bytes(shape)
@@ -240,6 +248,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out=No
     """out fp32 [S, Hq, D] = paged_attn_decode(...) on the current (or given) stream."""
     _validate(q, k_cache, v_cache, block_tables, context_lens, torch.bfloat16)
     shape = shape_of(q, k_cache, block_tables, split_tokens)
+    _check_out(out, q)
     with _on(stream):
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
@@ -260,9 +269,9 @@ def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale: float
     the library's static device scratch; `out` fp32 [S, Hq, D] is the caller's
     and nothing is allocated."""
     _validate(q, k_cache, v_cache, block_tables, context_lens, torch.bfloat16)
-    if out is None or out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape) or \
-            not out.is_contiguous() or not out.is_cuda:
+    if out is None:
         raise ValueError("out must be a contiguous fp32 device tensor shaped like q")
+    _check_out(out, q)
     shape = shape_of(q, k_cache, block_tables, split_tokens)
     _check(load().paged_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache),
                                             _ptr(block_tables), _ptr(context_lens),
@@ -282,6 +291,7 @@ def decode_int8(q, k_cache, v_cache, k_scales, v_scales, block_tables, context_l
         if tuple(t.shape) != tuple(k_cache.shape[:3]):
             raise ValueError(f"{name} must be [num_blocks, block_size, num_kv_heads]")
     shape = shape_of(q, k_cache, block_tables, split_tokens)
+    _check_out(out, q)
     with _on(stream):
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
@@ -308,6 +318,7 @@ def decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale: float, ou
         raise TypeError("fp8 cache must be float8_e4m3fn (or uint8 codes)")
     _validate(q, k_cache, v_cache, block_tables, context_lens, k_cache.dtype)
     shape = shape_of(q, k_cache, block_tables, split_tokens)
+    _check_out(out, q)
     with _on(stream):
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
@@ -606,6 +617,7 @@ def alloc_prefill_workspace(shape: PaPrefillShape, key_splits: int, device) -> O
 def _prefill_call(fn_plain, fn_split, lead, sh, key_splits, workspace, q, out, scale, stream):
     """One prefill call: the plain entry point for key_splits == 1, else the
     key-split one with `workspace` (allocated on `stream` when None)."""
+    _check_out(out, q)
     with _on(stream):
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)

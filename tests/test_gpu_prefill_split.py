@@ -220,3 +220,28 @@ def test_split_prefill_on_a_side_stream():
     for o in outs:
         assert torch.equal(o.view(torch.int32), main.view(torch.int32))
     assert_parity(outs[0], C.prefill_oracle(v, q, q_off), "split side stream")
+
+
+def test_wrappers_reject_a_caller_out_that_does_not_fit():
+    # A caller's out must be a contiguous fp32 device tensor shaped like q:
+    # anything else raises before a kernel could write past it.
+    note("out validation")
+    v, q, q_off = make_kind((300, 40), [64, 40], 8, 2, 128, 16, 628, "bf16")
+    bad = [torch.empty(q.shape[0] - 1, *q.shape[1:], dtype=torch.float32, device=DEV),
+           torch.empty(q.shape, dtype=torch.bfloat16, device=DEV),
+           torch.empty(q.shape[0], q.shape[1], 2 * q.shape[2], dtype=torch.float32, device=DEV)[..., ::2],
+           torch.empty(q.shape, dtype=torch.float32)]
+    for o in bad:
+        for ks in (1, 3):
+            with pytest.raises(ValueError):
+                B.prefill_views(v, q, q_off.to(DEV), 64, out=o, key_splits=ks)
+    # the decode of the same two sequences, one query each
+    dv = dict(v, q=q[:2].contiguous())
+    bad_d = [torch.empty(1, *q.shape[1:], dtype=torch.float32, device=DEV),
+             torch.empty(2, *q.shape[1:], dtype=torch.bfloat16, device=DEV),
+             torch.empty(2, q.shape[1], 2 * q.shape[2], dtype=torch.float32, device=DEV)[..., ::2],
+             torch.empty(2, *q.shape[1:], dtype=torch.float32)]
+    for o in bad_d:
+        with pytest.raises(ValueError):
+            B.decode_views(dv, out=o)
+    torch.cuda.synchronize()
