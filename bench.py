@@ -724,7 +724,9 @@ def bench_prefill(args) -> int:
             "peak": HBM_PEAK_GBPS if hbm_bound else MFMA_BF16_PEAK_TFLOPS,
             "unit": "GB/s" if hbm_bound else "TFLOP/s",
             "frac": gbps / HBM_PEAK_GBPS if hbm_bound else tflops / MFMA_BF16_PEAK_TFLOPS,
-            "traffic": (None if split is not None or key_splits > 1
+            "traffic": (measured_traffic(f"{pw.name}_split", "serving")
+                        if split is not None and key_splits > 1
+                        else None if split is not None or key_splits > 1
                         else measured_traffic(pw.name, "prefill")),
             "algorithmic_flops_per_call": flops,
             "algorithmic_bytes_per_call": nbytes,

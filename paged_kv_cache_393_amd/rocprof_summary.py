@@ -21,6 +21,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 
@@ -41,9 +42,9 @@ OPERATIONS = {
     "write": (("kv_write_kernel",), (WRITE_SOURCE,)),
     "scores": (("token_scores_kernel",), (EVICT_SOURCE,)),
     "prefill": (("pa_prefill_kernel", "pa_prefill_merge_kernel"), (PREFILL_SOURCE,)),
-    # a serving batch: the chunks' prefill call and the decodes' call
-    "serving": (("pa_prefill_kernel", "pa_prefill_merge_kernel", "pa_decode_kernel", "pa_merge_kernel"),
-                (PREFILL_SOURCE, KERNEL_SOURCE)),
+    # a serving batch: the chunk's key-split prefill call and the decodes' call
+    "serving": (("pa_prefill_kernel_split", "pa_prefill_merge_kernel", "pa_decode_kernel",
+                 "pa_merge_kernel"), (PREFILL_SOURCE, KERNEL_SOURCE)),
     "compress": (("compress_select_kernel", "compress_split_keys_kernel", "compress_split_pass_kernel",
                   "compress_split_write_kernel", "compress_move_kernel", "compress_move_far_kernel"),
                  (COMPRESS_SOURCE,)),
@@ -56,6 +57,9 @@ def source_sha256(path: str = KERNEL_SOURCE) -> str:
 
 
 def short_name(name: str) -> str:
+    # the key-split form of the prefill kernel (its last template argument true)
+    if re.search(r"pa_prefill_kernel<[^>]*\btrue>", name):
+        return "pa_prefill_kernel_split"
     for k in KERNELS:
         if k in name:
             return k
