@@ -108,9 +108,10 @@ constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0) alone (gfx9 fie
 // iteration i reads K(i+1) and V(i-1) and loads K(i+kGroup+1) and
 // V(i+kGroup-1), the tiles of the next segment, into a ring of 2 kGroup
 // slots (slot = tile % ring): the slot a load overwrites was last read in
-// the previous segment.  bf16 tiles go straight to LDS and take segments of
-// two iterations (half the barriers); int8 / FP8 tiles come through
-// registers, one tile's worth, and take segments of one.
+// the previous segment.  bf16 tiles (K straight to LDS, V^T through the
+// staging waves' registers, a tile's worth in flight) take segments of four
+// iterations, a quarter of the barriers; int8 / FP8 tiles come through all
+// waves' registers, one tile's worth, and take segments of one.
 template <int KV>
 constexpr int kGroupOf = KV == 0 ? PF_BF16_GROUP : 1;
 
@@ -600,7 +601,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // two 8-B loads, issued at the start of an iteration, written at its end
     // as four 4-B V^T runs (one per dim, its 2 tokens).  The values are
     // written as fp16; a value beyond fp16 (magnitude >= 2^16, or infinite)
-    // sets lds_wide, and the workgroup then runs again in the safe mode,
+    // sets the wave's lds_wide flag, and the workgroup then runs again in the safe mode,
     // which writes them as bf16.  Tokens past the context read as 0 (the
     // buffer range).
     const bool v_stager = kVt && wave >= kVWave0 && wave < kVWave0 + kVWaves;   // wave-uniform
