@@ -236,11 +236,42 @@ __device__ __forceinline__ u32x4_t fp8x8_to_f16x8(const u32x2_t w) {
 // (later first).  Workgroup-uniform; contains barriers.
 constexpr int kRankSeqs = 2048;
 constexpr int kRankBuckets = 64;
-__device__ __forceinline__ int work_bucket(const PrefillParams &p, int s) {
-    const int64_t rows = (int64_t)(p.q_offsets[s + 1] - p.q_offsets[s]) * p.group;
-    const int64_t w = rows * (int64_t)max(p.context_lens[s], 0);
+__device__ __forceinline__ int bucket_of(int nq, int ctx, int group) {
+    const int64_t rows = (int64_t)nq * group;
+    const int64_t w = rows * (int64_t)max(ctx, 0);
     if (rows <= 0 || w <= 0) return 0;
     return min(kRankBuckets - 1, 64 - __builtin_clzll((unsigned long long)w));
+}
+__device__ __forceinline__ int work_bucket(const PrefillParams &p, int s) {
+    return bucket_of(p.q_offsets[s + 1] - p.q_offsets[s], p.context_lens[s], p.group);
+}
+
+// The sequence of rank r with its query offsets and context length.  Up to
+// 64 sequences, every wave finds it on its own, without LDS or barriers:
+// lane i holds sequence i's lengths and the key (bucket << 6) | i, unique and
+// ordered as the dispatch order (heavier bucket, then later index, first);
+// the key of rank r (r keys above it) is built bit by bit from the top, a
+// bit kept when at least r + 1 keys reach the prefix.  The lengths come from
+// the lanes, so they cost no second round trip.
+struct SeqInfo {
+    int s, q0, q1, ctx;
+};
+__device__ __forceinline__ SeqInfo small_batch_rank(const PrefillParams &p, int r) {
+    const int lane = threadIdx.x & 63;
+    const bool in = lane < p.num_seqs;
+    const int qa = in ? p.q_offsets[lane] : 0;
+    const int qb = in ? p.q_offsets[lane + 1] : 0;
+    const int cl = in ? p.context_lens[lane] : 0;
+    const int key = in ? (bucket_of(qb - qa, cl, p.group) << 6) | lane : -1;
+    int ans = 0;
+#pragma unroll
+    for (int bit = 11; bit >= 0; --bit) {
+        const int t = ans | (1 << bit);
+        if (__popcll(__ballot(key >= t)) >= r + 1) ans = t;
+    }
+    const int sq = ans & 63;
+    return {sq, __builtin_amdgcn_readlane(qa, sq), __builtin_amdgcn_readlane(qb, sq),
+            __builtin_amdgcn_readlane(cl, sq)};
 }
 
 __device__ __forceinline__ int sequence_of_rank(const PrefillParams &p, int r, uint8_t *lds_b,
@@ -349,7 +380,16 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int per_pair = p.tiles_x * splits;
     const int P = (y / per_pair) * 8 + xcd;
     if (P >= p.num_kv_heads * p.num_seqs) return;    // uniform: the whole workgroup
-    const int s = sequence_of_rank(p, P / p.num_kv_heads, lds_rank_b, lds_rank_cnt, lds_rank_sel);
+    SeqInfo si;
+    if (p.num_seqs <= 64) {
+        si = small_batch_rank(p, P / p.num_kv_heads);
+    } else {
+        si.s = sequence_of_rank(p, P / p.num_kv_heads, lds_rank_b, lds_rank_cnt, lds_rank_sel);
+        si.q0 = p.q_offsets[si.s];
+        si.q1 = p.q_offsets[si.s + 1];
+        si.ctx = p.context_lens[si.s];
+    }
+    const int s = si.s;
     const int g = P % p.num_kv_heads;
     const int bx = p.tiles_x - 1 - (y % per_pair) / splits;
     const int piece = (y % per_pair) % splits;
@@ -365,13 +405,13 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int hgrp = lane >> 4;       // lane group: k-elements / accumulator rows
     const int l16 = lane & 15;
     const int G = p.group;
-    const int q0 = p.q_offsets[s];
-    const int nq = p.q_offsets[s + 1] - q0;
+    const int q0 = si.q0;
+    const int nq = si.q1 - q0;
     const int R = nq * G;
     if (bx * kRowsPerGroup >= R) return;             // uniform: no row of the workgroup exists
     const int row0 = bx * kRowsPerGroup + wave * kRowsPerWave;
     const bool wave_live = row0 < R;
-    const int ctx = p.context_lens[s];
+    const int ctx = si.ctx;
     const int Hq = p.num_q_heads;
     const int Hkv = p.num_kv_heads;
     constexpr int kElem = KV == kBf16 ? 2 : 1;             // bytes per cache element
