@@ -85,9 +85,6 @@ typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 #ifndef PF_BF16_GROUP
 #define PF_BF16_GROUP 4
 #endif
-#ifndef PF_XCD_MAP
-#define PF_XCD_MAP 1
-#endif
 
 #ifndef PF_WAVES
 #define PF_WAVES 16
@@ -368,7 +365,6 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     __shared__ __attribute__((aligned(16))) float lds_sc[KV == kInt8 ? 2 : 1][kRing][kTileTokens];
     constexpr int kVsc = KV == kInt8 ? 1 : 0;
 
-#if PF_XCD_MAP
     // Workgroup L runs on XCD L % 8 (round-robin dispatch).  (sequence, kv
     // head) pair P -- heaviest sequences first -- goes to XCD P % 8, and an
     // XCD runs its pairs in order, all row tiles of a pair together, so the
@@ -393,13 +389,6 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int g = P % p.num_kv_heads;
     const int bx = p.tiles_x - 1 - (y % per_pair) / splits;
     const int piece = (y % per_pair) % splits;
-#else
-    const int s = gridDim.z - 1 - blockIdx.z;
-    const int splits = kSplit ? p.key_splits : 1;
-    const int bx = p.tiles_x - 1 - (int)blockIdx.x / splits;
-    const int piece = (int)blockIdx.x % splits;
-    const int g = blockIdx.y;
-#endif
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int hgrp = lane >> 4;       // lane group: k-elements / accumulator rows
@@ -1351,15 +1340,10 @@ int prefill_common(int kind, const void *q, const void *k_cache, const void *v_c
     const int64_t units = (int64_t)sh->num_kv_heads * sh->num_seqs * tiles;
     const int64_t merge_blocks = units * (kRowsPerGroup / (kMergeThreads / (sh->head_dim / 4)));
     if (merge_blocks >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
-#if PF_XCD_MAP
     const int64_t pairs = (int64_t)sh->num_kv_heads * sh->num_seqs;
     const int64_t n_wg = 8 * ((pairs + 7) / 8) * tiles * key_splits;
     if (n_wg >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)n_wg);
-#else
-    if (tiles * key_splits > 0x7fffffff) return PA_ERR_UNSUPPORTED;
-    const dim3 grid((unsigned)(tiles * key_splits), (unsigned)sh->num_kv_heads, (unsigned)sh->num_seqs);
-#endif
     const dim3 block(kThreads);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (key_splits > 1) launch_prefill<true>(kind, sh->head_dim, grid, block, st, p);
