@@ -245,3 +245,15 @@ def test_wrappers_reject_a_caller_out_that_does_not_fit():
         with pytest.raises(ValueError):
             B.decode_views(dv, out=o)
     torch.cuda.synchronize()
+
+
+def test_full_size_eight_chunk_batch_key_split():
+    # The 8-chunk prefill batch at full size with two runs per row tile (the
+    # plan keeps it unsplit: 512 workgroups already cover the GPU); every
+    # query of every chunk against the oracle.
+    note("full-size prefill, 8 chunks, key split 2")
+    pw = I.PREFILL_WORKLOADS["prefill_llama3_8b"]
+    inp = I.make_prefill_inputs(pw, DEV)
+    out = B.prefill_views(inp, inp["q"], inp["q_offsets"], inp["max_q_len"], key_splits=2)
+    torch.cuda.synchronize()
+    assert_parity(out, C.prefill_oracle(inp, inp["q"], inp["q_offsets"]), "prefill_llama3_8b key split 2")
