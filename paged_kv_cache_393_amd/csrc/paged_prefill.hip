@@ -642,6 +642,13 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int vs_half = vs_w & 1;
     const int vs_p = lane & 7, vs_q = lane >> 3;
     const int vs_dim = 32 * (vs_w >> 1) + 4 * vs_q;          // the lane's first dim
+    // Bytes, within a V^T slot, of the lane's two writes for dims vs_dim, +1
+    // and vs_dim + 2, +3: tokens 2 p, 2 p + 1 of half h sit at byte
+    // 8 h + 4 (p % 2) of chunk p / 2 (two chunk swizzles).  Opaque lane
+    // constants, so each write address is one add to the slot's base.
+    int vs_off01 = TL::vt_chunk(vs_dim, vs_p >> 1) + 8 * vs_half + 4 * (vs_p & 1);
+    int vs_off23 = TL::vt_chunk(vs_dim + 2, vs_p >> 1) + 8 * vs_half + 4 * (vs_p & 1);
+    __asm__ volatile("" : "+v"(vs_off01), "+v"(vs_off23));
     u32x2_t vst[2];
     auto vstage_issue = [&](int tile) __attribute__((always_inline)) {
         const int tb = tok0 + tile * kTileTokens + 16 * vs_half;
@@ -657,11 +664,8 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         constexpr bool kSafe = decltype(safe)::value;
         // (opaque: keeps the conversion below inside the staging waves' branch)
         __asm__ volatile("" : "+v"(vst[0]), "+v"(vst[1]));
-        // tokens 2 p, 2 p + 1 of half h sit at byte 8 h + 4 (p % 2) of chunk
-        // p / 2; dims vs_dim + k, k = 0..3, take two chunk swizzles
-        const int in_chunk = 8 * vs_half + 4 * (vs_p & 1);
-        char *row01 = lds_v[slot] + TL::vt_chunk(vs_dim, vs_p >> 1) + in_chunk;
-        char *row23 = lds_v[slot] + TL::vt_chunk(vs_dim + 2, vs_p >> 1) + in_chunk;
+        char *row01 = lds_v[slot] + vs_off01;
+        char *row23 = lds_v[slot] + vs_off23;
         auto at = [&](int k) __attribute__((always_inline)) {
             return (uint32_t *)((k < 2 ? row01 : row23) + (k & 1) * TL::kVtPitch);
         };
