@@ -257,3 +257,30 @@ def test_full_size_eight_chunk_batch_key_split():
     out = B.prefill_views(inp, inp["q"], inp["q_offsets"], inp["max_q_len"], key_splits=2)
     torch.cuda.synchronize()
     assert_parity(out, C.prefill_oracle(inp, inp["q"], inp["q_offsets"]), "prefill_llama3_8b key split 2")
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("key_splits", [1, 3])
+def test_prefill_more_than_64_sequences(kind, key_splits):
+    # Batches of more than 64 sequences take the dispatch ranking through LDS
+    # (up to 64, each wave ranks alone): 100 sequences of mixed chunks,
+    # decodes, empty query sets and an empty context, unsplit and key-split.
+    note(f"prefill {kind} 100 sequences K={key_splits}")
+    rng = np.random.default_rng(640 + key_splits)
+    ctx = [int(c) for c in rng.integers(1, 700, size=100)]
+    ctx[7] = 0
+    nq = [0 if c == 0 else int(min(c, rng.choice([1, 1, 1, 5, 40, 130])) ) for c in ctx]
+    nq[11] = 0
+    v, q, q_off = make_kind(tuple(ctx), nq, 8, 2, 128, 16, 641 + key_splits, kind)
+    assert_parity(run_split(v, q, q_off, key_splits), C.prefill_oracle(v, q, q_off),
+                  f"{kind} 100 sequences K={key_splits}")
+
+
+def test_split_prefill_loose_max_q_len_bit_identical():
+    # A max_q_len above every sequence's query count adds row tiles that
+    # exit (in the prefill and the merge): the output is the same to the bit.
+    note("split prefill loose max_q_len")
+    v, q, q_off = make_kind((300, 1300), [64, 512], 16, 4, 128, 16, 629, "bf16")
+    a = run_split(v, q, q_off, 4).clone()
+    b = run_split(v, q, q_off, 4, max_q=2048)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
