@@ -284,3 +284,16 @@ def test_split_prefill_loose_max_q_len_bit_identical():
     a = run_split(v, q, q_off, 4).clone()
     b = run_split(v, q, q_off, 4, max_q=2048)
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("key_splits", [1, 2])
+def test_prefill_more_than_2048_sequences_keep_index_order(key_splits):
+    # Past 2048 sequences the dispatch order is the index order (no ranking):
+    # 2100 short sequences, one to three queries each.
+    note(f"prefill 2100 sequences K={key_splits}")
+    rng = np.random.default_rng(650)
+    ctx = [int(c) for c in rng.integers(1, 70, size=2100)]
+    nq = [int(min(c, rng.integers(1, 4))) for c in ctx]
+    v, q, q_off = make_kind(tuple(ctx), nq, 8, 2, 64, 16, 651, "bf16")
+    assert_parity(run_split(v, q, q_off, key_splits), C.prefill_oracle(v, q, q_off),
+                  f"2100 sequences K={key_splits}")
