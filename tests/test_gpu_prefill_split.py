@@ -7,7 +7,11 @@ inside contexts of every length class: shorter than K tiles (fewer runs, or
 one run written directly beside merged row tiles in the same call), long
 contexts whose block-table window starts mid-table, running maxima that move
 between runs, the bf16 second pass in some runs only, and every cache kind.
-Bit-exact: a poisoned workspace, and repeated calls.
+Bit-exact: a poisoned workspace, repeated calls, a side stream, a loose
+max_q_len.  Also here, split and unsplit: the three dispatch orders (up to 64
+sequences ranked per wave, up to 2048 through LDS, beyond that by index), the
+full-size 8-chunk batch and serving chunk, and the wrappers' checks on a
+caller's out.
 """
 import numpy as np
 import pytest
