@@ -264,7 +264,7 @@ __device__ __forceinline__ SeqInfo small_batch_rank(const PrefillParams &p, int 
 #pragma unroll
     for (int bit = 11; bit >= 0; --bit) {
         const int t = ans | (1 << bit);
-        if (__popcll(__ballot(key >= t)) >= r + 1) ans = t;
+        if (__popcll(__ballot(key >= t)) >= (unsigned)(r + 1)) ans = t;
     }
     const int sq = ans & 63;
     return {sq, __builtin_amdgcn_readlane(qa, sq), __builtin_amdgcn_readlane(qb, sq),
