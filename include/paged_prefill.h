@@ -106,9 +106,11 @@ int paged_attn_prefill_fp8(const void *q, const uint8_t *k_cache, const uint8_t 
  * `workspace`, and a second kernel combines the runs of each row: out =
  * sum_k e^(m_k - M) acc_k / sum_k e^(m_k - M) l_k (M the largest m_k): one
  * softmax over the row's whole visible context, as the unsplit call and the
- * decode's merge compute it (ybb.press page, section 2.2), equal to the
- * unsplit call's result up to fp32 rounding order.  A unit with a single run
- * writes out directly.
+ * decode's merge compute it (ybb.press page, section 2.2).  It differs from
+ * the unsplit call's result by rounding only: fp32 summation order, and on
+ * the bf16 and FP8 paths the fp16 weights rounded against each run's own
+ * running maximum (within the same error bound; 1.2e-4 apart at most on a
+ * 512-token Llama-3-8B chunk).  A unit with a single run writes out directly.
  *
  * paged_attn_prefill_plan: a key_splits for `shape` on the current device:
  * the smallest K for which the units' runs cover the compute units (one
@@ -124,7 +126,7 @@ int paged_attn_prefill_fp8(const void *q, const uint8_t *k_cache, const uint8_t 
  * workspace is read) or the shape or key_splits is invalid.
  *
  * paged_attn_prefill_split / _int8 / _fp8: the prefill calls above, with the
- * same arguments and numerics, plus key_splits (1 .. 64; 1 is the unsplit
+ * same arguments and per-run arithmetic, plus key_splits (1 .. 64; 1 is the unsplit
  * call and ignores the workspace) and a caller-owned device workspace
  * (16-byte aligned, at least paged_attn_prefill_workspace_bytes; contents
  * need no initialisation; calls that may run concurrently must not share
