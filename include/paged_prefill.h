@@ -72,8 +72,15 @@ int paged_attn_prefill(const void *q, const void *k_cache, const void *v_cache,
  * element = code * scale): k_cache / v_cache int8 codes [num_blocks,
  * block_size, Hkv, head_dim] (8-byte aligned), k_scales / v_scales fp32
  * [num_blocks, block_size, Hkv] (4-byte aligned), as written by
- * paged_kv_write_int8.  The codes enter the matrix products exactly (bf16);
- * the K scales multiply the scores, the V scales the weights.
+ * paged_kv_write_int8.  The K codes enter the scores' product exactly (bf16)
+ * and the K scales multiply the scores.  Each V scale s = m 2^e (mantissa m
+ * in [1, 2)) is split: the V codes enter the weighted sum times 2^e, exactly,
+ * as fp16; the weights enter as fp16 (2^-11 relative rounding) carrying m,
+ * and the row sums add each rounded weight over m (an extra matrix product
+ * with 1/m as an fp16 pair), so the rounding cancels in the quotient as on
+ * the bf16 path.  A workgroup that meets a V scale outside 2^-14 .. 2^9
+ * (other than 0: negative, tiny, huge or not finite) computes its rows again
+ * with the weights times the whole V scales as a bf16 pair (exact to 2^-17).
  */
 int paged_attn_prefill_int8(const void *q, const int8_t *k_cache, const int8_t *v_cache,
                             const float *k_scales, const float *v_scales,

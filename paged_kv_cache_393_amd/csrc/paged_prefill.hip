@@ -34,10 +34,17 @@
 // into a bf16 high part and remainder.  The tiles run in segments of four,
 // one barrier each, through a ring of 8.
 // FP8 caches stage K and V through registers, V as fp16 (every E4M3 value is
-// one), and take the weights as fp16 likewise; int8 caches stage bf16 codes
-// (exact) and take the weights times the V scales as a bf16 pair (high part +
-// remainder, exact to 2^-17: int8 V scales can push the weights past fp16).
-// Both read V token-major through LDS transpose reads, one barrier per tile.
+// one), and take the weights as fp16 likewise.  int8 caches stage K as bf16
+// codes (exact); each token's V scale s = m 2^e (mantissa m in [1, 2)) is
+// split: V enters as fp16 codes times 2^e (exact), the weights as fp16 with
+// log2 m added to their scores (so they come out times m), and one more
+// product per tile, of the weights with 1/m as an fp16 pair, gives row sums
+// of the very weights each value c 2^e / (1/m) = c s is taken with -- the
+// rounding cancels in the quotient as on the bf16 path.  A workgroup that
+// meets a V scale outside 2^-14 .. 2^9 (other than 0) runs again with bf16
+// codes and the weights times the whole scales as a bf16 pair (exact to
+// 2^-17).  Both read V token-major through LDS transpose reads, one barrier
+// per tile.
 // Key split (paged_attn_prefill_split*): one chunk of one sequence is only
 // (kv heads x row tiles) workgroups, a quarter of the compute units for a
 // 512-token Llama-3-8B chunk, each walking ~46 tiles.  The split form cuts a
@@ -224,6 +231,24 @@ __device__ __forceinline__ u32x4_t fp8x8_to_f16x8(const u32x2_t w) {
     return r;
 }
 
+// Eight int8 codes c -> eight fp16 values c * f, f = 2^e with -14 <= e <= 8
+// (or 0), exactly: c * 2^e lies between 2^-14 and 2^15 in magnitude, normal
+// fp16.  The fp16 with bits 0x64 : (c ^ 0x80) is 1024 + 128 + c.
+__device__ __forceinline__ u32x4_t i8x8_to_f16x8_times(const u32x2_t w, const f16x2_t f) {
+    const f16x2_t bias = f16x2_t{1152.0f16, 1152.0f16};
+    u32x4_t r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t x = w[h] ^ 0x80808080u;
+        // bytes (x0, 0x64, x1, 0x64) and (x2, 0x64, x3, 0x64)
+        const uint32_t a = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);
+        const uint32_t b = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);
+        r[2 * h] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, a) - bias) * f);
+        r[2 * h + 1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2_t, b) - bias) * f);
+    }
+    return r;
+}
+
 // Dispatch order of the sequences, heaviest first.  A sequence's work is
 // about its query rows times its visible context; sequences go by work
 // bucket (0 for no rows, else 1 + floor(log2(rows * context)), at most 63),
@@ -346,24 +371,36 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     static_assert(kVWave0 + kVWaves <= kWaves && kVWaves <= 8, "staging waves");
     // bf16 and FP8: the weighted sum on fp16 (V as fp16: exact for every
     // E4M3 value, and for every bf16 value of magnitude below 2^16), the
-    // weights times 2^kPBias
+    // weights times 2^kPBias.  int8: the same weights, in both modes (the key
+    // pieces of a row tile may run in different modes), also on fp16 in the
+    // fast mode (below).
     constexpr bool kF16 = KV == kFp8 || KV == kBf16;
-    constexpr float kPBias = kF16 ? 7.f : 0.f;
+    constexpr float kPBias = 7.f;
     constexpr int kGroup = kGroupOf<KV>;
     constexpr int kRing = 2 * kGroup;
     constexpr bool kVt = KV == kBf16;     // V staged transposed (V^T), as fp16
     __shared__ __attribute__((aligned(1024))) char lds_k[kRing][TL::kBytes];
     __shared__ __attribute__((aligned(1024))) char lds_v[kRing][kVt ? TL::kVtBytes : TL::kBytes];   // fp16 V^T, or bf16 / fp16 V
-    // V^T: set by a staging wave, in its own slot, when it met a value beyond
-    // fp16 (see vstage_store)
+    // Set by a wave, in its own slot, when it met a value the fast mode does
+    // not hold: bf16 V beyond fp16 (see vstage_store), an int8 V scale out of
+    // the fast range (see qstore)
     __shared__ int lds_wide[kWaves];
     __shared__ int lds_pmax[kWaves];
     __shared__ uint8_t lds_rank_b[kRankSeqs];
     __shared__ int lds_rank_cnt[kWaves > kRankBuckets ? kWaves : kRankBuckets];
     __shared__ int lds_rank_sel[2];
-    // int8: the tiles' K and V scales (one per token of the kv head)
+    // int8: per token of the kv head, stored with the K tile (see qstore):
+    // its K scale [0] and, fast mode, log2 of its V scale's mantissa over c
+    // [1]; and its V scale, two tiles before its V tile, in a ring of four
+    // (read until the weighted sum of its tile, an iteration after that tile)
     __shared__ __attribute__((aligned(16))) float lds_sc[KV == kInt8 ? 2 : 1][kRing][kTileTokens];
-    constexpr int kVsc = KV == kInt8 ? 1 : 0;
+    constexpr int kVsRing = 4;
+    __shared__ __attribute__((aligned(16))) float lds_vs[KV == kInt8 ? kVsRing : 1][kTileTokens];
+    // int8 fast mode: the A operand of the row-sum product (see
+    // weighted_values): row 0 the V scale mantissas' reciprocals rounded to
+    // fp16, row 1 the remainder times 2^10, rows 2..15 zero; [slot][row]
+    // [lane group][k-element]
+    __shared__ __attribute__((aligned(16))) _Float16 lds_rs[KV == kInt8 ? kRing : 1][16][4][8];
 
     // Workgroup L runs on XCD L % 8 (round-robin dispatch).  (sequence, kv
     // head) pair P -- heaviest sequences first -- goes to XCD P % 8, and an
@@ -411,6 +448,9 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     const int bs_log2 = p.log2_block_size;
     const int bs_mask = (1 << bs_log2) - 1;
     const float c = p.scale_log2;      // |scale| log2(e); a negative scale negates q
+    // int8 fast mode: 1 / c (see qstore), if c is within 2^-100 .. 2^100
+    const bool i8_fast_ok = KV == kInt8 && c >= 0x1p-100f && c <= 0x1p100f;
+    const float inv_c = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, __builtin_amdgcn_rcpf(c))));
 
     // Columns of this lane: row r = row0 + 16 cb + l16 -> query token r / G,
     // head g*G + r % G, position ctx - nq + r / G.  Columns past R compute
@@ -455,7 +495,14 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         if (lane == 0) lds_wide[wave] = 0;
         wg_pmax = ctx - nq + (min(R, (bx + 1) * kRowsPerGroup) - 1) / G;
     } else {
-        if (lane == 0) lds_pmax[wave] = wave_live ? pmax : -1;
+        if (lane == 0) {
+            lds_pmax[wave] = wave_live ? pmax : -1;
+            lds_wide[wave] = 0;
+        }
+        if constexpr (KV == kInt8) {
+            constexpr int kRsChunks = (int)sizeof(lds_rs) / 16;
+            if ((int)threadIdx.x < kRsChunks) ((u32x4_t *)&lds_rs[0][0][0][0])[threadIdx.x] = u32x4_t{0u, 0u, 0u, 0u};
+        }
         __syncthreads();
         wg_pmax = lds_pmax[0];
 #pragma unroll
@@ -546,9 +593,9 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // ---- int8 / FP8 tiles come through registers: each thread loads 8 codes
     // (8 B) of one token of a K or V tile, load number tid + jj * threads
     // (K loads first), one iteration ahead, and at the end of the next
-    // iteration writes them into the same LDS layouts, as bf16 (FP8 V: as
-    // fp16; int8 scales go to lds_sc), so the loads have a whole iteration to
-    // land.
+    // iteration writes them into the same LDS layouts, as bf16 (FP8 V and
+    // int8 V in the fast mode: as fp16; int8 scales go to lds_sc and lds_vs),
+    // so the loads have a whole iteration to land.
     // 8-B code loads per thread per iteration (K + V): 8 D per tile over the
     // workgroup; with more threads than loads (D = 64) the later waves load
     // nothing (qload_ok, wave-uniform).
@@ -556,6 +603,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     constexpr int kCodeChunks = D / 8;                   // 8-code chunks per token
     u32x2_t st_codes[kQLoads];
     float st_scale[kQLoads];
+    float st_vscale[kQLoads];    // int8, K loads: the token's V scale
     // keys and values read: the workgroup's tiles, within the context
     const int kv_end = min(ctx, tok0 + n_tiles * kTileTokens);
     // K or V: wave-uniform (4 D loads per tile and kind, a multiple of 64)
@@ -593,7 +641,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)(((uint64_t)hi << 32) | lo), 0,
                                                  __builtin_amdgcn_readfirstlane(range), kRsrcFlags);
     };
-    auto qissue = [&](int tile, int jj, int phys) __attribute__((always_inline)) {
+    auto qissue = [&](int tile, int jj, int phys, auto safe) __attribute__((always_inline)) {
         const bool is_v = qload_is_v(jj);
         const int tb = tok0 + tile * kTileTokens + 16 * qload_half(jj);
         const int rows = min(16, max(0, kv_end - tb));   // none past the tiles or the context is read
@@ -602,26 +650,72 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         const __amdgpu_buffer_rsrc_t rs = make_rsrc((is_v ? vbase : kbase) + slot0 * rb32, rows * (int)rb32);
         st_codes[jj] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
             rs, (int)((uint32_t)r16 * rb32 + (uint32_t)(qload_chunk(jj) * 8)), 0, 0));
+        // int8: the tile's K and V scales, loaded (every lane of a token, one
+        // dword line a wave) by the K wave of each half that holds chunk 0,
+        // the one that stores them (see qstore)
         if constexpr (KV == kInt8) {
-            // every lane of the token loads its scale (one dword line per wave)
-            const float *sb = (is_v ? p.v_scales : p.k_scales) + slot0 * Hkv + g;
-            const __amdgpu_buffer_rsrc_t ss = make_rsrc(sb, rows * Hkv * 4);
-            st_scale[jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ss, r16 * Hkv * 4, 0, 0));
+            if (!is_v && qload_wpart(jj) % kChunkGroups == 0) {
+                const int64_t so = slot0 * Hkv + g;
+                const __amdgpu_buffer_rsrc_t ks = make_rsrc(p.k_scales + so, rows * Hkv * 4);
+                const __amdgpu_buffer_rsrc_t vs = make_rsrc(p.v_scales + so, rows * Hkv * 4);
+                st_scale[jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ks, r16 * Hkv * 4, 0, 0));
+                st_vscale[jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vs, r16 * Hkv * 4, 0, 0));
+            }
         }
     };
     // tile `tile` of load jj; past the tiles the codes read as 0
-    auto qissue_tile = [&](int tile, int jj) __attribute__((always_inline)) {
-        qissue(tile, jj, phys_at(tok0 + tile * kTileTokens + 16 * qload_half(jj)));
+    auto qissue_tile = [&](int tile, int jj, auto safe) __attribute__((always_inline)) {
+        qissue(tile, jj, phys_at(tok0 + tile * kTileTokens + 16 * qload_half(jj)), safe);
     };
-    auto qstore = [&](int jj, int slot) __attribute__((always_inline)) {
+    // int8, fast mode: a V scale s = m 2^e (mantissa m in [1, 2)) multiplies
+    // the codes by 2^e in the fp16 V tile; the weights take m through their
+    // scores (lds_sc[1] = log2(m) / c), and the row sums 1/m through lds_rs
+    // (stored with the V tile).  A zero scale gives V = 0 and m = 1.  A scale
+    // neither 0 nor within 2^-14 <= s < 2^9 (negative, tiny, huge or not
+    // finite) sets the wave's lds_wide flag, and the workgroup then runs
+    // again in the safe mode: V as bf16 codes, the weights times the whole
+    // scales as a bf16 pair.  K tile ktile, V tile vtile (its scales are in
+    // lds_vs since the K tile two before).
+    auto mantissa = [](float sc) __attribute__((always_inline)) {
+        return __uint_as_float((__float_as_uint(sc) & 0x007fffffu) | 0x3f800000u);
+    };
+    auto qstore = [&](int jj, int slot, int ktile, int vtile, auto safe) __attribute__((always_inline)) {
+        constexpr bool kI8Fast = KV == kInt8 && !decltype(safe)::value;
         const int tok = qload_token(jj), ch = qload_chunk(jj);
-        if (qload_is_v(jj))
-            *(u32x4_t *)(lds_v[slot] + TL::v_offset(tok, ch)) =
-                kF16 ? fp8x8_to_f16x8(st_codes[jj]) : codes_to_bf16x8<KV>(st_codes[jj]);
-        else
+        if (qload_is_v(jj)) {
+            u32x4_t val;
+            if constexpr (kI8Fast) {
+                const float sv = lds_vs[KV == kInt8 ? vtile % kVsRing : 0][tok];
+                const uint32_t sb = __float_as_uint(sv);
+                const _Float16 p2 = (_Float16)__uint_as_float(sb & 0x7f800000u);   // 2^e (or 0), exact
+                val = i8x8_to_f16x8_times(st_codes[jj], f16x2_t{p2, p2});
+                if (ch == 0) {
+                    // k-element 4 (tok / 16) + tok % 4 of lane group (tok % 16) / 4
+                    const float r = __builtin_amdgcn_rcpf(mantissa(sv));
+                    const _Float16 rh = (_Float16)r;
+                    _Float16 *at = &lds_rs[slot][0][(tok & 15) >> 2][4 * (tok >> 4) + (tok & 3)];
+                    at[0] = rh;
+                    at[4 * 8] = (_Float16)((r - (float)rh) * 1024.f);     // row 1
+                }
+            } else {
+                val = kF16 ? fp8x8_to_f16x8(st_codes[jj]) : codes_to_bf16x8<KV>(st_codes[jj]);
+            }
+            *(u32x4_t *)(lds_v[slot] + TL::v_offset(tok, ch)) = val;
+        } else {
             *(u32x4_t *)(lds_k[slot] + TL::k_offset(tok, ch)) = codes_to_bf16x8<KV>(st_codes[jj]);
-        if constexpr (KV == kInt8)
-            if (ch == 0) lds_sc[qload_is_v(jj) ? 1 : 0][slot][tok] = st_scale[jj];
+            if constexpr (KV == kInt8) {
+                if (ch == 0) {
+                    lds_sc[0][slot][tok] = st_scale[jj];
+                    lds_vs[KV == kInt8 ? ktile % kVsRing : 0][tok] = st_vscale[jj];
+                    if constexpr (kI8Fast) {
+                        const uint32_t sb = __float_as_uint(st_vscale[jj]);
+                        const bool fast = sb == 0u || (sb >= 0x38800000u && sb < 0x44000000u);
+                        if (!fast) lds_wide[wave] = 1;
+                        lds_sc[KV == kInt8 ? 1 : 0][slot][tok] = __builtin_amdgcn_logf(mantissa(st_vscale[jj])) * inv_c;
+                    }
+                }
+            }
+        }
     };
 
     // ---- bf16 V^T staging.  Staging wave w takes the 16-token half w % 2 and
@@ -702,7 +796,9 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // so the 2 kNc accumulation chains interleave.  int8: times the tokens' K
     // scales (the K tile holds the codes).
     typedef f32x4_t Scores[2][kNc];
-    auto scores = [&](const char *kl, const float *ksc, Scores &S) __attribute__((always_inline)) {
+    // int8 fast mode: plus log2 of the token's V scale mantissa over c, so
+    // that its weight comes out times that mantissa.
+    auto scores = [&](const char *kl, const float *ksc, Scores &S, auto safe) __attribute__((always_inline)) {
         bf16x8_t kop[2][kSteps];
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
@@ -721,20 +817,30 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
                 const f32x4_t ks = *(const f32x4_t *)(ksc + 16 * bb + 4 * hgrp);
+                if constexpr (!decltype(safe)::value) {
+                    // lds_sc[1] of the same slot
+                    const f32x4_t lm = *(const f32x4_t *)(ksc + kRing * kTileTokens + 16 * bb + 4 * hgrp);
 #pragma unroll
-                for (int cb = 0; cb < kNc; ++cb) S[bb][cb] *= ks;
+                    for (int cb = 0; cb < kNc; ++cb) S[bb][cb] = S[bb][cb] * ks + lm;
+                } else {
+#pragma unroll
+                    for (int cb = 0; cb < kNc; ++cb) S[bb][cb] *= ks;
+                }
             }
         }
     };
 
     f32x4_t acc[kDpl][kNc];               // set by each pass (run)
     float m_run[kNc], l_run[kNc];
+    // int8 fast mode: the row-sum product's accumulators (lanes 0..15: row
+    // sum = [0] + 2^-10 [1] of their row), rescaled with acc
+    f32x4_t acc_rs[kNc];
 
     // ---- online softmax of tile t's scores S into the weights (bf16 high
     // part and remainder, both rounded to nearest even: hi + lo is the fp32
-    // weight to 2^-17; FP8: fp16 times 2^kPBias; int8: fp32, split with the V
-    // scales in the weighted sum), masked on the tiles that cross a row's
-    // position.  The running max moves only when a row's tile max exceeds it
+    // weight to 2^-17; FP8 and int8 fast mode: fp16 times 2^kPBias; int8 safe
+    // mode: fp32, split with the V scales in the weighted sum), masked on the
+    // tiles that cross a row's position.  The running max moves only when a row's tile max exceeds it
     // by more than 8 (log2 units): weights stay <= 2^(8 + kPBias) <= 2^15 and
     // the accumulators are rarely rescaled.  Returns whether any row of the wave moved; alpha[cb] is then
     // log2 of that row's rescale factor (0 where it did not move).
@@ -755,8 +861,9 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         lo8 = __builtin_bit_cast(bf16x8_t, pl);
     };
     auto softmax = [&](const int t, const Scores &S, Weights &Phi, Weights &Plo, float (&alpha)[kNc],
-                       auto masked) __attribute__((always_inline)) {
+                       auto masked, auto safe) __attribute__((always_inline)) {
         constexpr bool kMasked = decltype(masked)::value;
+        constexpr bool kI8Fast = KV == kInt8 && !decltype(safe)::value;
         const int t0 = tok0 + t * kTileTokens;
         bool vis[kNc][8];
         float mx[kNc];
@@ -784,7 +891,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                 // whose max stays -inf
                 // (unsplit: every row sees token 0 in its first tile)
                 alpha[cb] = !kSplit ? m_run[cb] - m_new : m_new > m_run[cb] ? m_run[cb] - m_new : 0.f;
-                l_run[cb] *= __builtin_amdgcn_exp2f(alpha[cb]);
+                if constexpr (!kI8Fast) l_run[cb] *= __builtin_amdgcn_exp2f(alpha[cb]);
                 m_run[cb] = m_new;
             }
         }
@@ -796,9 +903,18 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
             for (int e = 0; e < 8; ++e) {
                 const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 2][cb][e & 3], c, nm));
                 pr[e] = vis[cb][e] ? w : 0.f;
-                if constexpr (!kF16) psum += pr[e];
+                if constexpr (!kF16 && !kI8Fast) psum += pr[e];
             }
-            if constexpr (kF16) {
+            if constexpr (kI8Fast) {
+                // fp16 weights (their scores carry the V scale mantissas); the
+                // row sums come from the weighted sums' extra product
+                u32x4_t pw;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    pw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{pr[2 * e], pr[2 * e + 1]}, f16x2_t));
+                Phi[cb] = __builtin_bit_cast(bf16x8_t, pw);
+                Plo[cb] = bf16x8_t{};
+            } else if constexpr (kF16) {
                 // the row sum adds the weights as rounded to fp16, the values
                 // the weighted sum multiplies: their rounding then cancels in
                 // the quotient where one weight dominates
@@ -814,8 +930,10 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                                                              __builtin_bit_cast(uint32_t, hv[2]), __builtin_bit_cast(uint32_t, hv[3])});
                 Plo[cb] = bf16x8_t{};
             }
-            l_run[cb] += psum;
-            if constexpr (KV == kInt8) {
+            if constexpr (!kI8Fast) l_run[cb] += psum;
+            if constexpr (kI8Fast) {
+                // weights packed above
+            } else if constexpr (KV == kInt8) {
                 // fp32 weights, split once the V scales are in LDS (next step)
                 Phi[cb] = __builtin_bit_cast(bf16x8_t, f32x4_t{pr[0], pr[1], pr[2], pr[3]});
                 Plo[cb] = __builtin_bit_cast(bf16x8_t, f32x4_t{pr[4], pr[5], pr[6], pr[7]});
@@ -827,7 +945,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         }
         return grow;
     };
-    auto rescale = [&](const float (&alpha)[kNc]) __attribute__((always_inline)) {
+    auto rescale = [&](const float (&alpha)[kNc], auto safe) __attribute__((always_inline)) {
         float f[kNc];
 #pragma unroll
         for (int cb = 0; cb < kNc; ++cb) f[cb] = __builtin_amdgcn_exp2f(alpha[cb]);
@@ -835,6 +953,9 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         for (int j = 0; j < kDpl; ++j)
 #pragma unroll
             for (int cb = 0; cb < kNc; ++cb) acc[j][cb] *= f[cb];
+        if constexpr (KV == kInt8 && !decltype(safe)::value)
+#pragma unroll
+            for (int cb = 0; cb < kNc; ++cb) acc_rs[cb] *= f[cb];
     };
 
     // ---- O^T += V^T P^T for one tile.  The A operand of output block j
@@ -880,10 +1001,16 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
             }
         }
     };
-    auto weighted_values = [&](const char *vl, const float *vsc, const Weights &Pin_hi, const Weights &Pin_lo)
-                               __attribute__((always_inline)) {
+    // int8: fast mode, the weights arrive as fp16 (see softmax), and one more
+    // product with the reciprocals of the V scale mantissas (lds_rs) gives
+    // the row sums of the values the codes times 2^e are taken with; safe
+    // mode, the weights times the whole V scales as a bf16 pair (exact to
+    // 2^-17), bf16 codes.
+    auto weighted_values = [&](const char *vl, const float *vsc, const _Float16 *rs, const Weights &Pin_hi,
+                               const Weights &Pin_lo, auto safe) __attribute__((always_inline)) {
+        constexpr bool kOneF16 = kF16 || (KV == kInt8 && !decltype(safe)::value);
         Weights Phi, Plo;
-        if constexpr (KV == kInt8) {
+        if constexpr (KV == kInt8 && !kOneF16) {
             // the weights times their tokens' V scales (token order e -> 16 (e/4) + 4 (l/16) + e%4)
             const f32x4_t vs0 = *(const f32x4_t *)(vsc + 4 * hgrp);
             const f32x4_t vs1 = *(const f32x4_t *)(vsc + 16 + 4 * hgrp);
@@ -912,11 +1039,21 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
             const bf16x8_t vop = __builtin_bit_cast(
                 bf16x8_t, u32x4_t{__builtin_bit_cast(u32x2_t, x0).x, __builtin_bit_cast(u32x2_t, x0).y,
                                   __builtin_bit_cast(u32x2_t, x1).x, __builtin_bit_cast(u32x2_t, x1).y});
-            if constexpr (kF16) {
+            if constexpr (kOneF16) {
 #pragma unroll
                 for (int cb = 0; cb < kNc; ++cb)
                     acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                         __builtin_bit_cast(f16x8_t, vop), __builtin_bit_cast(f16x8_t, Phi[cb]), acc[j][cb], 0, 0, 0);
+                if constexpr (KV == kInt8) {
+                    if (j == kDpl - 1) {
+                        // row l16 of the A operand, k-elements of lane group hgrp
+                        const f16x8_t rop = *(const f16x8_t *)(rs + (l16 * 4 + hgrp) * 8);
+#pragma unroll
+                        for (int cb = 0; cb < kNc; ++cb)
+                            acc_rs[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                rop, __builtin_bit_cast(f16x8_t, Phi[cb]), acc_rs[cb], 0, 0, 0);
+                    }
+                }
             } else {
 #pragma unroll
                 for (int cb = 0; cb < kNc; ++cb)
@@ -933,7 +1070,8 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         if constexpr (kVt)
             weighted_values_vt(lds_v[t % kRing], Ph, safe);
         else
-            weighted_values(lds_v[t % kRing], lds_sc[kVsc][t % kRing], Ph, Pl);
+            weighted_values(lds_v[t % kRing], lds_vs[KV == kInt8 ? t % kVsRing : 0], &lds_rs[KV == kInt8 ? t % kRing : 0][0][0][0],
+                            Ph, Pl, safe);
     };
 
     // ---- one pass over the workgroup's tiles, from a clean state.  `safe`
@@ -948,6 +1086,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     for (int cb = 0; cb < kNc; ++cb) {
         m_run[cb] = -INFINITY;
         l_run[cb] = 0.f;
+        acc_rs[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     wbase = tok0 >> bs_log2;
     win = load_window(wbase);
@@ -977,19 +1116,19 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
 #pragma unroll
             for (int jj = 0; jj < kQLoads; ++jj) {
                 if (!qload_ok(jj) || qload_is_v(jj)) continue;
-                qissue_tile(t, jj);
-                qstore(jj, t % kRing);
+                qissue_tile(t, jj, safe);
+                qstore(jj, t % kRing, t, 0, safe);
             }
         }
         // in flight into iteration 0: K(2) and V(0)
 #pragma unroll
         for (int jj = 0; jj < kQLoads; ++jj)
-            if (qload_ok(jj)) qissue_tile(qload_is_v(jj) ? 0 : 2, jj);
+            if (qload_ok(jj)) qissue_tile(qload_is_v(jj) ? 0 : 2, jj, safe);
     }
     __syncthreads();
     Scores S;                  // scores of the tile whose softmax is next
     Weights Phi, Plo;          // weights of the tile whose weighted sum is next
-    if (wave_live) scores(lds_k[0], lds_sc[0][0], S);
+    if (wave_live) scores(lds_k[0], lds_sc[0][0], S, safe);
     __syncthreads();           // K(0) read by every wave before iteration 0 loads over it
 
     // ---- iteration i (K(i+1) and V(i-1) in LDS; the tiles of the next
@@ -1014,11 +1153,11 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         const bool do_qk = kFull || i + 1 < my_steps;
         // the rescale the last softmax asked for: after the weighted sum of
         // tile i-2 (last iteration), before that of tile i-1
-        if (pend_grow) rescale(pend_alpha);
+        if (pend_grow) rescale(pend_alpha, safe);
         pend_grow = false;
-        if (do_sm) pend_grow = softmax(i, Sc, Pn_hi, Pn_lo, pend_alpha, masked);
+        if (do_sm) pend_grow = softmax(i, Sc, Pn_hi, Pn_lo, pend_alpha, masked, safe);
         if (do_pv) pv(i - 1, Ph, Pl, safe);
-        if (do_qk) scores(lds_k[(i + 1) % kRing], lds_sc[0][(i + 1) % kRing], Sn);
+        if (do_qk) scores(lds_k[(i + 1) % kRing], lds_sc[0][(i + 1) % kRing], Sn, safe);
         // The weights are only read by the next step's weighted sum; left
         // alone, the compiler sinks their computation into that step, so one
         // block of a pair holds two softmaxes and the other bare matrix
@@ -1028,7 +1167,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
 #pragma unroll
             for (int cb = 0; cb < kNc; ++cb) {
                 __asm__ volatile("" ::"v"(__builtin_bit_cast(u32x4_t, Pn_hi[cb])));
-                if constexpr (!kF16) __asm__ volatile("" ::"v"(__builtin_bit_cast(u32x4_t, Pn_lo[cb])));
+                if constexpr (!kF16 && decltype(safe)::value) __asm__ volatile("" ::"v"(__builtin_bit_cast(u32x4_t, Pn_lo[cb])));
             }
         }
     };
@@ -1059,9 +1198,9 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // last one); at the end of a segment (`sync`: i is the segment's last
     // iteration or the workgroup's last) this wave's loads have landed, then
     // the barrier.  int8 / FP8 (segments of one): K(i+2) and V(i), loaded
-    // during the last iteration, are written to LDS as bf16 -- into the slots
-    // no wave reads this iteration -- and K(i+3), V(i+1) issued into the same
-    // registers, then the barrier.
+    // during the last iteration, are written to LDS (as above) -- into the
+    // slots no wave reads this iteration -- and K(i+3), V(i+1) issued into the
+    // same registers, then the barrier.
     auto tile_done = [&](const int i, auto more, const bool sync) __attribute__((always_inline)) {
         if constexpr (KV == kBf16) {
             if (v_stager && i + kGroup - 1 < n_tiles) {
@@ -1073,11 +1212,11 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         } else {
 #pragma unroll
             for (int jj = 0; jj < kQLoads; ++jj)
-                if (qload_ok(jj)) qstore(jj, i % kRing);
+                if (qload_ok(jj)) qstore(jj, i % kRing, i + 2, i, safe);
             if (decltype(more)::value || i + 1 < n_tiles) {
 #pragma unroll
                 for (int jj = 0; jj < kQLoads; ++jj)
-                    if (qload_ok(jj)) qissue_tile(i + (qload_is_v(jj) ? 1 : 3), jj);
+                    if (qload_ok(jj)) qissue_tile(i + (qload_is_v(jj) ? 1 : 3), jj, safe);
             }
         }
         __syncthreads();
@@ -1131,20 +1270,37 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     for (; i < n_tiles; ++i) general(i);
     // the last tile's weighted sum (V(n_tiles-1) landed in the last iteration)
     if (wave_live && my_steps == n_tiles) {
-        if (pend_grow) rescale(pend_alpha);
+        if (pend_grow) rescale(pend_alpha, safe);
         pv(n_tiles - 1, Phi2, Plo2, safe);
     }
     };
 
-    run(std::false_type{});
-    if constexpr (kVt) {
-        // every staging write of the pass came before its last barrier
-        int wide = 0;
+    // int8: the fast mode needs c within 2^-100 .. 2^100; else the safe mode runs alone
+    bool rs_product = false;      // int8: the row sums are in acc_rs
+    if constexpr (KV == kInt8) {
+        bool again = true;
+        if (i8_fast_ok) {
+            run(std::false_type{});
+            // every flag write of the pass came before its last barrier
+            int wide = 0;
 #pragma unroll
-        for (int w = kVWave0; w < kVWave0 + kVWaves; ++w) wide |= lds_wide[w];
-        if (__builtin_amdgcn_readfirstlane(wide) != 0) {
-            __syncthreads();   // the pass's last LDS reads are done before the rerun loads over them
-            run(std::true_type{});
+            for (int w = 0; w < kWaves; ++w) wide |= lds_wide[w];
+            again = __builtin_amdgcn_readfirstlane(wide) != 0;
+            if (again) __syncthreads();   // the pass's last LDS reads are done before the rerun loads over them
+        }
+        if (again) run(std::true_type{});
+        rs_product = !again;
+    } else {
+        run(std::false_type{});
+        if constexpr (kVt) {
+            // every staging write of the pass came before its last barrier
+            int wide = 0;
+#pragma unroll
+            for (int w = kVWave0; w < kVWave0 + kVWaves; ++w) wide |= lds_wide[w];
+            if (__builtin_amdgcn_readfirstlane(wide) != 0) {
+                __syncthreads();   // the pass's last LDS reads are done before the rerun loads over them
+                run(std::true_type{});
+            }
         }
     }
 
@@ -1161,6 +1317,8 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         float l = l_run[cb];
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
+        if constexpr (KV == kInt8)
+            if (rs_product) l = __shfl(__builtin_fmaf(acc_rs[cb][1], 0x1p-10f, acc_rs[cb][0]), l16);
         if (!colv[cb]) continue;
         const int r = row0 + 16 * cb + l16;
         if (kSplit && pieces > 1) {

@@ -5,9 +5,13 @@ C-ABI against the fp64 oracle, with the decode's bar: max |gpu - oracle| <=
 (exact for bf16 values below 2^16 and every E4M3 value) and the softmax
 weights as fp16 (2^-11 relative rounding, the row sums adding the same
 rounded weights); a bf16 V beyond fp16 sends the workgroup to a second pass
-with bf16 V and the weights split exactly into a bf16 pair.  int8: the
-weights times the V scales as a bf16 pair (exact to 2^-17).  Checked below
-up to 4096 tokens.  Bit-exact: padding poison, loose max_q_len.
+with bf16 V and the weights split exactly into a bf16 pair.  int8: the codes
+times the power of two of their V scale as fp16, the weights times the
+scale's mantissa as fp16, and the row sums adding each rounded weight over
+that mantissa; a V scale outside 2^-14 .. 2^9 (and not 0) sends the
+workgroup to a second pass with the weights times the whole scales as a bf16
+pair (exact to 2^-17).  Checked below up to 4096 tokens.  Bit-exact: padding
+poison, loose max_q_len.
 """
 import numpy as np
 import pytest
@@ -364,6 +368,63 @@ def test_prefill_bf16_values_past_fp16_range_in_some_dims(D):
     unit = np.where(np.abs(ref).max(axis=-1, keepdims=True) > 64.0, 65536.0, 1.0)
     assert (unit > 1).any() and (unit == 1).any()
     assert_parity(torch.from_numpy(got / unit), ref / unit, "V dims 40..47 x 2^16")
+
+
+def _set_v_scales(v, s, tokens, g, value, bs):
+    """int8 V scale of the given tokens of sequence s, kv head g."""
+    bt = v["block_tables"].cpu()
+    for t in tokens:
+        v["v_scales"][int(bt[s, t // bs]), t % bs, g] = value
+
+
+def _weighted_abs_units(v, q, q_off):
+    """Per output row, max over dims of sum_t p_t |V_t| (the oracle on |codes|
+    and |scales|), at least 1: the size of the values a row's weights take.
+    The fp16 weights' rounding moves each output by a fraction of it."""
+    ab = C.prefill_oracle(dict(v, v_cache=v["v_cache"].abs(), v_scales=v["v_scales"].abs()), q, q_off)
+    return np.maximum(np.abs(ab).max(axis=-1, keepdims=True), 1.0)
+
+
+@pytest.mark.parametrize("case,value", [("zero", 0.0), ("huge", 600.0), ("tiny", 1e-6),
+                                        ("negative", -0.03), ("large_fast", 1.5), ("small_fast", 1e-4)])
+def test_int8_prefill_v_scales_at_and_past_the_fast_range(case, value):
+    # The int8 prefill takes V scales s = m 2^e with s = 0 or 2^-14 <= s < 2^9
+    # in its fast mode (codes times 2^e as fp16, the weights times m); a
+    # workgroup that meets any other scale (huge, tiny, negative) runs again
+    # with the codes as bf16 and the weights times the whole scales as a
+    # bf16 pair.  Tokens 100..139 of sequence 1, kv head 0, take the scale.
+    # Compared in units of sum_t p_t |V_t| where that exceeds 1.
+    note(f"prefill int8 V scales {case} = {value}")
+    ctx, nq = (300, 700, 90), [50, 300, 90]
+    v, q, q_off = make_kind(ctx, nq, 8, 2, 128, 16, 536, "int8")
+    _set_v_scales(v, 1, range(100, 140), 0, value, 16)
+    got = run_kind(v, q, q_off).double().cpu().numpy()
+    ref = C.prefill_oracle(v, q, q_off)
+    unit = _weighted_abs_units(v, q, q_off)
+    if abs(value) >= 1.0:
+        assert (unit > 8).any()
+    assert_parity(torch.from_numpy(got / unit), ref / unit, f"int8 V scales {case}")
+
+
+def test_int8_prefill_every_scale_in_the_fast_range():
+    # V scales spread over the whole fast range, 2^-14 .. 2^9 (below), one
+    # exponent per 16-token block, so every weight takes a different mantissa
+    # and the fp16 V tiles hold codes times 2^-14 .. 2^8.  Compared in units
+    # of sum_t p_t |V_t| where that exceeds 1.
+    note("prefill int8 V scales 2^-14 .. 2^9")
+    ctx, nq = (700, 333), [300, 333]
+    bs = 16
+    v, q, q_off = make_kind(ctx, nq, 8, 2, 128, bs, 537, "int8")
+    gen = torch.Generator().manual_seed(537)
+    nb = v["v_scales"].shape[0]
+    e = torch.randint(-14, 9, (nb, 1, 1), generator=gen).float()
+    m = 1.0 + torch.rand((nb, bs, v["v_scales"].shape[2]), generator=gen) * 0.999
+    v["v_scales"].copy_((m * torch.exp2(e)).to(v["v_scales"].device))
+    got = run_kind(v, q, q_off).double().cpu().numpy()
+    ref = C.prefill_oracle(v, q, q_off)
+    unit = _weighted_abs_units(v, q, q_off)
+    assert (unit > 1000).any()
+    assert_parity(torch.from_numpy(got / unit), ref / unit, "int8 V scales 2^-14 .. 2^9")
 
 
 @pytest.mark.parametrize("kind", ["int8", "fp8"])

@@ -114,6 +114,25 @@ def test_split_prefill_any_scale(scale):
                   f"split scale {scale}")
 
 
+def test_split_prefill_int8_second_pass_in_some_runs():
+    # int8 V scales of 600 (past the fast range) on tokens 100..139 of
+    # sequence 1, kv head 0: only the runs holding those tiles take the
+    # second pass (bf16 codes, the weights times the whole scales); the merge
+    # combines them with fast runs.  Large outputs compared in units of the
+    # largest V.
+    note("split prefill int8 second pass in some runs")
+    ctx, nq = (300, 700, 90), [50, 300, 90]
+    v, q, q_off = make_kind(ctx, nq, 8, 2, 128, 16, 627, "int8")
+    bt = v["block_tables"].cpu()
+    for t in range(100, 140):
+        v["v_scales"][int(bt[1, t // 16]), t % 16, 0] = 600.0
+    got = run_split(v, q, q_off, 5).double().cpu().numpy()
+    ref = C.prefill_oracle(v, q, q_off)
+    unit = np.where(np.abs(ref).max(axis=-1, keepdims=True) > 8.0, 127.0 * 600.0, 1.0)
+    assert (unit > 1).any() and (unit == 1).any()
+    assert_parity(torch.from_numpy(got / unit), ref / unit, "split int8 V x 600")
+
+
 def test_split_prefill_bf16_second_pass_in_some_runs():
     # V x 2^16 on tokens 100..139 of sequence 1, kv head 0: only the runs
     # holding those tiles take the bf16 second pass; the merge combines them
