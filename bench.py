@@ -689,6 +689,10 @@ def bench_prefill(args) -> int:
         whole = B.prefill_views(v, v["q"], v["q_offsets"], v["max_q_len"])
         torch.cuda.synchronize()
         split_check = split_max_diff(split, whole)
+        # the batch's output, as the two calls left it, for the oracle's check
+        out.index_copy_(0, split["rows_c"], split["chunk_out"])
+        out.index_copy_(0, split["rows_d"], split["decode_out"])
+        torch.cuda.synchronize()
     copy_for_counters(args, dev, stream)
     record = {
         "metric": "chunked-prefill attention query tokens/s and achieved bf16 matrix-core "
