@@ -44,7 +44,7 @@
 // meets a V scale outside 2^-14 .. 2^9 (other than 0) runs again with bf16
 // codes and the weights times the whole scales as a bf16 pair (exact to
 // 2^-17).  Both read V token-major through LDS transpose reads, one barrier
-// per tile.
+// per two tiles (FP8) or per tile (int8).
 // Key split (paged_attn_prefill_split*): one chunk of one sequence is only
 // (kv heads x row tiles) workgroups, a quarter of the compute units for a
 // 512-token Llama-3-8B chunk, each walking ~46 tiles.  The split form cuts a
@@ -92,6 +92,9 @@ typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 #ifndef PF_BF16_GROUP
 #define PF_BF16_GROUP 4
 #endif
+#ifndef PF_FP8_GROUP
+#define PF_FP8_GROUP 2
+#endif
 
 #ifndef PF_WAVES
 #define PF_WAVES 16
@@ -115,9 +118,10 @@ constexpr int kWaitVmcnt0 = 0x0F70;        // s_waitcnt vmcnt(0) alone (gfx9 fie
 // the previous segment.  bf16 tiles (K straight to LDS, V^T through the
 // staging waves' registers, a tile's worth in flight) take segments of four
 // iterations, a quarter of the barriers; int8 / FP8 tiles come through all
-// waves' registers, one tile's worth, and take segments of one.
+// waves' registers, one tile's worth per iteration of a segment: FP8 takes
+// segments of two, int8 (its registers full) segments of one.
 template <int KV>
-constexpr int kGroupOf = KV == 0 ? PF_BF16_GROUP : 1;
+constexpr int kGroupOf = KV == 0 ? PF_BF16_GROUP : KV == 2 ? PF_FP8_GROUP : 1;
 
 // Element kinds of the cache read: bf16, int8 codes with an fp32 scale per
 // (slot, kv head), FP8 E4M3 codes.
@@ -592,18 +596,22 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
 
     // ---- int8 / FP8 tiles come through registers: each thread loads 8 codes
     // (8 B) of one token of a K or V tile, load number tid + jj * threads
-    // (K loads first), one iteration ahead, and at the end of the next
-    // iteration writes them into the same LDS layouts, as bf16 (FP8 V and
-    // int8 V in the fast mode: as fp16; int8 scales go to lds_sc and lds_vs),
-    // so the loads have a whole iteration to land.
+    // (K loads first), for each tile of the next segment (one register set a
+    // tile) at the end of a segment, and at the end of the next segment
+    // writes them into the same LDS layouts, as bf16 (FP8 V and int8 V in the
+    // fast mode: as fp16; int8 scales go to lds_sc and lds_vs), so the loads
+    // have a whole segment to land.
     // 8-B code loads per thread per iteration (K + V): 8 D per tile over the
     // workgroup; with more threads than loads (D = 64) the later waves load
     // nothing (qload_ok, wave-uniform).
     constexpr int kQLoads = 8 * D / kThreads > 0 ? 8 * D / kThreads : 1;
     constexpr int kCodeChunks = D / 8;                   // 8-code chunks per token
-    u32x2_t st_codes[kQLoads];
-    float st_scale[kQLoads];
-    float st_vscale[kQLoads];    // int8, K loads: the token's V scale
+    // one set of registers per tile of a segment (int8 / FP8; set g holds
+    // the loads of the segment's g-th K and V tiles)
+    constexpr int kSets = KV == kBf16 ? 1 : kGroup;
+    u32x2_t st_codes[kSets][kQLoads];
+    float st_scale[kSets][kQLoads];
+    float st_vscale[kSets][kQLoads];    // int8, K loads: the token's V scale
     // keys and values read: the workgroup's tiles, within the context
     const int kv_end = min(ctx, tok0 + n_tiles * kTileTokens);
     // K or V: wave-uniform (4 D loads per tile and kind, a multiple of 64)
@@ -641,14 +649,14 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)(((uint64_t)hi << 32) | lo), 0,
                                                  __builtin_amdgcn_readfirstlane(range), kRsrcFlags);
     };
-    auto qissue = [&](int tile, int jj, int phys, auto safe) __attribute__((always_inline)) {
+    auto qissue = [&](int tile, int jj, int set, int phys, auto safe) __attribute__((always_inline)) {
         const bool is_v = qload_is_v(jj);
         const int tb = tok0 + tile * kTileTokens + 16 * qload_half(jj);
         const int rows = min(16, max(0, kv_end - tb));   // none past the tiles or the context is read
         const int64_t slot0 = ((int64_t)phys << bs_log2) + (tb & bs_mask);
         const int r16 = qload_token(jj) & 15;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc((is_v ? vbase : kbase) + slot0 * rb32, rows * (int)rb32);
-        st_codes[jj] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+        st_codes[set][jj] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
             rs, (int)((uint32_t)r16 * rb32 + (uint32_t)(qload_chunk(jj) * 8)), 0, 0));
         // int8: the tile's K and V scales, loaded (every lane of a token, one
         // dword line a wave) by the K wave of each half that holds chunk 0,
@@ -658,14 +666,14 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                 const int64_t so = slot0 * Hkv + g;
                 const __amdgpu_buffer_rsrc_t ks = make_rsrc(p.k_scales + so, rows * Hkv * 4);
                 const __amdgpu_buffer_rsrc_t vs = make_rsrc(p.v_scales + so, rows * Hkv * 4);
-                st_scale[jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ks, r16 * Hkv * 4, 0, 0));
-                st_vscale[jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vs, r16 * Hkv * 4, 0, 0));
+                st_scale[set][jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ks, r16 * Hkv * 4, 0, 0));
+                st_vscale[set][jj] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vs, r16 * Hkv * 4, 0, 0));
             }
         }
     };
     // tile `tile` of load jj; past the tiles the codes read as 0
-    auto qissue_tile = [&](int tile, int jj, auto safe) __attribute__((always_inline)) {
-        qissue(tile, jj, phys_at(tok0 + tile * kTileTokens + 16 * qload_half(jj)), safe);
+    auto qissue_tile = [&](int tile, int jj, int set, auto safe) __attribute__((always_inline)) {
+        qissue(tile, jj, set, phys_at(tok0 + tile * kTileTokens + 16 * qload_half(jj)), safe);
     };
     // int8, fast mode: a V scale s = m 2^e (mantissa m in [1, 2)) multiplies
     // the codes by 2^e in the fp16 V tile; the weights take m through their
@@ -674,21 +682,24 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // neither 0 nor within 2^-14 <= s < 2^9 (negative, tiny, huge or not
     // finite) sets the wave's lds_wide flag, and the workgroup then runs
     // again in the safe mode: V as bf16 codes, the weights times the whole
-    // scales as a bf16 pair.  K tile ktile, V tile vtile (its scales are in
-    // lds_vs since the K tile two before).
+    // scales as a bf16 pair.  Register set `set` holds K tile ktile or V tile
+    // vtile (whose scales are in lds_vs since the K tile two before), each
+    // stored into its ring slot.
     auto mantissa = [](float sc) __attribute__((always_inline)) {
         return __uint_as_float((__float_as_uint(sc) & 0x007fffffu) | 0x3f800000u);
     };
-    auto qstore = [&](int jj, int slot, int ktile, int vtile, auto safe) __attribute__((always_inline)) {
+    auto qstore = [&](int jj, int set, int ktile, int vtile, auto safe) __attribute__((always_inline)) {
         constexpr bool kI8Fast = KV == kInt8 && !decltype(safe)::value;
         const int tok = qload_token(jj), ch = qload_chunk(jj);
+        const auto &codes = st_codes[set][jj];
         if (qload_is_v(jj)) {
+            const int slot = vtile % kRing;
             u32x4_t val;
             if constexpr (kI8Fast) {
                 const float sv = lds_vs[KV == kInt8 ? vtile % kVsRing : 0][tok];
                 const uint32_t sb = __float_as_uint(sv);
                 const _Float16 p2 = (_Float16)__uint_as_float(sb & 0x7f800000u);   // 2^e (or 0), exact
-                val = i8x8_to_f16x8_times(st_codes[jj], f16x2_t{p2, p2});
+                val = i8x8_to_f16x8_times(codes, f16x2_t{p2, p2});
                 if (ch == 0) {
                     // k-element 4 (tok / 16) + tok % 4 of lane group (tok % 16) / 4
                     const float r = __builtin_amdgcn_rcpf(mantissa(sv));
@@ -698,20 +709,22 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                     at[4 * 8] = (_Float16)((r - (float)rh) * 1024.f);     // row 1
                 }
             } else {
-                val = kF16 ? fp8x8_to_f16x8(st_codes[jj]) : codes_to_bf16x8<KV>(st_codes[jj]);
+                val = kF16 ? fp8x8_to_f16x8(codes) : codes_to_bf16x8<KV>(codes);
             }
             *(u32x4_t *)(lds_v[slot] + TL::v_offset(tok, ch)) = val;
         } else {
-            *(u32x4_t *)(lds_k[slot] + TL::k_offset(tok, ch)) = codes_to_bf16x8<KV>(st_codes[jj]);
+            const int slot = ktile % kRing;
+            *(u32x4_t *)(lds_k[slot] + TL::k_offset(tok, ch)) = codes_to_bf16x8<KV>(codes);
             if constexpr (KV == kInt8) {
                 if (ch == 0) {
-                    lds_sc[0][slot][tok] = st_scale[jj];
-                    lds_vs[KV == kInt8 ? ktile % kVsRing : 0][tok] = st_vscale[jj];
+                    const float vsc = st_vscale[set][jj];
+                    lds_sc[0][slot][tok] = st_scale[set][jj];
+                    lds_vs[KV == kInt8 ? ktile % kVsRing : 0][tok] = vsc;
                     if constexpr (kI8Fast) {
-                        const uint32_t sb = __float_as_uint(st_vscale[jj]);
+                        const uint32_t sb = __float_as_uint(vsc);
                         const bool fast = sb == 0u || (sb >= 0x38800000u && sb < 0x44000000u);
                         if (!fast) lds_wide[wave] = 1;
-                        lds_sc[KV == kInt8 ? 1 : 0][slot][tok] = __builtin_amdgcn_logf(mantissa(st_vscale[jj])) * inv_c;
+                        lds_sc[KV == kInt8 ? 1 : 0][slot][tok] = __builtin_amdgcn_logf(mantissa(vsc)) * inv_c;
                     }
                 }
             }
@@ -1112,18 +1125,28 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     } else {
-        for (int t = 0; t < min(2, n_tiles); ++t) {
+        for (int t = 0; t < min(kGroup + 1, n_tiles); ++t) {
 #pragma unroll
             for (int jj = 0; jj < kQLoads; ++jj) {
                 if (!qload_ok(jj) || qload_is_v(jj)) continue;
-                qissue_tile(t, jj, safe);
-                qstore(jj, t % kRing, t, 0, safe);
+                qissue_tile(t, jj, 0, safe);
+                qstore(jj, 0, t, 0, safe);
             }
         }
-        // in flight into iteration 0: K(2) and V(0)
+        for (int t = 0; t < min(kGroup - 1, n_tiles); ++t) {
 #pragma unroll
-        for (int jj = 0; jj < kQLoads; ++jj)
-            if (qload_ok(jj)) qissue_tile(qload_is_v(jj) ? 0 : 2, jj, safe);
+            for (int jj = 0; jj < kQLoads; ++jj) {
+                if (!qload_ok(jj) || !qload_is_v(jj)) continue;
+                qissue_tile(t, jj, 0, safe);
+                qstore(jj, 0, 0, t, safe);
+            }
+        }
+        // in flight into the first segment: K(kGroup+1+g) and V(kGroup-1+g)
+#pragma unroll
+        for (int g = 0; g < kSets; ++g)
+#pragma unroll
+            for (int jj = 0; jj < kQLoads; ++jj)
+                if (qload_ok(jj)) qissue_tile(qload_is_v(jj) ? kGroup - 1 + g : kGroup + 1 + g, jj, g, safe);
     }
     __syncthreads();
     Scores S;                  // scores of the tile whose softmax is next
@@ -1173,10 +1196,13 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     };
     auto loads = [&](const int i) __attribute__((always_inline)) {
         // The oldest block iteration i loads is V(i+kGroup-1)'s first (int8 /
-        // FP8: V(i+1)'s, one iteration ahead); once it leaves the window,
-        // slide (the newest, K(i+kGroup+1)'s last (K(i+3)'s), is at most 96
-        // tokens further, under 64 blocks, so a slide never skips a window).
-        if (((tok0 + (i + (KV == kBf16 ? kGroup - 1 : 1)) * kTileTokens) >> bs_log2) >= wbase + 64) {
+        // FP8: V(i+kGroup)'s, issued at the segment's end); once it leaves the
+        // window, slide.  The newest, K(i+kGroup+1)'s last (int8 / FP8:
+        // K(i+2 kGroup+1)'s), is under 64 blocks further (static_assert
+        // below), so a slide never skips a window.
+        static_assert((KV == kBf16 ? 2 : kGroup + 1) * kTileTokens + kTileTokens - 1 < 64 * 16,
+                      "a segment's loads span under 64 blocks of 16 tokens");
+        if (((tok0 + (i + (KV == kBf16 ? kGroup - 1 : kGroup)) * kTileTokens) >> bs_log2) >= wbase + 64) {
             wbase += 64;
             win = win_next;
             win_next = load_window(wbase + 64);
@@ -1197,10 +1223,12 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // segment: its last reader, the weighted sum of V(i+1-kRing), ran in the
     // last one); at the end of a segment (`sync`: i is the segment's last
     // iteration or the workgroup's last) this wave's loads have landed, then
-    // the barrier.  int8 / FP8 (segments of one): K(i+2) and V(i), loaded
-    // during the last iteration, are written to LDS (as above) -- into the
-    // slots no wave reads this iteration -- and K(i+3), V(i+1) issued into the
-    // same registers, then the barrier.
+    // the barrier.  int8 / FP8, at the end of a segment (base its first
+    // iteration): K(base+kGroup+1+g) and V(base+kGroup-1+g), loaded since the
+    // last segment's end, are written to LDS (as above) -- into slots no wave
+    // reads in this segment -- then K(base+2 kGroup+1+g), V(base+2 kGroup-1+g)
+    // issued into the same registers, then the barrier.  The last segment may
+    // be short: its stores are still those the last segment's end issued.
     auto tile_done = [&](const int i, auto more, const bool sync) __attribute__((always_inline)) {
         if constexpr (KV == kBf16) {
             if (v_stager && i + kGroup - 1 < n_tiles) {
@@ -1210,13 +1238,22 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
             if (!sync) return;
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         } else {
+            if (!sync) return;
+            // base: the segment's first iteration; the registers hold what the
+            // last segment's end issued
+            const int base = i - i % kGroup;
 #pragma unroll
-            for (int jj = 0; jj < kQLoads; ++jj)
-                if (qload_ok(jj)) qstore(jj, i % kRing, i + 2, i, safe);
-            if (decltype(more)::value || i + 1 < n_tiles) {
+            for (int g = 0; g < kSets; ++g)
 #pragma unroll
                 for (int jj = 0; jj < kQLoads; ++jj)
-                    if (qload_ok(jj)) qissue_tile(i + (qload_is_v(jj) ? 1 : 3), jj, safe);
+                    if (qload_ok(jj)) qstore(jj, g, base + kGroup + 1 + g, base + kGroup - 1 + g, safe);
+            if (decltype(more)::value || i + 1 < n_tiles) {
+#pragma unroll
+                for (int g = 0; g < kSets; ++g)
+#pragma unroll
+                    for (int jj = 0; jj < kQLoads; ++jj)
+                        if (qload_ok(jj))
+                            qissue_tile(qload_is_v(jj) ? base + 2 * kGroup - 1 + g : base + 2 * kGroup + 1 + g, jj, g, safe);
             }
         }
         __syncthreads();
