@@ -385,18 +385,19 @@ def _weighted_abs_units(v, q, q_off):
     return np.maximum(np.abs(ab).max(axis=-1, keepdims=True), 1.0)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("case,value", [("zero", 0.0), ("huge", 600.0), ("tiny", 1e-6),
                                         ("negative", -0.03), ("large_fast", 1.5), ("small_fast", 1e-4)])
-def test_int8_prefill_v_scales_at_and_past_the_fast_range(case, value):
+def test_int8_prefill_v_scales_at_and_past_the_fast_range(case, value, D):
     # The int8 prefill takes V scales s = m 2^e with s = 0 or 2^-14 <= s < 2^9
     # in its fast mode (codes times 2^e as fp16, the weights times m); a
     # workgroup that meets any other scale (huge, tiny, negative) runs again
     # with the codes as bf16 and the weights times the whole scales as a
     # bf16 pair.  Tokens 100..139 of sequence 1, kv head 0, take the scale.
     # Compared in units of sum_t p_t |V_t| where that exceeds 1.
-    note(f"prefill int8 V scales {case} = {value}")
+    note(f"prefill int8 V scales {case} = {value}, D={D}")
     ctx, nq = (300, 700, 90), [50, 300, 90]
-    v, q, q_off = make_kind(ctx, nq, 8, 2, 128, 16, 536, "int8")
+    v, q, q_off = make_kind(ctx, nq, 8, 2, D, 16, 536 + D, "int8")
     _set_v_scales(v, 1, range(100, 140), 0, value, 16)
     got = run_kind(v, q, q_off).double().cpu().numpy()
     ref = C.prefill_oracle(v, q, q_off)

@@ -114,15 +114,16 @@ def test_split_prefill_any_scale(scale):
                   f"split scale {scale}")
 
 
-def test_split_prefill_int8_second_pass_in_some_runs():
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_prefill_int8_second_pass_in_some_runs(D):
     # int8 V scales of 600 (past the fast range) on tokens 100..139 of
     # sequence 1, kv head 0: only the runs holding those tiles take the
     # second pass (bf16 codes, the weights times the whole scales); the merge
     # combines them with fast runs.  Large outputs compared in units of the
     # largest V.
-    note("split prefill int8 second pass in some runs")
+    note(f"split prefill int8 second pass in some runs, D={D}")
     ctx, nq = (300, 700, 90), [50, 300, 90]
-    v, q, q_off = make_kind(ctx, nq, 8, 2, 128, 16, 627, "int8")
+    v, q, q_off = make_kind(ctx, nq, 8, 2, D, 16, 627 + D, "int8")
     bt = v["block_tables"].cpu()
     for t in range(100, 140):
         v["v_scales"][int(bt[1, t // 16]), t % 16, 0] = 600.0
