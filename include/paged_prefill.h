@@ -80,7 +80,9 @@ int paged_attn_prefill(const void *q, const void *k_cache, const void *v_cache,
  * with 1/m as an fp16 pair), so the rounding cancels in the quotient as on
  * the bf16 path.  A workgroup that meets a V scale outside 2^-14 .. 2^9
  * (other than 0: negative, tiny, huge or not finite) computes its rows again
- * with the weights times the whole V scales as a bf16 pair (exact to 2^-17).
+ * with the weights times the whole V scales as a bf16 pair (exact to 2^-17);
+ * so does every workgroup when |scale| log2(e) lies outside 2^-100 .. 2^100
+ * (scale 0 included).
  */
 int paged_attn_prefill_int8(const void *q, const int8_t *k_cache, const int8_t *v_cache,
                             const float *k_scales, const float *v_scales,
