@@ -1020,7 +1020,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // mode, the weights times the whole V scales as a bf16 pair (exact to
     // 2^-17), bf16 codes.
     auto weighted_values = [&](const char *vl, const float *vsc, const _Float16 *rs, const Weights &Pin_hi,
-                               const Weights &Pin_lo, auto safe) __attribute__((always_inline)) {
+                               const Weights &Pin_lo, auto safe, auto full) __attribute__((always_inline)) {
         constexpr bool kOneF16 = kF16 || (KV == kInt8 && !decltype(safe)::value);
         Weights Phi, Plo;
         if constexpr (KV == kInt8 && !kOneF16) {
@@ -1041,10 +1041,18 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                 Plo[cb] = Pin_lo[cb];
             }
         }
+        // int8, outside the unmasked middle tiles: the lane's transpose-read
+        // offsets from an opaque lane id, so the middle tiles' copies are not
+        // kept past their loop
+        int ln = (int)threadIdx.x;
+        if constexpr (KV == kInt8 && !decltype(full)::value) __asm__ volatile("" : "+v"(ln));
+        const int xl16 = ln & 15, xh = (ln >> 4) & 3;
+        const int xtok = 4 * xh + (xl16 >> 2);
+        const int xlane = xtok * TL::kRowBytes + 8 * (xl16 & 1);
 #pragma unroll
         for (int j = 0; j < kDpl; ++j) {
-            const int chunk = 2 * j + ((l16 >> 1) & 1);
-            const char *a0 = vl + tr_lane + ((chunk ^ TL::v_swz(tr_tok)) * 16);
+            const int chunk = 2 * j + ((xl16 >> 1) & 1);
+            const char *a0 = vl + xlane + ((chunk ^ TL::v_swz(xtok)) * 16);
             const i16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) i16x4_t *)(a0));
             const i16x4_t x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -1060,7 +1068,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
                 if constexpr (KV == kInt8) {
                     if (j == kDpl - 1) {
                         // row l16 of the A operand, k-elements of lane group hgrp
-                        const f16x8_t rop = *(const f16x8_t *)(rs + (l16 * 4 + hgrp) * 8);
+                        const f16x8_t rop = *(const f16x8_t *)(rs + (xl16 * 4 + xh) * 8);
 #pragma unroll
                         for (int cb = 0; cb < kNc; ++cb)
                             acc_rs[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -1079,12 +1087,12 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     };
 
     // The weighted sum of tile t (its V landed at least one barrier ago).
-    auto pv = [&](const int t, const Weights &Ph, const Weights &Pl, auto safe) __attribute__((always_inline)) {
+    auto pv = [&](const int t, const Weights &Ph, const Weights &Pl, auto safe, auto full) __attribute__((always_inline)) {
         if constexpr (kVt)
             weighted_values_vt(lds_v[t % kRing], Ph, safe);
         else
             weighted_values(lds_v[t % kRing], lds_vs[KV == kInt8 ? t % kVsRing : 0], &lds_rs[KV == kInt8 ? t % kRing : 0][0][0][0],
-                            Ph, Pl, safe);
+                            Ph, Pl, safe, full);
     };
 
     // ---- one pass over the workgroup's tiles, from a clean state.  `safe`
@@ -1179,7 +1187,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
         if (pend_grow) rescale(pend_alpha, safe);
         pend_grow = false;
         if (do_sm) pend_grow = softmax(i, Sc, Pn_hi, Pn_lo, pend_alpha, masked, safe);
-        if (do_pv) pv(i - 1, Ph, Pl, safe);
+        if (do_pv) pv(i - 1, Ph, Pl, safe, full);
         if (do_qk) scores(lds_k[(i + 1) % kRing], lds_sc[0][(i + 1) % kRing], Sn, safe);
         // The weights are only read by the next step's weighted sum; left
         // alone, the compiler sinks their computation into that step, so one
@@ -1308,7 +1316,7 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     // the last tile's weighted sum (V(n_tiles-1) landed in the last iteration)
     if (wave_live && my_steps == n_tiles) {
         if (pend_grow) rescale(pend_alpha, safe);
-        pv(n_tiles - 1, Phi2, Plo2, safe);
+        pv(n_tiles - 1, Phi2, Plo2, safe, std::false_type{});
     }
     };
 
