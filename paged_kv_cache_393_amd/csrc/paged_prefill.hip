@@ -490,13 +490,17 @@ __global__ __launch_bounds__(kThreads, PF_WAVES_PER_EU) void pa_prefill_kernel(c
     }
     pmax = __builtin_amdgcn_readfirstlane(pmax);      // wave-uniform after the reduction
     pmin = __builtin_amdgcn_readfirstlane(pmin);
-    // The workgroup's last position.  bf16: its last row's (positions grow
-    // with the row), with no barrier, so the block-table window loads right
-    // after the q loads.  int8 / FP8: the waves' maxima through LDS (the
-    // barrier keeps their prologue within 128 registers).
+    // The workgroup's last position.  bf16 and int8: its last row's
+    // (positions grow with the row), with no barrier, so the block-table
+    // window loads right after the q loads.  FP8: the waves' maxima through
+    // LDS (without the barrier its kernel spills).
     int wg_pmax;
-    if constexpr (kVt) {
+    if constexpr (kVt || KV == kInt8) {
         if (lane == 0) lds_wide[wave] = 0;
+        if constexpr (KV == kInt8) {
+            constexpr int kRsChunks = (int)sizeof(lds_rs) / 16;
+            if ((int)threadIdx.x < kRsChunks) ((u32x4_t *)&lds_rs[0][0][0][0])[threadIdx.x] = u32x4_t{0u, 0u, 0u, 0u};
+        }
         wg_pmax = ctx - nq + (min(R, (bx + 1) * kRowsPerGroup) - 1) / G;
     } else {
         if (lane == 0) {
