@@ -370,6 +370,18 @@ def test_prefill_bf16_values_past_fp16_range_in_some_dims(D):
     assert_parity(torch.from_numpy(got / unit), ref / unit, "V dims 40..47 x 2^16")
 
 
+@pytest.mark.parametrize("kind", ["bf16", "int8", "fp8"])
+def test_prefill_workgroups_of_one_to_seven_tiles(kind):
+    # Sequences whose workgroups walk 1 .. 7 tiles of 32 tokens: even and odd
+    # counts, so the cache kinds staged in segments of several tiles (bf16
+    # four, FP8 two) end on a short segment as well as on a whole one.
+    note(f"prefill {kind} workgroups of 1..7 tiles")
+    ctx = (32, 64, 96, 128, 160, 192, 224, 33, 65, 97)
+    nq = [32, 32, 32, 32, 32, 32, 32, 1, 33, 5]
+    v, q, q_off = make_kind(ctx, nq, 8, 2, 128, 16, 538, kind)
+    assert_parity(run_kind(v, q, q_off), C.prefill_oracle(v, q, q_off), f"{kind} 1..7 tiles")
+
+
 def _set_v_scales(v, s, tokens, g, value, bs):
     """int8 V scale of the given tokens of sequence s, kv head g."""
     bt = v["block_tables"].cpu()
